@@ -1,0 +1,11 @@
+"""The CPU oracle against its pins (no GPU needed)."""
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    ok, detail = pin(oracle.cca_oracle)
+    assert ok, detail

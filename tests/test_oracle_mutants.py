@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+This is what makes the pins worth trusting: a dropped term, a wrong index or
+a transposed operand anywhere in the oracle must turn at least one pin red.
+"""
+import numpy as np
+import pytest
+
+import oracle.cca_oracle as o
+from tests import oracle_pins
+
+
+def _first_query_row(j, g):
+    return j * g  # the group's FIRST token instead of its last
+
+
+def _window_without_self(t, g, k):
+    return max(0, t // g - k) * g, t - 1  # query does not see itself
+
+
+def _window_one_group_early(t, g, k):
+    return max(0, t // g - k - 1) * g, t  # window overlaps the last visible core token
+
+
+def _all_complete_groups_visible(t, g, k):
+    return (t + 1) // g  # core tokens of every complete group, overlapping the window
+
+
+def _pool_weights_unscaled(Q, K, g, scale):
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    m = K.shape[0] // g
+    return np.stack([o.softmax(K[j * g:(j + 1) * g] @ Q[j * g + g - 1]) for j in range(m)]).reshape(m, g)
+
+
+def _pool_keys_from_values(Q, K, V, g, scale):
+    A = o.pool_weights(Q, K, g, scale)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    m = A.shape[0]
+    Kc = np.stack([A[j] @ V[j * g:(j + 1) * g] for j in range(m)]).reshape(m, -1)
+    Vc = np.stack([A[j] @ V[j * g:(j + 1) * g] for j in range(m)]).reshape(m, -1)
+    return Kc, Vc, A
+
+
+def _softmax_unnormalised(x):
+    x = np.asarray(x, np.float64)
+    return np.exp(x - x.max(axis=-1, keepdims=True))
+
+
+def _pairs_dropped_self(L, g, k):
+    t = np.arange(L, dtype=np.int64)
+    n_c = np.maximum(0, t // g - k)
+    return int(n_c.sum()), int((t - n_c * g).sum())
+
+
+def _cache_tokens_small_ring(n, g, k):
+    return {"stored_core": n // g, "ring_slots": k * g, "visible_core": max(0, n // g - k),
+            "visible_raw": n - max(0, n // g - k) * g, "full": n}
+
+
+MUTANTS = {
+    "pool scored by first query": ("group_query_row", _first_query_row),
+    "window excludes the query itself": ("raw_window", _window_without_self),
+    "window overlaps a core token": ("raw_window", _window_one_group_early),
+    "core of all complete groups visible": ("visible_core_count", _all_complete_groups_visible),
+    "pool softmax without temperature": ("pool_weights", _pool_weights_unscaled),
+    "core keys pooled from values": ("pool", _pool_keys_from_values),
+    "softmax denominator dropped": ("softmax", _softmax_unnormalised),
+    "pair count drops the diagonal": ("attention_pairs", _pairs_dropped_self),
+    "ring one group short": ("kv_cache_tokens", _cache_tokens_small_ring),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(o, attr, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            ok, _ = pin(o)
+        except Exception:  # a crash also counts as the pin noticing
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant '{name}'"
