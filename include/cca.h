@@ -1,0 +1,184 @@
+/*
+ * cca.h -- C ABI of libcca.so: Core Context Aware (CCA) attention on MI355X (gfx950).
+ *
+ * Method source: the page "ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展"
+ * (a write-up of "Core Context Aware Transformers for Long Context Language
+ * Modeling"), referred to below as [CCA].  Its equations did not survive text
+ * extraction, so they are named by what they define.
+ *
+ * Problem statement, per (batch b, head h) slice, following [CCA]:
+ *   Q, K, V : [L, d] per-head queries, keys, values (already projected; any
+ *             positional encoding has been applied by the caller).
+ *   g       : group size; groups are positions [j*g, (j+1)*g), j < m = floor(L/g).
+ *   k_local : number of previous groups kept raw (local window w = k_local*g).
+ *   scale   : softmax temperature of both the pooling and the attention
+ *             (callers normally pass 1/sqrt(d)).
+ *   Pooling ([CCA] global-aware pooling, core-token and core K/V equations):
+ *     a_j = softmax_i(scale * Q[j*g+g-1] . K[j*g+i]),
+ *     Kc[j] = sum_i a_j,i K[j*g+i],  Vc[j] = sum_i a_j,i V[j*g+i].
+ *   Attention ([CCA] locality-preserving module and global-local fusion,
+ *   local-window, unified K/V and per-position output equations):
+ *     query t, beta = floor(t/g), n_c = max(0, beta - k_local);
+ *     keys = Kc[0:n_c] followed by K[n_c*g .. t]; one softmax over all of them;
+ *     O[t] = sum of softmax weights times the matching Vc / V rows.
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are plain HIP device addresses; the library never
+ *     allocates, frees, or keeps them.  The caller owns every buffer.
+ *   - Tensors are dense row-major in the stated shapes, element type given by
+ *     a cca_dtype_t, base addresses aligned to 16 bytes.
+ *   - All device work is enqueued on `stream` (0 = legacy default stream);
+ *     no entry point synchronises the host with the device.
+ *   - Arguments are validated on the host before anything is enqueued.  On any
+ *     non-zero return nothing has been enqueued and no output or descriptor
+ *     field has been modified, except CCA_ERR_HIP, which reports a failed
+ *     kernel launch (see hipGetLastError); then outputs are undefined.
+ *   - Calls on one stream are ordered; concurrent calls on different streams
+ *     that write the same buffers race (the library has no locks).
+ */
+#ifndef CCA_H
+#define CCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCA_OK = 0,
+  CCA_ERR_INVALID = -1,     /* null pointer, misaligned pointer, bad size or count */
+  CCA_ERR_UNSUPPORTED = -2, /* head dim not 64/128, dtype combination not built */
+  CCA_ERR_WORKSPACE = -3,   /* decode workspace smaller than cca_decode_workspace_bytes() */
+  CCA_ERR_HIP = -4,         /* a kernel launch failed */
+  CCA_ERR_CAPACITY = -5     /* the cache has no room for another token */
+} cca_status_t;
+
+typedef enum {
+  CCA_F32 = 0,  /* IEEE float32 */
+  CCA_BF16 = 1  /* bfloat16 (upper half of a float32; conversions round to nearest even) */
+} cca_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* cca_status_string(int status);
+
+/*
+ * Pooling into core tokens ([CCA] global-aware pooling, core-token and core
+ * K/V equations).
+ *   q, k, v : device, [B, H, L, d] of dtype dt (only rows j*g+g-1 of q are read).
+ *   kc, vc  : device, [B, H, floor(L/g), d] of dtype dt, written.  Math is
+ *             float32; results are rounded once to dt.  A trailing partial
+ *             group (L mod g tokens) produces no core token.
+ *   d in {64, 128}; g >= 1; L >= 0 (L < g writes nothing).
+ */
+int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
+                int B, int H, int64_t L, int d, int g, float scale,
+                int dt, hipStream_t stream);
+
+/*
+ * Prefill: pooling followed by the fused core+local causal attention
+ * ([CCA] all three modules; one softmax per query over the unified K/V).
+ *   q, k, v : device, [B, H, L, d] of dtype dt.
+ *   kc, vc  : device, [B, H, floor(L/g), d] of dtype dt: written by the pooling
+ *             step and then read by the attention step (the caller may keep
+ *             them, e.g. to seed a decode cache with cca_cache_load_prefill).
+ *   out     : device, [B, H, L, d] of dtype out_dt, written.  out_dt is CCA_F32
+ *             or equal to dt.  Accumulation is float32; for dt = CCA_BF16 the
+ *             QK^T and PV products run on bf16 matrix cores with the softmax
+ *             weights rounded to bf16, for dt = CCA_F32 on float32 matrix cores.
+ *   k_local >= 0 (any value >= floor((L-1)/g) gives plain causal attention).
+ */
+int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc, void* out,
+                int B, int H, int64_t L, int d, int g, int k_local, float scale,
+                int dt, int out_dt, hipStream_t stream);
+
+/*
+ * Compressed KV cache for decode ([CCA] Triton section: the fused operator
+ * serves decode with a KV cache holding core tokens plus local raw tokens;
+ * compute/memory efficiency section, Fig. 3).  Plain-old-data descriptor;
+ * every device buffer is caller-owned.
+ *   core_k, core_v : device, [B, H, max_groups, d]: core token j of every
+ *                    completed group j (pooled as soon as the group completes).
+ *   ring_k, ring_v : device, [B, H, (k_local+1)*g, d]: raw token u lives in
+ *                    slot u mod ((k_local+1)*g); the ring always holds the raw
+ *                    window of the newest token.
+ *   n_tokens       : tokens appended so far (same for every sequence).
+ *   n_pooled       : core tokens written = floor(n_tokens/g).
+ * The library updates n_tokens/n_pooled on the host only after it has
+ * successfully enqueued the matching device work.
+ */
+typedef struct {
+  void* core_k;
+  void* core_v;
+  void* ring_k;
+  void* ring_v;
+  int B, H, d, g, k_local;
+  int dt;              /* cca_dtype_t of every cache buffer */
+  int64_t max_groups;  /* capacity of core_k/core_v in core tokens */
+  int64_t n_tokens;
+  int64_t n_pooled;
+} cca_cache_t;
+
+/* Ring slots of a cache: (k_local+1)*g. */
+int64_t cca_cache_ring_slots(const cca_cache_t* c);
+
+/*
+ * Seed an empty cache (n_tokens == 0) with the state after a prefill of L tokens.
+ *   k, v   : device, [B, H, L, d] of the cache dtype (the prefill's K and V).
+ *   kc, vc : device, [B, H, floor(L/g), d] (the prefill's pooled core tokens).
+ * Copies every core token into core_k/core_v and the raw window of token L
+ * (positions max(0, floor(L/g)-k_local)*g .. L-1) into its ring slots, then
+ * sets n_tokens = L, n_pooled = floor(L/g).  Needs floor(L/g) <= max_groups.
+ */
+int cca_cache_load_prefill(cca_cache_t* c, const void* k, const void* v,
+                           const void* kc, const void* vc, int64_t L, hipStream_t stream);
+
+/*
+ * Append one token per sequence: q, k, v are device [B, H, d] of the cache dtype.
+ * Writes k, v into ring slot t mod R (t = n_tokens).  When the token completes
+ * a group (t+1 divisible by g) that group is pooled in place from the ring
+ * with this token's query (the group's last query, [CCA] core-token equation)
+ * into core_k/core_v[t/g].  Returns CCA_ERR_CAPACITY when the completed group
+ * would not fit in max_groups.
+ */
+int cca_cache_append(cca_cache_t* c, const void* q, const void* k, const void* v,
+                     float scale, hipStream_t stream);
+
+/* Bytes of device workspace cca_decode_step needs for this cache (depends only
+ * on B, H, d and the capacity max_groups + ring slots). */
+size_t cca_decode_workspace_bytes(const cca_cache_t* c);
+
+/*
+ * Attention of the newest token against the cache (row n_tokens-1 of the
+ * prefill output, [CCA] per-position output equation).
+ *   q         : device [B, H, d] of the cache dtype: the query of the token
+ *               appended last (call cca_cache_append first).
+ *   out       : device [B, H, d] of out_dt (CCA_F32 or the cache dtype).
+ *   workspace : device, >= cca_decode_workspace_bytes(c) bytes, 16-byte
+ *               aligned; scratch for per-chunk partial softmax states, no
+ *               contents needed on entry, clobbered on return.
+ * Reads the cache only.  Requires n_tokens >= 1.
+ */
+int cca_decode_step(const cca_cache_t* c, const void* q, void* out, int out_dt,
+                    void* workspace, size_t workspace_bytes, float scale,
+                    hipStream_t stream);
+
+/*
+ * KV-cache accounting ([CCA] compute/memory efficiency, Fig. 3: the cache
+ * holds core plus local tokens instead of every token).  Host-only integer
+ * arithmetic, no device work.  After n_tokens tokens with group size g and
+ * k_local raw groups:
+ *   *resident_bytes = B*H*2*d*elem * (floor(n_tokens/g) + (k_local+1)*g)
+ *   *full_bytes     = B*H*2*d*elem * n_tokens            (standard KV cache)
+ * elem = 2 for CCA_BF16, 4 for CCA_F32.  Either output pointer may be NULL.
+ */
+int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt,
+                       int64_t* resident_bytes, int64_t* full_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCA_H */

@@ -1,0 +1,248 @@
+"""ctypes binding of libcca.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module checks tensor shapes,
+dtypes and devices (the C ABI receives raw pointers and cannot), allocates
+outputs with torch when the caller does not pass them, and forwards the
+current torch stream.  If the library is missing it raises; there is no
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcca.so")
+
+CCA_F32, CCA_BF16 = 0, 1
+_DT = {torch.float32: CCA_F32, torch.bfloat16: CCA_BF16}
+_TORCH_DT = {CCA_F32: torch.float32, CCA_BF16: torch.bfloat16}
+
+_lib = None
+
+
+class CCAError(RuntimeError):
+    pass
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of cca_cache_t (include/cca.h)."""
+
+    _fields_ = [
+        ("core_k", ctypes.c_void_p),
+        ("core_v", ctypes.c_void_p),
+        ("ring_k", ctypes.c_void_p),
+        ("ring_v", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("d", ctypes.c_int),
+        ("g", ctypes.c_int),
+        ("k_local", ctypes.c_int),
+        ("dt", ctypes.c_int),
+        ("max_groups", ctypes.c_int64),
+        ("n_tokens", ctypes.c_int64),
+        ("n_pooled", ctypes.c_int64),
+    ]
+
+
+EXPORTS = {
+    # name: (restype, argtypes)
+    "cca_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "cca_pool_kv": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                          ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "cca_prefill": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                          ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                          ctypes.c_int, ctypes.c_void_p]),
+    "cca_cache_ring_slots": (ctypes.c_int64, [ctypes.POINTER(CacheDesc)]),
+    "cca_cache_load_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
+                               + [ctypes.c_int64, ctypes.c_void_p]),
+    "cca_cache_append": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 3
+                         + [ctypes.c_float, ctypes.c_void_p]),
+    "cca_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc)]),
+    "cca_decode_step": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
+    "cca_kv_cache_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64)]),
+}
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libcca.so (once).  Raises CCAError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise CCAError(f"{path} not found: build it with `python -m long_context_sparse_cca_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = _lib.cca_status_string(status).decode()
+        raise CCAError(f"{what}: {msg} (status {status})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, shape, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise CCAError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise CCAError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise CCAError(f"{name}: dtype {t.dtype} != {dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise CCAError(f"{name} must be a contiguous device tensor")
+
+
+def _dtype_code(dtype) -> int:
+    if dtype not in _DT:
+        raise CCAError(f"unsupported dtype {dtype}")
+    return _DT[dtype]
+
+
+def _core_buffer(B, H, m, d, like):
+    # a zero-length result still needs a real (non-null, aligned) base address
+    return torch.empty((B, H, max(m, 1), d), dtype=like.dtype, device=like.device)[:, :, :m]
+
+
+def pool_kv(q, k, v, g: int, scale: float | None = None, kc=None, vc=None):
+    """Core keys/values [B,H,L//g,d] of q,k,v [B,H,L,d]: cca_pool_kv."""
+    lib = load_library()
+    B, H, L, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, (B, H, L, d), q.dtype, name)
+    m = L // g if g >= 1 else 0
+    if kc is None:
+        kc = _core_buffer(B, H, m, d, q)
+    if vc is None:
+        vc = _core_buffer(B, H, m, d, q)
+    _need(kc, (B, H, m, d), q.dtype, "kc")
+    _need(vc, (B, H, m, d), q.dtype, "vc")
+    _check(lib.cca_pool_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), B, H, L, d, g, scale,
+                           _dtype_code(q.dtype), _stream()), "cca_pool_kv")
+    return kc, vc
+
+
+def prefill(q, k, v, g: int, k_local: int, scale: float | None = None, out_dtype=None, out=None,
+            kc=None, vc=None, return_core: bool = False):
+    """CCA prefill output [B,H,L,d] (pooling + fused attention): cca_prefill."""
+    lib = load_library()
+    B, H, L, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, (B, H, L, d), q.dtype, name)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    m = L // g if g >= 1 else 0
+    if kc is None:
+        kc = _core_buffer(B, H, m, d, q)
+    if vc is None:
+        vc = _core_buffer(B, H, m, d, q)
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    _need(kc, (B, H, m, d), q.dtype, "kc")
+    _need(vc, (B, H, m, d), q.dtype, "vc")
+    _need(out, (B, H, L, d), out_dtype, "out")
+    _check(lib.cca_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, L, d, g, k_local,
+                           scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()), "cca_prefill")
+    if return_core:
+        return out, kc, vc
+    return out
+
+
+class KVCache:
+    """Compressed CCA KV cache: core-token array + raw ring (tensors owned here)."""
+
+    def __init__(self, B: int, H: int, d: int, g: int, k_local: int, max_tokens: int, dtype=torch.bfloat16,
+                 device="cuda"):
+        lib = load_library()
+        self.max_groups = max(1, max_tokens // g)
+        self.R = (k_local + 1) * g
+        self.dtype = dtype
+        self.core_k = torch.zeros((B, H, self.max_groups, d), dtype=dtype, device=device)
+        self.core_v = torch.zeros_like(self.core_k)
+        self.ring_k = torch.zeros((B, H, self.R, d), dtype=dtype, device=device)
+        self.ring_v = torch.zeros_like(self.ring_k)
+        self.desc = CacheDesc(_ptr(self.core_k), _ptr(self.core_v), _ptr(self.ring_k), _ptr(self.ring_v),
+                              B, H, d, g, k_local, _dtype_code(dtype), self.max_groups, 0, 0)
+        ws_bytes = lib.cca_decode_workspace_bytes(ctypes.byref(self.desc))
+        self.workspace = torch.empty((ws_bytes + 15) // 16 * 4, dtype=torch.float32, device=device)
+        self.ws_bytes = ws_bytes
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.desc.n_tokens)
+
+    @property
+    def shape_bhd(self):
+        return (self.desc.B, self.desc.H, self.desc.d)
+
+    def load_prefill(self, k, v, kc, vc):
+        """Seed the empty cache with the state after a prefill of L = k.shape[2] tokens."""
+        B, H, d = self.shape_bhd
+        L = k.shape[2]
+        m = L // self.desc.g
+        _need(k, (B, H, L, d), self.dtype, "k")
+        _need(v, (B, H, L, d), self.dtype, "v")
+        _need(kc, (B, H, m, d), self.dtype, "kc")
+        _need(vc, (B, H, m, d), self.dtype, "vc")
+        _check(_lib.cca_cache_load_prefill(ctypes.byref(self.desc), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), L,
+                                           _stream()), "cca_cache_load_prefill")
+
+    def append(self, q, k, v, scale: float | None = None):
+        """Append one token per sequence (q, k, v: [B,H,d])."""
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, (B, H, d), self.dtype, name)
+        _check(_lib.cca_cache_append(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), scale, _stream()),
+               "cca_cache_append")
+
+    def decode(self, q, out_dtype=None, out=None, scale: float | None = None):
+        """Attention output [B,H,d] of the newest token (q: its query)."""
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        _need(q, (B, H, d), self.dtype, "q")
+        if out is None:
+            out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+        _need(out, (B, H, d), out_dtype, "out")
+        _check(_lib.cca_decode_step(ctypes.byref(self.desc), _ptr(q), _ptr(out), _dtype_code(out_dtype),
+                                    _ptr(self.workspace), self.ws_bytes, scale, _stream()), "cca_decode_step")
+        return out
+
+
+def cache_append(cache: KVCache, q, k, v, scale=None):
+    cache.append(q, k, v, scale)
+
+
+def decode_step(cache: KVCache, q, out_dtype=None, out=None, scale=None):
+    return cache.decode(q, out_dtype, out, scale)
+
+
+def kv_cache_bytes(n_tokens: int, g: int, k_local: int, B: int, H: int, d: int, dtype=torch.bfloat16):
+    """(resident compressed bytes, full KV bytes): cca_kv_cache_bytes (host arithmetic)."""
+    lib = load_library()
+    res = ctypes.c_int64()
+    full = ctypes.c_int64()
+    _check(lib.cca_kv_cache_bytes(n_tokens, g, k_local, B, H, d, _dtype_code(dtype), ctypes.byref(res),
+                                  ctypes.byref(full)), "cca_kv_cache_bytes")
+    return res.value, full.value

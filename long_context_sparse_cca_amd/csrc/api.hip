@@ -1,0 +1,144 @@
+// C ABI of libcca.so: host-side validation, then stream-ordered kernel launches.
+// Every declaration, with its argument contract, is in include/cca.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "cca_internal.h"
+
+namespace {
+
+constexpr int kMaxGroup = 4096;  // pooling keeps one float score per group row in LDS
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int H, int64_t L, int d, int g, int dt) {
+  if (dt != CCA_F32 && dt != CCA_BF16) return CCA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || L < 0 || g < 1 || g > kMaxGroup) return CCA_ERR_INVALID;
+  if ((int64_t)B * H > (int64_t)1 << 24) return CCA_ERR_INVALID;
+  return CCA_OK;
+}
+
+int check_cache(const cca_cache_t* c) {
+  if (c == nullptr) return CCA_ERR_INVALID;
+  int s = check_shape(c->B, c->H, 0, c->d, c->g, c->dt);
+  if (s != CCA_OK) return s;
+  if (!aligned16(c->core_k) || !aligned16(c->core_v) || !aligned16(c->ring_k) || !aligned16(c->ring_v))
+    return CCA_ERR_INVALID;
+  if (c->k_local < 0 || c->max_groups < 1 || c->n_tokens < 0) return CCA_ERR_INVALID;
+  if ((int64_t)(c->k_local + 1) * c->g > ((int64_t)1 << 30)) return CCA_ERR_INVALID;
+  if (c->n_pooled != c->n_tokens / c->g) return CCA_ERR_INVALID;
+  if (c->n_pooled > c->max_groups) return CCA_ERR_INVALID;
+  return CCA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CCA_OK : CCA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cca_status_string(int status) {
+  switch (status) {
+    case CCA_OK: return "ok";
+    case CCA_ERR_INVALID: return "invalid argument";
+    case CCA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case CCA_ERR_WORKSPACE: return "decode workspace too small";
+    case CCA_ERR_HIP: return "HIP kernel launch failed";
+    case CCA_ERR_CAPACITY: return "cache capacity exceeded";
+    default: return "unknown status";
+  }
+}
+
+int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc, int B, int H, int64_t L, int d,
+                int g, float scale, int dt, hipStream_t stream) {
+  int s = check_shape(B, H, L, d, g, dt);
+  if (s != CCA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc)) return CCA_ERR_INVALID;
+  if (!isfinite(scale)) return CCA_ERR_INVALID;
+  const int64_t BH = (int64_t)B * H;
+  if (BH * (L / g) >= INT32_MAX) return CCA_ERR_INVALID;
+  return hip_status(cca::launch_pool(dt, d, q, k, v, kc, vc, (int)BH, L, g, scale, stream));
+}
+
+int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int B, int H, int64_t L,
+                int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
+  int s = check_shape(B, H, L, d, g, dt);
+  if (s != CCA_OK) return s;
+  if (out_dt != CCA_F32 && out_dt != dt) return CCA_ERR_UNSUPPORTED;
+  if (k_local < 0 || !isfinite(scale)) return CCA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc) || !aligned16(out))
+    return CCA_ERR_INVALID;
+  const int64_t BH = (int64_t)B * H;
+  if (BH * (L / g) >= INT32_MAX || BH * ((L + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
+  if (L == 0) return CCA_OK;
+  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, (int)BH, L, g, scale, stream);
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  e = cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, (int)BH, L, g, k_local, scale,
+                                    stream);
+  return hip_status(e);
+}
+
+int64_t cca_cache_ring_slots(const cca_cache_t* c) {
+  if (c == nullptr) return 0;
+  return (int64_t)(c->k_local + 1) * c->g;
+}
+
+int cca_cache_load_prefill(cca_cache_t* c, const void* k, const void* v, const void* kc, const void* vc, int64_t L,
+                           hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (c->n_tokens != 0 || L < 1) return CCA_ERR_INVALID;
+  if (!aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
+  const int64_t m = L / c->g;
+  if (m > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
+  if (m > c->max_groups) return CCA_ERR_CAPACITY;
+  hipError_t e = cca::launch_cache_load(c, k, v, kc, vc, L, stream);
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  c->n_tokens = L;
+  c->n_pooled = m;
+  return CCA_OK;
+}
+
+int cca_cache_append(cca_cache_t* c, const void* q, const void* k, const void* v, float scale, hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !isfinite(scale)) return CCA_ERR_INVALID;
+  const int64_t t = c->n_tokens;
+  if ((t + 1) / c->g > c->max_groups) return CCA_ERR_CAPACITY;
+  hipError_t e = cca::launch_cache_append(c, q, k, v, scale, stream);
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  c->n_tokens = t + 1;
+  c->n_pooled = (t + 1) / c->g;
+  return CCA_OK;
+}
+
+size_t cca_decode_workspace_bytes(const cca_cache_t* c) {
+  if (c == nullptr || c->B < 1 || c->H < 1 || (c->d != 64 && c->d != 128)) return 0;
+  const size_t BH = (size_t)c->B * c->H;
+  const size_t nc = (size_t)cca::decode_num_chunks(c);
+  return BH * nc * ((size_t)c->d + 2) * sizeof(float);
+}
+
+int cca_decode_step(const cca_cache_t* c, const void* q, void* out, int out_dt, void* workspace,
+                    size_t workspace_bytes, float scale, hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !isfinite(scale)) return CCA_ERR_INVALID;
+  if (c->n_tokens < 1) return CCA_ERR_INVALID;
+  if (workspace_bytes < cca_decode_workspace_bytes(c)) return CCA_ERR_WORKSPACE;
+  return hip_status(cca::launch_decode(c, q, out, out_dt == CCA_F32, workspace, scale, stream));
+}
+
+int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt, int64_t* resident_bytes,
+                       int64_t* full_bytes) {
+  if (n_tokens < 0 || g < 1 || k_local < 0 || B < 1 || H < 1 || d < 1) return CCA_ERR_INVALID;
+  if (dt != CCA_F32 && dt != CCA_BF16) return CCA_ERR_UNSUPPORTED;
+  const int64_t per_token = (int64_t)B * H * 2 * d * (dt == CCA_BF16 ? 2 : 4);
+  if (resident_bytes) *resident_bytes = per_token * (n_tokens / g + (int64_t)(k_local + 1) * g);
+  if (full_bytes) *full_bytes = per_token * n_tokens;
+  return CCA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Device-side helpers shared by the CCA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cca {
+
+constexpr int kWave = 64;
+
+// bfloat16 is stored as its 16-bit pattern; arithmetic happens in float32.
+struct bf16_t {
+  uint16_t bits;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even float32 -> bfloat16 bits (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Element traits: loads of 16-byte chunks and conversion to float.
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;  // elements per 16-byte chunk
+  __device__ __forceinline__ static void chunk_to_f32(const uint4& c, float* f) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static float load1(const bf16_t* p) { return bf16_bits_to_f32(p->bits); }
+  __device__ __forceinline__ static void store1(bf16_t* p, float v) { p->bits = f32_to_bf16_bits(v); }
+};
+
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerChunk = 4;
+  __device__ __forceinline__ static void chunk_to_f32(const uint4& c, float* f) {
+    f[0] = __uint_as_float(c.x);
+    f[1] = __uint_as_float(c.y);
+    f[2] = __uint_as_float(c.z);
+    f[3] = __uint_as_float(c.w);
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Butterfly reductions over the lanes of a wave that differ in the bits of `mask_bits`.
+__device__ __forceinline__ float wave_max_xor(float v, int lo_bit, int hi_bit) {
+  for (int b = lo_bit; b < hi_bit; b <<= 1) v = fmaxf(v, __shfl_xor(v, b, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor(float v, int lo_bit, int hi_bit) {
+  for (int b = lo_bit; b < hi_bit; b <<= 1) v += __shfl_xor(v, b, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Finite stand-in for -infinity as the initial running max: keeps
+// exp2(m_old - m_new) finite when a row has seen only masked keys.
+constexpr float kNegBig = -1.0e30f;
+
+}  // namespace cca

@@ -1,0 +1,29 @@
+// Internal launch interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include "cca_device.h"
+#include "cca.h"
+
+namespace cca {
+
+// Each launcher enqueues its kernels on `stream` and returns the launch status.
+// Arguments have been validated by the caller (api.hip).
+hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
+                       int BH, int64_t L, int g, float scale, hipStream_t stream);
+
+hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v,
+                                    const void* kc, const void* vc, void* out, int out_f32, int BH,
+                                    int64_t L, int g, int k_local, float scale, hipStream_t stream);
+
+hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc,
+                             const void* vc, int64_t L, hipStream_t stream);
+
+hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* k, const void* v,
+                               float scale, hipStream_t stream);
+
+int decode_num_chunks(const cca_cache_t* c);
+
+hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace,
+                         float scale, hipStream_t stream);
+
+}  // namespace cca

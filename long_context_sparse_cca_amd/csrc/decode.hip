@@ -1,0 +1,348 @@
+// Decode against the compressed CCA KV cache (core-token array + raw ring).
+//
+// Method: the CCA write-up ("ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展"):
+// the Triton section says the fused operator serves decode with a KV cache,
+// and the compute/memory-efficiency section (Fig. 3) that the cache holds the
+// core tokens plus the local raw tokens.  A group is pooled as soon as its last
+// token arrives (its query is the group's last query, global-aware pooling
+// section); the core token becomes visible once the group has left the
+// window (locality-preserving module, group-aligned window).
+//
+//   cca_cache_load_kernel   : seed the cache from a prefill (core tokens + raw tail)
+//   cca_append_kernel       : write the newest k,v into its ring slot; pool a completed group
+//   cca_decode_split_kernel : one chunk of the visible keys per workgroup -> (m, l, acc[d])
+//   cca_decode_merge_kernel : log-sum-exp combination of the chunk states -> out[d]
+#include <algorithm>
+
+#include "cca_internal.h"
+#include "pool_group.h"
+
+namespace cca {
+namespace {
+
+// ---------------------------------------------------------------------------
+// row copies (cache seeding)
+// ---------------------------------------------------------------------------
+// For every slice bh and row r < nrows: dst[bh][(dst_row0 + r) % dst_mod] = src[bh][src_row0 + r],
+// for the two (src, dst) pairs (K and V).  Rows are `cpr` 16-byte chunks.
+__global__ __launch_bounds__(256) void cca_copy_rows_kernel(const uint4* __restrict__ src0, uint4* __restrict__ dst0,
+                                                            const uint4* __restrict__ src1, uint4* __restrict__ dst1,
+                                                            int64_t BH, int64_t nrows, int cpr, int64_t src_rows,
+                                                            int64_t src_row0, int64_t dst_rows, int64_t dst_row0,
+                                                            int64_t dst_mod) {
+  const int64_t total = BH * nrows * cpr;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = idx % cpr;
+    const int64_t rr = idx / cpr;
+    const int64_t r = rr % nrows;
+    const int64_t bh = rr / nrows;
+    const int64_t s = (bh * src_rows + src_row0 + r) * cpr + c;
+    const int64_t d = (bh * dst_rows + (dst_row0 + r) % dst_mod) * cpr + c;
+    dst0[d] = src0[s];
+    dst1[d] = src1[s];
+  }
+}
+
+hipError_t copy_rows(const void* s0, void* d0, const void* s1, void* d1, int64_t BH, int64_t nrows, int cpr,
+                     int64_t src_rows, int64_t src_row0, int64_t dst_rows, int64_t dst_row0, int64_t dst_mod,
+                     hipStream_t stream) {
+  const int64_t total = BH * nrows * cpr;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(cca_copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint4*)s0,
+                     (uint4*)d0, (const uint4*)s1, (uint4*)d1, BH, nrows, cpr, src_rows, src_row0, dst_rows,
+                     dst_row0, dst_mod);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// append one token per sequence (+ in-place pooling of a completed group)
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void cca_append_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                        const T* __restrict__ v, T* __restrict__ ring_k,
+                                                        T* __restrict__ ring_v, T* __restrict__ core_k,
+                                                        T* __restrict__ core_v, int64_t R, int64_t max_groups,
+                                                        int64_t t, int g, float scale) {
+  extern __shared__ float w_lds[];
+  const int64_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  constexpr int CPR = D * (int)sizeof(T) / 16;
+  const T* qt = q + (size_t)bh * D;
+  const T* kt = k + (size_t)bh * D;
+  const T* vt = v + (size_t)bh * D;
+  const int64_t slot = t % R;
+  T* rk = ring_k + ((size_t)bh * R + slot) * D;
+  T* rv = ring_v + ((size_t)bh * R + slot) * D;
+  if (lane < CPR) {
+    st16(reinterpret_cast<uint4*>(rk) + lane, ld16(reinterpret_cast<const uint4*>(kt) + lane));
+    st16(reinterpret_cast<uint4*>(rv) + lane, ld16(reinterpret_cast<const uint4*>(vt) + lane));
+  }
+  if ((t + 1) % g != 0) return;
+  // the group [beta*g, beta*g+g) occupies slots slot-g+1 .. slot (R is a multiple of g)
+  const int64_t beta = t / g;
+  const int64_t first = slot - (g - 1);
+  const T* gk = ring_k + ((size_t)bh * R + first) * D;
+  const T* gv = ring_v + ((size_t)bh * R + first) * D;
+  T* ck = core_k + ((size_t)bh * max_groups + beta) * D;
+  T* cv = core_v + ((size_t)bh * max_groups + beta) * D;
+  pool_group_wave<T, D>(qt, gk, gv, kt, vt, g, scale, ck, cv, w_lds);
+}
+
+template <typename T, int D>
+hipError_t launch_append_t(const cca_cache_t* c, const void* q, const void* k, const void* v, float scale,
+                           hipStream_t stream) {
+  const int64_t BH = (int64_t)c->B * c->H;
+  const int64_t R = (int64_t)(c->k_local + 1) * c->g;
+  hipLaunchKernelGGL((cca_append_kernel<T, D>), dim3((unsigned)BH), dim3(64), (size_t)c->g * sizeof(float), stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k,
+                     (T*)c->core_v, R, c->max_groups, c->n_tokens, c->g, scale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// split-KV decode
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct DecodeCfg {
+  static constexpr int NWAVE = 4;
+  static constexpr int NT = NWAVE * kWave;
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per lane (one 16-byte chunk)
+  static constexpr int LPK = D / EPC;                 // lanes per key
+  static constexpr int KPW = kWave / LPK;             // keys per wave per load
+  static constexpr int U = 4;                         // loads in flight per lane (per K and V)
+  static constexpr int KPI = NWAVE * KPW * U;         // keys per workgroup iteration
+};
+
+// Workspace layout (floats): acc [BH][NC][D], then ml [BH][NC][2] (running max in
+// log2 units, running sum).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void cca_decode_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ core_k, const T* __restrict__ core_v,
+    const T* __restrict__ ring_k, const T* __restrict__ ring_v, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, int64_t max_groups, int64_t R, int64_t n_c, int64_t raw_lo, int64_t n_keys,
+    int64_t chunk, int nchunks, float scale) {
+  using C = DecodeCfg<T, D>;
+  __shared__ float red[C::NWAVE][D + 2];
+  const int64_t bh = blockIdx.x;
+  const int ci = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const int kg = lane / C::LPK;      // key slot within the wave
+  const int part = lane % C::LPK;    // which 16-byte chunk of the row
+  const int64_t start = (int64_t)ci * chunk;
+  const int64_t end = min(n_keys, start + chunk);
+
+  float qf[C::EPC];
+  Elem<T>::chunk_to_f32(ld16(q + (size_t)bh * D + part * C::EPC), qf);
+  const float sc = scale * kLog2e;
+#pragma unroll
+  for (int e = 0; e < C::EPC; ++e) qf[e] *= sc;
+
+  const T* ck = core_k + (size_t)bh * max_groups * D;
+  const T* cv = core_v + (size_t)bh * max_groups * D;
+  const T* rk = ring_k + (size_t)bh * R * D;
+  const T* rv = ring_v + (size_t)bh * R * D;
+
+  float m_run = kNegBig, l_run = 0.f;
+  float acc[C::EPC];
+#pragma unroll
+  for (int e = 0; e < C::EPC; ++e) acc[e] = 0.f;
+
+  for (int64_t base = start; base < end; base += C::KPI) {
+    uint4 kr[C::U], vr[C::U];
+    bool ok[C::U];
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      const int64_t n = base + (int64_t)(u * C::NWAVE + wave) * C::KPW + kg;
+      ok[u] = n < end;
+      const int64_t nn = ok[u] ? n : start;
+      const T* kp;
+      const T* vp;
+      if (nn < n_c) {
+        kp = ck + (size_t)nn * D;
+        vp = cv + (size_t)nn * D;
+      } else {
+        const int64_t slot = (raw_lo + (nn - n_c)) % R;
+        kp = rk + (size_t)slot * D;
+        vp = rv + (size_t)slot * D;
+      }
+      kr[u] = ld16(kp + part * C::EPC);
+      vr[u] = ld16(vp + part * C::EPC);
+    }
+    float s[C::U];
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      float kf[C::EPC];
+      Elem<T>::chunk_to_f32(kr[u], kf);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < C::EPC; ++e) dot = fmaf(qf[e], kf[e], dot);
+#pragma unroll
+      for (int b = 1; b < C::LPK; b <<= 1) dot += __shfl_xor(dot, b, kWave);
+      s[u] = ok[u] ? dot : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int u = 1; u < C::U; ++u) mx = fmaxf(mx, s[u]);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < C::EPC; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      const float p = fast_exp2(s[u] - m_new);
+      l_run += p;
+      float vf[C::EPC];
+      Elem<T>::chunk_to_f32(vr[u], vf);
+#pragma unroll
+      for (int e = 0; e < C::EPC; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+  }
+
+  // combine the key slots of the wave (lanes with equal `part`)
+#pragma unroll
+  for (int b = C::LPK; b < kWave; b <<= 1) {
+    const float mo = __shfl_xor(m_run, b, kWave);
+    const float lo = __shfl_xor(l_run, b, kWave);
+    const float M = fmaxf(m_run, mo);
+    const float a1 = fast_exp2(m_run - M), a2 = fast_exp2(mo - M);
+    l_run = l_run * a1 + lo * a2;
+#pragma unroll
+    for (int e = 0; e < C::EPC; ++e) {
+      const float ao = __shfl_xor(acc[e], b, kWave);
+      acc[e] = acc[e] * a1 + ao * a2;
+    }
+    m_run = M;
+  }
+  if (lane < C::LPK) {
+#pragma unroll
+    for (int e = 0; e < C::EPC; ++e) red[wave][part * C::EPC + e] = acc[e];
+    if (lane == 0) {
+      red[wave][D] = m_run;
+      red[wave][D + 1] = l_run;
+    }
+  }
+  __syncthreads();
+  // combine the waves: thread x < D owns column x
+  const size_t rec = (size_t)bh * nchunks + ci;
+  if (tid < D) {
+    float M = red[0][D];
+#pragma unroll
+    for (int w = 1; w < C::NWAVE; ++w) M = fmaxf(M, red[w][D]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::NWAVE; ++w) {
+      const float f = fast_exp2(red[w][D] - M);
+      a = fmaf(f, red[w][tid], a);
+      l = fmaf(f, red[w][D + 1], l);
+    }
+    ws_acc[rec * D + tid] = a;
+    if (tid == 0) {
+      ws_ml[rec * 2] = M;
+      ws_ml[rec * 2 + 1] = l;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __restrict__ ws_acc,
+                                                              const float* __restrict__ ws_ml, void* __restrict__ out,
+                                                              int out_bf16, int nchunks) {
+  const int64_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  constexpr int CPL = D / kWave;
+  const float* ml = ws_ml + (size_t)bh * nchunks * 2;
+  float M = kNegBig;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ml[2 * c]);
+  float l = 0.f, a[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) a[e] = 0.f;
+  for (int c = 0; c < nchunks; ++c) {
+    const float f = fast_exp2(ml[2 * c] - M);
+    l = fmaf(f, ml[2 * c + 1], l);
+    const float* ac = ws_acc + ((size_t)bh * nchunks + c) * D + lane * CPL;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) a[e] = fmaf(f, ac[e], a[e]);
+  }
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    const size_t o = (size_t)bh * D + lane * CPL + e;
+    if (out_bf16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(a[e] * inv);
+    else reinterpret_cast<float*>(out)[o] = a[e] * inv;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace,
+                           float scale, hipStream_t stream) {
+  const int64_t BH = (int64_t)c->B * c->H;
+  const int64_t R = (int64_t)(c->k_local + 1) * c->g;
+  const int64_t t = c->n_tokens - 1;
+  const int64_t n_c = std::max<int64_t>(0, t / c->g - c->k_local);
+  const int64_t raw_lo = n_c * c->g;
+  const int64_t n_keys = n_c + (t - raw_lo + 1);
+  const int nchunks = decode_num_chunks(c);
+  int64_t chunk = (n_keys + nchunks - 1) / nchunks;
+  chunk = (chunk + 15) / 16 * 16;
+  float* ws_acc = (float*)workspace;
+  float* ws_ml = ws_acc + (size_t)BH * nchunks * D;
+  hipLaunchKernelGGL((cca_decode_split_kernel<T, D>), dim3((unsigned)BH, nchunks), dim3(256), 0, stream,
+                     (const T*)q, (const T*)c->core_k, (const T*)c->core_v, (const T*)c->ring_k, (const T*)c->ring_v,
+                     ws_acc, ws_ml, c->max_groups, R, n_c, raw_lo, n_keys, chunk, nchunks, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
+  hipLaunchKernelGGL((cca_decode_merge_kernel<D>), dim3((unsigned)BH), dim3(64), 0, stream, ws_acc, ws_ml, out,
+                     out_bf16, nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_num_chunks(const cca_cache_t* c) {
+  // enough workgroups to keep every CU streaming, chunks of >= ~512 keys
+  const int64_t cap = c->max_groups + (int64_t)(c->k_local + 1) * c->g;
+  int64_t n = (cap + 511) / 512;
+  n = std::max<int64_t>(1, std::min<int64_t>(n, 64));
+  return (int)n;
+}
+
+hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc, const void* vc,
+                             int64_t L, hipStream_t stream) {
+  const int64_t BH = (int64_t)c->B * c->H;
+  const int esz = (c->dt == CCA_BF16) ? 2 : 4;
+  const int cpr = c->d * esz / 16;
+  const int64_t m = L / c->g;
+  const int64_t R = (int64_t)(c->k_local + 1) * c->g;
+  hipError_t e = copy_rows(kc, c->core_k, vc, c->core_v, BH, m, cpr, m, 0, c->max_groups, 0, INT64_MAX, stream);
+  if (e != hipSuccess) return e;
+  const int64_t lo = std::max<int64_t>(0, m - c->k_local) * c->g;
+  return copy_rows(k, c->ring_k, v, c->ring_v, BH, L - lo, cpr, L, lo, R, lo, R, stream);
+}
+
+hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* k, const void* v, float scale,
+                               hipStream_t stream) {
+  if (c->dt == CCA_BF16) {
+    if (c->d == 128) return launch_append_t<bf16_t, 128>(c, q, k, v, scale, stream);
+    return launch_append_t<bf16_t, 64>(c, q, k, v, scale, stream);
+  }
+  if (c->d == 128) return launch_append_t<float, 128>(c, q, k, v, scale, stream);
+  return launch_append_t<float, 64>(c, q, k, v, scale, stream);
+}
+
+hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace, float scale,
+                         hipStream_t stream) {
+  if (c->dt == CCA_BF16) {
+    if (c->d == 128) return launch_decode_t<bf16_t, 128>(c, q, out, out_f32, workspace, scale, stream);
+    return launch_decode_t<bf16_t, 64>(c, q, out, out_f32, workspace, scale, stream);
+  }
+  if (c->d == 128) return launch_decode_t<float, 128>(c, q, out, 1, workspace, scale, stream);
+  return launch_decode_t<float, 64>(c, q, out, 1, workspace, scale, stream);
+}
+
+}  // namespace cca

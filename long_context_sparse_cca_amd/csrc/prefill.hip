@@ -1,0 +1,376 @@
+// Fused CCA prefill attention for gfx950: one online softmax per query over the
+// union of the visible core tokens and the group-aligned raw window.
+//
+// Method: the CCA write-up ("ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展"),
+// locality-preserving module (local-window equation) and global-local fusion
+// (unified K/V and per-position output equations): query t of group
+// beta = t/g sees core tokens Kc[0 : beta-k) and raw keys K[(beta-k)*g .. t]
+// (lower bound clamped at 0), and one softmax spans both.  The Triton section
+// of the same page describes fusing both parts into one flash-style operator;
+// this kernel is an MI355X design of that idea, not a translation.
+//
+// Structure (per workgroup = 4 waves = 128 consecutive queries of one (b,h)):
+//   * key tiles of BN keys are staged in LDS: K row-major, V transposed so that
+//     the PV product reads 4 or 8 consecutive keys per lane;
+//   * the tile loop visits the core tiles [0, n_c_max) then the raw tiles
+//     [rl_min, t_max]; each wave classifies every 32-key sub-block as skipped,
+//     fully visible or masked for its own 32 queries;
+//   * S^T = K Q^T on MFMA (32x32 output: lane = query, 16 keys per lane), so the
+//     running max / sum are per-lane scalars and a row max needs one shuffle;
+//   * O^T += V^T P^T on MFMA with P rounded to the input type (bf16) or kept fp32.
+#include "cca_internal.h"
+
+namespace cca {
+namespace {
+
+template <typename T, int D>
+struct PrefillCfg {
+  static constexpr int BM = 128;                        // queries per workgroup
+  static constexpr int NWAVE = 4;
+  static constexpr int NT = NWAVE * kWave;              // threads
+  static constexpr int EB = sizeof(T);
+  static constexpr int EPC = 16 / EB;                   // elements per 16-byte chunk
+  static constexpr int BN = (EB == 2) ? 64 : 32;        // keys per LDS tile
+  static constexpr int NSB = BN / 32;                   // 32-key sub-blocks per tile
+  static constexpr int KP = D + 16 / EB;                // K tile pitch (elements), +16 B
+  static constexpr int VP = BN + 4;                     // V^T tile pitch (elements)
+  static constexpr int KPT = 8 / EB;                    // keys packed per 8-byte V^T store
+  static constexpr int CPR = D / EPC;                   // chunks per row
+  static constexpr int KCH = BN * CPR / NT;             // K chunks per thread
+  static constexpr int VUNITS = (BN / KPT) * CPR;       // V^T transpose units
+  static constexpr int VU = (VUNITS + NT - 1) / NT;     // units per thread
+  static constexpr int NDT = D / 32;                    // 32-wide output tiles along d
+  static constexpr int LDS_K = BN * KP;                 // elements
+  static constexpr int LDS_V = D * VP;
+  static_assert(BN * CPR % NT == 0, "K tile must split evenly");
+};
+
+enum : int { kSkip = 0, kFull = 1, kMask = 2 };
+
+// Workgroup -> (slice, query tile).  Consecutive workgroups are dealt round-robin
+// to the 8 XCDs; when the grid divides evenly, XCD x gets a contiguous range of
+// slices and, inside a slice, the query tiles from the heaviest (last) down, so
+// that the co-resident workgroups of one XCD sweep the same core K/V in its L2.
+__device__ __forceinline__ void map_block(int nblocks, int ntiles, int& bh, int& tile) {
+  const int bid = blockIdx.x;
+  int li = bid;
+  if ((nblocks & 7) == 0) li = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+  bh = li / ntiles;
+  tile = ntiles - 1 - (li - bh * ntiles);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void cca_prefill_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ Kc, const T* __restrict__ Vc, void* __restrict__ Out, int out_f32,
+    int BH, int64_t L, int g, int k_local, float scale, int ntiles) {
+  using C = PrefillCfg<T, D>;
+  __shared__ __attribute__((aligned(16))) T lds_k[C::LDS_K];
+  __shared__ __attribute__((aligned(16))) T lds_v[C::LDS_V];
+
+  int bh, qtile;
+  map_block(BH * ntiles, ntiles, bh, qtile);
+  const int64_t m = L / g;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int64_t q0 = (int64_t)qtile * C::BM;
+  const int64_t q_last = min(q0 + C::BM - 1, L - 1);
+  const int64_t nc_wg = max<int64_t>(0, q_last / g - k_local);      // core tokens any row sees
+  const int64_t rl_wg = max<int64_t>(0, q0 / g - k_local) * g;      // first raw key any row sees
+  const int n_core_tiles = (int)((nc_wg + C::BN - 1) / C::BN);
+  const int n_raw_tiles = (int)((q_last - rl_wg + C::BN) / C::BN);
+  const int n_tiles = n_core_tiles + n_raw_tiles;
+
+  // ---- this wave's queries
+  const int64_t qa = q0 + wave * 32;
+  const bool wave_live = qa < L;
+  const int64_t qb = min(qa + 31, L - 1);
+  const int64_t q_lane = min(qa + l32, L - 1);
+  const int64_t cl_lane = q_lane / g - k_local;                      // core visible iff j < cl_lane
+  const int64_t rl_lane = max<int64_t>(0, cl_lane) * g;              // raw visible iff rl <= u <= q
+  const int64_t cl_min = qa / g - k_local, cl_max = qb / g - k_local;
+  const int64_t rl_min = max<int64_t>(0, cl_min) * g, rl_max = max<int64_t>(0, cl_max) * g;
+
+  const T* Qs = Q + (size_t)bh * L * D;
+  const T* Ks = K + (size_t)bh * L * D;
+  const T* Vs = V + (size_t)bh * L * D;
+  const T* Kcs = Kc + (size_t)bh * m * D;
+  const T* Vcs = Vc + (size_t)bh * m * D;
+
+  // ---- Q operand in registers (B operand of S^T = K Q^T).
+  // bf16: slice s of 16 dims, lane half hf holds dims 16s+8hf .. +8.
+  // f32 : lane half hf holds dims hf*D/2 + s for the D/2 single-K MFMAs.
+  constexpr int QREG = (C::EB == 2) ? D / 16 : D / 8;
+  uint4 qop[QREG];
+  {
+    const T* qrow = Qs + (size_t)q_lane * D;
+#pragma unroll
+    for (int s = 0; s < QREG; ++s) {
+      if constexpr (C::EB == 2) qop[s] = ld16(qrow + s * 16 + hf * 8);
+      else qop[s] = ld16(qrow + hf * (D / 2) + s * 4);
+    }
+  }
+
+  f32x16_t acc[C::NDT];
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+  const float sc = scale * kLog2e;
+
+  // ---- tile staging: global -> registers (prefetch) -> LDS
+  uint4 kreg[C::KCH];
+  uint4 vreg[C::VU][C::KPT];
+
+  auto tile_src = [&](int it, const T*& ks, const T*& vs, int64_t& base, int64_t& lim) {
+    if (it < n_core_tiles) {
+      ks = Kcs; vs = Vcs; base = (int64_t)it * C::BN; lim = m - 1;
+    } else {
+      ks = Ks; vs = Vs; base = rl_wg + (int64_t)(it - n_core_tiles) * C::BN; lim = L - 1;
+    }
+  };
+  auto load_tile = [&](int it) {
+    const T *ks, *vs; int64_t base, lim;
+    tile_src(it, ks, vs, base, lim);
+#pragma unroll
+    for (int i = 0; i < C::KCH; ++i) {
+      const int id = tid + i * C::NT;
+      const int row = id / C::CPR, c = id % C::CPR;
+      const int64_t gr = min(base + row, lim);
+      kreg[i] = ld16(ks + (size_t)gr * D + c * C::EPC);
+    }
+#pragma unroll
+    for (int u = 0; u < C::VU; ++u) {
+      const int id = tid + u * C::NT;
+      if (id < C::VUNITS) {
+        const int c = id % C::CPR, a = id / C::CPR;
+#pragma unroll
+        for (int e = 0; e < C::KPT; ++e) {
+          const int64_t gr = min(base + a * C::KPT + e, lim);
+          vreg[u][e] = ld16(vs + (size_t)gr * D + c * C::EPC);
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::KCH; ++i) {
+      const int id = tid + i * C::NT;
+      const int row = id / C::CPR, c = id % C::CPR;
+      st16(lds_k + row * C::KP + c * C::EPC, kreg[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < C::VU; ++u) {
+      const int id = tid + u * C::NT;
+      if (id < C::VUNITS) {
+        const int c = id % C::CPR, a = id / C::CPR;
+        // transpose: KPT keys x EPC dims -> EPC rows of KPT consecutive keys (8 bytes each)
+#pragma unroll
+        for (int x = 0; x < C::EPC; ++x) {
+          uint2 w;
+          if constexpr (C::EB == 2) {
+            const uint16_t* h0 = reinterpret_cast<const uint16_t*>(&vreg[u][0]);
+            const uint16_t* h1 = reinterpret_cast<const uint16_t*>(&vreg[u][1]);
+            const uint16_t* h2 = reinterpret_cast<const uint16_t*>(&vreg[u][2]);
+            const uint16_t* h3 = reinterpret_cast<const uint16_t*>(&vreg[u][3]);
+            w.x = (uint32_t)h0[x] | ((uint32_t)h1[x] << 16);
+            w.y = (uint32_t)h2[x] | ((uint32_t)h3[x] << 16);
+          } else {
+            w.x = reinterpret_cast<const uint32_t*>(&vreg[u][0])[x];
+            w.y = reinterpret_cast<const uint32_t*>(&vreg[u][1])[x];
+          }
+          *reinterpret_cast<uint2*>(lds_v + (c * C::EPC + x) * C::VP + a * C::KPT) = w;
+        }
+      }
+    }
+  };
+
+  if (n_tiles > 0) load_tile(0);
+  for (int it = 0; it < n_tiles; ++it) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (it + 1 < n_tiles) load_tile(it + 1);
+    if (!wave_live) continue;
+
+    const bool core = it < n_core_tiles;
+    const int64_t tbase = core ? (int64_t)it * C::BN : rl_wg + (int64_t)(it - n_core_tiles) * C::BN;
+
+    int cls[C::NSB];
+    bool any = false;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      const int64_t kb = tbase + sb * 32;
+      int c;
+      if (core) {
+        c = (kb >= cl_max) ? kSkip : ((kb + 32 <= cl_min) ? kFull : kMask);
+      } else {
+        if (kb + 31 < rl_min || kb > qb) c = kSkip;
+        else if (kb >= rl_max && kb + 31 <= qa) c = kFull;
+        else c = kMask;
+      }
+      cls[sb] = c;
+      any |= (c != kSkip);
+    }
+    if (!any) continue;
+
+    f32x16_t s[C::NSB];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      if (cls[sb] == kSkip) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+      if constexpr (C::EB == 2) {
+        const T* krow = lds_k + (sb * 32 + l32) * C::KP + hf * 8;
+#pragma unroll
+        for (int d16 = 0; d16 < D / 16; ++d16) {
+          bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + d16 * 16));
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, qop[d16]), s[sb], 0, 0, 0);
+        }
+      } else {
+        const T* krow = lds_k + (sb * 32 + l32) * C::KP + hf * (D / 2);
+#pragma unroll
+        for (int c4 = 0; c4 < D / 8; ++c4) {
+          const float4 a = *reinterpret_cast<const float4*>(krow + c4 * 4);
+          const float4 b = __builtin_bit_cast(float4, qop[c4]);
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, s[sb], 0, 0, 0);
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, s[sb], 0, 0, 0);
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, s[sb], 0, 0, 0);
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, s[sb], 0, 0, 0);
+        }
+      }
+      if (cls[sb] == kMask) {
+        const int64_t kb = tbase + sb * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t key = kb + 8 * i + 4 * hf + j;
+            const bool vis = core ? (key < cl_lane) : (key >= rl_lane && key <= q_lane);
+            if (!vis) s[sb][4 * i + j] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[sb][r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_run, tmax * sc);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      if (cls[sb] == kSkip) continue;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(s[sb][r], sc, -m_new));
+        l_run += p[r];
+      }
+      if constexpr (C::EB == 2) {
+        // P^T as B operand: keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u..8u+7
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t pb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
+#pragma unroll
+          for (int dt = 0; dt < C::NDT; ++dt) {
+            const T* vrow = lds_v + (dt * 32 + l32) * C::VP + sb * 32 + 16 * u + 4 * hf;
+            uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+            uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb, acc[dt], 0, 0, 0);
+          }
+        }
+      } else {
+        // one single-K MFMA per S register 4i+j (key 8i+4hf+j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int dt = 0; dt < C::NDT; ++dt) {
+            const float4 a = *reinterpret_cast<const float4*>(lds_v + (dt * 32 + l32) * C::VP + sb * 32 + 8 * i + 4 * hf);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * i + 0], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * i + 1], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * i + 2], acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * i + 3], acc[dt], 0, 0, 0);
+          }
+      }
+    }
+  }
+
+  if (!wave_live) return;
+  // ---- normalise and store: lane (query l32, half hf) holds O[q][dt*32 + 8i + 4hf + j]
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float inv = 1.0f / l_tot;
+  const int64_t q_row = qa + l32;
+  if (q_row >= L) return;
+  if (out_f32) {
+    float* o = reinterpret_cast<float*>(Out) + ((size_t)bh * L + q_row) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 v = make_float4(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv, acc[dt][4 * i + 2] * inv,
+                               acc[dt][4 * i + 3] * inv);
+        *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) = v;
+      }
+  } else if constexpr (C::EB == 2) {
+    T* o = reinterpret_cast<T*>(Out) + ((size_t)bh * L + q_row) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv);
+        w.y = pack_bf16x2(acc[dt][4 * i + 2] * inv, acc[dt][4 * i + 3] * inv);
+        *reinterpret_cast<uint2*>(o + dt * 32 + 8 * i + 4 * hf) = w;
+      }
+  }
+}
+
+}  // namespace
+}  // namespace cca
+
+namespace cca {
+namespace {
+
+template <typename T, int D>
+hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                            void* out, int out_f32, int BH, int64_t L, int g, int k_local, float scale,
+                            hipStream_t stream) {
+  using C = PrefillCfg<T, D>;
+  const int ntiles = (int)((L + C::BM - 1) / C::BM);
+  const int64_t nblocks = (int64_t)BH * ntiles;
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((cca_prefill_kernel<T, D>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, L, g,
+                     k_local, scale, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
+                                    const void* vc, void* out, int out_f32, int BH, int64_t L, int g,
+                                    int k_local, float scale, hipStream_t stream) {
+  if (dt == CCA_BF16) {
+    if (d == 128) return launch_prefill_t<bf16_t, 128>(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
+    return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
+  }
+  if (d == 128) return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, L, g, k_local, scale, stream);
+  return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, L, g, k_local, scale, stream);
+}
+
+}  // namespace cca

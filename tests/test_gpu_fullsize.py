@@ -1,0 +1,88 @@
+"""Full-size workloads, in the launch configuration the benchmark times, on sampled outputs.
+
+Inputs are drawn on the GPU (seeded torch generator, 1% heavy-hitter keys x4,
+bf16); the sampled (b, h) slices are copied back so the oracle sees exactly
+the GPU's inputs.  The oracle pools the sampled slice completely and computes
+the sampled rows one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_cca_amd import binding
+from long_context_sparse_cca_amd.synth import torch_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+H, D, G, KL = 32, 128, 16, 64
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _rows(L, rng):
+    fixed = [0, 1, G - 1, G, 127, 128, KL * G - 1, KL * G, KL * G + G - 1, L // 2, L - G - 1, L - G, L - 2, L - 1]
+    extra = rng.integers(0, L, size=24).tolist()
+    return sorted({r for r in fixed + extra if 0 <= r < L})
+
+
+@pytest.mark.parametrize("L", [8192, 32768, 131072])
+def test_prefill_fullsize_sampled(gpu, L):
+    _say(f"full-size prefill L={L}")
+    q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, gpu, seed=0, heavy_frac=0.01)
+    out = binding.prefill(q, k, v, G, KL, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(L)
+    scale = 1.0 / math.sqrt(D)
+    for h in (0, 17, H - 1):
+        Q = q[0, h].float().cpu().numpy().astype(np.float64)
+        K = k[0, h].float().cpu().numpy().astype(np.float64)
+        V = v[0, h].float().cpu().numpy().astype(np.float64)
+        Kc, Vc, _ = oracle.pool(Q, K, V, G, scale)
+        rows = _rows(L, rng)
+        got = out[0, h, rows].cpu().numpy()
+        for i, t in enumerate(rows):
+            want = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
+            err = np.abs(got[i] - want).max()
+            assert err <= TOL_BF16, f"head {h} row {t}: max abs err {err:.3e}"
+
+
+def test_decode_fullsize_sampled(gpu):
+    """B=8, 131072-token context seeded from a prefill, 256 decode steps (16 pooling steps)."""
+    B, L0, S = 8, 131072, 256
+    T = L0 + S
+    _say("full-size decode: generating inputs")
+    q, k, v = torch_inputs(B, H, T, D, torch.bfloat16, gpu, seed=1, heavy_frac=0.01)
+    scale = 1.0 / math.sqrt(D)
+    cache = binding.KVCache(B, H, D, G, KL, max_tokens=T, dtype=torch.bfloat16, device=gpu)
+    kc, vc = binding.pool_kv(q[:, :, :L0].contiguous(), k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), G,
+                             scale)
+    cache.load_prefill(k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc, vc)
+    del kc, vc
+    _say("full-size decode: stepping")
+    qs = q[:, :, L0:].permute(2, 0, 1, 3).contiguous()
+    ks = k[:, :, L0:].permute(2, 0, 1, 3).contiguous()
+    vs = v[:, :, L0:].permute(2, 0, 1, 3).contiguous()
+    outs = torch.empty((S, B, H, D), dtype=torch.float32, device=gpu)
+    for s in range(S):
+        cache.append(qs[s], ks[s], vs[s], scale)
+        cache.decode(qs[s], out_dtype=torch.float32, out=outs[s])
+    torch.cuda.synchronize()
+    got = outs.cpu().numpy()
+    for (b, h) in [(0, 0), (3, 17), (7, 31)]:
+        Q = q[b, h].float().cpu().numpy().astype(np.float64)
+        K = k[b, h].float().cpu().numpy().astype(np.float64)
+        V = v[b, h].float().cpu().numpy().astype(np.float64)
+        Kc, Vc, _ = oracle.pool(Q, K, V, G, scale)
+        for s in range(S):
+            t = L0 + s
+            want = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
+            err = np.abs(got[s, b, h] - want).max()
+            assert err <= TOL_BF16, f"slice ({b},{h}) step {s}: max abs err {err:.3e}"

@@ -1,0 +1,160 @@
+"""HIP path vs the CPU oracle on small shapes (pooling and fused prefill).
+
+Sizes span several 128-query tiles and key tiles, with ragged tails, k = 0,
+g = 1 (plain causal attention), windows wider than the sequence, L < g, L = 1.
+Tolerances (max-abs): fp32 inputs 1e-4; bf16 inputs with fp32 accumulation 2e-2.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_sparse_cca_amd import binding
+from long_context_sparse_cca_amd.synth import np_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _dev(x, dt, device):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=TDT[dt]).contiguous()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# (B, H, L, d, g, k, dtype, seed)
+PREFILL_CASES = [
+    (1, 2, 256, 64, 16, 1, "f32", 0),      # the small fp32 configuration
+    (1, 2, 256, 64, 16, 1, "bf16", 0),
+    (1, 2, 1000, 128, 16, 4, "bf16", 1),   # several tiles, ragged last tile
+    (2, 3, 517, 64, 7, 3, "bf16", 2),      # g not a power of two, ragged group
+    (1, 2, 333, 128, 1, 0, "f32", 3),      # g = 1: plain causal attention
+    (1, 2, 640, 128, 16, 100, "bf16", 4),  # window wider than the sequence
+    (1, 1, 700, 128, 16, 0, "f32", 5),     # k = 0
+    (1, 1, 1, 64, 16, 1, "f32", 6),        # L = 1
+    (1, 1, 15, 128, 16, 1, "bf16", 7),     # L < g: no core token at all
+    (1, 1, 300, 128, 64, 2, "f32", 8),     # g = 64
+    (1, 1, 2100, 128, 32, 5, "bf16", 9),   # core tiles with masked sub-blocks in the middle
+    (1, 1, 410, 64, 3, 11, "f32", 10),
+]
+
+
+def _case_id(c):
+    B, H, L, d, g, k, dt, seed = c
+    return f"B{B}H{H}L{L}d{d}g{g}k{k}-{dt}"
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=_case_id)
+def test_prefill_matches_oracle(gpu, case):
+    B, H, L, d, g, k, dt, seed = case
+    _say(f"prefill case {_case_id(case)} seed {seed}")
+    Q, K, V = np_inputs(B, H, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    out, kc, vc = binding.prefill(q, kk, v, g, k, scale, out_dtype=torch.float32, return_core=True)
+    torch.cuda.synchronize()
+    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, scale)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+    assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
+    # core tokens: one rounding to the storage dtype on top of fp32 math
+    m = L // g
+    if m:
+        for b in range(B):
+            for h in range(H):
+                Kc, Vc, _ = oracle.pool(Q[b, h], K[b, h], V[b, h], g, scale)
+                gk = kc[b, h].float().cpu().numpy()
+                gv = vc[b, h].float().cpu().numpy()
+                ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -22
+                for got, ref in ((gk, Kc), (gv, Vc)):
+                    bound = TOL[dt] + ulp * np.abs(ref)
+                    assert np.all(np.abs(got - ref) <= bound), f"core err {np.abs(got - ref).max():.3e}"
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES[:4], ids=_case_id)
+def test_prefill_bf16_output(gpu, case):
+    """Output in the input dtype: same tolerance (one extra rounding of |O| < 4)."""
+    B, H, L, d, g, k, dt, seed = case
+    if dt != "bf16":
+        pytest.skip("bf16 output only")
+    _say(f"prefill bf16-out case {_case_id(case)}")
+    Q, K, V = np_inputs(B, H, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    out = binding.prefill(q, kk, v, g, k)
+    torch.cuda.synchronize()
+    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, 1.0 / math.sqrt(d))
+    err = np.abs(out.float().cpu().numpy() - want).max()
+    assert err <= TOL[dt], f"max abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("case", [(1, 2, 256, 64, 16, "f32", 0), (2, 3, 300, 128, 16, "bf16", 1),
+                                  (1, 2, 77, 64, 5, "f32", 2), (1, 1, 64, 128, 1, "bf16", 3),
+                                  (1, 1, 200, 128, 200, "f32", 4), (1, 1, 10, 64, 16, "bf16", 5)],
+                         ids=lambda c: f"B{c[0]}H{c[1]}L{c[2]}d{c[3]}g{c[4]}-{c[5]}")
+def test_pool_matches_oracle(gpu, case):
+    B, H, L, d, g, dt, seed = case
+    _say(f"pool case {case}")
+    Q, K, V = np_inputs(B, H, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    kc, vc = binding.pool_kv(q, kk, v, g, scale)
+    torch.cuda.synchronize()
+    assert kc.shape == (B, H, L // g, d)
+    ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -22
+    tol = 1e-5 if dt == "f32" else 1e-3
+    for b in range(B):
+        for h in range(H):
+            Kc, Vc, _ = oracle.pool(Q[b, h], K[b, h], V[b, h], g, scale)
+            for got, ref in ((kc[b, h], Kc), (vc[b, h], Vc)):
+                got = got.float().cpu().numpy()
+                assert np.all(np.abs(got - ref) <= tol + ulp * np.abs(ref)), f"err {np.abs(got - ref).max():.3e}"
+
+
+def test_prefill_deterministic(gpu):
+    """Two runs give bit-identical outputs (no atomics anywhere on the path)."""
+    Q, K, V = np_inputs(1, 2, 900, 128, "bf16", 11)
+    q, kk, v = (_dev(x, "bf16", gpu) for x in (Q, K, V))
+    a = binding.prefill(q, kk, v, 16, 4, out_dtype=torch.float32)
+    b = binding.prefill(q, kk, v, 16, 4, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_prefill_writes_only_its_output(gpu):
+    """Guard canaries around the output and core buffers stay untouched."""
+    B, H, L, d, g, k = 1, 2, 300, 128, 16, 2
+    Q, K, V = np_inputs(B, H, L, d, "bf16", 12)
+    q, kk, v = (_dev(x, "bf16", gpu) for x in (Q, K, V))
+    n_out = B * H * L * d
+    m = L // g
+    n_core = B * H * m * d
+    pad = 4096
+    big = torch.full((n_out + 2 * pad,), 12345.0, dtype=torch.float32, device=gpu)
+    core_big = torch.full((2, n_core + 2 * pad), -7.0, dtype=torch.bfloat16, device=gpu)
+    out = big[pad:pad + n_out].view(B, H, L, d)
+    kc = core_big[0, pad:pad + n_core].view(B, H, m, d)
+    vc = core_big[1, pad:pad + n_core].view(B, H, m, d)
+    binding.prefill(q, kk, v, g, k, out_dtype=torch.float32, out=out, kc=kc, vc=vc)
+    torch.cuda.synchronize()
+    assert torch.all(big[:pad] == 12345.0) and torch.all(big[pad + n_out:] == 12345.0)
+    assert torch.all(core_big[:, :pad] == -7.0) and torch.all(core_big[:, pad + n_core:] == -7.0)
+
+
+def test_invalid_arguments_enqueue_nothing(gpu):
+    Q, K, V = np_inputs(1, 1, 64, 96, "f32", 13)
+    q, kk, v = (_dev(x, "f32", gpu) for x in (Q, K, V))
+    with pytest.raises(binding.CCAError, match="unsupported"):
+        binding.prefill(q, kk, v, 16, 1)
+    Q, K, V = np_inputs(1, 1, 64, 64, "f32", 13)
+    q, kk, v = (_dev(x, "f32", gpu) for x in (Q, K, V))
+    with pytest.raises(binding.CCAError, match="invalid"):
+        binding.prefill(q, kk, v, 16, -1)
+    with pytest.raises(binding.CCAError, match="unsupported"):
+        binding.prefill(q, kk, v, 16, 1, out_dtype=torch.bfloat16)
