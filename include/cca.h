@@ -70,8 +70,9 @@ const char* cca_status_string(int status);
  *   q, k, v : device, [B, H, L, d] of dtype dt (only rows j*g+g-1 of q are read).
  *   kc, vc  : device, [B, H, floor(L/g), d] of dtype dt, written.  Math is
  *             float32; results are rounded once to dt.  A trailing partial
- *             group (L mod g tokens) produces no core token.
- *   d in {64, 128}; g >= 1; L >= 0 (L < g writes nothing).
+ *             group (L mod g tokens) produces no core token.  When
+ *             floor(L/g) == 0 they are not touched and may be NULL.
+ *   d in {64, 128}; 1 <= g <= 4096; L >= 0 (L < g writes nothing).
  */
 int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
                 int B, int H, int64_t L, int d, int g, float scale,
@@ -84,6 +85,7 @@ int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
  *   kc, vc  : device, [B, H, floor(L/g), d] of dtype dt: written by the pooling
  *             step and then read by the attention step (the caller may keep
  *             them, e.g. to seed a decode cache with cca_cache_load_prefill).
+ *             May be NULL when floor(L/g) == 0.
  *   out     : device, [B, H, L, d] of dtype out_dt, written.  out_dt is CCA_F32
  *             or equal to dt.  Accumulation is float32; for dt = CCA_BF16 the
  *             QK^T and PV products run on bf16 matrix cores with the softmax

@@ -54,7 +54,8 @@ int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
                 int g, float scale, int dt, hipStream_t stream) {
   int s = check_shape(B, H, L, d, g, dt);
   if (s != CCA_OK) return s;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc)) return CCA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
+  if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   if (!isfinite(scale)) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
   if (BH * (L / g) >= INT32_MAX) return CCA_ERR_INVALID;
@@ -67,8 +68,8 @@ int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc,
   if (s != CCA_OK) return s;
   if (out_dt != CCA_F32 && out_dt != dt) return CCA_ERR_UNSUPPORTED;
   if (k_local < 0 || !isfinite(scale)) return CCA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kc) || !aligned16(vc) || !aligned16(out))
-    return CCA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return CCA_ERR_INVALID;
+  if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
   if (BH * (L / g) >= INT32_MAX || BH * ((L + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
   if (L == 0) return CCA_OK;
