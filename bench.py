@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""CCA attention benchmark on one MI355X: prefill tokens/s and decode step latency at 128K.
+
+One step = one pass of the whole hot path on synthetic inputs:
+  * prefill of one attention layer, B=1, H=32, d=128, L=131072, g=16, k=64, bf16:
+    pooling into core tokens (cca_pool_kv) + fused core/local attention (cca_attention);
+  * decode, B=8, H=32, d=128, context 131072 tokens held as core tokens plus a
+    1040-slot raw ring: 256 steps of append (pooling every 16th step) + decode.
+The decode cache is re-seeded from the prefilled state before each step's
+decode phase (outside the per-phase timings).
+
+Prints one JSON line.  `value` is the prefill throughput (tokens/s); decode
+latency, KV-cache bytes, the roofline of the dominant kernel (the fused
+attention, bf16 MFMA bound) and a CPU-oracle baseline ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CCA prefill tokens/s & decode step latency at 128K; % MFMA / HBM roofline"
+H, D, G, KL = 32, 128, 16, 64
+PREFILL_B, PREFILL_L = 1, 131072
+DEC_B, DEC_L0, DEC_STEPS = 8, 131072, 256
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEAVY = 0.01
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--phase", choices=["all", "prefill", "decode"], default="all",
+                    help="profiling aid: run only one phase (the JSON line is then not the benchmark result)")
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_sparse_cca_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kind: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, out, seconds: float):
+    """Time the CPU oracle on a bounded sample of the prefill workload (head 0)."""
+    import numpy as np
+
+    import oracle
+    try:
+        import threadpoolctl
+        threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+    except Exception:  # noqa: BLE001
+        threads = 1
+    threads = threads or 1
+    scale = 1.0 / math.sqrt(D)
+    Q = q[0, 0].float().cpu().numpy().astype(np.float64)
+    K = k[0, 0].float().cpu().numpy().astype(np.float64)
+    V = v[0, 0].float().cpu().numpy().astype(np.float64)
+    got = out[0, 0].float().cpu().numpy()
+    t0 = time.perf_counter()
+    Kc, Vc, _ = oracle.pool(Q, K, V, G, scale)
+    t_pool = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rows = rng.permutation(PREFILL_L)
+    n = 0
+    err = 0.0
+    t1 = time.perf_counter()
+    while n < len(rows) and (time.perf_counter() - t1) < seconds:
+        t = int(rows[n])
+        ref = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
+        err = max(err, float(np.abs(got[t] - ref).max()))
+        n += 1
+    t_rows = time.perf_counter() - t1
+    per_row = t_rows / n
+    layer_s = H * PREFILL_B * (t_pool + PREFILL_L * per_row)
+    return {
+        "value": PREFILL_B * PREFILL_L / layer_s,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"head 0 of the prefill input: full pooling ({t_pool:.2f} s) + {n} uniformly drawn query rows "
+                   f"({t_rows:.1f} s); extrapolated to all {H} heads x {PREFILL_L} rows"),
+        "cpu": platform.processor() or platform.machine(),
+        "parity_max_abs_err_sampled_rows": err,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the CCA path here has no "
+              "multi-GPU code. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from long_context_sparse_cca_amd import accounting, binding
+    from long_context_sparse_cca_amd.synth import torch_inputs
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(D)
+    do_prefill = args.phase in ("all", "prefill")
+    do_decode = args.phase in ("all", "decode")
+
+    # ---- inputs (resident in HBM before timing)
+    if do_prefill:
+        q, k, v = torch_inputs(PREFILL_B, H, PREFILL_L, D, torch.bfloat16, dev, seed=args.seed, heavy_frac=HEAVY)
+        m = PREFILL_L // G
+        kc = torch.empty((PREFILL_B, H, m, D), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        out = torch.empty_like(q)
+    if do_decode:
+        dq, dk, dv = torch_inputs(DEC_B, H, DEC_L0 + DEC_STEPS, D, torch.bfloat16, dev, seed=args.seed + 1,
+                                  heavy_frac=HEAVY)
+        k0 = dk[:, :, :DEC_L0].contiguous()
+        v0 = dv[:, :, :DEC_L0].contiguous()
+        kc0, vc0 = binding.pool_kv(dq[:, :, :DEC_L0].contiguous(), k0, v0, G, scale)
+        qs = dq[:, :, DEC_L0:].permute(2, 0, 1, 3).contiguous()
+        ks = dk[:, :, DEC_L0:].permute(2, 0, 1, 3).contiguous()
+        vs = dv[:, :, DEC_L0:].permute(2, 0, 1, 3).contiguous()
+        del dq, dk, dv
+        cache = binding.KVCache(DEC_B, H, D, G, KL, max_tokens=DEC_L0 + DEC_STEPS, dtype=torch.bfloat16, device=dev)
+        dout = torch.empty((DEC_B, H, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    pe = [ev() for _ in range(3)]
+    de = [ev() for _ in range(3 * DEC_STEPS)]
+    t_pool, t_attn, t_app, t_dec, t_decstep = [], [], [], [], []
+
+    def one_step(record: bool):
+        if do_prefill:
+            pe[0].record(stream)
+            binding.pool_kv(q, k, v, G, scale, kc=kc, vc=vc)
+            pe[1].record(stream)
+            binding.attention(q, k, v, kc, vc, G, KL, scale, out=out)
+            pe[2].record(stream)
+        if do_decode:
+            cache.desc.n_tokens = 0
+            cache.desc.n_pooled = 0
+            cache.load_prefill(k0, v0, kc0, vc0)
+            for s in range(DEC_STEPS):
+                de[3 * s].record(stream)
+                cache.append(qs[s], ks[s], vs[s], scale)
+                de[3 * s + 1].record(stream)
+                cache.decode(qs[s], out=dout, scale=scale)
+                de[3 * s + 2].record(stream)
+        torch.cuda.synchronize()
+        if not record:
+            return
+        if do_prefill:
+            t_pool.append(pe[0].elapsed_time(pe[1]))
+            t_attn.append(pe[1].elapsed_time(pe[2]))
+        if do_decode:
+            a = sum(de[3 * s].elapsed_time(de[3 * s + 1]) for s in range(DEC_STEPS))
+            d = sum(de[3 * s + 1].elapsed_time(de[3 * s + 2]) for s in range(DEC_STEPS))
+            w = de[0].elapsed_time(de[3 * DEC_STEPS - 1])
+            t_app.append(a / DEC_STEPS)
+            t_dec.append(d / DEC_STEPS)
+            t_decstep.append(w / DEC_STEPS)
+
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")  # noqa: E731
+    res = {
+        "metric": METRIC,
+        "value": None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic: Q,K,V ~ N(0,1), 1% of key rows x4 (heavy hitters), bf16 RNE; seed {args.seed}",
+        "config": {
+            "workload": ("CCA prefill of one attention layer B=1 H=32 d=128 L=131072 g=16 k=64 bf16, then CCA "
+                         "decode B=8 H=32 d=128 context 131072 (8128..8143 core + 1025..1040 raw keys), 256 steps"),
+            "prefill": {"B": PREFILL_B, "H": H, "d": D, "L": PREFILL_L, "g": G, "k_local": KL},
+            "decode": {"B": DEC_B, "H": H, "d": D, "context": DEC_L0, "steps": DEC_STEPS, "g": G, "k_local": KL},
+            "phase": args.phase,
+        },
+    }
+    src_attn = source_hash("prefill.hip", "cca_device.h")
+    if do_prefill:
+        ms_pool, ms_attn = mean(t_pool), mean(t_attn)
+        ms_prefill = ms_pool + ms_attn
+        flops = accounting.prefill_flops(PREFILL_B, H, PREFILL_L, D, G, KL)
+        pool_b = accounting.pool_bytes(PREFILL_B, H, PREFILL_L, D, G, 2)
+        tflops = flops / (ms_attn * 1e-3) / 1e12
+        res["value"] = PREFILL_B * PREFILL_L / (ms_prefill * 1e-3)
+        res["prefill"] = {
+            "ms": ms_prefill, "pool_ms": ms_pool, "attention_ms": ms_attn,
+            "attention_tflops": tflops, "attention_flops": flops,
+            "pool_gbs": pool_b / (ms_pool * 1e-3) / 1e9, "pool_bytes": pool_b,
+            "pool_hbm_frac": pool_b / (ms_pool * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        }
+        res["roofline"] = {
+            "kernel": "cca_prefill_kernel<bf16,128>",
+            "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS,
+            "traffic": load_traffic("prefill_attention", src_attn),
+            "per_unit": "4*d FLOPs per visible (query, key) pair; pairs in closed form",
+        }
+        res_b, full_b = accounting.kv_cache_bytes(PREFILL_L, G, KL, PREFILL_B, H, D, 2)
+        lib_res, lib_full = binding.kv_cache_bytes(PREFILL_L, G, KL, PREFILL_B, H, D, torch.bfloat16)
+        assert (lib_res, lib_full) == (res_b, full_b)
+        res["kv_cache"] = {"resident_bytes": res_b, "full_kv_bytes": full_b, "fraction": res_b / full_b,
+                           "reduction": 1 - res_b / full_b, "page_reduction_128k": 0.93}
+    if do_decode:
+        nchunks = cache.ws_bytes // (DEC_B * H * (D + 2) * 4)   # chunk count the library chose
+        byt = [accounting.decode_bytes(DEC_B, H, D, DEC_L0 + s, G, KL, 2, nchunks) for s in range(DEC_STEPS)]
+        mean_bytes = sum(byt) / len(byt)
+        us_dec = mean(t_dec) * 1e3
+        gbs = mean_bytes / (us_dec * 1e-6) / 1e9
+        res["decode"] = {
+            "us_per_step": mean(t_decstep) * 1e3, "append_us": mean(t_app) * 1e3, "decode_us": us_dec,
+            "bytes_per_step": mean_bytes,
+            "roofline": {"kernel": "cca_decode_split_kernel<bf16,128> + merge", "bound": "hbm", "achieved": gbs,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": load_traffic("decode", source_hash("decode.hip", "cca_device.h"))},
+        }
+        if not do_prefill:
+            res["value"] = None
+    if do_prefill and not args.no_cpu_baseline and args.phase == "all":
+        res["cpu_baseline"] = cpu_baseline(q, k, v, out, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -97,6 +97,15 @@ int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc,
                 int dt, int out_dt, hipStream_t stream);
 
 /*
+ * The attention step of cca_prefill alone, for callers that already hold the
+ * pooled core tokens of the same q, k, v (e.g. from cca_pool_kv).  Same
+ * arguments and contract as cca_prefill, except that kc and vc are read only.
+ */
+int cca_attention(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out,
+                  int B, int H, int64_t L, int d, int g, int k_local, float scale,
+                  int dt, int out_dt, hipStream_t stream);
+
+/*
  * Compressed KV cache for decode ([CCA] Triton section: the fused operator
  * serves decode with a KV cache holding core tokens plus local raw tokens;
  * compute/memory efficiency section, Fig. 3).  Plain-old-data descriptor;

@@ -7,7 +7,7 @@ does, and fails loudly if the library has not been built.
 """
 
 __all__ = [
-    "pool_kv", "prefill", "KVCache", "cache_append", "decode_step",
+    "pool_kv", "prefill", "attention", "KVCache", "cache_append", "decode_step",
     "kv_cache_bytes", "load_library", "CCAError",
 ]
 

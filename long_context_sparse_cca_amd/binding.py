@@ -57,6 +57,9 @@ EXPORTS = {
     "cca_prefill": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                                           ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                                           ctypes.c_int, ctypes.c_void_p]),
+    "cca_attention": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                            ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                            ctypes.c_int, ctypes.c_void_p]),
     "cca_cache_ring_slots": (ctypes.c_int64, [ctypes.POINTER(CacheDesc)]),
     "cca_cache_load_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                + [ctypes.c_int64, ctypes.c_void_p]),
@@ -165,6 +168,25 @@ def prefill(q, k, v, g: int, k_local: int, scale: float | None = None, out_dtype
                            scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()), "cca_prefill")
     if return_core:
         return out, kc, vc
+    return out
+
+
+def attention(q, k, v, kc, vc, g: int, k_local: int, scale: float | None = None, out_dtype=None, out=None):
+    """Attention step only, given the pooled core tokens kc, vc: cca_attention."""
+    lib = load_library()
+    B, H, L, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, (B, H, L, d), q.dtype, name)
+    m = L // g if g >= 1 else 0
+    _need(kc, (B, H, m, d), q.dtype, "kc")
+    _need(vc, (B, H, m, d), q.dtype, "vc")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    _need(out, (B, H, L, d), out_dtype, "out")
+    _check(lib.cca_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, L, d, g, k_local,
+                             scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()), "cca_attention")
     return out
 
 

@@ -62,8 +62,10 @@ int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
   return hip_status(cca::launch_pool(dt, d, q, k, v, kc, vc, (int)BH, L, g, scale, stream));
 }
 
-int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int B, int H, int64_t L,
-                int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
+namespace {
+
+int check_prefill(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out, int B,
+                  int H, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt) {
   int s = check_shape(B, H, L, d, g, dt);
   if (s != CCA_OK) return s;
   if (out_dt != CCA_F32 && out_dt != dt) return CCA_ERR_UNSUPPORTED;
@@ -72,12 +74,28 @@ int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc,
   if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
   if (BH * (L / g) >= INT32_MAX || BH * ((L + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
-  if (L == 0) return CCA_OK;
-  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, (int)BH, L, g, scale, stream);
+  return CCA_OK;
+}
+
+}  // namespace
+
+int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int B, int H, int64_t L,
+                int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
+  int s = check_prefill(q, k, v, kc, vc, out, B, H, L, d, g, k_local, scale, dt, out_dt);
+  if (s != CCA_OK || L == 0) return s;
+  const int BH = B * H;
+  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, BH, L, g, scale, stream);
   if (e != hipSuccess) return CCA_ERR_HIP;
-  e = cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, (int)BH, L, g, k_local, scale,
-                                    stream);
+  e = cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, BH, L, g, k_local, scale, stream);
   return hip_status(e);
+}
+
+int cca_attention(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out, int B, int H,
+                  int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
+  int s = check_prefill(q, k, v, kc, vc, out, B, H, L, d, g, k_local, scale, dt, out_dt);
+  if (s != CCA_OK || L == 0) return s;
+  return hip_status(cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, L, g,
+                                                  k_local, scale, stream));
 }
 
 int64_t cca_cache_ring_slots(const cca_cache_t* c) {

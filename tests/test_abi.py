@@ -76,3 +76,14 @@ def test_kv_cache_bytes_match_oracle(lib, n, g, k, B, H, d, dt):
     r, f = ctypes.c_int64(), ctypes.c_int64()
     assert lib.cca_kv_cache_bytes(n, g, k, B, H, d, dt, ctypes.byref(r), ctypes.byref(f)) == 0
     assert (r.value, f.value) == oracle.kv_cache_bytes(n, g, k, B, H, d, 2 if dt == 1 else 4)
+
+
+@pytest.mark.parametrize("L,g,k", [(131072, 16, 64), (8192, 16, 64), (256, 16, 1), (1000, 7, 3), (37, 4, 1),
+                                   (10, 16, 1), (5, 1, 0), (100, 3, 50), (4097, 64, 2)])
+def test_benchmark_pair_count_matches_oracle(L, g, k):
+    """The closed form the benchmark uses for FLOPs equals the oracle's per-query enumeration."""
+    from long_context_sparse_cca_amd import accounting
+    assert accounting.attention_pairs(L, g, k) == oracle.attention_pairs(L, g, k)
+    assert accounting.kv_cache_bytes(L, g, k, 2, 3, 64, 2) == oracle.kv_cache_bytes(L, g, k, 2, 3, 64, 2)
+    assert sum(accounting.attention_pairs(L, g, k)) == sum(
+        accounting.decode_keys(t, g, k) for t in range(L))

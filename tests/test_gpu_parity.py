@@ -158,3 +158,14 @@ def test_invalid_arguments_enqueue_nothing(gpu):
         binding.prefill(q, kk, v, 16, -1)
     with pytest.raises(binding.CCAError, match="unsupported"):
         binding.prefill(q, kk, v, 16, 1, out_dtype=torch.bfloat16)
+
+
+def test_attention_entry_matches_prefill(gpu):
+    """cca_attention on core tokens from cca_pool_kv reproduces cca_prefill bit for bit."""
+    Q, K, V = np_inputs(1, 2, 700, 128, "bf16", 14)
+    q, kk, v = (_dev(x, "bf16", gpu) for x in (Q, K, V))
+    a, kc, vc = binding.prefill(q, kk, v, 16, 3, out_dtype=torch.float32, return_core=True)
+    kc2, vc2 = binding.pool_kv(q, kk, v, 16)
+    b = binding.attention(q, kk, v, kc2, vc2, 16, 3, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2) and torch.equal(a, b)
