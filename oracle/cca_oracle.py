@@ -35,6 +35,15 @@ What is computed, per (batch, head) slice with Q, K, V of shape [L, d]:
      core tokens Kc[0:n_c] plus raw keys K[n_c*g .. t] (inclusive).
   4. Output: one softmax over the whole visible set (unified K/V).
 
+Storage precision of the core tokens (reading; recorded in the design doc): the
+core K/V are the projections of the core tokens ([P1] core K/V equation) and
+live in the KV cache ([P1] Triton section).  In a model computing in bf16 those
+are bf16 tensors, and the page's 93% KV-cache reduction at 128K (Fig. 3) is
+what 2-byte core tokens give.  `pool`, `cca_slice` and `decode_stream` therefore
+take `core_dtype`: None keeps the core tokens exact (float64); "bf16" / "f32"
+round each element once, to nearest even, to that storage type before use.
+Everything else stays float64.
+
 Readings taken where the pages are silent (recorded in the design doc too):
   * pooling temperature = the attention scale (1/sqrt(d) by default) --
     PARITY UNPINNED against the pages: every invariant below is invariant to
@@ -54,6 +63,7 @@ import numpy as np
 
 __all__ = [
     "softmax",
+    "round_storage",
     "group_query_row",
     "n_core_groups",
     "pool_weights",
@@ -82,6 +92,31 @@ def softmax(x: np.ndarray) -> np.ndarray:
     z = x - x.max(axis=-1, keepdims=True)
     e = np.exp(z)
     return e / e.sum(axis=-1, keepdims=True)
+
+
+def round_storage(x: np.ndarray, core_dtype) -> np.ndarray:
+    """Round float64 values once to the storage type of the core tokens.
+
+    None: unchanged.  "f32": IEEE float32 (numpy's cast rounds to nearest
+    even).  "bf16": the 16 high bits of the float32 pattern, ties to even,
+    computed from the float64 value directly (round-to-odd to float32 first, so
+    the double rounding cannot create a false tie).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if core_dtype is None:
+        return x
+    if core_dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if core_dtype != "bf16":
+        raise ValueError(core_dtype)
+    f = x.astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    # round-to-odd: if the float32 cast was inexact, force its last bit to 1
+    inexact = f.astype(np.float64) != x
+    u = np.where(inexact, u | 1, u)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def group_query_row(j: int, g: int) -> int:
@@ -146,13 +181,14 @@ def pool_weights(Q: np.ndarray, K: np.ndarray, g: int, scale: float) -> np.ndarr
     return A
 
 
-def pool(Q, K, V, g: int, scale: float):
+def pool(Q, K, V, g: int, scale: float, core_dtype=None):
     """Core keys and values of one slice: (Kc [m,d], Vc [m,d], weights [m,g]).
 
     [P1] global-aware pooling: core token = importance-weighted sum of the
     group's tokens (core-token equation); the core K/V are that core token
     projected by W_K and W_V (core K/V equation).  By linearity the same
     weights applied to the projected K and V give the same result.
+    `core_dtype` rounds the core K/V to their storage type (see module doc).
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -164,14 +200,14 @@ def pool(Q, K, V, g: int, scale: float):
     for j in range(m):
         Kc[j] = A[j] @ K[j * g:(j + 1) * g]
         Vc[j] = A[j] @ V[j * g:(j + 1) * g]
-    return Kc, Vc, A
+    return round_storage(Kc, core_dtype), round_storage(Vc, core_dtype), A
 
 
 # ---------------------------------------------------------------------------
 # step 3-4: attention over the unified visible set
 # ---------------------------------------------------------------------------
 
-def cca_slice(Q, K, V, g: int, k: int, scale: float) -> np.ndarray:
+def cca_slice(Q, K, V, g: int, k: int, scale: float, core_dtype=None) -> np.ndarray:
     """CCA output [L, d] of one slice, evaluated one query group at a time.
 
     [P1] global-local fusion: the core K/V of earlier groups and the raw K/V
@@ -184,7 +220,7 @@ def cca_slice(Q, K, V, g: int, k: int, scale: float) -> np.ndarray:
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     L, d = Q.shape
-    Kc, Vc, _ = pool(Q, K, V, g, scale)
+    Kc, Vc, _ = pool(Q, K, V, g, scale, core_dtype)
     out = np.empty((L, d), dtype=np.float64)
     n_groups_total = (L + g - 1) // g
     for beta in range(n_groups_total):
@@ -213,12 +249,12 @@ def _over_slices(fn, Q, K, V, *args):
     return out
 
 
-def cca(Q, K, V, g: int, k: int, scale: float | None = None) -> np.ndarray:
+def cca(Q, K, V, g: int, k: int, scale: float | None = None, core_dtype=None) -> np.ndarray:
     """CCA prefill output for arrays [..., L, d] (any leading batch/head dims)."""
     d = np.asarray(Q).shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    return _over_slices(cca_slice, Q, K, V, g, k, scale)
+    return _over_slices(cca_slice, Q, K, V, g, k, scale, core_dtype)
 
 
 def cca_masked_dense(Q, K, V, g: int, k: int, scale: float) -> np.ndarray:
@@ -303,7 +339,7 @@ def cca_row(q_t, t: int, K, V, Kc, Vc, g: int, k: int, scale: float) -> np.ndarr
 # step 5: decode through an explicit compressed cache
 # ---------------------------------------------------------------------------
 
-def decode_stream(Q, K, V, g: int, k: int, scale: float, t_begin: int = 0) -> np.ndarray:
+def decode_stream(Q, K, V, g: int, k: int, scale: float, t_begin: int = 0, core_dtype=None) -> np.ndarray:
     """Feed one slice token by token through an explicit compressed KV cache.
 
     [P1] Triton acceleration section (the operator supports the KV cache in
@@ -336,8 +372,8 @@ def decode_stream(Q, K, V, g: int, k: int, scale: float, t_begin: int = 0) -> np
             base = (beta * g) % R
             assert np.array_equal(ring_pos[base:base + g], np.arange(beta * g, beta * g + g))
             a = softmax(scale * (ring_k[base:base + g] @ Q[t]))
-            core_k.append(a @ ring_k[base:base + g])
-            core_v.append(a @ ring_v[base:base + g])
+            core_k.append(round_storage(a @ ring_k[base:base + g], core_dtype))
+            core_v.append(round_storage(a @ ring_v[base:base + g], core_dtype))
         if t < t_begin:
             continue
         n_c = max(0, t // g - k)

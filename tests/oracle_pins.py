@@ -244,3 +244,44 @@ ALL_PINS = [
     pin_kv_reduction_matches_page,
     pin_pair_count_closed_form,
 ]
+
+
+def pin_storage_rounding_is_rne(o):
+    """round_storage matches torch's float64 -> bfloat16 / float32 conversions (library routines)."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-3, 4, 20000),
+                        # exact bf16 ties: round to the even neighbour
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -8 * 1.5])])
+    # torch rounds float64 -> float32 -> bfloat16; on float32 values that is one rounding
+    x32 = x.astype(np.float32).astype(np.float64)
+    want16 = torch.from_numpy(x32).float().to(torch.bfloat16).to(torch.float64).numpy()
+    want32 = torch.from_numpy(x).to(torch.float32).to(torch.float64).numpy()
+    ok = np.array_equal(o.round_storage(x32, "bf16"), want16) and np.array_equal(o.round_storage(x, "f32"), want32)
+    ok = ok and np.array_equal(o.round_storage(x, None), x)
+    # a value just above a bf16 tie rounds up when rounded once (through float32 it would tie to even)
+    ok = ok and o.round_storage(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]), "bf16")[0] == 1.0 + 2.0 ** -7
+    # stored core tokens are the exact ones rounded once
+    Q, K, V = np_inputs(1, 1, 40, 8, "bf16", 12)
+    Kc, Vc, _ = o.pool(Q[0, 0], K[0, 0], V[0, 0], 4, 0.3)
+    Kb, Vb, _ = o.pool(Q[0, 0], K[0, 0], V[0, 0], 4, 0.3, "bf16")
+    ok = ok and np.array_equal(Kb, want_b(Kc)) and np.array_equal(Vb, want_b(Vc))
+    return bool(ok), ""
+
+
+def want_b(x):
+    return torch.from_numpy(np.asarray(x, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def pin_stored_core_decode_matches_prefill(o):
+    """With bf16 storage of the core tokens, streaming decode still reproduces prefill rows."""
+    worst = 0.0
+    for (L, g, k, d, seed) in _cases():
+        Q, K, V = np_inputs(1, 1, L, d, "bf16", seed)
+        q, kk, v = Q[0, 0], K[0, 0], V[0, 0]
+        s = 1.0 / math.sqrt(d)
+        worst = max(worst, _err(o.decode_stream(q, kk, v, g, k, s, core_dtype="bf16"),
+                                o.cca_slice(q, kk, v, g, k, s, core_dtype="bf16")))
+    return worst < TOL, f"max err {worst:.3e}"
+
+
+ALL_PINS.extend([pin_storage_rounding_is_rne, pin_stored_core_decode_matches_prefill])

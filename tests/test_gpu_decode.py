@@ -59,7 +59,7 @@ def test_decode_matches_prefill_rows(gpu, case):
     got = outs.cpu().numpy()
     for b in range(B):
         for h in range(H):
-            want = oracle.cca_slice(Q[b, h], K[b, h], V[b, h], g, k, scale)[L0:]
+            want = oracle.cca_slice(Q[b, h], K[b, h], V[b, h], g, k, scale, core_dtype=dt)[L0:]
             err = np.abs(got[:, b, h] - want).max()
             assert err <= TOL[dt], f"slice ({b},{h}) max abs err {err:.3e}"
 

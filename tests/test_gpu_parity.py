@@ -3,6 +3,8 @@
 Sizes span several 128-query tiles and key tiles, with ragged tails, k = 0,
 g = 1 (plain causal attention), windows wider than the sequence, L < g, L = 1.
 Tolerances (max-abs): fp32 inputs 1e-4; bf16 inputs with fp32 accumulation 2e-2.
+The oracle stores the core tokens in the input dtype (one rounding of the exact
+fp64 core token), the reading under which the core K/V are tensors of the model.
 """
 import math
 import sys
@@ -61,7 +63,7 @@ def test_prefill_matches_oracle(gpu, case):
     scale = 1.0 / math.sqrt(d)
     out, kc, vc = binding.prefill(q, kk, v, g, k, scale, out_dtype=torch.float32, return_core=True)
     torch.cuda.synchronize()
-    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, scale)
+    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, scale, core_dtype=dt)
     err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
     assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
     # core tokens: one rounding to the storage dtype on top of fp32 math
@@ -89,7 +91,8 @@ def test_prefill_bf16_output(gpu, case):
     q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
     out = binding.prefill(q, kk, v, g, k)
     torch.cuda.synchronize()
-    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, 1.0 / math.sqrt(d))
+    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, 1.0 / math.sqrt(d),
+                      core_dtype=dt)
     err = np.abs(out.float().cpu().numpy() - want).max()
     assert err <= TOL[dt], f"max abs err {err:.3e}"
 
