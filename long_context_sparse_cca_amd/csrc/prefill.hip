@@ -33,19 +33,26 @@ struct PrefillCfg {
   static constexpr int BN = (EB == 2) ? 64 : 32;        // keys per LDS tile
   static constexpr int NSB = BN / 32;                   // 32-key sub-blocks per tile
   static constexpr int KP = D + 16 / EB;                // K tile pitch (elements), +16 B
-  static constexpr int VP = BN + 4;                     // V^T tile pitch (elements)
+  static constexpr int VP = BN + 16 / EB;               // V^T tile pitch (elements), +16 B
   static constexpr int KPT = 8 / EB;                    // keys packed per 8-byte V^T store
-  static constexpr int CPR = D / EPC;                   // chunks per row
+  static constexpr int CPR = D / EPC;                   // 16-byte chunks per row
   static constexpr int KCH = BN * CPR / NT;             // K chunks per thread
-  static constexpr int VUNITS = (BN / KPT) * CPR;       // V^T transpose units
+  static constexpr int KG = BN / KPT;                   // key groups per V tile
+  static constexpr int VUNITS = KG * CPR;               // V^T transpose units
   static constexpr int VU = (VUNITS + NT - 1) / NT;     // units per thread
   static constexpr int NDT = D / 32;                    // 32-wide output tiles along d
-  static constexpr int LDS_K = BN * KP;                 // elements
+  static constexpr int LDS_K = BN * KP;                 // elements per buffer
   static constexpr int LDS_V = D * VP;
   static_assert(BN * CPR % NT == 0, "K tile must split evenly");
 };
 
 enum : int { kSkip = 0, kFull = 1, kMask = 2 };
+
+// Running-max threshold (log2 units) below which the accumulators are not
+// rescaled: exp2(s - m_run) then stays <= 2^8, far from overflow in fp32 and
+// bf16, and the final division by the row sum is exact in real arithmetic for
+// any reference point, so skipping the rescale changes nothing but rounding.
+constexpr float kRescaleThreshold = 8.0f;
 
 // Workgroup -> (slice, query tile).  Consecutive workgroups are dealt round-robin
 // to the 8 XCDs; when the grid divides evenly, XCD x gets a contiguous range of
@@ -59,14 +66,22 @@ __device__ __forceinline__ void map_block(int nblocks, int ntiles, int& bh, int&
   tile = ntiles - 1 - (li - bh * ntiles);
 }
 
+// Column of key j (0..BN-1) in a bf16 V^T row.  Inside each 16-key chunk the
+// quads are stored in the order (0-3, 8-11, 4-7, 12-15): lane half hf of the PV
+// product then reads its 8 keys {4hf..4hf+3, 8+4hf..8+4hf+3} as one 16-byte load.
+__device__ __forceinline__ int vt_col_bf16(int quad) {  // quad = first key / 4
+  const int q4 = quad & 3;
+  return (quad >> 2) * 16 + (q4 & 1) * 8 + (q4 >> 1) * 4;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void cca_prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ Kc, const T* __restrict__ Vc, void* __restrict__ Out, int out_f32,
     int BH, int64_t L, int g, int k_local, float scale, int ntiles) {
   using C = PrefillCfg<T, D>;
-  __shared__ __attribute__((aligned(16))) T lds_k[C::LDS_K];
-  __shared__ __attribute__((aligned(16))) T lds_v[C::LDS_V];
+  __shared__ __attribute__((aligned(16))) T lds_k[2][C::LDS_K];
+  __shared__ __attribute__((aligned(16))) T lds_v[2][C::LDS_V];
 
   int bh, qtile;
   map_block(BH * ntiles, ntiles, bh, qtile);
@@ -123,20 +138,18 @@ __global__ __launch_bounds__(256) void cca_prefill_kernel(
   float m_run = kNegBig, l_run = 0.f;
   const float sc = scale * kLog2e;
 
-  // ---- tile staging: global -> registers (prefetch) -> LDS
+  // ---- tile staging: global -> registers (prefetch) -> LDS (double buffered)
   uint4 kreg[C::KCH];
   uint4 vreg[C::VU][C::KPT];
 
-  auto tile_src = [&](int it, const T*& ks, const T*& vs, int64_t& base, int64_t& lim) {
+  auto load_tile = [&](int it) {
+    const T *ks, *vs;
+    int64_t base, lim;
     if (it < n_core_tiles) {
       ks = Kcs; vs = Vcs; base = (int64_t)it * C::BN; lim = m - 1;
     } else {
       ks = Ks; vs = Vs; base = rl_wg + (int64_t)(it - n_core_tiles) * C::BN; lim = L - 1;
     }
-  };
-  auto load_tile = [&](int it) {
-    const T *ks, *vs; int64_t base, lim;
-    tile_src(it, ks, vs, base, lim);
 #pragma unroll
     for (int i = 0; i < C::KCH; ++i) {
       const int id = tid + i * C::NT;
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256) void cca_prefill_kernel(
     for (int u = 0; u < C::VU; ++u) {
       const int id = tid + u * C::NT;
       if (id < C::VUNITS) {
-        const int c = id % C::CPR, a = id / C::CPR;
+        const int a = id % C::KG, c = id / C::KG;   // key group fastest: conflict-free V^T stores
 #pragma unroll
         for (int e = 0; e < C::KPT; ++e) {
           const int64_t gr = min(base + a * C::KPT + e, lim);
@@ -157,157 +170,159 @@ __global__ __launch_bounds__(256) void cca_prefill_kernel(
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::KCH; ++i) {
       const int id = tid + i * C::NT;
       const int row = id / C::CPR, c = id % C::CPR;
-      st16(lds_k + row * C::KP + c * C::EPC, kreg[i]);
+      st16(&lds_k[buf][row * C::KP + c * C::EPC], kreg[i]);
     }
 #pragma unroll
     for (int u = 0; u < C::VU; ++u) {
       const int id = tid + u * C::NT;
       if (id < C::VUNITS) {
-        const int c = id % C::CPR, a = id / C::CPR;
+        const int a = id % C::KG, c = id / C::KG;
         // transpose: KPT keys x EPC dims -> EPC rows of KPT consecutive keys (8 bytes each)
 #pragma unroll
         for (int x = 0; x < C::EPC; ++x) {
           uint2 w;
+          int col;
           if constexpr (C::EB == 2) {
-            const uint16_t* h0 = reinterpret_cast<const uint16_t*>(&vreg[u][0]);
-            const uint16_t* h1 = reinterpret_cast<const uint16_t*>(&vreg[u][1]);
-            const uint16_t* h2 = reinterpret_cast<const uint16_t*>(&vreg[u][2]);
-            const uint16_t* h3 = reinterpret_cast<const uint16_t*>(&vreg[u][3]);
-            w.x = (uint32_t)h0[x] | ((uint32_t)h1[x] << 16);
-            w.y = (uint32_t)h2[x] | ((uint32_t)h3[x] << 16);
+            const uint32_t* h0 = reinterpret_cast<const uint32_t*>(&vreg[u][0]);
+            const uint32_t* h1 = reinterpret_cast<const uint32_t*>(&vreg[u][1]);
+            const uint32_t* h2 = reinterpret_cast<const uint32_t*>(&vreg[u][2]);
+            const uint32_t* h3 = reinterpret_cast<const uint32_t*>(&vreg[u][3]);
+            const int sh = (x & 1) * 16;
+            w.x = ((h0[x >> 1] >> sh) & 0xffffu) | (((h1[x >> 1] >> sh) & 0xffffu) << 16);
+            w.y = ((h2[x >> 1] >> sh) & 0xffffu) | (((h3[x >> 1] >> sh) & 0xffffu) << 16);
+            col = vt_col_bf16(a);
           } else {
             w.x = reinterpret_cast<const uint32_t*>(&vreg[u][0])[x];
             w.y = reinterpret_cast<const uint32_t*>(&vreg[u][1])[x];
+            col = a * C::KPT;
           }
-          *reinterpret_cast<uint2*>(lds_v + (c * C::EPC + x) * C::VP + a * C::KPT) = w;
+          *reinterpret_cast<uint2*>(&lds_v[buf][(c * C::EPC + x) * C::VP + col]) = w;
         }
       }
     }
   };
 
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(it + 1);
-    if (!wave_live) continue;
+    const int buf = it & 1;
+    if (it + 1 < n_tiles) load_tile(it + 1);   // global loads stay in flight during the compute
 
-    const bool core = it < n_core_tiles;
-    const int64_t tbase = core ? (int64_t)it * C::BN : rl_wg + (int64_t)(it - n_core_tiles) * C::BN;
-
-    int cls[C::NSB];
-    bool any = false;
+    if (wave_live) {
+      const bool core = it < n_core_tiles;
+      const int64_t tbase = core ? (int64_t)it * C::BN : rl_wg + (int64_t)(it - n_core_tiles) * C::BN;
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      const int64_t kb = tbase + sb * 32;
-      int c;
-      if (core) {
-        c = (kb >= cl_max) ? kSkip : ((kb + 32 <= cl_min) ? kFull : kMask);
-      } else {
-        if (kb + 31 < rl_min || kb > qb) c = kSkip;
-        else if (kb >= rl_max && kb + 31 <= qa) c = kFull;
-        else c = kMask;
-      }
-      cls[sb] = c;
-      any |= (c != kSkip);
-    }
-    if (!any) continue;
-
-    f32x16_t s[C::NSB];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      if (cls[sb] == kSkip) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-      if constexpr (C::EB == 2) {
-        const T* krow = lds_k + (sb * 32 + l32) * C::KP + hf * 8;
-#pragma unroll
-        for (int d16 = 0; d16 < D / 16; ++d16) {
-          bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + d16 * 16));
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, qop[d16]), s[sb], 0, 0, 0);
-        }
-      } else {
-        const T* krow = lds_k + (sb * 32 + l32) * C::KP + hf * (D / 2);
-#pragma unroll
-        for (int c4 = 0; c4 < D / 8; ++c4) {
-          const float4 a = *reinterpret_cast<const float4*>(krow + c4 * 4);
-          const float4 b = __builtin_bit_cast(float4, qop[c4]);
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, s[sb], 0, 0, 0);
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, s[sb], 0, 0, 0);
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, s[sb], 0, 0, 0);
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, s[sb], 0, 0, 0);
-        }
-      }
-      if (cls[sb] == kMask) {
+      for (int sb = 0; sb < C::NSB; ++sb) {
         const int64_t kb = tbase + sb * 32;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int64_t key = kb + 8 * i + 4 * hf + j;
-            const bool vis = core ? (key < cl_lane) : (key >= rl_lane && key <= q_lane);
-            if (!vis) s[sb][4 * i + j] = -INFINITY;
-          }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[sb][r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax * sc);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        int cls;
+        if (core) {
+          cls = (kb >= cl_max) ? kSkip : ((kb + 32 <= cl_min) ? kFull : kMask);
+        } else {
+          if (kb + 31 < rl_min || kb > qb) cls = kSkip;
+          else if (kb >= rl_max && kb + 31 <= qa) cls = kFull;
+          else cls = kMask;
+        }
+        if (cls == kSkip) continue;
 
+        // ---- S^T = K Q^T for 32 keys x 32 queries
+        f32x16_t s;
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      if (cls[sb] == kSkip) continue;
-      float p[16];
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        if constexpr (C::EB == 2) {
+          const T* krow = &lds_k[buf][(sb * 32 + l32) * C::KP + hf * 8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[sb][r], sc, -m_new));
-        l_run += p[r];
-      }
-      if constexpr (C::EB == 2) {
-        // P^T as B operand: keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u..8u+7
+          for (int d16 = 0; d16 < D / 16; ++d16) {
+            bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + d16 * 16));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, qop[d16]), s, 0, 0, 0);
+          }
+        } else {
+          const T* krow = &lds_k[buf][(sb * 32 + l32) * C::KP + hf * (D / 2)];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
-#pragma unroll
-          for (int dt = 0; dt < C::NDT; ++dt) {
-            const T* vrow = lds_v + (dt * 32 + l32) * C::VP + sb * 32 + 16 * u + 4 * hf;
-            uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb, acc[dt], 0, 0, 0);
+          for (int c4 = 0; c4 < D / 8; ++c4) {
+            const float4 a = *reinterpret_cast<const float4*>(krow + c4 * 4);
+            const float4 b = __builtin_bit_cast(float4, qop[c4]);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, s, 0, 0, 0);
           }
         }
-      } else {
-        // one single-K MFMA per S register 4i+j (key 8i+4hf+j)
+        if (cls == kMask) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int dt = 0; dt < C::NDT; ++dt) {
-            const float4 a = *reinterpret_cast<const float4*>(lds_v + (dt * 32 + l32) * C::VP + sb * 32 + 8 * i + 4 * hf);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * i + 0], acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * i + 1], acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * i + 2], acc[dt], 0, 0, 0);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * i + 3], acc[dt], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+              const int64_t key = kb + 8 * i + 4 * hf + j;
+              const bool vis = core ? (key < cl_lane) : (key >= rl_lane && key <= q_lane);
+              if (!vis) s[4 * i + j] = -INFINITY;
+            }
+        }
+
+        // ---- online softmax with a lazily moved reference point
+        float bmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) bmax = fmaxf(fmaxf(bmax, s[r]), s[r + 1]);
+        bmax = fmaxf(bmax, s[15]);
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave)) * sc;
+        if (__any(bmax > m_run + kRescaleThreshold)) {
+          const float m_new = fmaxf(m_run, bmax);
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        }
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], sc, -m_run));
+
+        if constexpr (C::EB == 2) {
+          // P^T as B operand: keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u..8u+7.
+          // The row sum takes the bf16-rounded weights, the values the MFMA multiplies.
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            bf16x8_t pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) l_run += (float)pb[e];
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+              const uint4 w = *reinterpret_cast<const uint4*>(
+                  &lds_v[buf][(dt * 32 + l32) * C::VP + sb * 32 + 16 * u + 8 * hf]);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb, acc[dt], 0, 0, 0);
+            }
           }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) l_run += p[r];
+          // one single-K MFMA per S register 4i+j (key 8i+4hf+j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+              const float4 a = *reinterpret_cast<const float4*>(
+                  &lds_v[buf][(dt * 32 + l32) * C::VP + sb * 32 + 8 * i + 4 * hf]);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, p[4 * i + 0], acc[dt], 0, 0, 0);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, p[4 * i + 1], acc[dt], 0, 0, 0);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, p[4 * i + 2], acc[dt], 0, 0, 0);
+              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, p[4 * i + 3], acc[dt], 0, 0, 0);
+            }
+        }
       }
     }
+    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   if (!wave_live) return;
