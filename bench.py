@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--phase", choices=["all", "prefill", "decode"], default="all",
-                    help="profiling aid: run only one phase (the JSON line is then not the benchmark result)")
+    ap.add_argument("--phase", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="profiling aid: run only one phase (the JSON line is then not the benchmark result); "
+                         "'copy' runs a plain 1 GiB device copy whose counter readings calibrate FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -137,6 +138,19 @@ def main():
     binding.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.phase == "copy":
+        n = 1 << 29  # bf16 elements: 1 GiB
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"phase": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "ms": dt * 1e3,
+                          "gbs": 4 * n / dt / 1e9}), flush=True)
+        return
     stream = torch.cuda.current_stream()
     scale = 1.0 / math.sqrt(D)
     do_prefill = args.phase in ("all", "prefill")
