@@ -90,7 +90,8 @@ int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
  *             or equal to dt.  Accumulation is float32; for dt = CCA_BF16 the
  *             QK^T and PV products run on bf16 matrix cores with the softmax
  *             weights rounded to bf16, for dt = CCA_F32 on float32 matrix cores.
- *   k_local >= 0 (any value >= floor((L-1)/g) gives plain causal attention).
+ *   k_local >= 0 (any value >= floor((L-1)/g) gives plain causal attention);
+ *   L <= INT32_MAX; B*H*ceil(L/128) and B*H*floor(L/g) below INT32_MAX.
  */
 int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc, void* out,
                 int B, int H, int64_t L, int d, int g, int k_local, float scale,

@@ -73,7 +73,7 @@ int check_prefill(const void* q, const void* k, const void* v, const void* kc, c
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return CCA_ERR_INVALID;
   if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
-  if (BH * (L / g) >= INT32_MAX || BH * ((L + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
+  if (L > INT32_MAX || BH * (L / g) >= INT32_MAX || BH * ((L + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
   return CCA_OK;
 }
 

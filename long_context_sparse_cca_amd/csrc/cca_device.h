@@ -81,4 +81,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // exp2(m_old - m_new) finite when a row has seen only masked keys.
 constexpr float kNegBig = -1.0e30f;
 
+// Workgroup -> (slice, query tile).  Consecutive workgroups are dealt round-robin
+// to the 8 XCDs; when the grid divides evenly, XCD x gets a contiguous range of
+// slices and, inside a slice, the query tiles from the heaviest (last) down, so
+// that the co-resident workgroups of one XCD sweep the same core K/V in its L2.
+__device__ __forceinline__ void map_block(int nblocks, int ntiles, int& bh, int& tile) {
+  const int bid = blockIdx.x;
+  int li = bid;
+  if ((nblocks & 7) == 0) li = (bid & 7) * (nblocks >> 3) + (bid >> 3);
+  bh = li / ntiles;
+  tile = ntiles - 1 - (li - bh * ntiles);
+}
+
 }  // namespace cca

@@ -15,6 +15,11 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
                                     const void* kc, const void* vc, void* out, int out_f32, int BH,
                                     int64_t L, int g, int k_local, float scale, hipStream_t stream);
 
+// bf16, head dim 128 fast path of the fused attention (prefill_bf16.hip).
+hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                                    void* out, int out_f32, int BH, int64_t L, int g, int k_local, float scale,
+                                    hipStream_t stream);
+
 hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc,
                              const void* vc, int64_t L, hipStream_t stream);
 

@@ -54,18 +54,6 @@ enum : int { kSkip = 0, kFull = 1, kMask = 2 };
 // any reference point, so skipping the rescale changes nothing but rounding.
 constexpr float kRescaleThreshold = 8.0f;
 
-// Workgroup -> (slice, query tile).  Consecutive workgroups are dealt round-robin
-// to the 8 XCDs; when the grid divides evenly, XCD x gets a contiguous range of
-// slices and, inside a slice, the query tiles from the heaviest (last) down, so
-// that the co-resident workgroups of one XCD sweep the same core K/V in its L2.
-__device__ __forceinline__ void map_block(int nblocks, int ntiles, int& bh, int& tile) {
-  const int bid = blockIdx.x;
-  int li = bid;
-  if ((nblocks & 7) == 0) li = (bid & 7) * (nblocks >> 3) + (bid >> 3);
-  bh = li / ntiles;
-  tile = ntiles - 1 - (li - bh * ntiles);
-}
-
 // Column of key j (0..BN-1) in a bf16 V^T row.  Inside each 16-key chunk the
 // quads are stored in the order (0-3, 8-11, 4-7, 12-15): lane half hf of the PV
 // product then reads its 8 keys {4hf..4hf+3, 8+4hf..8+4hf+3} as one 16-byte load.
@@ -381,7 +369,7 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
                                     const void* vc, void* out, int out_f32, int BH, int64_t L, int g,
                                     int k_local, float scale, hipStream_t stream) {
   if (dt == CCA_BF16) {
-    if (d == 128) return launch_prefill_t<bf16_t, 128>(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
+    if (d == 128) return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
     return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
   }
   if (d == 128) return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, L, g, k_local, scale, stream);

@@ -1,0 +1,306 @@
+// Fused CCA prefill attention, bf16 inputs, head dim 128: the gfx950 fast path.
+//
+// Same computation as the generic kernel in prefill.hip (the CCA write-up,
+// "ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展": query t of
+// group beta = t/g attends, in one softmax, to the core tokens Kc[0 : beta-k) and
+// the raw keys K[(beta-k)*g .. t]; locality-preserving module and global-local
+// fusion sections), restructured around three CDNA4 features:
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4): no
+//     staging registers and no VALU work to fill the tiles;
+//   * tiles stay row-major in LDS with a 16-byte XOR swizzle of the chunk index
+//     (chunk c of row r sits at c ^ swz(r)), which keeps both operand reads
+//     below free of bank conflicts without padding;
+//   * the V^T operand of the PV product is read with ds_read_b64_tr_b16, the
+//     LDS transpose read: in each 16-lane group, lane j receives element j%4 of
+//     the 8-byte pieces read by lanes 4e + j/4 (e = 0..3).  With lane s reading
+//     key row kbase + s/4, dims d0 + 4(s%4) .. +3, lane j ends up holding the
+//     four keys kbase..kbase+3 at dim d0 + j, i.e. one quarter of an MFMA A operand.
+// Softmax bookkeeping uses v_permlane32_swap for the cross-half row max / sum and
+// v_dot2_f32_bf16 against (1, 1) for the row sum of the bf16-rounded weights.
+#include "cca_internal.h"
+
+namespace cca {
+namespace {
+
+constexpr int kBM = 128;                 // queries per workgroup (4 waves x 32)
+constexpr int kBN = 64;                  // keys per tile
+constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;        // 256
+constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
+constexpr int kBufBytes = 2 * kTileBytes;    // K tile + V tile
+constexpr float kThreshold = 8.0f;       // lazy-rescale threshold (log2 units)
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 16-byte chunk swizzle of a tile row (16 chunks per 256-byte row).  Rows r and
+// r' < 16 apart get distinct values, and the 4 rows of one transpose read
+// (4-aligned) get values in distinct chunk pairs.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
+    int L, int g, int k_local, float scale, int ntiles) {
+  // one array per buffer: the LDS-DMA fill of one buffer then provably does not
+  // alias the operand reads of the other, so no wait is forced between them
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBufBytes];
+
+  int bh, qtile;
+  map_block(BH * ntiles, ntiles, bh, qtile);
+  const int m = L / g;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int q0 = qtile * kBM;
+  const int q_last = min(q0 + kBM - 1, L - 1);
+  const int nc_wg = max(0, q_last / g - k_local);        // core tokens any row sees
+  const int rl_wg = max(0, q0 / g - k_local) * g;        // first raw key any row sees
+  const int n_core_tiles = (nc_wg + kBN - 1) / kBN;
+  const int n_raw_tiles = (q_last - rl_wg + kBN) / kBN;
+  const int n_tiles = n_core_tiles + n_raw_tiles;
+
+  // ---- this wave's 32 queries (wave-uniform bounds in scalar registers)
+  const int qa = q0 + wave * 32;
+  const bool wave_live = qa < L;
+  const int qb = min(qa + 31, L - 1);
+  const int cl_min = qa / g - k_local, cl_max = qb / g - k_local;
+  const int rl_min = max(0, cl_min) * g, rl_max = max(0, cl_max) * g;
+  const int q_lane = min(qa + l32, L - 1);
+  const int cl_lane = q_lane / g - k_local;              // core j visible iff j < cl_lane
+  const int rl_lane = max(0, cl_lane) * g;               // raw u visible iff rl_lane <= u <= q_lane
+
+  const size_t slice = (size_t)bh * L * kD;
+  const bf16_t* Ks = K + slice;
+  const bf16_t* Vs = V + slice;
+  const bf16_t* Kcs = Kc + (size_t)bh * m * kD;
+  const bf16_t* Vcs = Vc + (size_t)bh * m * kD;
+
+  // ---- Q operand (B of S^T = K Q^T): slice d16 holds dims 16*d16 + 8*hf .. +8
+  uint4 qop[kD / 16];
+  {
+    const bf16_t* qrow = Q + slice + (size_t)q_lane * kD;
+#pragma unroll
+    for (int s = 0; s < kD / 16; ++s) qop[s] = ld16(qrow + s * 16 + hf * 8);
+  }
+
+  // ---- tile fill: wave w, instruction i writes rows 16w + 4i .. +3 (1 KB of LDS);
+  // lane l lands in physical chunk l%16 of row 16w + 4i + l/16 and so fetches the
+  // logical chunk (l%16) ^ swz(row).
+  int fill_row[4], fill_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 16 + i * 4 + (lane >> 4);
+    fill_row[i] = r;
+    fill_off[i] = ((lane & 15) ^ swz(r)) * 16;
+  }
+  auto issue_tile = [&](int it, int buf) {
+    const bf16_t *ks, *vs;
+    int base, lim;
+    if (it < n_core_tiles) {
+      ks = Kcs; vs = Vcs; base = it * kBN; lim = m - 1;
+    } else {
+      ks = Ks; vs = Vs; base = rl_wg + (it - n_core_tiles) * kBN; lim = L - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t goff = (size_t)min(base + fill_row[i], lim) * kRowBytes + fill_off[i];
+      uint8_t* dst = (buf ? lds1 : lds0) + (wave * 16 + i * 4) * kRowBytes;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)ks + goff),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)vs + goff),
+                                       (__attribute__((address_space(3))) void*)(dst + kTileBytes), 16, 0, 0);
+    }
+  };
+
+  // ---- operand read offsets inside a tile (bytes)
+  // K (A of QK^T): row l32 of the sub-block, logical chunk 2*d16 + hf.
+  int koff[kD / 16];
+#pragma unroll
+  for (int d16 = 0; d16 < kD / 16; ++d16) koff[d16] = l32 * kRowBytes + (((2 * d16 + hf) ^ swz(l32)) * 16);
+  // V (A of V^T P^T via transpose reads): 16-lane group G = lane/16 covers dims
+  // dt*32 + 16*(G&1) .. +15 for the four keys 16u + 4*(G>>1) + 8*r .. +3.
+  int voff[2][kD / 32];
+  {
+    const int s = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 4 * (grp >> 1) + 8 * r + (s >> 2);
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const int chunk = dt * 4 + 2 * (grp & 1) + ((s & 3) >> 1);
+        voff[r][dt] = row * kRowBytes + ((chunk ^ swz(row)) * 16) + (s & 1) * 8;
+      }
+    }
+  }
+
+  f32x16_t acc[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = kNegBig, l_run = 0.f;
+  const float sc = scale * kLog2e;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Visible window [lo, lo + span] of each lane in the key index space of a tile kind:
+  // core key j visible iff 0 <= j <= cl_lane - 1 (empty when cl_lane <= 0, encoded
+  // with a base below every key index); raw key u iff rl_lane <= u <= q_lane.
+  const int core_lo = (cl_lane > 0) ? 0 : -0x40000000;
+  const unsigned core_span = (unsigned)max(cl_lane - 1, 0);
+  const unsigned raw_span = (unsigned)(q_lane - rl_lane);
+
+  auto compute_tile = [&](const uint8_t* kt, const uint8_t* vt, int it) {
+    const bool core = it < n_core_tiles;
+    const int tbase = core ? it * kBN : rl_wg + (it - n_core_tiles) * kBN;
+    const int lo = core ? core_lo : rl_lane;
+    const unsigned span = core ? core_span : raw_span;
+#pragma unroll
+    for (int sb = 0; sb < kBN / 32; ++sb) {
+      const int kb = tbase + sb * 32;
+      int cls;
+      if (core) {
+        cls = (kb >= cl_max) ? 0 : ((kb + 32 <= cl_min) ? 1 : 2);
+      } else {
+        if (kb + 31 < rl_min || kb > qb) cls = 0;
+        else if (kb >= rl_max && kb + 31 <= qa) cls = 1;
+        else cls = 2;
+      }
+      if (cls == 0) continue;
+
+      f32x16_t s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int d16 = 0; d16 < kD / 16; ++d16) {
+        const uint4 a = *reinterpret_cast<const uint4*>(kt + sb * 32 * kRowBytes + koff[d16]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, qop[d16]), s, 0, 0, 0);
+      }
+      if (cls == 2) {
+        // key = kb + 8i + 4hf + j; visible iff (unsigned)(key - lo) <= span
+        const int k0 = kb + 4 * hf - lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool vis = (unsigned)(k0 + 8 * i + j) <= span;
+            s[4 * i + j] = vis ? s[4 * i + j] : -INFINITY;
+          }
+      }
+
+      float bmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) bmax = fmaxf(fmaxf(bmax, s[r]), s[r + 1]);
+      bmax = fmaxf(bmax, s[15]);
+      bmax = xhalf_max(bmax) * sc;
+      if (__builtin_amdgcn_ballot_w64(bmax > m_run + kThreshold) != 0) {
+        const float m_new = fmaxf(m_run, bmax);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
+
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // P^T (B operand): keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u .. 8u+7
+        bf16x2_t pp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[8 * u + 2 * e], sc, -m_run));
+          const float p1 = fast_exp2(fmaf(s[8 * u + 2 * e + 1], sc, -m_run));
+          pp[e] = bf16x2_t{(__bf16)p0, (__bf16)p1};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
+        }
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pp);
+        const int vrow = (sb * 32 + 16 * u) * kRowBytes;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt) {
+          const v4s_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s_t*)(vt + vrow + voff[0][dt]));
+          const v4s_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s_t*)(vt + vrow + voff[1][dt]));
+          const v4s_t both[2] = {lo4, hi4};
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both), pb, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (n_tiles > 0) issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed in LDS
+  __syncthreads();
+  // two tiles per trip, buffer 0 then buffer 1, so the accumulators flow straight through
+  for (int it = 0; it < n_tiles; it += 2) {
+    if (it + 1 < n_tiles) issue_tile(it + 1, 1);  // lands while tile `it` is being used
+    if (wave_live) compute_tile(lds0, lds0 + kTileBytes, it);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    if (it + 2 < n_tiles) issue_tile(it + 2, 0);
+    if (wave_live) compute_tile(lds1, lds1 + kTileBytes, it + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  // ---- normalise and store: lane (query l32, half hf) holds O[q][dt*32 + 8i + 4hf + j]
+  const float inv = 1.0f / xhalf_sum(l_run);
+  const int q_row = qa + l32;
+  if (q_row >= L) return;
+  if (out_f32) {
+    float* o = reinterpret_cast<float*>(Out) + slice + (size_t)q_row * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = make_float4(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv, acc[dt][4 * i + 2] * inv,
+                                     acc[dt][4 * i + 3] * inv);
+        *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) = v;
+      }
+  } else {
+    bf16_t* o = reinterpret_cast<bf16_t*>(Out) + slice + (size_t)q_row * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv);
+        w.y = pack_bf16x2(acc[dt][4 * i + 2] * inv, acc[dt][4 * i + 3] * inv);
+        *reinterpret_cast<uint2*>(o + dt * 32 + 8 * i + 4 * hf) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                                    void* out, int out_f32, int BH, int64_t L, int g, int k_local, float scale,
+                                    hipStream_t stream) {
+  const int ntiles = (int)((L + kBM - 1) / kBM);
+  const int64_t nblocks = (int64_t)BH * ntiles;
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, (const bf16_t*)q,
+                     (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out, out_f32, BH,
+                     (int)L, g, k_local, scale, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace cca
