@@ -33,10 +33,13 @@ constexpr float kThreshold = 8.0f;       // lazy-rescale threshold (log2 units)
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// 16-byte chunk swizzle of a tile row (16 chunks per 256-byte row).  Rows r and
-// r' < 16 apart get distinct values, and the 4 rows of one transpose read
-// (4-aligned) get values in distinct chunk pairs.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// 16-byte chunk swizzle of a tile row (16 chunks per 256-byte row).  It is a
+// bijection on any 16 consecutive rows (the K operand read: 16 lanes, 16 rows, one
+// logical chunk), and the 4 rows of one transpose read (4-aligned, 4 logical chunks
+// per row across a 32-lane pass) land in 4 distinct 64-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -100,12 +103,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- tile fill: wave w, instruction i writes rows 16w + 4i .. +3 (1 KB of LDS);
   // lane l lands in physical chunk l%16 of row 16w + 4i + l/16 and so fetches the
   // logical chunk (l%16) ^ swz(row).
-  int fill_row[4], fill_off[4];
+  int fill_row[4], fill_off[4], fill_lin[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 16 + i * 4 + (lane >> 4);
     fill_row[i] = r;
     fill_off[i] = ((lane & 15) ^ swz(r)) * 16;
+    fill_lin[i] = r * kRowBytes + fill_off[i];
   }
   auto issue_tile = [&](int it, int buf) {
     const bf16_t *ks, *vs;
@@ -115,14 +119,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
       ks = Ks; vs = Vs; base = rl_wg + (it - n_core_tiles) * kBN; lim = L - 1;
     }
+    uint8_t* dst0 = (buf ? lds1 : lds0) + wave * 16 * kRowBytes;
+    if (base + kBN - 1 <= lim) {
+      // whole tile in range: uniform tile base + per-lane 32-bit offset
+      const uint8_t* kt = (const uint8_t*)ks + (size_t)base * kRowBytes;
+      const uint8_t* vt = (const uint8_t*)vs + (size_t)base * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t goff = (size_t)min(base + fill_row[i], lim) * kRowBytes + fill_off[i];
-      uint8_t* dst = (buf ? lds1 : lds0) + (wave * 16 + i * 4) * kRowBytes;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)ks + goff),
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)vs + goff),
-                                       (__attribute__((address_space(3))) void*)(dst + kTileBytes), 16, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        uint8_t* dst = dst0 + i * 4 * kRowBytes;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + fill_lin[i]),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vt + fill_lin[i]),
+                                         (__attribute__((address_space(3))) void*)(dst + kTileBytes), 16, 0, 0);
+      }
+    } else {
+      // last tile of a range: rows past the end repeat the last valid row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t goff = (size_t)min(base + fill_row[i], lim) * kRowBytes + fill_off[i];
+        uint8_t* dst = dst0 + i * 4 * kRowBytes;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)ks + goff),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)vs + goff),
+                                         (__attribute__((address_space(3))) void*)(dst + kTileBytes), 16, 0, 0);
+      }
     }
   };
 
@@ -202,9 +222,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
       }
 
-      float bmax = fmaxf(fmaxf(s[0], s[1]), s[2]);
+      float bmax = max3f(s[0], s[1], s[2]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) bmax = fmaxf(fmaxf(bmax, s[r]), s[r + 1]);
+      for (int r = 3; r < 15; r += 2) bmax = max3f(bmax, s[r], s[r + 1]);
       bmax = fmaxf(bmax, s[15]);
       bmax = xhalf_max(bmax) * sc;
       if (__builtin_amdgcn_ballot_w64(bmax > m_run + kThreshold) != 0) {
