@@ -245,7 +245,7 @@ def main():
             "phase": args.phase,
         },
     }
-    src_attn = source_hash("prefill.hip", "cca_device.h")
+    src_attn = source_hash("prefill.hip", "prefill_bf16.hip", "cca_device.h")
     if do_prefill:
         ms_pool, ms_attn = mean(t_pool), mean(t_attn)
         ms_prefill = ms_pool + ms_attn
@@ -260,7 +260,7 @@ def main():
             "pool_hbm_frac": pool_b / (ms_pool * 1e-3) / 1e9 / PEAK_HBM_GBS,
         }
         res["roofline"] = {
-            "kernel": "cca_prefill_kernel<bf16,128>",
+            "kernel": "cca_prefill_bf16_d128_kernel",
             "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS,
             "traffic": load_traffic("prefill_attention", src_attn),

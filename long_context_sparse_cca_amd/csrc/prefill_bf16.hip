@@ -17,18 +17,26 @@
 //     four keys kbase..kbase+3 at dim d0 + j, i.e. one quarter of an MFMA A operand.
 // Softmax bookkeeping uses v_permlane32_swap for the cross-half row max / sum and
 // v_dot2_f32_bf16 against (1, 1) for the row sum of the bf16-rounded weights.
+// A workgroup is 8 waves (256 queries, 2 waves per SIMD) sharing each K/V tile;
+// each wave raises its priority while it issues its MFMA burst so that the two
+// waves of a SIMD tend to alternate between matrix and vector work.
 #include "cca_internal.h"
 
 namespace cca {
 namespace {
 
-constexpr int kBM = 128;                 // queries per workgroup (4 waves x 32)
+constexpr int kBM = 256;                 // queries per workgroup (8 waves x 32)
 constexpr int kBN = 64;                  // keys per tile
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;        // 256
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
 constexpr int kBufBytes = 2 * kTileBytes;    // K tile + V tile
-constexpr float kThreshold = 8.0f;       // lazy-rescale threshold (log2 units)
+// Lazy rescaling: the reference point of the exponentials moves only when a row's
+// max exceeds it by more than this (log2 units).  The weights then stay <= 2^16,
+// so the fp32 row sums and accumulators cannot overflow unless the sum of |V| over
+// a row exceeds ~2^112; the final division by the row sum makes the result
+// independent of the reference point up to rounding.
+constexpr float kThreshold = 16.0f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -50,7 +58,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
     int L, int g, int k_local, float scale, int ntiles) {
@@ -100,13 +108,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int s = 0; s < kD / 16; ++s) qop[s] = ld16(qrow + s * 16 + hf * 8);
   }
 
-  // ---- tile fill: wave w, instruction i writes rows 16w + 4i .. +3 (1 KB of LDS);
-  // lane l lands in physical chunk l%16 of row 16w + 4i + l/16 and so fetches the
+  // ---- tile fill: wave w, instruction i writes rows 8w + 4i .. +3 (1 KB of LDS);
+  // lane l lands in physical chunk l%16 of row 8w + 4i + l/16 and so fetches the
   // logical chunk (l%16) ^ swz(row).
-  int fill_row[4], fill_off[4], fill_lin[4];
+  int fill_row[2], fill_off[2], fill_lin[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 16 + i * 4 + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int r = wave * 8 + i * 4 + (lane >> 4);
     fill_row[i] = r;
     fill_off[i] = ((lane & 15) ^ swz(r)) * 16;
     fill_lin[i] = r * kRowBytes + fill_off[i];
@@ -119,13 +127,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
       ks = Ks; vs = Vs; base = rl_wg + (it - n_core_tiles) * kBN; lim = L - 1;
     }
-    uint8_t* dst0 = (buf ? lds1 : lds0) + wave * 16 * kRowBytes;
+    uint8_t* dst0 = (buf ? lds1 : lds0) + wave * 8 * kRowBytes;
     if (base + kBN - 1 <= lim) {
       // whole tile in range: uniform tile base + per-lane 32-bit offset
       const uint8_t* kt = (const uint8_t*)ks + (size_t)base * kRowBytes;
       const uint8_t* vt = (const uint8_t*)vs + (size_t)base * kRowBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         uint8_t* dst = dst0 + i * 4 * kRowBytes;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kt + fill_lin[i]),
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
       // last tile of a range: rows past the end repeat the last valid row
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         const size_t goff = (size_t)min(base + fill_row[i], lim) * kRowBytes + fill_off[i];
         uint8_t* dst = dst0 + i * 4 * kRowBytes;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)ks + goff),
@@ -201,15 +209,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       if (cls == 0) continue;
 
+      // all K operand reads in flight at once, then the MFMA chain consumes them in order
+      uint4 ka[kD / 16];
+#pragma unroll
+      for (int d16 = 0; d16 < kD / 16; ++d16)
+        ka[d16] = *reinterpret_cast<const uint4*>(kt + sb * 32 * kRowBytes + koff[d16]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       f32x16_t s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-      for (int d16 = 0; d16 < kD / 16; ++d16) {
-        const uint4 a = *reinterpret_cast<const uint4*>(kt + sb * 32 * kRowBytes + koff[d16]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+      for (int d16 = 0; d16 < kD / 16; ++d16)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[d16]),
                                                     __builtin_bit_cast(bf16x8_t, qop[d16]), s, 0, 0, 0);
-      }
+      // V operand transpose reads for this sub-block, issued behind the QK MFMAs so
+      // their latency hides under the softmax arithmetic
+      v4s_t vop[2][2][kD / 32];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int dt = 0; dt < kD / 32; ++dt)
+            vop[u][r][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
+                vt + (sb * 32 + 16 * u) * kRowBytes + voff[r][dt]));
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       if (cls == 2) {
         // key = kb + 8i + 4hf + j; visible iff (unsigned)(key - lo) <= span
         const int k0 = kb + 4 * hf - lo;
@@ -250,14 +276,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
         }
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pp);
-        const int vrow = (sb * 32 + 16 * u) * kRowBytes;
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
-          const v4s_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s_t*)(vt + vrow + voff[0][dt]));
-          const v4s_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s_t*)(vt + vrow + voff[1][dt]));
-          const v4s_t both[2] = {lo4, hi4};
+          const v4s_t both[2] = {vop[u][0][dt], vop[u][1][dt]};
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both), pb, acc[dt], 0, 0, 0);
         }
       }
@@ -317,7 +338,7 @@ hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v,
   const int ntiles = (int)((L + kBM - 1) / kBM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, (const bf16_t*)q,
+  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel, dim3((unsigned)nblocks), dim3(512), 0, stream, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out, out_f32, BH,
                      (int)L, g, k_local, scale, ntiles);
   return hipGetLastError();
