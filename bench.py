@@ -5,7 +5,8 @@ One step = one pass of the whole hot path on synthetic inputs:
   * prefill of one attention layer, B=1, H=32, d=128, L=131072, g=16, k=64, bf16:
     pooling into core tokens (cca_pool_kv) + fused core/local attention (cca_attention);
   * decode, B=8, H=32, d=128, context 131072 tokens held as core tokens plus a
-    1040-slot raw ring: 256 steps of append (pooling every 16th step) + decode.
+    1040-slot raw ring: 256 steps, each one launch that appends the token (pooling
+    every 16th step) and computes its attention (cca_cache_append_decode).
 The decode cache is re-seeded from the prefilled state before each step's
 decode phase (outside the per-phase timings).
 
@@ -179,8 +180,8 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     pe = [ev() for _ in range(3)]
-    de = [ev() for _ in range(3 * DEC_STEPS)]
-    t_pool, t_attn, t_app, t_dec, t_decstep = [], [], [], [], []
+    de = [ev() for _ in range(2 * DEC_STEPS)]
+    t_pool, t_attn, t_dec, t_decstep = [], [], [], []
 
     def one_step(record: bool):
         if do_prefill:
@@ -194,11 +195,9 @@ def main():
             cache.desc.n_pooled = 0
             cache.load_prefill(k0, v0, kc0, vc0)
             for s in range(DEC_STEPS):
-                de[3 * s].record(stream)
-                cache.append(qs[s], ks[s], vs[s], scale)
-                de[3 * s + 1].record(stream)
-                cache.decode(qs[s], out=dout, scale=scale)
-                de[3 * s + 2].record(stream)
+                de[2 * s].record(stream)
+                cache.append_decode(qs[s], ks[s], vs[s], out=dout, scale=scale)
+                de[2 * s + 1].record(stream)
         torch.cuda.synchronize()
         if not record:
             return
@@ -206,12 +205,10 @@ def main():
             t_pool.append(pe[0].elapsed_time(pe[1]))
             t_attn.append(pe[1].elapsed_time(pe[2]))
         if do_decode:
-            a = sum(de[3 * s].elapsed_time(de[3 * s + 1]) for s in range(DEC_STEPS))
-            d = sum(de[3 * s + 1].elapsed_time(de[3 * s + 2]) for s in range(DEC_STEPS))
-            w = de[0].elapsed_time(de[3 * DEC_STEPS - 1])
-            t_app.append(a / DEC_STEPS)
-            t_dec.append(d / DEC_STEPS)
-            t_decstep.append(w / DEC_STEPS)
+            d = sum(de[2 * s].elapsed_time(de[2 * s + 1]) for s in range(DEC_STEPS))
+            w = de[0].elapsed_time(de[2 * DEC_STEPS - 1])
+            t_dec.append(d / DEC_STEPS)       # kernel time per step
+            t_decstep.append(w / DEC_STEPS)   # step-to-step time, launch gaps included
 
     for _ in range(args.warmup):
         one_step(False)
@@ -278,11 +275,12 @@ def main():
         us_dec = mean(t_dec) * 1e3
         gbs = mean_bytes / (us_dec * 1e-6) / 1e9
         res["decode"] = {
-            "us_per_step": mean(t_decstep) * 1e3, "append_us": mean(t_app) * 1e3, "decode_us": us_dec,
+            "us_per_step": mean(t_decstep) * 1e3, "kernel_us": us_dec, "chunks": nchunks,
             "bytes_per_step": mean_bytes,
-            "roofline": {"kernel": "cca_decode_split_kernel<bf16,128> + merge", "bound": "hbm", "achieved": gbs,
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                         "traffic": load_traffic("decode", source_hash("decode.hip", "cca_device.h"))},
+            "roofline": {"kernel": "cca_decode_kernel<bf16,128,append> + cca_decode_merge_kernel",
+                         "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": load_traffic("decode", source_hash("decode.hip", "pool_group.h", "cca_device.h"))},
         }
         if not do_prefill:
             res["value"] = None

@@ -158,8 +158,9 @@ int cca_cache_load_prefill(cca_cache_t* c, const void* k, const void* v,
 int cca_cache_append(cca_cache_t* c, const void* q, const void* k, const void* v,
                      float scale, hipStream_t stream);
 
-/* Bytes of device workspace cca_decode_step needs for this cache (depends only
- * on B, H, d and the capacity max_groups + ring slots). */
+/* Bytes of device workspace cca_decode_step / cca_cache_append_decode need for
+ * this cache (depends only on B, H, d and the capacity max_groups + ring
+ * slots).  0 for an invalid descriptor. */
 size_t cca_decode_workspace_bytes(const cca_cache_t* c);
 
 /*
@@ -169,13 +170,31 @@ size_t cca_decode_workspace_bytes(const cca_cache_t* c);
  *               appended last (call cca_cache_append first).
  *   out       : device [B, H, d] of out_dt (CCA_F32 or the cache dtype).
  *   workspace : device, >= cca_decode_workspace_bytes(c) bytes, 16-byte
- *               aligned; scratch for per-chunk partial softmax states, no
- *               contents needed on entry, clobbered on return.
+ *               aligned: per-chunk partial softmax states; no contents needed
+ *               on entry, clobbered on return (concurrent calls sharing a
+ *               workspace race).
+ * The visible keys of each (b,h) are split into chunks handled by separate
+ * workgroups; a second, small kernel merges their partial states.
  * Reads the cache only.  Requires n_tokens >= 1.
  */
 int cca_decode_step(const cca_cache_t* c, const void* q, void* out, int out_dt,
                     void* workspace, size_t workspace_bytes, float scale,
                     hipStream_t stream);
+
+/*
+ * cca_cache_append followed by cca_decode_step, in one launch: appends the
+ * token (q, k, v: device [B, H, d]) exactly as cca_cache_append does (ring slot,
+ * in-place pooling of a completed group) and writes its attention output to
+ * out.  The new token's key/value are read from k, v for its own attention; a
+ * group pooled by this call is not yet visible to this token (it is still in
+ * the raw window), so the result equals the two-call sequence.  Same
+ * workspace contract as cca_decode_step; same CCA_ERR_CAPACITY rule as
+ * cca_cache_append.  Updates n_tokens/n_pooled after a successful launch.
+ * (Two kernel launches instead of three.)
+ */
+int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const void* v,
+                            void* out, int out_dt, void* workspace, size_t workspace_bytes,
+                            float scale, hipStream_t stream);
 
 /*
  * KV-cache accounting ([CCA] compute/memory efficiency, Fig. 3: the cache

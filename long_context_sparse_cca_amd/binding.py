@@ -68,6 +68,8 @@ EXPORTS = {
     "cca_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc)]),
     "cca_decode_step": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
+    "cca_cache_append_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
+                                + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
     "cca_kv_cache_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_int64)]),
@@ -237,6 +239,21 @@ class KVCache:
             _need(t, (B, H, d), self.dtype, name)
         _check(_lib.cca_cache_append(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), scale, _stream()),
                "cca_cache_append")
+
+    def append_decode(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
+        """Append one token and return its attention output [B,H,d] (one launch)."""
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, (B, H, d), self.dtype, name)
+        if out is None:
+            out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+        _need(out, (B, H, d), out_dtype, "out")
+        _check(_lib.cca_cache_append_decode(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                            _dtype_code(out_dtype), _ptr(self.workspace), self.ws_bytes, scale,
+                                            _stream()), "cca_cache_append_decode")
+        return out
 
     def decode(self, q, out_dtype=None, out=None, scale: float | None = None):
         """Attention output [B,H,d] of the newest token (q: its query)."""

@@ -133,10 +133,10 @@ int cca_cache_append(cca_cache_t* c, const void* q, const void* k, const void* v
 }
 
 size_t cca_decode_workspace_bytes(const cca_cache_t* c) {
-  if (c == nullptr || c->B < 1 || c->H < 1 || (c->d != 64 && c->d != 128)) return 0;
-  const size_t BH = (size_t)c->B * c->H;
-  const size_t nc = (size_t)cca::decode_num_chunks(c);
-  return BH * nc * ((size_t)c->d + 2) * sizeof(float);
+  if (c == nullptr || c->B < 1 || c->H < 1 || (c->d != 64 && c->d != 128) || c->g < 1 || c->k_local < 0 ||
+      c->max_groups < 1)
+    return 0;
+  return cca::decode_workspace_bytes(c);
 }
 
 int cca_decode_step(const cca_cache_t* c, const void* q, void* out, int out_dt, void* workspace,
@@ -148,6 +148,24 @@ int cca_decode_step(const cca_cache_t* c, const void* q, void* out, int out_dt, 
   if (c->n_tokens < 1) return CCA_ERR_INVALID;
   if (workspace_bytes < cca_decode_workspace_bytes(c)) return CCA_ERR_WORKSPACE;
   return hip_status(cca::launch_decode(c, q, out, out_dt == CCA_F32, workspace, scale, stream));
+}
+
+int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const void* v, void* out, int out_dt,
+                            void* workspace, size_t workspace_bytes, float scale, hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+      !isfinite(scale))
+    return CCA_ERR_INVALID;
+  const int64_t t = c->n_tokens;
+  if ((t + 1) / c->g > c->max_groups) return CCA_ERR_CAPACITY;
+  if (workspace_bytes < cca_decode_workspace_bytes(c)) return CCA_ERR_WORKSPACE;
+  hipError_t e = cca::launch_append_decode(c, q, k, v, out, out_dt == CCA_F32, workspace, scale, stream);
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  c->n_tokens = t + 1;
+  c->n_pooled = (t + 1) / c->g;
+  return CCA_OK;
 }
 
 int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt, int64_t* resident_bytes,

@@ -76,6 +76,15 @@ __device__ __forceinline__ float wave_sum_xor(float v, int lo_bit, int hi_bit) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders the LDS accesses of the lanes of one wave around this point (for LDS
+// scratch that a single wave owns): the LDS operations of a wave complete in
+// order, so a compiler-level fence plus a wave barrier suffice.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 // Finite stand-in for -infinity as the initial running max: keeps
 // exp2(m_old - m_new) finite when a row has seen only masked keys.

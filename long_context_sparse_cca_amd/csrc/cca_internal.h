@@ -27,8 +27,13 @@ hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* 
                                float scale, hipStream_t stream);
 
 int decode_num_chunks(const cca_cache_t* c);
+size_t decode_workspace_bytes(const cca_cache_t* c);
 
 hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace,
                          float scale, hipStream_t stream);
+
+// Append (ring write + in-place pooling) and decode of the new token in one launch.
+hipError_t launch_append_decode(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
+                                int out_f32, void* workspace, float scale, hipStream_t stream);
 
 }  // namespace cca

@@ -10,7 +10,8 @@
 //
 //   cca_cache_load_kernel   : seed the cache from a prefill (core tokens + raw tail)
 //   cca_append_kernel       : write the newest k,v into its ring slot; pool a completed group
-//   cca_decode_split_kernel : one chunk of the visible keys per workgroup -> (m, l, acc[d])
+//   cca_decode_kernel       : one chunk of the visible keys per workgroup -> (m, l, acc[d]);
+//                             optionally also performs the append of the new token
 //   cca_decode_merge_kernel : log-sum-exp combination of the chunk states -> out[d]
 #include <algorithm>
 
@@ -102,7 +103,7 @@ hipError_t launch_append_t(const cca_cache_t* c, const void* q, const void* k, c
 }
 
 // ---------------------------------------------------------------------------
-// split-KV decode
+// split-KV decode with the chunk merge fused in (and, optionally, the append)
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DecodeCfg {
@@ -116,15 +117,28 @@ struct DecodeCfg {
 };
 
 // Workspace layout (floats): acc [BH][NC][D], then ml [BH][NC][2] (running max in
-// log2 units, running sum).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void cca_decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ core_k, const T* __restrict__ core_v,
-    const T* __restrict__ ring_k, const T* __restrict__ ring_v, float* __restrict__ ws_acc,
-    float* __restrict__ ws_ml, int64_t max_groups, int64_t R, int64_t n_c, int64_t raw_lo, int64_t n_keys,
-    int64_t chunk, int nchunks, float scale) {
+// log2 units, running sum) of every chunk.
+struct DecodeWs {
+  float* acc;
+  float* ml;
+};
+
+// One workgroup = one chunk of the key index space [0, n_keys) of one slice:
+// keys [0, n_c) are core tokens, keys [n_c, n_keys) the raw window read from the ring
+// (with APPEND, the last key is the new token, read from the inputs).  It writes its
+// partial softmax state; cca_decode_merge_kernel combines the chunks of a slice.
+// With APPEND, wave 0 of chunk 0 also writes the new token into its ring slot and,
+// when the token completes a group, pools that group into the core array (the new
+// core token is not visible to this step, so nothing here reads it).
+template <typename T, int D, bool APPEND>
+__global__ __launch_bounds__(256) void cca_decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ core_k,
+    T* __restrict__ core_v, T* __restrict__ ring_k, T* __restrict__ ring_v, DecodeWs ws, int64_t max_groups,
+    int64_t R, int64_t t, int g, int64_t n_c, int64_t raw_lo, int64_t n_keys, int64_t chunk, int nchunks,
+    float scale) {
   using C = DecodeCfg<T, D>;
   __shared__ float red[C::NWAVE][D + 2];
+  extern __shared__ float pool_lds[];
   const int64_t bh = blockIdx.x;
   const int ci = blockIdx.y;
   const int tid = threadIdx.x;
@@ -133,9 +147,32 @@ __global__ __launch_bounds__(256) void cca_decode_split_kernel(
   const int part = lane % C::LPK;    // which 16-byte chunk of the row
   const int64_t start = (int64_t)ci * chunk;
   const int64_t end = min(n_keys, start + chunk);
+  const T* qrow = q + (size_t)bh * D;
+
+  if constexpr (APPEND) {
+    if (ci == 0 && wave == 0) {
+      const T* kt = k_new + (size_t)bh * D;
+      const T* vt = v_new + (size_t)bh * D;
+      const int64_t slot = t % R;
+      constexpr int CPR = D * (int)sizeof(T) / 16;
+      if (lane < CPR) {
+        st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bh * R + slot) * D) + lane,
+             ld16(reinterpret_cast<const uint4*>(kt) + lane));
+        st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bh * R + slot) * D) + lane,
+             ld16(reinterpret_cast<const uint4*>(vt) + lane));
+      }
+      if ((t + 1) % g == 0) {
+        const int64_t beta = t / g;
+        const int64_t first = slot - (g - 1);
+        pool_group_wave<T, D>(qrow, ring_k + ((size_t)bh * R + first) * D, ring_v + ((size_t)bh * R + first) * D,
+                              kt, vt, g, scale, core_k + ((size_t)bh * max_groups + beta) * D,
+                              core_v + ((size_t)bh * max_groups + beta) * D, pool_lds);
+      }
+    }
+  }
 
   float qf[C::EPC];
-  Elem<T>::chunk_to_f32(ld16(q + (size_t)bh * D + part * C::EPC), qf);
+  Elem<T>::chunk_to_f32(ld16(qrow + part * C::EPC), qf);
   const float sc = scale * kLog2e;
 #pragma unroll
   for (int e = 0; e < C::EPC; ++e) qf[e] *= sc;
@@ -163,6 +200,9 @@ __global__ __launch_bounds__(256) void cca_decode_split_kernel(
       if (nn < n_c) {
         kp = ck + (size_t)nn * D;
         vp = cv + (size_t)nn * D;
+      } else if (APPEND && nn == n_keys - 1) {
+        kp = k_new + (size_t)bh * D;   // the token appended by this very launch
+        vp = v_new + (size_t)bh * D;
       } else {
         const int64_t slot = (raw_lo + (nn - n_c)) % R;
         kp = rk + (size_t)slot * D;
@@ -227,7 +267,7 @@ __global__ __launch_bounds__(256) void cca_decode_split_kernel(
     }
   }
   __syncthreads();
-  // combine the waves: thread x < D owns column x
+  // combine the waves: thread x < D owns column x; publish the chunk's partial state
   const size_t rec = (size_t)bh * nchunks + ci;
   if (tid < D) {
     float M = red[0][D];
@@ -240,10 +280,10 @@ __global__ __launch_bounds__(256) void cca_decode_split_kernel(
       a = fmaf(f, red[w][tid], a);
       l = fmaf(f, red[w][D + 1], l);
     }
-    ws_acc[rec * D + tid] = a;
+    ws.acc[rec * D + tid] = a;
     if (tid == 0) {
-      ws_ml[rec * 2] = M;
-      ws_ml[rec * 2 + 1] = l;
+      ws.ml[rec * 2] = M;
+      ws.ml[rec * 2 + 1] = l;
     }
   }
 }
@@ -277,39 +317,62 @@ __global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __res
   }
 }
 
-template <typename T, int D>
-hipError_t launch_decode_t(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace,
-                           float scale, hipStream_t stream) {
+template <typename T, int D, bool APPEND>
+hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_new, const void* v_new, void* out,
+                           int out_f32, void* workspace, float scale, hipStream_t stream) {
   const int64_t BH = (int64_t)c->B * c->H;
   const int64_t R = (int64_t)(c->k_local + 1) * c->g;
-  const int64_t t = c->n_tokens - 1;
+  const int64_t t = APPEND ? c->n_tokens : c->n_tokens - 1;   // position of the query
   const int64_t n_c = std::max<int64_t>(0, t / c->g - c->k_local);
   const int64_t raw_lo = n_c * c->g;
   const int64_t n_keys = n_c + (t - raw_lo + 1);
   const int nchunks = decode_num_chunks(c);
   int64_t chunk = (n_keys + nchunks - 1) / nchunks;
   chunk = (chunk + 15) / 16 * 16;
-  float* ws_acc = (float*)workspace;
-  float* ws_ml = ws_acc + (size_t)BH * nchunks * D;
-  hipLaunchKernelGGL((cca_decode_split_kernel<T, D>), dim3((unsigned)BH, nchunks), dim3(256), 0, stream,
-                     (const T*)q, (const T*)c->core_k, (const T*)c->core_v, (const T*)c->ring_k, (const T*)c->ring_v,
-                     ws_acc, ws_ml, c->max_groups, R, n_c, raw_lo, n_keys, chunk, nchunks, scale);
+  DecodeWs ws;
+  ws.acc = (float*)workspace;
+  ws.ml = ws.acc + (size_t)BH * nchunks * D;
+  const size_t dyn_lds = APPEND ? (size_t)c->g * sizeof(float) : 0;
+  hipLaunchKernelGGL((cca_decode_kernel<T, D, APPEND>), dim3((unsigned)BH, nchunks), dim3(256), dyn_lds, stream,
+                     (const T*)q, (const T*)k_new, (const T*)v_new, (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k,
+                     (T*)c->ring_v, ws, c->max_groups, R, t, c->g, n_c, raw_lo, n_keys, chunk, nchunks, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
-  hipLaunchKernelGGL((cca_decode_merge_kernel<D>), dim3((unsigned)BH), dim3(64), 0, stream, ws_acc, ws_ml, out,
+  hipLaunchKernelGGL((cca_decode_merge_kernel<D>), dim3((unsigned)BH), dim3(64), 0, stream, ws.acc, ws.ml, out,
                      out_bf16, nchunks);
   return hipGetLastError();
+}
+
+template <bool APPEND>
+hipError_t launch_decode_any(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
+                             int out_f32, void* workspace, float scale, hipStream_t stream) {
+  if (c->dt == CCA_BF16) {
+    if (c->d == 128) return launch_decode_t<bf16_t, 128, APPEND>(c, q, k, v, out, out_f32, workspace, scale, stream);
+    return launch_decode_t<bf16_t, 64, APPEND>(c, q, k, v, out, out_f32, workspace, scale, stream);
+  }
+  if (c->d == 128) return launch_decode_t<float, 128, APPEND>(c, q, k, v, out, 1, workspace, scale, stream);
+  return launch_decode_t<float, 64, APPEND>(c, q, k, v, out, 1, workspace, scale, stream);
 }
 
 }  // namespace
 
 int decode_num_chunks(const cca_cache_t* c) {
-  // enough workgroups to keep every CU streaming, chunks of >= ~512 keys
+  // About 1024 workgroups in total (4 per CU of a 256-CU MI355X; measured best
+  // against 2..19 per slice at B=8, H=32): long contiguous chunks, all resident
+  // at once.  At least 256 keys of the cache's capacity per chunk, at most 64
+  // chunks per slice.
+  const int64_t BH = (int64_t)c->B * c->H;
   const int64_t cap = c->max_groups + (int64_t)(c->k_local + 1) * c->g;
-  int64_t n = (cap + 511) / 512;
+  int64_t n = (1024 + BH - 1) / BH;
+  n = std::min<int64_t>(n, std::max<int64_t>(1, cap / 256));
   n = std::max<int64_t>(1, std::min<int64_t>(n, 64));
   return (int)n;
+}
+
+size_t decode_workspace_bytes(const cca_cache_t* c) {
+  const size_t BH = (size_t)c->B * c->H;
+  return BH * (size_t)decode_num_chunks(c) * ((size_t)c->d + 2) * sizeof(float);
 }
 
 hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc, const void* vc,
@@ -337,12 +400,12 @@ hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* 
 
 hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace, float scale,
                          hipStream_t stream) {
-  if (c->dt == CCA_BF16) {
-    if (c->d == 128) return launch_decode_t<bf16_t, 128>(c, q, out, out_f32, workspace, scale, stream);
-    return launch_decode_t<bf16_t, 64>(c, q, out, out_f32, workspace, scale, stream);
-  }
-  if (c->d == 128) return launch_decode_t<float, 128>(c, q, out, 1, workspace, scale, stream);
-  return launch_decode_t<float, 64>(c, q, out, 1, workspace, scale, stream);
+  return launch_decode_any<false>(c, q, nullptr, nullptr, out, out_f32, workspace, scale, stream);
+}
+
+hipError_t launch_append_decode(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
+                                int out_f32, void* workspace, float scale, hipStream_t stream) {
+  return launch_decode_any<true>(c, q, k, v, out, out_f32, workspace, scale, stream);
 }
 
 }  // namespace cca

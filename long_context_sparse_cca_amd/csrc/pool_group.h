@@ -29,11 +29,12 @@ __device__ __forceinline__ void load_n(const T* p, float* f) {
   }
 }
 
-// One wave (64 lanes, the whole workgroup) pools rows 0..g-1 of a group.
+// One wave pools rows 0..g-1 of a group (the other waves of its workgroup, if
+// any, are not involved: only wave-level synchronisation is used).
 //   rows r < g-1 are read at k_rows + r*D / v_rows + r*D; row g-1 at k_last / v_last
 //   (the decode cache passes the newest token there, the prefill passes row g-1);
 //   q_hat is the query of the group's last token;
-//   w_lds is workgroup LDS scratch of g floats.
+//   w_lds is LDS scratch of g floats owned by this wave.
 // Math in float32; kc/vc receive one rounding to T.
 template <typename T, int D>
 __device__ __forceinline__ void pool_group_wave(const T* __restrict__ q_hat, const T* __restrict__ k_rows,
@@ -71,7 +72,7 @@ __device__ __forceinline__ void pool_group_wave(const T* __restrict__ q_hat, con
     part += __shfl_xor(part, 2, kWave);
     if (seg == 0 && r < g) w_lds[r] = part * sc;
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- softmax over the group (base-2 exponent of pre-scaled scores)
   float mx = -INFINITY;
@@ -81,9 +82,9 @@ __device__ __forceinline__ void pool_group_wave(const T* __restrict__ q_hat, con
   for (int r = lane; r < g; r += kWave) sum += fast_exp2(w_lds[r] - mx);
   sum = wave_sum_xor(sum, 1, kWave);
   const float inv = 1.0f / sum;
-  __syncthreads();
+  wave_lds_sync();
   for (int r = lane; r < g; r += kWave) w_lds[r] = fast_exp2(w_lds[r] - mx) * inv;
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- pass 2: weighted sums, each lane owns D/64 consecutive columns
   constexpr int CPL = D / kWave;

@@ -67,7 +67,9 @@ def test_validation_without_gpu(lib):
 def test_workspace_size(lib):
     d = binding.CacheDesc(16, 16, 16, 16, 8, 32, 128, 16, 64, 1, 8208, 0, 0)
     n = lib.cca_decode_workspace_bytes(ctypes.byref(d))
-    assert n > 0 and n % (8 * 32 * 130 * 4) == 0
+    assert n > 0 and n % (8 * 32 * 130 * 4) == 0   # whole chunks of (d+2)-float partial states
+    d.max_groups = 0
+    assert lib.cca_decode_workspace_bytes(ctypes.byref(d)) == 0
 
 
 @pytest.mark.parametrize("n,g,k,B,H,d,dt", [(131072, 16, 64, 1, 32, 128, 1), (1000, 7, 3, 2, 4, 64, 0),

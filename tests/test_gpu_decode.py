@@ -88,3 +88,48 @@ def test_decode_bf16_output_matches_f32_output(gpu):
     torch.cuda.synchronize()
     assert b.dtype == torch.bfloat16
     assert torch.equal(a.to(torch.bfloat16), b)
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=_id)
+def test_fused_append_decode_matches_prefill_rows(gpu, case):
+    """cca_cache_append_decode (append + attention in one launch) against the oracle and the two-call path."""
+    B, H, d, g, k, L0, T, dt, seed = case
+    print(f"fused decode case {_id(case)}", flush=True)
+    Q, K, V = np_inputs(B, H, T, d, dt, seed)
+    q, kk, v = (torch.from_numpy(x).to(device=gpu, dtype=TDT[dt]).contiguous() for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    caches = [binding.KVCache(B, H, d, g, k, max_tokens=T + g, dtype=TDT[dt], device=gpu) for _ in range(2)]
+    if L0 > 0:
+        kc, vc = binding.pool_kv(q[:, :, :L0].contiguous(), kk[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(),
+                                 g, scale)
+        for c in caches:
+            c.load_prefill(kk[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc, vc)
+    fused = torch.empty((T - L0, B, H, d), dtype=torch.float32, device=gpu)
+    split = torch.empty_like(fused)
+    for t in range(L0, T):
+        qt, kt, vt = q[:, :, t].contiguous(), kk[:, :, t].contiguous(), v[:, :, t].contiguous()
+        caches[0].append_decode(qt, kt, vt, out_dtype=torch.float32, out=fused[t - L0], scale=scale)
+        caches[1].append(qt, kt, vt, scale)
+        caches[1].decode(qt, out_dtype=torch.float32, out=split[t - L0], scale=scale)
+    torch.cuda.synchronize()
+    assert caches[0].n_tokens == T
+    # same cache contents and the same outputs as the two-call sequence
+    assert torch.equal(caches[0].ring_k, caches[1].ring_k) and torch.equal(caches[0].core_v, caches[1].core_v)
+    assert torch.equal(fused, split)
+    got = fused.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            want = oracle.cca_slice(Q[b, h], K[b, h], V[b, h], g, k, scale, core_dtype=dt)[L0:]
+            err = np.abs(got[:, b, h] - want).max()
+            assert err <= TOL[dt], f"slice ({b},{h}) max abs err {err:.3e}"
+
+
+def test_fused_append_decode_capacity_error(gpu):
+    B, H, d, g, k = 1, 1, 64, 4, 1
+    cache = binding.KVCache(B, H, d, g, k, max_tokens=8, dtype=torch.float32, device=gpu)
+    x = torch.zeros((B, H, d), device=gpu)
+    for _ in range(11):
+        cache.append_decode(x, x, x)
+    with pytest.raises(binding.CCAError, match="capacity"):
+        cache.append_decode(x, x, x)
+    assert cache.n_tokens == 11
