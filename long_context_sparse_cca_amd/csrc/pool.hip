@@ -1,6 +1,8 @@
 // Prefill pooling: every complete group of every (b,h) slice becomes one core
 // key and one core value (the CCA write-up, global-aware pooling section,
-// core-token and core K/V equations).  One wave per group; HBM-bound.
+// core-token and core K/V equations).  One wave per group; HBM-bound.  A
+// dedicated kernel covers bf16, d = 128, g = 16; other shapes use the generic
+// group routine shared with the decode cache.
 #include "cca_internal.h"
 #include "pool_group.h"
 
@@ -22,6 +24,85 @@ __global__ __launch_bounds__(64) void cca_pool_kernel(const T* __restrict__ Q, c
   pool_group_wave<T, D>(Q + last, K + base, V + base, K + last, V + last, g, scale, Kc + out, Vc + out, w_lds);
 }
 
+// bf16, d = 128, g = 16: one wave per group, every load of the group issued up
+// front.  Lane (rq = lane/16, c = lane%16) owns the 16-byte column chunk c
+// (dims 8c..8c+7) of the rows rq, rq+4, rq+8, rq+12.
+__global__ __launch_bounds__(256) void cca_pool_bf16_d128_g16_kernel(const bf16_t* __restrict__ Q,
+                                                                   const bf16_t* __restrict__ K,
+                                                                   const bf16_t* __restrict__ V,
+                                                                   bf16_t* __restrict__ Kc, bf16_t* __restrict__ Vc,
+                                                                   int64_t L, int64_t m, int64_t n_groups,
+                                                                   float scale) {
+  constexpr int D = 128, G = 16;
+  const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gid >= n_groups) return;
+  const int lane = threadIdx.x & 63;
+  const int rq = lane >> 4, c = lane & 15;
+  const int64_t bh = gid / m, j = gid - bh * m;
+  const bf16_t* kg = K + ((size_t)bh * L + (size_t)j * G) * D;
+  const bf16_t* vg = V + ((size_t)bh * L + (size_t)j * G) * D;
+  const bf16_t* qh = Q + ((size_t)bh * L + (size_t)j * G + G - 1) * D;
+  uint4 kr[4], vr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kr[i] = ld16(kg + (size_t)(rq + 4 * i) * D + 8 * c);
+    vr[i] = ld16(vg + (size_t)(rq + 4 * i) * D + 8 * c);
+  }
+  float qf[8];
+  Elem<bf16_t>::chunk_to_f32(ld16(qh + 8 * c), qf);
+  const float sc = scale * kLog2e;
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float kf[8];
+    Elem<bf16_t>::chunk_to_f32(kr[i], kf);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
+    d = wave_sum_xor(d, 1, 16);   // over the 16 column chunks of the row
+    s[i] = d * sc;
+  }
+  float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  mx = wave_max_xor(mx, 16, 64);  // over the 4 row quarters
+  float p[4], sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = fast_exp2(s[i] - mx);
+    sum += p[i];
+  }
+  sum = wave_sum_xor(sum, 16, 64);
+  const float inv = 1.0f / sum;
+  float ak[8], av[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ak[e] = av[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float kf[8], vf[8];
+    Elem<bf16_t>::chunk_to_f32(kr[i], kf);
+    Elem<bf16_t>::chunk_to_f32(vr[i], vf);
+    const float a = p[i] * inv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ak[e] = fmaf(a, kf[e], ak[e]);
+      av[e] = fmaf(a, vf[e], av[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ak[e] = wave_sum_xor(ak[e], 16, 64);
+    av[e] = wave_sum_xor(av[e], 16, 64);
+  }
+  if (rq == 0) {
+    uint4 ko, vo;
+    ko.x = pack_bf16x2(ak[0], ak[1]); ko.y = pack_bf16x2(ak[2], ak[3]);
+    ko.z = pack_bf16x2(ak[4], ak[5]); ko.w = pack_bf16x2(ak[6], ak[7]);
+    vo.x = pack_bf16x2(av[0], av[1]); vo.y = pack_bf16x2(av[2], av[3]);
+    vo.z = pack_bf16x2(av[4], av[5]); vo.w = pack_bf16x2(av[6], av[7]);
+    st16(Kc + ((size_t)bh * m + j) * D + 8 * c, ko);
+    st16(Vc + ((size_t)bh * m + j) * D + 8 * c, vo);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_pool_t(const void* q, const void* k, const void* v, void* kc, void* vc, int BH, int64_t L,
                          int g, float scale, hipStream_t stream) {
@@ -38,6 +119,14 @@ hipError_t launch_pool_t(const void* q, const void* k, const void* v, void* kc, 
 hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc, int BH,
                        int64_t L, int g, float scale, hipStream_t stream) {
   if (dt == CCA_BF16) {
+    if (d == 128 && g == 16) {
+      const int64_t m = L / 16, n = (int64_t)BH * m;
+      if (n == 0) return hipSuccess;
+      hipLaunchKernelGGL(cca_pool_bf16_d128_g16_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, L, m, n,
+                         scale);
+      return hipGetLastError();
+    }
     if (d == 128) return launch_pool_t<bf16_t, 128>(q, k, v, kc, vc, BH, L, g, scale, stream);
     return launch_pool_t<bf16_t, 64>(q, k, v, kc, vc, BH, L, g, scale, stream);
   }
