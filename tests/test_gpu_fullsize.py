@@ -93,3 +93,30 @@ def test_decode_fullsize_sampled(gpu):
             want = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
             err = np.abs(got[s, b, h] - want).max()
             assert err <= TOL_BF16, f"slice ({b},{h}) step {s}: max abs err {err:.3e}"
+
+
+def test_dense_mode_fullsize_sampled(gpu):
+    """k >= floor((L-1)/g) turns the same kernels into standard causal attention (L = 65536)."""
+    L = 65536
+    _say(f"full-size dense-mode prefill L={L}")
+    q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, gpu, seed=2, heavy_frac=0.01)
+    out = binding.prefill(q, k, v, G, L, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    scale = 1.0 / math.sqrt(D)
+    for h in (0, H - 1):
+        Q = q[0, h].float().cpu().numpy().astype(np.float64)
+        K = k[0, h].float().cpu().numpy().astype(np.float64)
+        V = v[0, h].float().cpu().numpy().astype(np.float64)
+        rows = sorted(set([0, 1, 255, 256, L // 2, L - 1] + rng.integers(0, L, 10).tolist()))
+        got = out[0, h, rows].cpu().numpy()
+        worst = 0.0
+        for i, t in enumerate(rows):
+            # plain causal softmax attention over keys 0..t (no core token is visible)
+            s = (K[:t + 1] @ Q[t]) * scale
+            p = np.exp(s - s.max())
+            want = (p / p.sum()) @ V[:t + 1]
+            err = np.abs(got[i] - want).max()
+            worst = max(worst, err)
+            assert err <= TOL_BF16, f"head {h} row {t}: max abs err {err:.3e}"
+        _say(f"dense L={L} head {h}: max err {worst:.2e}")
