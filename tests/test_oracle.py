@@ -9,3 +9,13 @@ from tests import oracle_pins
 def test_pin(pin):
     ok, detail = pin(oracle.cca_oracle)
     assert ok, detail
+
+
+import oracle.cca_serving
+from tests import serving_pins
+
+
+@pytest.mark.parametrize("pin", serving_pins.ALL_SERVING_PINS, ids=lambda f: f.__name__)
+def test_serving_pin(pin):
+    ok, detail = pin(oracle.cca_serving)
+    assert ok, detail

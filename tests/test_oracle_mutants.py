@@ -85,3 +85,46 @@ def test_some_pin_catches(name, monkeypatch):
         if not ok:
             failed.append(pin.__name__)
     assert failed, f"no pin caught mutant '{name}'"
+
+
+import oracle.cca_serving as serving
+from tests import serving_pins
+
+
+def _kv_head_modulo(h, H, H_kv):
+    return h % H_kv  # interleaved grouping instead of consecutive runs
+
+
+def _mean_is_first_head(Qh):
+    return np.asarray(Qh, np.float64)[0]
+
+
+def _mean_is_sum(Qh):
+    return np.asarray(Qh, np.float64).sum(axis=0)
+
+
+def _pool_gqa_per_head_last(Qh, K, V, g, scale, core_dtype=None):
+    return o.pool(np.asarray(Qh, np.float64)[-1], K, V, g, scale, core_dtype)
+
+
+SERVING_MUTANTS = {
+    "kv head of h is h mod H_kv": ("kv_head_of", _kv_head_modulo),
+    "pooling query is the first head's": ("mean_query", _mean_is_first_head),
+    "pooling query is the sum of the heads": ("mean_query", _mean_is_sum),
+    "gqa pooling with the last head only": ("pool_gqa", _pool_gqa_per_head_last),
+}
+
+
+@pytest.mark.parametrize("name", list(SERVING_MUTANTS))
+def test_some_serving_pin_catches(name, monkeypatch):
+    attr, fn = SERVING_MUTANTS[name]
+    monkeypatch.setattr(serving, attr, fn)
+    failed = []
+    for pin in serving_pins.ALL_SERVING_PINS:
+        try:
+            ok, _ = pin(serving)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"no serving pin caught mutant '{name}'"
