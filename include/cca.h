@@ -107,6 +107,33 @@ int cca_attention(const void* q, const void* k, const void* v, const void* kc, c
                   int dt, int out_dt, hipStream_t stream);
 
 /*
+ * Grouped-query attention (GQA): H query heads share H_kv key/value heads,
+ * H a multiple of H_kv, r = H / H_kv.  The pages define CCA for one query
+ * head per key/value head; with r > 1 this library takes the following
+ * reading (with r = 1 the calls below are exactly the ones above):
+ *   - query head h reads key/value head h / r (runs of r consecutive heads);
+ *   - a group of key/value head h_kv is pooled ONCE, scored by the mean over
+ *     its r query heads of the group's last-token query (the importance score
+ *     with a mean query of "Latent-Condensed Transformer for Efficient Long
+ *     Context Modeling", section 2; its section 3 extends that method to GQA),
+ *     so the core tokens, like the raw K/V, exist per key/value head.
+ *   q, out : device, [B, H, L, d];  k, v : device, [B, H_kv, L, d];
+ *   kc, vc : device, [B, H_kv, floor(L/g), d].
+ * Everything else (dtypes, NULL core buffers when floor(L/g) == 0, limits,
+ * error behaviour) is as for cca_pool_kv / cca_prefill / cca_attention;
+ * H_kv < 1 or H not a multiple of H_kv gives CCA_ERR_INVALID.
+ */
+int cca_pool_kv_gqa(const void* q, const void* k, const void* v, void* kc, void* vc,
+                    int B, int H, int H_kv, int64_t L, int d, int g, float scale,
+                    int dt, hipStream_t stream);
+int cca_prefill_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, void* out,
+                    int B, int H, int H_kv, int64_t L, int d, int g, int k_local, float scale,
+                    int dt, int out_dt, hipStream_t stream);
+int cca_attention_gqa(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out,
+                      int B, int H, int H_kv, int64_t L, int d, int g, int k_local, float scale,
+                      int dt, int out_dt, hipStream_t stream);
+
+/*
  * Compressed KV cache for decode ([CCA] Triton section: the fused operator
  * serves decode with a KV cache holding core tokens plus local raw tokens;
  * compute/memory efficiency section, Fig. 3).  Plain-old-data descriptor;

@@ -60,6 +60,17 @@ EXPORTS = {
     "cca_attention": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                                             ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                                             ctypes.c_int, ctypes.c_void_p]),
+    "cca_pool_kv_gqa": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "cca_prefill_gqa": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                              ctypes.c_int, ctypes.c_void_p]),
+    "cca_attention_gqa": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                                ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                                ctypes.c_int, ctypes.c_void_p]),
     "cca_cache_ring_slots": (ctypes.c_int64, [ctypes.POINTER(CacheDesc)]),
     "cca_cache_load_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                + [ctypes.c_int64, ctypes.c_void_p]),
@@ -128,67 +139,94 @@ def _core_buffer(B, H, m, d, like):
     return torch.empty((B, H, max(m, 1), d), dtype=like.dtype, device=like.device)[:, :, :m]
 
 
-def pool_kv(q, k, v, g: int, scale: float | None = None, kc=None, vc=None):
-    """Core keys/values [B,H,L//g,d] of q,k,v [B,H,L,d]: cca_pool_kv."""
-    lib = load_library()
+def _heads(q, k, v):
+    """(B, H, H_kv, L, d) of q [B,H,L,d] and k, v [B,H_kv,L,d] (H a multiple of H_kv)."""
     B, H, L, d = q.shape
+    if k.dim() != 4:
+        raise CCAError("k must be [B, H_kv, L, d]")
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv != 0:
+        raise CCAError(f"query heads {H} must be a multiple of key/value heads {Hkv}")
+    _need(q, (B, H, L, d), q.dtype, "q")
+    _need(k, (B, Hkv, L, d), q.dtype, "k")
+    _need(v, (B, Hkv, L, d), q.dtype, "v")
+    return B, H, Hkv, L, d
+
+
+def pool_kv(q, k, v, g: int, scale: float | None = None, kc=None, vc=None):
+    """Core keys/values [B,H_kv,L//g,d] of q [B,H,L,d], k, v [B,H_kv,L,d].
+
+    cca_pool_kv when H == H_kv, else cca_pool_kv_gqa (each key/value head
+    pooled once with the mean of its query heads' last-token queries).
+    """
+    lib = load_library()
+    B, H, Hkv, L, d = _heads(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, (B, H, L, d), q.dtype, name)
     m = L // g if g >= 1 else 0
     if kc is None:
-        kc = _core_buffer(B, H, m, d, q)
+        kc = _core_buffer(B, Hkv, m, d, q)
     if vc is None:
-        vc = _core_buffer(B, H, m, d, q)
-    _need(kc, (B, H, m, d), q.dtype, "kc")
-    _need(vc, (B, H, m, d), q.dtype, "vc")
-    _check(lib.cca_pool_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), B, H, L, d, g, scale,
-                           _dtype_code(q.dtype), _stream()), "cca_pool_kv")
+        vc = _core_buffer(B, Hkv, m, d, q)
+    _need(kc, (B, Hkv, m, d), q.dtype, "kc")
+    _need(vc, (B, Hkv, m, d), q.dtype, "vc")
+    if Hkv == H:
+        st = lib.cca_pool_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), B, H, L, d, g, scale,
+                             _dtype_code(q.dtype), _stream())
+    else:
+        st = lib.cca_pool_kv_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), B, H, Hkv, L, d, g, scale,
+                                 _dtype_code(q.dtype), _stream())
+    _check(st, "cca_pool_kv")
     return kc, vc
 
 
 def prefill(q, k, v, g: int, k_local: int, scale: float | None = None, out_dtype=None, out=None,
             kc=None, vc=None, return_core: bool = False):
-    """CCA prefill output [B,H,L,d] (pooling + fused attention): cca_prefill."""
+    """CCA prefill output [B,H,L,d] (pooling + fused attention): cca_prefill / cca_prefill_gqa."""
     lib = load_library()
-    B, H, L, d = q.shape
+    B, H, Hkv, L, d = _heads(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, (B, H, L, d), q.dtype, name)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     m = L // g if g >= 1 else 0
     if kc is None:
-        kc = _core_buffer(B, H, m, d, q)
+        kc = _core_buffer(B, Hkv, m, d, q)
     if vc is None:
-        vc = _core_buffer(B, H, m, d, q)
+        vc = _core_buffer(B, Hkv, m, d, q)
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
-    _need(kc, (B, H, m, d), q.dtype, "kc")
-    _need(vc, (B, H, m, d), q.dtype, "vc")
+    _need(kc, (B, Hkv, m, d), q.dtype, "kc")
+    _need(vc, (B, Hkv, m, d), q.dtype, "vc")
     _need(out, (B, H, L, d), out_dtype, "out")
-    _check(lib.cca_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, L, d, g, k_local,
-                           scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()), "cca_prefill")
+    if Hkv == H:
+        st = lib.cca_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, L, d, g, k_local,
+                             scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream())
+    else:
+        st = lib.cca_prefill_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, Hkv, L, d, g,
+                                 k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream())
+    _check(st, "cca_prefill")
     if return_core:
         return out, kc, vc
     return out
 
 
 def attention(q, k, v, kc, vc, g: int, k_local: int, scale: float | None = None, out_dtype=None, out=None):
-    """Attention step only, given the pooled core tokens kc, vc: cca_attention."""
+    """Attention step only, given the pooled core tokens kc, vc: cca_attention / cca_attention_gqa."""
     lib = load_library()
-    B, H, L, d = q.shape
+    B, H, Hkv, L, d = _heads(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, (B, H, L, d), q.dtype, name)
     m = L // g if g >= 1 else 0
-    _need(kc, (B, H, m, d), q.dtype, "kc")
-    _need(vc, (B, H, m, d), q.dtype, "vc")
+    _need(kc, (B, Hkv, m, d), q.dtype, "kc")
+    _need(vc, (B, Hkv, m, d), q.dtype, "vc")
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
     _need(out, (B, H, L, d), out_dtype, "out")
-    _check(lib.cca_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, L, d, g, k_local,
-                             scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()), "cca_attention")
+    if Hkv == H:
+        st = lib.cca_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, L, d, g, k_local,
+                               scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream())
+    else:
+        st = lib.cca_attention_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), B, H, Hkv, L, d, g,
+                                   k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream())
+    _check(st, "cca_attention")
     return out
 
 

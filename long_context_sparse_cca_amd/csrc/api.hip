@@ -50,24 +50,31 @@ const char* cca_status_string(int status) {
   }
 }
 
-int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc, int B, int H, int64_t L, int d,
-                int g, float scale, int dt, hipStream_t stream) {
+int cca_pool_kv_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, int B, int H, int H_kv,
+                    int64_t L, int d, int g, float scale, int dt, hipStream_t stream) {
   int s = check_shape(B, H, L, d, g, dt);
   if (s != CCA_OK) return s;
+  if (H_kv < 1 || H % H_kv != 0) return CCA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
   if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   if (!isfinite(scale)) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
-  if (BH * (L / g) >= INT32_MAX) return CCA_ERR_INVALID;
-  return hip_status(cca::launch_pool(dt, d, q, k, v, kc, vc, (int)BH, L, g, scale, stream));
+  if (BH * (L / g) >= INT32_MAX || BH * L >= ((int64_t)1 << 40)) return CCA_ERR_INVALID;
+  return hip_status(cca::launch_pool(dt, d, q, k, v, kc, vc, B * H_kv, L, g, H / H_kv, scale, stream));
+}
+
+int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc, int B, int H, int64_t L, int d,
+                int g, float scale, int dt, hipStream_t stream) {
+  return cca_pool_kv_gqa(q, k, v, kc, vc, B, H, H, L, d, g, scale, dt, stream);
 }
 
 namespace {
 
 int check_prefill(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out, int B,
-                  int H, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt) {
+                  int H, int H_kv, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt) {
   int s = check_shape(B, H, L, d, g, dt);
   if (s != CCA_OK) return s;
+  if (H_kv < 1 || H % H_kv != 0) return CCA_ERR_INVALID;
   if (out_dt != CCA_F32 && out_dt != dt) return CCA_ERR_UNSUPPORTED;
   if (k_local < 0 || !isfinite(scale)) return CCA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return CCA_ERR_INVALID;
@@ -79,23 +86,36 @@ int check_prefill(const void* q, const void* k, const void* v, const void* kc, c
 
 }  // namespace
 
+int cca_prefill_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int B, int H,
+                    int H_kv, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt,
+                    hipStream_t stream) {
+  int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, out_dt);
+  if (s != CCA_OK || L == 0) return s;
+  const int nq = H / H_kv;
+  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, B * H_kv, L, g, nq, scale, stream);
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  e = cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, nq, L, g, k_local, scale,
+                                    stream);
+  return hip_status(e);
+}
+
 int cca_prefill(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int B, int H, int64_t L,
                 int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
-  int s = check_prefill(q, k, v, kc, vc, out, B, H, L, d, g, k_local, scale, dt, out_dt);
+  return cca_prefill_gqa(q, k, v, kc, vc, out, B, H, H, L, d, g, k_local, scale, dt, out_dt, stream);
+}
+
+int cca_attention_gqa(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out, int B,
+                      int H, int H_kv, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt,
+                      hipStream_t stream) {
+  int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, out_dt);
   if (s != CCA_OK || L == 0) return s;
-  const int BH = B * H;
-  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, BH, L, g, scale, stream);
-  if (e != hipSuccess) return CCA_ERR_HIP;
-  e = cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, BH, L, g, k_local, scale, stream);
-  return hip_status(e);
+  return hip_status(cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, H / H_kv,
+                                                  L, g, k_local, scale, stream));
 }
 
 int cca_attention(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out, int B, int H,
                   int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
-  int s = check_prefill(q, k, v, kc, vc, out, B, H, L, d, g, k_local, scale, dt, out_dt);
-  if (s != CCA_OK || L == 0) return s;
-  return hip_status(cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, L, g,
-                                                  k_local, scale, stream));
+  return cca_attention_gqa(q, k, v, kc, vc, out, B, H, H, L, d, g, k_local, scale, dt, out_dt, stream);
 }
 
 int64_t cca_cache_ring_slots(const cca_cache_t* c) {

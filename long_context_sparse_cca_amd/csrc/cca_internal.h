@@ -8,17 +8,20 @@ namespace cca {
 
 // Each launcher enqueues its kernels on `stream` and returns the launch status.
 // Arguments have been validated by the caller (api.hip).
+// Grouped-query attention: nq = H / H_kv query heads share each key/value head.
+// Query/output slices are (b, h) = b*H + h; key/value and core slices are
+// (b, h_kv) = b*H_kv + h_kv, and query slice s reads key/value slice s / nq.
 hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
-                       int BH, int64_t L, int g, float scale, hipStream_t stream);
+                       int BHkv, int64_t L, int g, int nq, float scale, hipStream_t stream);
 
 hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v,
-                                    const void* kc, const void* vc, void* out, int out_f32, int BH,
+                                    const void* kc, const void* vc, void* out, int out_f32, int BH, int nq,
                                     int64_t L, int g, int k_local, float scale, hipStream_t stream);
 
 // bf16, head dim 128 fast path of the fused attention (prefill_bf16.hip).
 hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
-                                    void* out, int out_f32, int BH, int64_t L, int g, int k_local, float scale,
-                                    hipStream_t stream);
+                                    void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
+                                    float scale, hipStream_t stream);
 
 hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc,
                              const void* vc, int64_t L, hipStream_t stream);

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64) void cca_append_kernel(const T* __restrict__ q,
   const T* gv = ring_v + ((size_t)bh * R + first) * D;
   T* ck = core_k + ((size_t)bh * max_groups + beta) * D;
   T* cv = core_v + ((size_t)bh * max_groups + beta) * D;
-  pool_group_wave<T, D>(qt, gk, gv, kt, vt, g, scale, ck, cv, w_lds);
+  pool_group_wave<T, D>(qt, 0, 1, gk, gv, kt, vt, g, scale, ck, cv, w_lds);
 }
 
 template <typename T, int D>
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
       if ((t + 1) % g == 0) {
         const int64_t beta = t / g;
         const int64_t first = slot - (g - 1);
-        pool_group_wave<T, D>(qrow, ring_k + ((size_t)bh * R + first) * D, ring_v + ((size_t)bh * R + first) * D,
+        pool_group_wave<T, D>(qrow, 0, 1, ring_k + ((size_t)bh * R + first) * D, ring_v + ((size_t)bh * R + first) * D,
                               kt, vt, g, scale, core_k + ((size_t)bh * max_groups + beta) * D,
                               core_v + ((size_t)bh * max_groups + beta) * D, pool_lds);
       }

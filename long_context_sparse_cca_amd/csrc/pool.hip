@@ -1,6 +1,8 @@
 // Prefill pooling: every complete group of every (b,h) slice becomes one core
 // key and one core value (the CCA write-up, global-aware pooling section,
-// core-token and core K/V equations).  One wave per group; HBM-bound.  A
+// core-token and core K/V equations).  With grouped-query attention a
+// key/value head is pooled once, scored by the mean of the last-token queries
+// of the query heads that share it.  One wave per group; HBM-bound.  A
 // dedicated kernel covers bf16, d = 128, g = 16; other shapes use the generic
 // group routine shared with the decode cache.
 #include "cca_internal.h"
@@ -9,19 +11,23 @@
 namespace cca {
 namespace {
 
+// Slices: K, V, Kc, Vc are indexed by the key/value slice bkv = b*H_kv + h_kv; the
+// nq = H / H_kv query heads sharing it are the query slices bkv*nq .. bkv*nq + nq-1.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void cca_pool_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const T* __restrict__ V, T* __restrict__ Kc,
-                                                      T* __restrict__ Vc, int64_t L, int g, int64_t m,
+                                                      T* __restrict__ Vc, int64_t L, int g, int64_t m, int nq,
                                                       float scale) {
   extern __shared__ float w_lds[];
-  const int64_t gid = blockIdx.x;  // (bh, j) flattened
-  const int64_t bh = gid / m;
-  const int64_t j = gid - bh * m;
-  const size_t base = ((size_t)bh * L + (size_t)j * g) * D;
+  const int64_t gid = blockIdx.x;  // (bkv, j) flattened
+  const int64_t bkv = gid / m;
+  const int64_t j = gid - bkv * m;
+  const size_t base = ((size_t)bkv * L + (size_t)j * g) * D;
   const size_t last = base + (size_t)(g - 1) * D;
-  const size_t out = ((size_t)bh * m + j) * D;
-  pool_group_wave<T, D>(Q + last, K + base, V + base, K + last, V + last, g, scale, Kc + out, Vc + out, w_lds);
+  const size_t qlast = ((size_t)bkv * nq * L + (size_t)j * g + g - 1) * D;
+  const size_t out = ((size_t)bkv * m + j) * D;
+  pool_group_wave<T, D>(Q + qlast, (int64_t)L * D, nq, K + base, V + base, K + last, V + last, g, scale, Kc + out,
+                        Vc + out, w_lds);
 }
 
 // bf16, d = 128, g = 16: one wave per group, every load of the group issued up
@@ -31,17 +37,17 @@ __global__ __launch_bounds__(256) void cca_pool_bf16_d128_g16_kernel(const bf16_
                                                                    const bf16_t* __restrict__ K,
                                                                    const bf16_t* __restrict__ V,
                                                                    bf16_t* __restrict__ Kc, bf16_t* __restrict__ Vc,
-                                                                   int64_t L, int64_t m, int64_t n_groups,
+                                                                   int64_t L, int64_t m, int64_t n_groups, int nq,
                                                                    float scale) {
   constexpr int D = 128, G = 16;
   const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gid >= n_groups) return;
   const int lane = threadIdx.x & 63;
   const int rq = lane >> 4, c = lane & 15;
-  const int64_t bh = gid / m, j = gid - bh * m;
+  const int64_t bh = gid / m, j = gid - bh * m;   // bh: key/value slice
   const bf16_t* kg = K + ((size_t)bh * L + (size_t)j * G) * D;
   const bf16_t* vg = V + ((size_t)bh * L + (size_t)j * G) * D;
-  const bf16_t* qh = Q + ((size_t)bh * L + (size_t)j * G + G - 1) * D;
+  const bf16_t* qh = Q + ((size_t)bh * nq * L + (size_t)j * G + G - 1) * D;
   uint4 kr[4], vr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -50,6 +56,18 @@ __global__ __launch_bounds__(256) void cca_pool_bf16_d128_g16_kernel(const bf16_
   }
   float qf[8];
   Elem<bf16_t>::chunk_to_f32(ld16(qh + 8 * c), qf);
+  if (nq > 1) {
+    // grouped-query attention: the mean of the nq heads' last-token queries
+    for (int h = 1; h < nq; ++h) {
+      float f[8];
+      Elem<bf16_t>::chunk_to_f32(ld16(qh + (size_t)h * L * D + 8 * c), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[e] += f[e];
+    }
+    const float inv = 1.0f / (float)nq;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[e] *= inv;
+  }
   const float sc = scale * kLog2e;
   float s[4];
 #pragma unroll
@@ -104,34 +122,34 @@ __global__ __launch_bounds__(256) void cca_pool_bf16_d128_g16_kernel(const bf16_
 }
 
 template <typename T, int D>
-hipError_t launch_pool_t(const void* q, const void* k, const void* v, void* kc, void* vc, int BH, int64_t L,
-                         int g, float scale, hipStream_t stream) {
+hipError_t launch_pool_t(const void* q, const void* k, const void* v, void* kc, void* vc, int BHkv, int64_t L,
+                         int g, int nq, float scale, hipStream_t stream) {
   const int64_t m = L / g;
-  const int64_t n = (int64_t)BH * m;
+  const int64_t n = (int64_t)BHkv * m;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((cca_pool_kernel<T, D>), dim3((unsigned)n), dim3(64), (size_t)g * sizeof(float), stream,
-                     (const T*)q, (const T*)k, (const T*)v, (T*)kc, (T*)vc, L, g, m, scale);
+                     (const T*)q, (const T*)k, (const T*)v, (T*)kc, (T*)vc, L, g, m, nq, scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc, int BH,
-                       int64_t L, int g, float scale, hipStream_t stream) {
+hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc, int BHkv,
+                       int64_t L, int g, int nq, float scale, hipStream_t stream) {
   if (dt == CCA_BF16) {
     if (d == 128 && g == 16) {
-      const int64_t m = L / 16, n = (int64_t)BH * m;
+      const int64_t m = L / 16, n = (int64_t)BHkv * m;
       if (n == 0) return hipSuccess;
       hipLaunchKernelGGL(cca_pool_bf16_d128_g16_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
-                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, L, m, n,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, L, m, n, nq,
                          scale);
       return hipGetLastError();
     }
-    if (d == 128) return launch_pool_t<bf16_t, 128>(q, k, v, kc, vc, BH, L, g, scale, stream);
-    return launch_pool_t<bf16_t, 64>(q, k, v, kc, vc, BH, L, g, scale, stream);
+    if (d == 128) return launch_pool_t<bf16_t, 128>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
+    return launch_pool_t<bf16_t, 64>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
   }
-  if (d == 128) return launch_pool_t<float, 128>(q, k, v, kc, vc, BH, L, g, scale, stream);
-  return launch_pool_t<float, 64>(q, k, v, kc, vc, BH, L, g, scale, stream);
+  if (d == 128) return launch_pool_t<float, 128>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
+  return launch_pool_t<float, 64>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
 }
 
 }  // namespace cca

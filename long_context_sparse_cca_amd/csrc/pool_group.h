@@ -33,11 +33,14 @@ __device__ __forceinline__ void load_n(const T* p, float* f) {
 // any, are not involved: only wave-level synchronisation is used).
 //   rows r < g-1 are read at k_rows + r*D / v_rows + r*D; row g-1 at k_last / v_last
 //   (the decode cache passes the newest token there, the prefill passes row g-1);
-//   q_hat is the query of the group's last token;
+//   the scoring query is the mean of the nq query rows q_hat + h*q_stride, h < nq:
+//   the queries of the group's last token in the nq heads that share this
+//   key/value head (one row, nq = 1, without grouped-query attention);
 //   w_lds is LDS scratch of g floats owned by this wave.
 // Math in float32; kc/vc receive one rounding to T.
 template <typename T, int D>
-__device__ __forceinline__ void pool_group_wave(const T* __restrict__ q_hat, const T* __restrict__ k_rows,
+__device__ __forceinline__ void pool_group_wave(const T* __restrict__ q_hat, int64_t q_stride, int nq,
+                                                const T* __restrict__ k_rows,
                                                 const T* __restrict__ v_rows, const T* __restrict__ k_last,
                                                 const T* __restrict__ v_last, int g, float scale,
                                                 T* __restrict__ kc, T* __restrict__ vc,
@@ -54,6 +57,20 @@ __device__ __forceinline__ void pool_group_wave(const T* __restrict__ q_hat, con
   float qf[SEG];
 #pragma unroll
   for (int c = 0; c < SEGC; ++c) Elem<T>::chunk_to_f32(ld16(q_hat + seg * SEG + c * EPC), qf + c * EPC);
+  if (nq > 1) {
+    for (int h = 1; h < nq; ++h) {
+#pragma unroll
+      for (int c = 0; c < SEGC; ++c) {
+        float f[EPC];
+        Elem<T>::chunk_to_f32(ld16(q_hat + (size_t)h * q_stride + seg * SEG + c * EPC), f);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) qf[c * EPC + e] += f[e];
+      }
+    }
+    const float inv = 1.0f / (float)nq;
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) qf[e] *= inv;
+  }
   const float sc = scale * kLog2e;
   for (int r0 = 0; r0 < g; r0 += kWave / LPR) {
     const int r = r0 + rsub;

@@ -66,7 +66,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ Kc, const T* __restrict__ Vc, void* __restrict__ Out, int out_f32,
-    int BH, int64_t L, int g, int k_local, float scale, int ntiles) {
+    int BH, int nq, int64_t L, int g, int k_local, float scale, int ntiles) {
   using C = PrefillCfg<T, D>;
   __shared__ __attribute__((aligned(16))) T lds_k[2][C::LDS_K];
   __shared__ __attribute__((aligned(16))) T lds_v[2][C::LDS_V];
@@ -98,11 +98,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t cl_min = qa / g - k_local, cl_max = qb / g - k_local;
   const int64_t rl_min = max<int64_t>(0, cl_min) * g, rl_max = max<int64_t>(0, cl_max) * g;
 
+  const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
   const T* Qs = Q + (size_t)bh * L * D;
-  const T* Ks = K + (size_t)bh * L * D;
-  const T* Vs = V + (size_t)bh * L * D;
-  const T* Kcs = Kc + (size_t)bh * m * D;
-  const T* Vcs = Vc + (size_t)bh * m * D;
+  const T* Ks = K + (size_t)bkv * L * D;
+  const T* Vs = V + (size_t)bkv * L * D;
+  const T* Kcs = Kc + (size_t)bkv * m * D;
+  const T* Vcs = Vc + (size_t)bkv * m * D;
 
   // ---- Q operand in registers (B operand of S^T = K Q^T).
   // bf16: slice s of 16 dims, lane half hf holds dims 16s+8hf .. +8.
@@ -351,14 +352,14 @@ namespace {
 
 template <typename T, int D>
 hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const void* kc, const void* vc,
-                            void* out, int out_f32, int BH, int64_t L, int g, int k_local, float scale,
+                            void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local, float scale,
                             hipStream_t stream) {
   using C = PrefillCfg<T, D>;
   const int ntiles = (int)((L + C::BM - 1) / C::BM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL((cca_prefill_kernel<T, D>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, L, g,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq, L, g,
                      k_local, scale, ntiles);
   return hipGetLastError();
 }
@@ -366,14 +367,15 @@ hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const v
 }  // namespace
 
 hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
-                                    const void* vc, void* out, int out_f32, int BH, int64_t L, int g,
+                                    const void* vc, void* out, int out_f32, int BH, int nq, int64_t L, int g,
                                     int k_local, float scale, hipStream_t stream) {
   if (dt == CCA_BF16) {
-    if (d == 128) return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
-    return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, L, g, k_local, scale, stream);
+    if (d == 128)
+      return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream);
+    return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream);
   }
-  if (d == 128) return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, L, g, k_local, scale, stream);
-  return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, L, g, k_local, scale, stream);
+  if (d == 128) return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream);
+  return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream);
 }
 
 }  // namespace cca

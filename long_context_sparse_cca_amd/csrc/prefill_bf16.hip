@@ -61,7 +61,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
-    int L, int g, int k_local, float scale, int ntiles) {
+    int nq, int L, int g, int k_local, float scale, int ntiles) {
   // one array per buffer: the LDS-DMA fill of one buffer then provably does not
   // alias the operand reads of the other, so no wait is forced between them
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
@@ -95,10 +95,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rl_lane = max(0, cl_lane) * g;               // raw u visible iff rl_lane <= u <= q_lane
 
   const size_t slice = (size_t)bh * L * kD;
-  const bf16_t* Ks = K + slice;
-  const bf16_t* Vs = V + slice;
-  const bf16_t* Kcs = Kc + (size_t)bh * m * kD;
-  const bf16_t* Vcs = Vc + (size_t)bh * m * kD;
+  const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
+  const bf16_t* Ks = K + (size_t)bkv * L * kD;
+  const bf16_t* Vs = V + (size_t)bkv * L * kD;
+  const bf16_t* Kcs = Kc + (size_t)bkv * m * kD;
+  const bf16_t* Vcs = Vc + (size_t)bkv * m * kD;
 
   // ---- Q operand (B of S^T = K Q^T): slice d16 holds dims 16*d16 + 8*hf .. +8
   uint4 qop[kD / 16];
@@ -333,14 +334,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
-                                    void* out, int out_f32, int BH, int64_t L, int g, int k_local, float scale,
-                                    hipStream_t stream) {
+                                    void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
+                                    float scale, hipStream_t stream) {
   const int ntiles = (int)((L + kBM - 1) / kBM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel, dim3((unsigned)nblocks), dim3(512), 0, stream, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out, out_f32, BH,
-                     (int)L, g, k_local, scale, ntiles);
+                     nq, (int)L, g, k_local, scale, ntiles);
   return hipGetLastError();
 }
 
