@@ -224,6 +224,38 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
                             float scale, hipStream_t stream);
 
 /*
+ * Serving decode step: every sequence of the batch at its own length, and
+ * grouped-query attention (see the GQA reading above cca_pool_kv_gqa).  The
+ * cache descriptor is the same; its H is the number of key/value heads and its
+ * n_tokens / n_pooled fields are neither read (beyond the consistency check of
+ * every cache call) nor written: per-sequence lengths live on the device.
+ *   lens    : device int32 [B]; lens[b] = tokens already in sequence b's cache,
+ *             i.e. the position of the token this call appends.  Read only: the
+ *             caller advances it (e.g. lens += 1 on the same stream) afterwards.
+ *   max_len : host value >= every lens[b]; validates capacity
+ *             ((max_len+1)/g <= max_groups, else CCA_ERR_CAPACITY) and sizes the
+ *             work split.  A sequence with lens[b] < 0 or > max_len gets NaN
+ *             outputs and its cache is left untouched.
+ *   H_q     : query heads, a multiple of c->H.
+ *   q       : device [B, H_q, d]: the new token's queries.
+ *   k, v    : device [B, c->H, d]: its keys and values.
+ *   out     : device [B, H_q, d] of out_dt (CCA_F32 or c->dt).
+ *   workspace : device, >= cca_serve_workspace_bytes(c, H_q) bytes.
+ * Per sequence this is cca_cache_append followed by the attention of the new
+ * token ([CCA] Triton section): the token is written to ring slot lens[b] mod
+ * ((k_local+1)*g) and, when it completes a group, that group is pooled into
+ * core slot lens[b]/g with the mean of the token's queries over the query heads
+ * sharing each key/value head; the token then attends to the core tokens
+ * before its raw window and to the window itself, itself included.  One kernel
+ * reads every cached key/value row once per key/value head for all the query
+ * heads that share it.
+ */
+size_t cca_serve_workspace_bytes(const cca_cache_t* c, int H_q);
+int cca_cache_append_decode_varlen(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q,
+                                   const void* q, const void* k, const void* v, void* out, int out_dt,
+                                   void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
+
+/*
  * KV-cache accounting ([CCA] compute/memory efficiency, Fig. 3: the cache
  * holds core plus local tokens instead of every token).  Host-only integer
  * arithmetic, no device work.  After n_tokens tokens with group size g and

@@ -81,6 +81,11 @@ EXPORTS = {
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
     "cca_cache_append_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
+    "cca_serve_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int]),
+    "cca_cache_append_decode_varlen": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64,
+                                                      ctypes.c_int] + [ctypes.c_void_p] * 4
+                                       + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float,
+                                          ctypes.c_void_p]),
     "cca_kv_cache_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_int64)]),
@@ -304,6 +309,80 @@ class KVCache:
         _need(out, (B, H, d), out_dtype, "out")
         _check(_lib.cca_decode_step(ctypes.byref(self.desc), _ptr(q), _ptr(out), _dtype_code(out_dtype),
                                     _ptr(self.workspace), self.ws_bytes, scale, _stream()), "cca_decode_step")
+        return out
+
+
+class ServeCache(KVCache):
+    """Compressed cache for serving: per-sequence lengths on the device, grouped-query heads.
+
+    H_kv key/value heads are cached; steps take H_q = r * H_kv query heads.
+    `lens` (int32 [B], device) holds each sequence's token count; `step`
+    appends one token to every sequence and advances `lens` by one.
+    """
+
+    def __init__(self, B: int, H_q: int, H_kv: int, d: int, g: int, k_local: int, max_tokens: int,
+                 dtype=torch.bfloat16, device="cuda"):
+        super().__init__(B, H_kv, d, g, k_local, max_tokens, dtype, device)
+        if H_q % H_kv != 0:
+            raise CCAError("H_q must be a multiple of H_kv")
+        self.H_q = H_q
+        self.lens = torch.zeros((B,), dtype=torch.int32, device=device)
+        self.lens_host = [0] * B
+        ws_bytes = _lib.cca_serve_workspace_bytes(ctypes.byref(self.desc), H_q)
+        self.serve_ws = torch.empty((ws_bytes + 15) // 16 * 4, dtype=torch.float32, device=device)
+        self.serve_ws_bytes = ws_bytes
+
+    def _seq_desc(self, b: int):
+        B, H, d = self.shape_bhd
+        esz = self.core_k.element_size()
+        per_core = H * self.max_groups * d * esz
+        per_ring = H * self.R * d * esz
+        return CacheDesc(self.desc.core_k + b * per_core, self.desc.core_v + b * per_core,
+                         self.desc.ring_k + b * per_ring, self.desc.ring_v + b * per_ring,
+                         1, H, d, self.desc.g, self.desc.k_local, self.desc.dt, self.max_groups, 0, 0)
+
+    def load_sequence(self, b: int, k, v, kc, vc):
+        """Seed sequence b (empty) with the state after a prefill of L_b = k.shape[2] tokens.
+
+        k, v: [1, H_kv, L_b, d]; kc, vc: [1, H_kv, L_b // g, d] (from `prefill(..., return_core=True)`).
+        Uses cca_cache_load_prefill on a one-sequence view of the cache.
+        """
+        _, H, d = self.shape_bhd
+        L = k.shape[2]
+        m = L // self.desc.g
+        _need(k, (1, H, L, d), self.dtype, "k")
+        _need(v, (1, H, L, d), self.dtype, "v")
+        _need(kc, (1, H, m, d), self.dtype, "kc")
+        _need(vc, (1, H, m, d), self.dtype, "vc")
+        if self.lens_host[b] != 0:
+            raise CCAError(f"sequence {b} is not empty")
+        desc = self._seq_desc(b)
+        _check(_lib.cca_cache_load_prefill(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), L, _stream()),
+               "cca_cache_load_prefill")
+        self.lens_host[b] = L
+        self.lens[b] = L
+
+    def step(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
+        """Append one token to every sequence and return its outputs [B, H_q, d].
+
+        q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen, then lens += 1.
+        """
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        _need(q, (B, self.H_q, d), self.dtype, "q")
+        _need(k, (B, H, d), self.dtype, "k")
+        _need(v, (B, H, d), self.dtype, "v")
+        if out is None:
+            out = torch.empty((B, self.H_q, d), dtype=out_dtype, device=q.device)
+        _need(out, (B, self.H_q, d), out_dtype, "out")
+        max_len = max(self.lens_host)
+        _check(_lib.cca_cache_append_decode_varlen(ctypes.byref(self.desc), _ptr(self.lens), max_len, self.H_q,
+                                                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(out_dtype),
+                                                   _ptr(self.serve_ws), self.serve_ws_bytes, scale, _stream()),
+               "cca_cache_append_decode_varlen")
+        self.lens += 1
+        self.lens_host = [x + 1 for x in self.lens_host]
         return out
 
 

@@ -398,6 +398,18 @@ hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* 
   return launch_append_t<float, 64>(c, q, k, v, scale, stream);
 }
 
+hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_bf16,
+                               int64_t nslices, int nchunks, hipStream_t stream) {
+  if (nslices == 0) return hipSuccess;
+  if (d == 128)
+    hipLaunchKernelGGL((cca_decode_merge_kernel<128>), dim3((unsigned)nslices), dim3(64), 0, stream, ws_acc, ws_ml,
+                       out, out_bf16, nchunks);
+  else
+    hipLaunchKernelGGL((cca_decode_merge_kernel<64>), dim3((unsigned)nslices), dim3(64), 0, stream, ws_acc, ws_ml,
+                       out, out_bf16, nchunks);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace, float scale,
                          hipStream_t stream) {
   return launch_decode_any<false>(c, q, nullptr, nullptr, out, out_f32, workspace, scale, stream);

@@ -1,0 +1,312 @@
+// Serving decode step over the compressed CCA cache: one new token per sequence,
+// each sequence at its own position, grouped-query attention.
+//
+// Method: the CCA write-up ("ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展"):
+// the token at position t attends, in one softmax, to the core tokens of the
+// groups before its raw window and to the raw keys (t/g - k)*g .. t (global-aware
+// pooling, locality-preserving module, global-local fusion sections); the fused
+// operator serves decode from a KV cache of core tokens plus local raw tokens
+// (Triton section, Fig. 3).  A group is pooled when its last token arrives.
+// With grouped-query attention the cache holds one core token per key/value
+// head, pooled with the mean of the last-token queries of the query heads that
+// share it (the mean-query importance of "Latent-Condensed Transformer for
+// Efficient Long Context Modeling", section 2, which its section 3 extends to
+// grouped-query attention).
+//
+// One workgroup = (sequence b, key/value head, block of RH query heads, chunk of
+// the key index space).  Every key/value row is loaded once per workgroup and
+// scored against all RH query heads, so grouped-query attention reads the cache
+// once per key/value head instead of once per query head.  Partial softmax
+// states go to the workspace; the decode merge kernel combines the chunks.
+#include <algorithm>
+
+#include "cca_internal.h"
+#include "pool_group.h"
+
+namespace cca {
+namespace {
+
+template <typename T, int D, int RH>
+struct ServeCfg {
+  static constexpr int NWAVE = 4;
+  static constexpr int NT = NWAVE * kWave;
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per lane (one 16-byte chunk)
+  static constexpr int LPK = D / EPC;                 // lanes per key row
+  static constexpr int KPW = kWave / LPK;             // key rows per wave per load
+  static constexpr int U = RH >= 8 ? 2 : 4;           // loads of K and V in flight per lane
+  static constexpr int KPI = NWAVE * KPW * U;         // key rows per workgroup iteration
+};
+
+template <typename T, int D, int RH>
+__global__ __launch_bounds__(256) void cca_serve_decode_kernel(
+    const int32_t* __restrict__ lens, int64_t max_len, const T* __restrict__ q, const T* __restrict__ k_new,
+    const T* __restrict__ v_new, T* __restrict__ core_k, T* __restrict__ core_v, T* __restrict__ ring_k,
+    T* __restrict__ ring_v, float* __restrict__ ws_acc, float* __restrict__ ws_ml, int Hkv, int nq, int nhb,
+    int64_t max_groups, int64_t R, int g, int k_local, int64_t chunk, int nchunks, float scale) {
+  using C = ServeCfg<T, D, RH>;
+  __shared__ float red[C::NWAVE][RH][D + 2];
+  extern __shared__ float pool_lds[];
+  const int64_t xb = blockIdx.x;
+  const int hb = (int)(xb % nhb);
+  const int64_t bkv = xb / nhb;             // key/value slice b*Hkv + hk
+  const int64_t b = bkv / Hkv;
+  const int hk = (int)(bkv - b * Hkv);
+  const int ci = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const int kg = lane / C::LPK;
+  const int part = lane % C::LPK;
+  const int Hq = Hkv * nq;
+  const int h0 = hk * nq + hb * RH;         // first query head of this block
+  const int64_t t = lens[b];                // position of the token appended by this call
+  const bool valid = t >= 0 && t <= max_len;
+
+  // ---- append: ring slot t mod R; pool the group the token completes (once per key/value slice)
+  if (valid && ci == 0 && hb == 0 && wave == 0) {
+    const T* kt = k_new + (size_t)bkv * D;
+    const T* vt = v_new + (size_t)bkv * D;
+    const int64_t slot = t % R;
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    if (lane < CPR) {
+      st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bkv * R + slot) * D) + lane,
+           ld16(reinterpret_cast<const uint4*>(kt) + lane));
+      st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + lane,
+           ld16(reinterpret_cast<const uint4*>(vt) + lane));
+    }
+    if ((t + 1) % g == 0) {
+      // the group occupies slots slot-g+1 .. slot (R is a multiple of g); its last row is the new token
+      const int64_t beta = t / g;
+      const int64_t first = slot - (g - 1);
+      pool_group_wave<T, D>(q + ((size_t)b * Hq + (size_t)hk * nq) * D, D, nq,
+                            ring_k + ((size_t)bkv * R + first) * D, ring_v + ((size_t)bkv * R + first) * D, kt, vt,
+                            g, scale, core_k + ((size_t)bkv * max_groups + beta) * D,
+                            core_v + ((size_t)bkv * max_groups + beta) * D, pool_lds);
+    }
+  }
+
+  // ---- this token's visible keys: core [0, n_c) then raw positions raw_lo .. t
+  int64_t n_c = 0, raw_lo = 0, n_keys = 0;
+  if (valid) {
+    n_c = t / g - k_local;
+    n_c = n_c > 0 ? n_c : 0;
+    raw_lo = n_c * g;
+    n_keys = n_c + (t - raw_lo + 1);
+  }
+  const int64_t start = (int64_t)ci * chunk;
+  const int64_t end = min(n_keys, start + chunk);
+
+  const float sc = scale * kLog2e;
+  float qf[RH][C::EPC];
+#pragma unroll
+  for (int j = 0; j < RH; ++j) {
+    Elem<T>::chunk_to_f32(ld16(q + ((size_t)b * Hq + h0 + j) * D + part * C::EPC), qf[j]);
+#pragma unroll
+    for (int e = 0; e < C::EPC; ++e) qf[j][e] *= sc;
+  }
+  const T* ck = core_k + (size_t)bkv * max_groups * D;
+  const T* cv = core_v + (size_t)bkv * max_groups * D;
+  const T* rk = ring_k + (size_t)bkv * R * D;
+  const T* rv = ring_v + (size_t)bkv * R * D;
+  const T* kt_new = k_new + (size_t)bkv * D;
+  const T* vt_new = v_new + (size_t)bkv * D;
+
+  float m_run[RH], l_run[RH], acc[RH][C::EPC];
+#pragma unroll
+  for (int j = 0; j < RH; ++j) {
+    m_run[j] = kNegBig;
+    l_run[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < C::EPC; ++e) acc[j][e] = 0.f;
+  }
+
+  for (int64_t base = start; base < end; base += C::KPI) {
+    uint4 kr[C::U], vr[C::U];
+    bool ok[C::U];
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      const int64_t n = base + (int64_t)(u * C::NWAVE + wave) * C::KPW + kg;
+      ok[u] = n < end;
+      const int64_t nn = ok[u] ? n : start;
+      const T* kp;
+      const T* vp;
+      if (nn < n_c) {
+        kp = ck + (size_t)nn * D;
+        vp = cv + (size_t)nn * D;
+      } else if (nn == n_keys - 1) {
+        kp = kt_new;   // the token appended by this very call
+        vp = vt_new;
+      } else {
+        const int64_t slot = (raw_lo + (nn - n_c)) % R;
+        kp = rk + (size_t)slot * D;
+        vp = rv + (size_t)slot * D;
+      }
+      kr[u] = ld16(kp + part * C::EPC);
+      vr[u] = ld16(vp + part * C::EPC);
+    }
+    float s[C::U][RH];
+    float vf[C::U][C::EPC];
+#pragma unroll
+    for (int u = 0; u < C::U; ++u) {
+      float kf[C::EPC];
+      Elem<T>::chunk_to_f32(kr[u], kf);
+      Elem<T>::chunk_to_f32(vr[u], vf[u]);
+#pragma unroll
+      for (int j = 0; j < RH; ++j) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < C::EPC; ++e) dot = fmaf(qf[j][e], kf[e], dot);
+#pragma unroll
+        for (int bb = 1; bb < C::LPK; bb <<= 1) dot += __shfl_xor(dot, bb, kWave);
+        s[u][j] = ok[u] ? dot : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RH; ++j) {
+      float mx = s[0][j];
+#pragma unroll
+      for (int u = 1; u < C::U; ++u) mx = fmaxf(mx, s[u][j]);
+      const float m_new = fmaxf(m_run[j], mx);
+      const float alpha = fast_exp2(m_run[j] - m_new);
+      m_run[j] = m_new;
+      l_run[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < C::EPC; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < C::U; ++u) {
+        const float p = fast_exp2(s[u][j] - m_new);
+        l_run[j] += p;
+#pragma unroll
+        for (int e = 0; e < C::EPC; ++e) acc[j][e] = fmaf(p, vf[u][e], acc[j][e]);
+      }
+    }
+  }
+
+  // ---- combine the key slots of the wave (lanes with equal `part`), then the waves
+#pragma unroll
+  for (int j = 0; j < RH; ++j) {
+#pragma unroll
+    for (int bb = C::LPK; bb < kWave; bb <<= 1) {
+      const float mo = __shfl_xor(m_run[j], bb, kWave);
+      const float lo = __shfl_xor(l_run[j], bb, kWave);
+      const float M = fmaxf(m_run[j], mo);
+      const float a1 = fast_exp2(m_run[j] - M), a2 = fast_exp2(mo - M);
+      l_run[j] = l_run[j] * a1 + lo * a2;
+#pragma unroll
+      for (int e = 0; e < C::EPC; ++e) {
+        const float ao = __shfl_xor(acc[j][e], bb, kWave);
+        acc[j][e] = acc[j][e] * a1 + ao * a2;
+      }
+      m_run[j] = M;
+    }
+    if (lane < C::LPK) {
+#pragma unroll
+      for (int e = 0; e < C::EPC; ++e) red[wave][j][part * C::EPC + e] = acc[j][e];
+      if (lane == 0) {
+        red[wave][j][D] = m_run[j];
+        red[wave][j][D + 1] = l_run[j];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < RH * D; idx += C::NT) {
+    const int j = idx / D, col = idx - j * D;
+    float M = red[0][j][D];
+#pragma unroll
+    for (int w = 1; w < C::NWAVE; ++w) M = fmaxf(M, red[w][j][D]);
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < C::NWAVE; ++w) {
+      const float f = fast_exp2(red[w][j][D] - M);
+      a = fmaf(f, red[w][j][col], a);
+      l = fmaf(f, red[w][j][D + 1], l);
+    }
+    const size_t rec = ((size_t)b * Hq + h0 + j) * nchunks + ci;
+    ws_acc[rec * D + col] = a;
+    if (col == 0) {
+      ws_ml[rec * 2] = M;
+      ws_ml[rec * 2 + 1] = l;
+    }
+  }
+}
+
+int heads_per_block(int nq) {
+  if (nq % 8 == 0) return 8;
+  if (nq % 4 == 0) return 4;
+  if (nq % 2 == 0) return 2;
+  return 1;
+}
+
+template <typename T, int D, int RH>
+hipError_t launch_serve_t(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q, const void* q,
+                          const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
+                          hipStream_t stream) {
+  const int nq = H_q / c->H;
+  const int nhb = nq / RH;
+  const int64_t R = (int64_t)(c->k_local + 1) * c->g;
+  const int nchunks = serve_num_chunks(c, H_q, max_len);
+  // Keys of a token at t <= max_len: n_c(t) <= n_c(max_len) core tokens plus at most
+  // min(t+1, (k_local+1)*g) raw ones.  (A shorter sequence can have more keys than
+  // the longest: the raw part grows with t mod g.)
+  const int64_t n_c_max = std::max<int64_t>(0, max_len / c->g - c->k_local);
+  const int64_t n_keys_max = n_c_max + std::min<int64_t>(max_len + 1, R);
+  int64_t chunk = (n_keys_max + nchunks - 1) / nchunks;
+  chunk = (chunk + 15) / 16 * 16;
+  float* ws_acc = (float*)workspace;
+  float* ws_ml = ws_acc + (size_t)c->B * H_q * nchunks * D;
+  const int64_t nblk = (int64_t)c->B * c->H * nhb;
+  hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH>), dim3((unsigned)nblk, nchunks), dim3(256),
+                     (size_t)c->g * sizeof(float), stream, lens, max_len, (const T*)q, (const T*)k, (const T*)v,
+                     (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k, (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb,
+                     c->max_groups, R, c->g, c->k_local, chunk, nchunks, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
+  return launch_decode_merge(D, ws_acc, ws_ml, out, out_bf16, (int64_t)c->B * H_q, nchunks, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_serve_d(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q, const void* q,
+                          const void* k, const void* v, void* out, int out_f32, void* ws, float scale,
+                          hipStream_t stream) {
+  switch (heads_per_block(H_q / c->H)) {
+    case 8: return launch_serve_t<T, D, 8>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
+    case 4: return launch_serve_t<T, D, 4>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
+    case 2: return launch_serve_t<T, D, 2>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
+    default: return launch_serve_t<T, D, 1>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
+  }
+}
+
+}  // namespace
+
+int serve_num_chunks(const cca_cache_t* c, int H_q, int64_t max_len) {
+  // About 1024 workgroups in total, as for the uniform decode; at least 256 keys
+  // of the cache's capacity per chunk, at most 64 chunks.  max_len is not used:
+  // the workspace size depends on the cache and the head count only.
+  (void)max_len;
+  const int nq = H_q / c->H;
+  const int64_t nblk = (int64_t)c->B * c->H * (nq / heads_per_block(nq));
+  const int64_t cap = c->max_groups + (int64_t)(c->k_local + 1) * c->g;
+  int64_t n = (1024 + nblk - 1) / nblk;
+  n = std::min<int64_t>(n, std::max<int64_t>(1, cap / 256));
+  n = std::max<int64_t>(1, std::min<int64_t>(n, 64));
+  return (int)n;
+}
+
+size_t serve_workspace_bytes(const cca_cache_t* c, int H_q) {
+  return (size_t)c->B * H_q * (size_t)serve_num_chunks(c, H_q, 0) * ((size_t)c->d + 2) * sizeof(float);
+}
+
+hipError_t launch_serve_append_decode(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q,
+                                      const void* q, const void* k, const void* v, void* out, int out_f32,
+                                      void* workspace, float scale, hipStream_t stream) {
+  if (c->dt == CCA_BF16) {
+    if (c->d == 128)
+      return launch_serve_d<bf16_t, 128>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, stream);
+    return launch_serve_d<bf16_t, 64>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, stream);
+  }
+  if (c->d == 128)
+    return launch_serve_d<float, 128>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, stream);
+  return launch_serve_d<float, 64>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, stream);
+}
+
+}  // namespace cca
