@@ -46,7 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the standard-attention comparison")
-    ap.add_argument("--phase", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the serving decode measurement (per-sequence lengths, grouped-query heads)")
+    ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "copy"], default="all",
                     help="profiling aid: run only one phase (the JSON line is then not the benchmark result); "
                          "'copy' runs a plain 1 GiB device copy whose counter readings calibrate FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
@@ -163,6 +165,52 @@ def dense_comparison(binding, accounting, dev, seed):
     return out
 
 
+def serving_decode(binding, accounting, dev, seed, steps: int = 64):
+    """Serving decode step with per-sequence lengths and grouped-query attention, outside the
+    timed steps: B=8 sequences at lengths 65536 + 9362*b (64K .. 128K), H_q=32 query heads
+    over H_kv=8 key/value heads (r=4), d=128, g=16, k=64, bf16; each step is one
+    cca_cache_append_decode_varlen call (append + pooling + attention of one token per sequence)."""
+    import torch
+
+    from long_context_sparse_cca_amd.synth import torch_inputs
+    B, Hq, Hkv = 8, 32, 8
+    lens0 = [65536 + 9362 * b for b in range(B)]
+    cache = binding.ServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + G, dtype=torch.bfloat16, device=dev)
+    for b, L in enumerate(lens0):
+        q, _, _ = torch_inputs(1, Hq, L, D, torch.bfloat16, dev, seed=seed + 10 + b, heavy_frac=HEAVY)
+        _, k, v = torch_inputs(1, Hkv, L, D, torch.bfloat16, dev, seed=seed + 30 + b, heavy_frac=HEAVY)
+        kc, vc = binding.pool_kv(q, k, v, G)
+        cache.load_sequence(b, k, v, kc, vc)
+        del q, k, v, kc, vc
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 50)
+    qs = torch.randn((steps, B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    ks = torch.randn((steps, B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    vs = torch.randn((steps, B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    lens_at = []
+    for s in range(steps):
+        lens_at.append(list(cache.lens_host))
+        ev[2 * s].record(stream)
+        cache.step(qs[s], ks[s], vs[s], out=out)
+        ev[2 * s + 1].record(stream)
+    torch.cuda.synchronize()
+    warm = 8
+    us = [ev[2 * s].elapsed_time(ev[2 * s + 1]) * 1e3 for s in range(warm, steps)]
+    nchunks = cache.serve_ws_bytes // (B * Hq * (D + 2) * 4)
+    byt = [accounting.serve_bytes(lens_at[s], Hq, Hkv, D, G, KL, 2, nchunks) for s in range(warm, steps)]
+    us_mean = sum(us) / len(us)
+    gbs = sum(byt) / len(byt) / (us_mean * 1e-6) / 1e9
+    return {"config": {"B": B, "H_q": Hq, "H_kv": Hkv, "d": D, "g": G, "k_local": KL,
+                       "lengths": lens0, "steps_timed": steps - warm},
+            "us_per_step": us_mean, "bytes_per_step": sum(byt) / len(byt),
+            "roofline": {"kernel": "cca_serve_decode_kernel<bf16,128,4> + cca_decode_merge_kernel", "bound": "hbm",
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,6 +237,10 @@ def main():
         dt = (time.perf_counter() - t0) / args.steps
         print(json.dumps({"phase": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "ms": dt * 1e3,
                           "gbs": 4 * n / dt / 1e9}), flush=True)
+        return
+    if args.phase == "serving":
+        print(json.dumps({"phase": "serving",
+                          "serving_decode": serving_decode(binding, accounting, dev, args.seed)}), flush=True)
         return
     stream = torch.cuda.current_stream()
     scale = 1.0 / math.sqrt(D)
@@ -322,6 +374,10 @@ def main():
         }
         if not do_prefill:
             res["value"] = None
+    if do_decode and not args.no_serving and args.phase == "all":
+        del cache, qs, ks, vs, k0, v0, kc0, vc0
+        torch.cuda.empty_cache()
+        res["serving_decode"] = serving_decode(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_dense and args.phase == "all":
         res["dense_comparison"] = dense_comparison(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_cpu_baseline and args.phase == "all":

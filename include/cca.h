@@ -230,12 +230,13 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
  * n_tokens / n_pooled fields are neither read (beyond the consistency check of
  * every cache call) nor written: per-sequence lengths live on the device.
  *   lens    : device int32 [B]; lens[b] = tokens already in sequence b's cache,
- *             i.e. the position of the token this call appends.  Read only: the
- *             caller advances it (e.g. lens += 1 on the same stream) afterwards.
+ *             i.e. the position of the token this call appends.  The call
+ *             advances it: after the call (in stream order) lens[b] is one larger
+ *             for every sequence whose length was in [0, max_len].
  *   max_len : host value >= every lens[b]; validates capacity
  *             ((max_len+1)/g <= max_groups, else CCA_ERR_CAPACITY) and sizes the
  *             work split.  A sequence with lens[b] < 0 or > max_len gets NaN
- *             outputs and its cache is left untouched.
+ *             outputs, and its cache and length are left untouched.
  *   H_q     : query heads, a multiple of c->H.
  *   q       : device [B, H_q, d]: the new token's queries.
  *   k, v    : device [B, c->H, d]: its keys and values.
@@ -251,7 +252,7 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
  * heads that share it.
  */
 size_t cca_serve_workspace_bytes(const cca_cache_t* c, int H_q);
-int cca_cache_append_decode_varlen(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q,
+int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                    const void* q, const void* k, const void* v, void* out, int out_dt,
                                    void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
 

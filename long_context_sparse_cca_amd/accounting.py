@@ -67,6 +67,17 @@ def decode_bytes(B: int, H: int, d: int, t: int, g: int, k: int, elem: int, n_ch
     return B * H * (kv + d * elem + partials + d * elem)
 
 
+def serve_bytes(lens, H_q: int, H_kv: int, d: int, g: int, k: int, elem: int, n_chunks: int) -> int:
+    """HBM bytes of one serving decode step (sequence b's new token at position lens[b]):
+    every visible K and V row once per key/value head (shared by its query heads), q,
+    the output, and the chunk partials of every query head (written then read back)."""
+    total = 0
+    for t in lens:
+        total += H_kv * decode_keys(int(t), g, k) * 2 * d * elem
+        total += H_q * (2 * d * elem + 2 * n_chunks * (d + 2) * 4)
+    return total
+
+
 def kv_cache_bytes(n_tokens: int, g: int, k: int, B: int, H: int, d: int, elem: int) -> tuple[int, int]:
     per_token = B * H * 2 * d * elem
     return per_token * (n_tokens // g + (k + 1) * g), per_token * n_tokens

@@ -317,7 +317,7 @@ class ServeCache(KVCache):
 
     H_kv key/value heads are cached; steps take H_q = r * H_kv query heads.
     `lens` (int32 [B], device) holds each sequence's token count; `step`
-    appends one token to every sequence and advances `lens` by one.
+    appends one token to every sequence (the library advances `lens` by one).
     """
 
     def __init__(self, B: int, H_q: int, H_kv: int, d: int, g: int, k_local: int, max_tokens: int,
@@ -365,7 +365,7 @@ class ServeCache(KVCache):
     def step(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
         """Append one token to every sequence and return its outputs [B, H_q, d].
 
-        q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen, then lens += 1.
+        q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen (which also advances `lens`).
         """
         B, H, d = self.shape_bhd
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -381,8 +381,7 @@ class ServeCache(KVCache):
                                                    _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(out_dtype),
                                                    _ptr(self.serve_ws), self.serve_ws_bytes, scale, _stream()),
                "cca_cache_append_decode_varlen")
-        self.lens += 1
-        self.lens_host = [x + 1 for x in self.lens_host]
+        self.lens_host = [x + 1 for x in self.lens_host]   # the call advanced `lens` on the device
         return out
 
 

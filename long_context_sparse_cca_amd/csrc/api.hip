@@ -195,7 +195,7 @@ size_t cca_serve_workspace_bytes(const cca_cache_t* c, int H_q) {
   return cca::serve_workspace_bytes(c, H_q);
 }
 
-int cca_cache_append_decode_varlen(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q,
+int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                    const void* q, const void* k, const void* v, void* out, int out_dt,
                                    void* workspace, size_t workspace_bytes, float scale, hipStream_t stream) {
   int s = check_cache(c);

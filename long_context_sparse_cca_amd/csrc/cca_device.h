@@ -74,6 +74,24 @@ __device__ __forceinline__ float wave_sum_xor(float v, int lo_bit, int hi_bit) {
   return v;
 }
 
+// Sum over aligned groups of N consecutive lanes (N in {1, 2, 4, 8, 16}) with DPP
+// row operations (no LDS traffic): two quad permutes, then the half-row and the
+// row mirror.  Every lane of a group ends with the bitwise-same total (each step
+// adds two equal partial sums in either order, and float addition commutes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Orders the LDS accesses of the lanes of one wave around this point (for LDS

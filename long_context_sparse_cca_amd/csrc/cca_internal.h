@@ -41,14 +41,17 @@ hipError_t launch_append_decode(const cca_cache_t* c, const void* q, const void*
 
 // Log-sum-exp combination of per-chunk decode partials (workspace layout: acc
 // [nslices][nchunks][d] floats, then ml [nslices][nchunks][2]) into out [nslices][d].
+// With lens non-null, lens[b] (b = slice / slices_per_seq) is then advanced by one
+// when it lies in [0, max_len].
 hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_bf16,
-                               int64_t nslices, int nchunks, hipStream_t stream);
+                               int64_t nslices, int nchunks, int32_t* lens, int slices_per_seq, int64_t max_len,
+                               hipStream_t stream);
 
 // Serving decode step: one new token per sequence at its own position lens[b]
 // (device), H_q = nq * c->H query heads (grouped-query attention), append fused.
 int serve_num_chunks(const cca_cache_t* c, int H_q, int64_t max_len);
 size_t serve_workspace_bytes(const cca_cache_t* c, int H_q);
-hipError_t launch_serve_append_decode(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q,
+hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream);
 

@@ -288,25 +288,50 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
   }
 }
 
+// One wave per slice.  Lane c reads chunk c's (max, sum) -- all chunks in parallel --
+// then every lane accumulates its D/64 columns over the chunks, the chunk weight
+// taken from lane c with a scalar read.  With `lens` non-null (serving step), the
+// first slice of every sequence then advances that sequence's length by one, after
+// the decode kernel of the same call has read it.
 template <int D>
 __global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __restrict__ ws_acc,
                                                               const float* __restrict__ ws_ml, void* __restrict__ out,
-                                                              int out_bf16, int nchunks) {
+                                                              int out_bf16, int nchunks, int32_t* __restrict__ lens,
+                                                              int slices_per_seq, int64_t max_len) {
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
   constexpr int CPL = D / kWave;
   const float* ml = ws_ml + (size_t)bh * nchunks * 2;
-  float M = kNegBig;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ml[2 * c]);
-  float l = 0.f, a[CPL];
+  float mc = kNegBig, lc = 0.f;
+  if (lane < nchunks) {
+    mc = ml[2 * lane];
+    lc = ml[2 * lane + 1];
+  }
+  const float M = wave_max_xor(mc, 1, kWave);
+  const float f = fast_exp2(mc - M);
+  const float l = wave_sum_xor(lane < nchunks ? f * lc : 0.f, 1, kWave);
+  float a[CPL];
 #pragma unroll
   for (int e = 0; e < CPL; ++e) a[e] = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float f = fast_exp2(ml[2 * c] - M);
-    l = fmaf(f, ml[2 * c + 1], l);
-    const float* ac = ws_acc + ((size_t)bh * nchunks + c) * D + lane * CPL;
+  const float* ac = ws_acc + (size_t)bh * nchunks * D + lane * CPL;
+  int c = 0;
+  for (; c + 4 <= nchunks; c += 4) {
+    float x[4][CPL];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) a[e] = fmaf(f, ac[e], a[e]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) x[u][e] = ac[(size_t)(c + u) * D + e];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float fc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), c + u));
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) a[e] = fmaf(fc, x[u][e], a[e]);
+    }
+  }
+  for (; c < nchunks; ++c) {
+    const float fc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), c));
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) a[e] = fmaf(fc, ac[(size_t)c * D + e], a[e]);
   }
   const float inv = 1.0f / l;
 #pragma unroll
@@ -314,6 +339,11 @@ __global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __res
     const size_t o = (size_t)bh * D + lane * CPL + e;
     if (out_bf16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(a[e] * inv);
     else reinterpret_cast<float*>(out)[o] = a[e] * inv;
+  }
+  if (lens != nullptr && lane == 0 && bh % slices_per_seq == 0) {
+    const int64_t b = bh / slices_per_seq;
+    const int32_t t = lens[b];
+    if (t >= 0 && t <= max_len) lens[b] = t + 1;
   }
 }
 
@@ -340,7 +370,7 @@ hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_ne
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
   hipLaunchKernelGGL((cca_decode_merge_kernel<D>), dim3((unsigned)BH), dim3(64), 0, stream, ws.acc, ws.ml, out,
-                     out_bf16, nchunks);
+                     out_bf16, nchunks, (int32_t*)nullptr, 1, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -399,14 +429,15 @@ hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* 
 }
 
 hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_bf16,
-                               int64_t nslices, int nchunks, hipStream_t stream) {
+                               int64_t nslices, int nchunks, int32_t* lens, int slices_per_seq, int64_t max_len,
+                               hipStream_t stream) {
   if (nslices == 0) return hipSuccess;
   if (d == 128)
     hipLaunchKernelGGL((cca_decode_merge_kernel<128>), dim3((unsigned)nslices), dim3(64), 0, stream, ws_acc, ws_ml,
-                       out, out_bf16, nchunks);
+                       out, out_bf16, nchunks, lens, slices_per_seq, max_len);
   else
     hipLaunchKernelGGL((cca_decode_merge_kernel<64>), dim3((unsigned)nslices), dim3(64), 0, stream, ws_acc, ws_ml,
-                       out, out_bf16, nchunks);
+                       out, out_bf16, nchunks, lens, slices_per_seq, max_len);
   return hipGetLastError();
 }
 

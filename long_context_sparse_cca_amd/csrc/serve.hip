@@ -155,8 +155,13 @@ __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < C::EPC; ++e) dot = fmaf(qf[j][e], kf[e], dot);
+        if constexpr (C::LPK <= 16) {
+          dot = lane_group_sum<C::LPK>(dot);
+        } else {
+          dot = lane_group_sum<16>(dot);
 #pragma unroll
-        for (int bb = 1; bb < C::LPK; bb <<= 1) dot += __shfl_xor(dot, bb, kWave);
+          for (int bb = 16; bb < C::LPK; bb <<= 1) dot += __shfl_xor(dot, bb, kWave);
+        }
         s[u][j] = ok[u] ? dot : -INFINITY;
       }
     }
@@ -237,7 +242,7 @@ int heads_per_block(int nq) {
 }
 
 template <typename T, int D, int RH>
-hipError_t launch_serve_t(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q, const void* q,
+hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, const void* q,
                           const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
                           hipStream_t stream) {
   const int nq = H_q / c->H;
@@ -261,11 +266,12 @@ hipError_t launch_serve_t(const cca_cache_t* c, const int32_t* lens, int64_t max
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
-  return launch_decode_merge(D, ws_acc, ws_ml, out, out_bf16, (int64_t)c->B * H_q, nchunks, stream);
+  return launch_decode_merge(D, ws_acc, ws_ml, out, out_bf16, (int64_t)c->B * H_q, nchunks, lens, H_q, max_len,
+                             stream);
 }
 
 template <typename T, int D>
-hipError_t launch_serve_d(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q, const void* q,
+hipError_t launch_serve_d(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, const void* q,
                           const void* k, const void* v, void* out, int out_f32, void* ws, float scale,
                           hipStream_t stream) {
   switch (heads_per_block(H_q / c->H)) {
@@ -296,7 +302,7 @@ size_t serve_workspace_bytes(const cca_cache_t* c, int H_q) {
   return (size_t)c->B * H_q * (size_t)serve_num_chunks(c, H_q, 0) * ((size_t)c->d + 2) * sizeof(float);
 }
 
-hipError_t launch_serve_append_decode(const cca_cache_t* c, const int32_t* lens, int64_t max_len, int H_q,
+hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream) {
   if (c->dt == CCA_BF16) {

@@ -117,6 +117,7 @@ def test_serve_out_of_range_length_gives_nan_and_leaves_cache(gpu):
     torch.cuda.synchronize()
     assert torch.isnan(out[1]).all()
     assert torch.equal(cache.ring_k[1], ring_before) and torch.equal(cache.core_k[1], core_before)
+    assert cache.lens.cpu().tolist() == [lens0[0] + 1, 10 ** 6]   # only the valid sequence advanced
     want = cca_serving.serve_rows(Q[0], K[0], V[0], [lens0[0]], g, k, scale, core_dtype=dt)
     err = np.abs(out[0].cpu().numpy()[:, None, :] - want).max()
     assert err <= TOL[dt]
