@@ -257,6 +257,36 @@ int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t 
                                    void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
 
 /*
+ * Chunked append: n new tokens for every sequence in one call (chunked prefill
+ * into an existing cache, several draft tokens, ...), with per-sequence lengths
+ * and grouped-query heads as in cca_cache_append_decode_varlen.  Returns the
+ * attention output of every new token: the token at position p = lens[b] + i
+ * attends to the core tokens before its raw window and to the raw keys
+ * (p/g - k_local)*g .. p, i.e. exactly the prefill output of row p ([CCA]
+ * locality-preserving module and global-local fusion; a token's output depends
+ * only on the tokens before it).  Afterwards the chunk is in the cache: its
+ * keys/values in their ring slots, every group it completes pooled into its core
+ * slot (mean query over the query heads sharing each key/value head), and
+ * lens[b] advanced by n.
+ *   n       : 1 <= n <= k_local*g + 1 (then no token of the chunk can see a core
+ *             token pooled from the same chunk); longer chunks are split by the
+ *             caller into consecutive calls.  CCA_ERR_INVALID otherwise.
+ *   lens, max_len, H_q : as for cca_cache_append_decode_varlen; capacity needs
+ *             (max_len + n)/g <= max_groups (else CCA_ERR_CAPACITY).  A sequence
+ *             with lens[b] outside [0, max_len] gets NaN outputs and is left as is.
+ *   q       : device [B, H_q, n, d];  k, v : device [B, c->H, n, d];
+ *   out     : device [B, H_q, n, d] of out_dt (CCA_F32 or c->dt).
+ *   workspace : device, >= cca_extend_workspace_bytes(c, n) bytes (start
+ *             positions plus a staging copy of the raw window of every
+ *             key/value head: about 2*B*H*((k_local+1)*g + n)*d elements).
+ * The attention runs on the same MFMA kernels as cca_attention.
+ */
+size_t cca_extend_workspace_bytes(const cca_cache_t* c, int n);
+int cca_cache_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n,
+                     const void* q, const void* k, const void* v, void* out, int out_dt,
+                     void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
+
+/*
  * KV-cache accounting ([CCA] compute/memory efficiency, Fig. 3: the cache
  * holds core plus local tokens instead of every token).  Host-only integer
  * arithmetic, no device work.  After n_tokens tokens with group size g and

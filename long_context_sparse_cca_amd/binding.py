@@ -86,6 +86,10 @@ EXPORTS = {
                                                       ctypes.c_int] + [ctypes.c_void_p] * 4
                                        + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float,
                                           ctypes.c_void_p]),
+    "cca_extend_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int]),
+    "cca_cache_extend": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int] + [ctypes.c_void_p] * 4
+                         + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
     "cca_kv_cache_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_int64)]),
@@ -331,6 +335,7 @@ class ServeCache(KVCache):
         ws_bytes = _lib.cca_serve_workspace_bytes(ctypes.byref(self.desc), H_q)
         self.serve_ws = torch.empty((ws_bytes + 15) // 16 * 4, dtype=torch.float32, device=device)
         self.serve_ws_bytes = ws_bytes
+        self._ext_ws = None   # staging workspace of `extend`, sized on first use
 
     def _seq_desc(self, b: int):
         B, H, d = self.shape_bhd
@@ -382,6 +387,37 @@ class ServeCache(KVCache):
                                                    _ptr(self.serve_ws), self.serve_ws_bytes, scale, _stream()),
                "cca_cache_append_decode_varlen")
         self.lens_host = [x + 1 for x in self.lens_host]   # the call advanced `lens` on the device
+        return out
+
+    def extend(self, q, k, v, out_dtype=None, scale: float | None = None):
+        """Append n tokens to every sequence and return their outputs [B, H_q, n, d].
+
+        q: [B, H_q, n, d]; k, v: [B, H_kv, n, d].  Chunks longer than k_local*g + 1 are
+        split into consecutive cca_cache_extend calls (each advances `lens`).
+        """
+        B, H, d = self.shape_bhd
+        n = q.shape[2]
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        _need(q, (B, self.H_q, n, d), self.dtype, "q")
+        _need(k, (B, H, n, d), self.dtype, "k")
+        _need(v, (B, H, n, d), self.dtype, "v")
+        out = torch.empty((B, self.H_q, n, d), dtype=out_dtype, device=q.device)
+        piece = self.desc.k_local * self.desc.g + 1
+        for a in range(0, n, piece):
+            e = min(n, a + piece)
+            m = e - a
+            qs, ks, vs = (x[:, :, a:e].contiguous() for x in (q, k, v))
+            os_ = torch.empty((B, self.H_q, m, d), dtype=out_dtype, device=q.device)
+            ws_bytes = _lib.cca_extend_workspace_bytes(ctypes.byref(self.desc), m)
+            if self._ext_ws is None or self._ext_ws.numel() * 4 < ws_bytes:
+                self._ext_ws = torch.empty(((ws_bytes + 15) // 16) * 4, dtype=torch.float32, device=q.device)
+            _check(_lib.cca_cache_extend(ctypes.byref(self.desc), _ptr(self.lens), max(self.lens_host), self.H_q, m,
+                                         _ptr(qs), _ptr(ks), _ptr(vs), _ptr(os_), _dtype_code(out_dtype),
+                                         _ptr(self._ext_ws), self._ext_ws.numel() * 4, scale, _stream()),
+                   "cca_cache_extend")
+            self.lens_host = [x + m for x in self.lens_host]   # the call advanced `lens` on the device
+            out[:, :, a:e] = os_
         return out
 
 

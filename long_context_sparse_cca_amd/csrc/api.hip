@@ -212,6 +212,33 @@ int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t 
                                                     workspace, scale, stream));
 }
 
+size_t cca_extend_workspace_bytes(const cca_cache_t* c, int n) {
+  if (c == nullptr || c->B < 1 || c->H < 1 || (c->d != 64 && c->d != 128) || c->g < 1 || c->k_local < 0 ||
+      c->max_groups < 1 || n < 1)
+    return 0;
+  return cca::extend_workspace_bytes(c, n);
+}
+
+int cca_cache_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
+                     const void* k, const void* v, void* out, int out_dt, void* workspace, size_t workspace_bytes,
+                     float scale, hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
+  if (H_q < 1 || H_q % c->H != 0 || (int64_t)c->B * H_q > ((int64_t)1 << 24)) return CCA_ERR_INVALID;
+  if (n < 1 || (int64_t)n > (int64_t)c->k_local * c->g + 1) return CCA_ERR_INVALID;
+  if (lens == nullptr || ((uintptr_t)lens & 3u) != 0 || max_len < 0 || max_len + n >= INT32_MAX)
+    return CCA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+      !isfinite(scale))
+    return CCA_ERR_INVALID;
+  if ((max_len + n) / c->g > c->max_groups) return CCA_ERR_CAPACITY;
+  if ((int64_t)c->B * H_q * ((n + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
+  if (workspace_bytes < cca_extend_workspace_bytes(c, n)) return CCA_ERR_WORKSPACE;
+  return hip_status(cca::launch_extend(c, lens, max_len, H_q, n, q, k, v, out, out_dt == CCA_F32, workspace, scale,
+                                       stream));
+}
+
 int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt, int64_t* resident_bytes,
                        int64_t* full_bytes) {
   if (n_tokens < 0 || g < 1 || k_local < 0 || B < 1 || H < 1 || d < 1) return CCA_ERR_INVALID;

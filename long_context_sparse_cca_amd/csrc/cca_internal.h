@@ -8,6 +8,19 @@ namespace cca {
 
 // Each launcher enqueues its kernels on `stream` and returns the launch status.
 // Arguments have been validated by the caller (api.hip).
+// Attention of new tokens over a cached prefix (chunked append), run by the
+// prefill attention kernels with offsets: query i of a slice sits at absolute
+// position pos[b] + i; the raw key at absolute position u is row u - raw0 of the
+// raw K/V slice, raw0 = max(0, pos[b]/g - k_local)*g (the first raw position any
+// query of the slice sees); core token j is row j of the core slice.
+struct ExtendArgs {
+  const int32_t* pos;  // device [B]: position of the first new token; < 0 marks an invalid sequence
+  int Hq;              // query heads: query slice bh belongs to sequence bh / Hq
+  int n;               // new tokens (queries) per slice
+  int64_t raw_rows;    // rows per raw K/V slice
+  int64_t core_rows;   // rows per core K/V slice
+};
+
 // Grouped-query attention: nq = H / H_kv query heads share each key/value head.
 // Query/output slices are (b, h) = b*H + h; key/value and core slices are
 // (b, h_kv) = b*H_kv + h_kv, and query slice s reads key/value slice s / nq.
@@ -22,6 +35,15 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
 hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                     void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
                                     float scale, hipStream_t stream);
+
+// Extend-mode attention (bf16 d=128 fast kernel or the generic one): q, out [B*H][n][d];
+// k, v [B*H_kv][ext.raw_rows][d]; kc, vc [B*H_kv][ext.core_rows][d].
+hipError_t launch_extend_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
+                                   const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
+                                   float scale, const ExtendArgs& ext, hipStream_t stream);
+hipError_t launch_extend_attention_bf16_d128(const void* q, const void* k, const void* v, const void* kc,
+                                             const void* vc, void* out, int out_f32, int BH, int nq, int g,
+                                             int k_local, float scale, const ExtendArgs& ext, hipStream_t stream);
 
 hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc,
                              const void* vc, int64_t L, hipStream_t stream);
@@ -54,5 +76,11 @@ size_t serve_workspace_bytes(const cca_cache_t* c, int H_q);
 hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream);
+
+// Chunked append of n tokens per sequence (extend.hip).
+size_t extend_workspace_bytes(const cca_cache_t* c, int n);
+hipError_t launch_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
+                         const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
+                         hipStream_t stream);
 
 }  // namespace cca

@@ -62,26 +62,52 @@ __device__ __forceinline__ int vt_col_bf16(int quad) {  // quad = first key / 4
   return (quad >> 2) * 16 + (q4 & 1) * 8 + (q4 >> 1) * 4;
 }
 
-template <typename T, int D>
+// EXT: attention of new tokens over a cached prefix (ExtendArgs): positions are absolute,
+// query i of the slice is at ext.pos[b] + i, raw key u is row u - raw0 of the raw slice.
+// Without EXT the slice is a whole sequence: pos0 = raw0 = 0, L queries, L raw rows.
+template <typename T, int D, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ Kc, const T* __restrict__ Vc, void* __restrict__ Out, int out_f32,
-    int BH, int nq, int64_t L, int g, int k_local, float scale, int ntiles) {
+    int BH, int nq, int64_t L, int g, int k_local, float scale, int ntiles, ExtendArgs ext) {
   using C = PrefillCfg<T, D>;
   __shared__ __attribute__((aligned(16))) T lds_k[2][C::LDS_K];
   __shared__ __attribute__((aligned(16))) T lds_v[2][C::LDS_V];
 
   int bh, qtile;
   map_block(BH * ntiles, ntiles, bh, qtile);
-  const int64_t m = L / g;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int64_t q0 = (int64_t)qtile * C::BM;
-  const int64_t q_last = min(q0 + C::BM - 1, L - 1);
+  // absolute position of query 0, first raw position of the raw slice, queries per slice
+  int64_t pos0 = 0, raw0 = 0, nQ = L, raw_rows = L, core_rows = L / g;
+  if constexpr (EXT) {
+    pos0 = ext.pos[bh / ext.Hq];
+    nQ = ext.n;
+    raw_rows = ext.raw_rows;
+    core_rows = ext.core_rows;
+    if (pos0 < 0) {
+      // invalid sequence: NaN outputs, nothing read
+      const int64_t i = (int64_t)qtile * C::BM + wave * 32 + l32;
+      if (i < nQ) {
+        const size_t o = ((size_t)bh * nQ + i) * D;
+        for (int c = hf; c < D; c += 2) {
+          if (out_f32) reinterpret_cast<float*>(Out)[o + c] = __builtin_nanf("");
+          else reinterpret_cast<uint16_t*>(Out)[o + c] = 0x7fc0;
+        }
+      }
+      return;
+    }
+    raw0 = max<int64_t>(0, pos0 / g - k_local) * g;
+  }
+  const int64_t Lend = pos0 + nQ;                       // one past the last query position
+  const int64_t m = core_rows;
+
+  const int64_t q0 = pos0 + (int64_t)qtile * C::BM;
+  const int64_t q_last = min(q0 + C::BM - 1, Lend - 1);
   const int64_t nc_wg = max<int64_t>(0, q_last / g - k_local);      // core tokens any row sees
   const int64_t rl_wg = max<int64_t>(0, q0 / g - k_local) * g;      // first raw key any row sees
   const int n_core_tiles = (int)((nc_wg + C::BN - 1) / C::BN);
@@ -90,18 +116,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- this wave's queries
   const int64_t qa = q0 + wave * 32;
-  const bool wave_live = qa < L;
-  const int64_t qb = min(qa + 31, L - 1);
-  const int64_t q_lane = min(qa + l32, L - 1);
+  const bool wave_live = qa < Lend;
+  const int64_t qb = min(qa + 31, Lend - 1);
+  const int64_t q_lane = min(qa + l32, Lend - 1);
   const int64_t cl_lane = q_lane / g - k_local;                      // core visible iff j < cl_lane
   const int64_t rl_lane = max<int64_t>(0, cl_lane) * g;              // raw visible iff rl <= u <= q
   const int64_t cl_min = qa / g - k_local, cl_max = qb / g - k_local;
   const int64_t rl_min = max<int64_t>(0, cl_min) * g, rl_max = max<int64_t>(0, cl_max) * g;
 
   const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
-  const T* Qs = Q + (size_t)bh * L * D;
-  const T* Ks = K + (size_t)bkv * L * D;
-  const T* Vs = V + (size_t)bkv * L * D;
+  const T* Qs = Q + (size_t)bh * nQ * D;                // query slice; row = position - pos0
+  const T* Ks = K + (size_t)bkv * raw_rows * D;
+  const T* Vs = V + (size_t)bkv * raw_rows * D;
   const T* Kcs = Kc + (size_t)bkv * m * D;
   const T* Vcs = Vc + (size_t)bkv * m * D;
 
@@ -111,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int QREG = (C::EB == 2) ? D / 16 : D / 8;
   uint4 qop[QREG];
   {
-    const T* qrow = Qs + (size_t)q_lane * D;
+    const T* qrow = Qs + (size_t)(q_lane - pos0) * D;
 #pragma unroll
     for (int s = 0; s < QREG; ++s) {
       if constexpr (C::EB == 2) qop[s] = ld16(qrow + s * 16 + hf * 8);
@@ -133,17 +159,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   auto load_tile = [&](int it) {
     const T *ks, *vs;
-    int64_t base, lim;
+    int64_t base, lim, off0;   // tile's first key, last valid key, key of row 0 of the slice
     if (it < n_core_tiles) {
-      ks = Kcs; vs = Vcs; base = (int64_t)it * C::BN; lim = m - 1;
+      ks = Kcs; vs = Vcs; base = (int64_t)it * C::BN; lim = m - 1; off0 = 0;
     } else {
-      ks = Ks; vs = Vs; base = rl_wg + (int64_t)(it - n_core_tiles) * C::BN; lim = L - 1;
+      ks = Ks; vs = Vs; base = rl_wg + (int64_t)(it - n_core_tiles) * C::BN; lim = Lend - 1; off0 = raw0;
     }
 #pragma unroll
     for (int i = 0; i < C::KCH; ++i) {
       const int id = tid + i * C::NT;
       const int row = id / C::CPR, c = id % C::CPR;
-      const int64_t gr = min(base + row, lim);
+      const int64_t gr = min(base + row, lim) - off0;
       kreg[i] = ld16(ks + (size_t)gr * D + c * C::EPC);
     }
 #pragma unroll
@@ -153,7 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int a = id % C::KG, c = id / C::KG;   // key group fastest: conflict-free V^T stores
 #pragma unroll
         for (int e = 0; e < C::KPT; ++e) {
-          const int64_t gr = min(base + a * C::KPT + e, lim);
+          const int64_t gr = min(base + a * C::KPT + e, lim) - off0;
           vreg[u][e] = ld16(vs + (size_t)gr * D + c * C::EPC);
         }
       }
@@ -318,10 +344,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- normalise and store: lane (query l32, half hf) holds O[q][dt*32 + 8i + 4hf + j]
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   const float inv = 1.0f / l_tot;
-  const int64_t q_row = qa + l32;
-  if (q_row >= L) return;
+  const int64_t q_row = qa + l32 - pos0;                 // row within the slice
+  if (q_row >= nQ) return;
   if (out_f32) {
-    float* o = reinterpret_cast<float*>(Out) + ((size_t)bh * L + q_row) * D;
+    float* o = reinterpret_cast<float*>(Out) + ((size_t)bh * nQ + q_row) * D;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -331,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) = v;
       }
   } else if constexpr (C::EB == 2) {
-    T* o = reinterpret_cast<T*>(Out) + ((size_t)bh * L + q_row) * D;
+    T* o = reinterpret_cast<T*>(Out) + ((size_t)bh * nQ + q_row) * D;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -358,9 +384,24 @@ hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const v
   const int ntiles = (int)((L + C::BM - 1) / C::BM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((cca_prefill_kernel<T, D>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
+  const ExtendArgs none{nullptr, 1, 0, 0, 0};
+  hipLaunchKernelGGL((cca_prefill_kernel<T, D, false>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq, L, g,
-                     k_local, scale, ntiles);
+                     k_local, scale, ntiles, none);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_extend_t(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out,
+                           int out_f32, int BH, int nq, int g, int k_local, float scale, const ExtendArgs& ext,
+                           hipStream_t stream) {
+  using C = PrefillCfg<T, D>;
+  const int ntiles = (ext.n + C::BM - 1) / C::BM;
+  const int64_t nblocks = (int64_t)BH * ntiles;
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((cca_prefill_kernel<T, D, true>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq,
+                     (int64_t)0, g, k_local, scale, ntiles, ext);
   return hipGetLastError();
 }
 
@@ -376,6 +417,18 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
   }
   if (d == 128) return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream);
   return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream);
+}
+
+hipError_t launch_extend_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
+                                   const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
+                                   float scale, const ExtendArgs& ext, hipStream_t stream) {
+  if (dt == CCA_BF16) {
+    if (d == 128)
+      return launch_extend_attention_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
+    return launch_extend_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
+  }
+  if (d == 128) return launch_extend_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, g, k_local, scale, ext, stream);
+  return launch_extend_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, g, k_local, scale, ext, stream);
 }
 
 }  // namespace cca

@@ -58,10 +58,14 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// EXT: attention of new tokens over a cached prefix (ExtendArgs): positions are absolute,
+// query i of the slice is at ext.pos[b] + i, raw key u is row u - raw0 of the raw slice.
+// Without EXT the slice is a whole sequence: pos0 = raw0 = 0, L queries, L raw rows.
+template <bool EXT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
-    int nq, int L, int g, int k_local, float scale, int ntiles) {
+    int nq, int L, int g, int k_local, float scale, int ntiles, ExtendArgs ext) {
   // one array per buffer: the LDS-DMA fill of one buffer then provably does not
   // alias the operand reads of the other, so no wait is forced between them
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
@@ -69,15 +73,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int bh, qtile;
   map_block(BH * ntiles, ntiles, bh, qtile);
-  const int m = L / g;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int q0 = qtile * kBM;
-  const int q_last = min(q0 + kBM - 1, L - 1);
+  // absolute position of query 0, first raw position of the raw slice, queries per slice
+  int pos0 = 0, raw0 = 0, nQ = L;
+  int64_t raw_rows = L, core_rows = L / g;
+  if constexpr (EXT) {
+    pos0 = ext.pos[bh / ext.Hq];
+    nQ = ext.n;
+    raw_rows = ext.raw_rows;
+    core_rows = ext.core_rows;
+    if (pos0 < 0) {
+      // invalid sequence: NaN outputs, nothing read
+      const int i = qtile * kBM + wave * 32 + l32;
+      if (i < nQ) {
+        const size_t o = ((size_t)bh * nQ + i) * kD;
+        for (int c = hf; c < kD; c += 2) {
+          if (out_f32) reinterpret_cast<float*>(Out)[o + c] = __builtin_nanf("");
+          else reinterpret_cast<uint16_t*>(Out)[o + c] = 0x7fc0;
+        }
+      }
+      return;
+    }
+    raw0 = max(0, pos0 / g - k_local) * g;
+  }
+  const int Lend = pos0 + nQ;                             // one past the last query position
+  const int m = (int)core_rows;
+
+  const int q0 = pos0 + qtile * kBM;
+  const int q_last = min(q0 + kBM - 1, Lend - 1);
   const int nc_wg = max(0, q_last / g - k_local);        // core tokens any row sees
   const int rl_wg = max(0, q0 / g - k_local) * g;        // first raw key any row sees
   const int n_core_tiles = (nc_wg + kBN - 1) / kBN;
@@ -86,25 +114,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- this wave's 32 queries (wave-uniform bounds in scalar registers)
   const int qa = q0 + wave * 32;
-  const bool wave_live = qa < L;
-  const int qb = min(qa + 31, L - 1);
+  const bool wave_live = qa < Lend;
+  const int qb = min(qa + 31, Lend - 1);
   const int cl_min = qa / g - k_local, cl_max = qb / g - k_local;
   const int rl_min = max(0, cl_min) * g, rl_max = max(0, cl_max) * g;
-  const int q_lane = min(qa + l32, L - 1);
+  const int q_lane = min(qa + l32, Lend - 1);
   const int cl_lane = q_lane / g - k_local;              // core j visible iff j < cl_lane
   const int rl_lane = max(0, cl_lane) * g;               // raw u visible iff rl_lane <= u <= q_lane
 
-  const size_t slice = (size_t)bh * L * kD;
+  const size_t slice = (size_t)bh * nQ * kD;             // query / output slice
   const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
-  const bf16_t* Ks = K + (size_t)bkv * L * kD;
-  const bf16_t* Vs = V + (size_t)bkv * L * kD;
-  const bf16_t* Kcs = Kc + (size_t)bkv * m * kD;
-  const bf16_t* Vcs = Vc + (size_t)bkv * m * kD;
+  const bf16_t* Ks = K + (size_t)bkv * raw_rows * kD;
+  const bf16_t* Vs = V + (size_t)bkv * raw_rows * kD;
+  const bf16_t* Kcs = Kc + (size_t)bkv * core_rows * kD;
+  const bf16_t* Vcs = Vc + (size_t)bkv * core_rows * kD;
 
   // ---- Q operand (B of S^T = K Q^T): slice d16 holds dims 16*d16 + 8*hf .. +8
   uint4 qop[kD / 16];
   {
-    const bf16_t* qrow = Q + slice + (size_t)q_lane * kD;
+    const bf16_t* qrow = Q + slice + (size_t)(q_lane - pos0) * kD;
 #pragma unroll
     for (int s = 0; s < kD / 16; ++s) qop[s] = ld16(qrow + s * 16 + hf * 8);
   }
@@ -122,17 +150,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   auto issue_tile = [&](int it, int buf) {
     const bf16_t *ks, *vs;
-    int base, lim;
+    int base, lim, off0;   // tile's first key, last valid key, key of row 0 of the slice
     if (it < n_core_tiles) {
-      ks = Kcs; vs = Vcs; base = it * kBN; lim = m - 1;
+      ks = Kcs; vs = Vcs; base = it * kBN; lim = m - 1; off0 = 0;
     } else {
-      ks = Ks; vs = Vs; base = rl_wg + (it - n_core_tiles) * kBN; lim = L - 1;
+      ks = Ks; vs = Vs; base = rl_wg + (it - n_core_tiles) * kBN; lim = Lend - 1; off0 = raw0;
     }
     uint8_t* dst0 = (buf ? lds1 : lds0) + wave * 8 * kRowBytes;
     if (base + kBN - 1 <= lim) {
       // whole tile in range: uniform tile base + per-lane 32-bit offset
-      const uint8_t* kt = (const uint8_t*)ks + (size_t)base * kRowBytes;
-      const uint8_t* vt = (const uint8_t*)vs + (size_t)base * kRowBytes;
+      const uint8_t* kt = (const uint8_t*)ks + (size_t)(base - off0) * kRowBytes;
+      const uint8_t* vt = (const uint8_t*)vs + (size_t)(base - off0) * kRowBytes;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint8_t* dst = dst0 + i * 4 * kRowBytes;
@@ -145,7 +173,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // last tile of a range: rows past the end repeat the last valid row
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const size_t goff = (size_t)min(base + fill_row[i], lim) * kRowBytes + fill_off[i];
+        const size_t goff = (size_t)(min(base + fill_row[i], lim) - off0) * kRowBytes + fill_off[i];
         uint8_t* dst = dst0 + i * 4 * kRowBytes;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)ks + goff),
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -305,8 +333,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (!wave_live) return;
   // ---- normalise and store: lane (query l32, half hf) holds O[q][dt*32 + 8i + 4hf + j]
   const float inv = 1.0f / xhalf_sum(l_run);
-  const int q_row = qa + l32;
-  if (q_row >= L) return;
+  const int q_row = qa + l32 - pos0;                     // row within the slice
+  if (q_row >= nQ) return;
   if (out_f32) {
     float* o = reinterpret_cast<float*>(Out) + slice + (size_t)q_row * kD;
 #pragma unroll
@@ -339,9 +367,22 @@ hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v,
   const int ntiles = (int)((L + kBM - 1) / kBM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel, dim3((unsigned)nblocks), dim3(512), 0, stream, (const bf16_t*)q,
-                     (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out, out_f32, BH,
-                     nq, (int)L, g, k_local, scale, ntiles);
+  const ExtendArgs none{nullptr, 1, 0, 0, 0};
+  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel<false>, dim3((unsigned)nblocks), dim3(512), 0, stream,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out,
+                     out_f32, BH, nq, (int)L, g, k_local, scale, ntiles, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_extend_attention_bf16_d128(const void* q, const void* k, const void* v, const void* kc,
+                                             const void* vc, void* out, int out_f32, int BH, int nq, int g,
+                                             int k_local, float scale, const ExtendArgs& ext, hipStream_t stream) {
+  const int ntiles = (ext.n + kBM - 1) / kBM;
+  const int64_t nblocks = (int64_t)BH * ntiles;
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel<true>, dim3((unsigned)nblocks), dim3(512), 0, stream,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out,
+                     out_f32, BH, nq, 0, g, k_local, scale, ntiles, ext);
   return hipGetLastError();
 }
 
