@@ -166,16 +166,19 @@ def dense_comparison(binding, accounting, dev, seed):
 
 
 def serving_decode(binding, accounting, dev, seed, steps: int = 64):
-    """Serving decode step with per-sequence lengths and grouped-query attention, outside the
-    timed steps: B=8 sequences at lengths 65536 + 9362*b (64K .. 128K), H_q=32 query heads
-    over H_kv=8 key/value heads (r=4), d=128, g=16, k=64, bf16; each step is one
-    cca_cache_append_decode_varlen call (append + pooling + attention of one token per sequence)."""
+    """Serving with per-sequence lengths and grouped-query attention, outside the timed steps:
+    B=8 sequences at lengths 65536 + 9362*b (64K .. 128K), H_q=32 query heads over H_kv=8
+    key/value heads (r=4), d=128, g=16, k=64, bf16.  Decode: each step is one
+    cca_cache_append_decode_varlen call (append + pooling + attention of one token per
+    sequence).  Chunked append: cca_cache_extend calls of 1024 tokens per sequence."""
     import torch
 
     from long_context_sparse_cca_amd.synth import torch_inputs
     B, Hq, Hkv = 8, 32, 8
     lens0 = [65536 + 9362 * b for b in range(B)]
-    cache = binding.ServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + G, dtype=torch.bfloat16, device=dev)
+    n_ext, chunks = 1024, 3
+    cache = binding.ServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + chunks * n_ext + G, dtype=torch.bfloat16,
+                               device=dev)
     for b, L in enumerate(lens0):
         q, _, _ = torch_inputs(1, Hq, L, D, torch.bfloat16, dev, seed=seed + 10 + b, heavy_frac=HEAVY)
         _, k, v = torch_inputs(1, Hkv, L, D, torch.bfloat16, dev, seed=seed + 30 + b, heavy_frac=HEAVY)
@@ -204,11 +207,34 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
     byt = [accounting.serve_bytes(lens_at[s], Hq, Hkv, D, G, KL, 2, nchunks) for s in range(warm, steps)]
     us_mean = sum(us) / len(us)
     gbs = sum(byt) / len(byt) / (us_mean * 1e-6) / 1e9
+    # chunked append: 1024 new tokens for every sequence per call (four 256-query tiles; one call takes up to k*g+1)
+    qe = torch.randn((B, Hq, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
+    ke = torch.randn((B, Hkv, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
+    ve = torch.randn((B, Hkv, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
+    cache.extend(qe, ke, ve)   # first call sizes the staging workspace
+    torch.cuda.synchronize()
+    ext_ms, ext_fl = [], []
+    for _ in range(chunks - 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lens_now = list(cache.lens_host)
+        e0.record(stream)
+        cache.extend(qe, ke, ve)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ext_ms.append(e0.elapsed_time(e1))
+        ext_fl.append(accounting.extend_flops(lens_now, n_ext, Hq, D, G, KL))
+    ms = sum(ext_ms) / len(ext_ms)
+    tf = sum(ext_fl) / len(ext_fl) / (ms * 1e-3) / 1e12
     return {"config": {"B": B, "H_q": Hq, "H_kv": Hkv, "d": D, "g": G, "k_local": KL,
                        "lengths": lens0, "steps_timed": steps - warm},
             "us_per_step": us_mean, "bytes_per_step": sum(byt) / len(byt),
             "roofline": {"kernel": "cca_serve_decode_kernel<bf16,128,4> + cca_decode_merge_kernel", "bound": "hbm",
-                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+            "chunked_append": {"tokens_per_sequence": n_ext, "ms_per_call": ms,
+                               "tokens_per_s": B * n_ext / (ms * 1e-3), "flops_per_call": sum(ext_fl) / len(ext_fl),
+                               "roofline": {"kernel": "cca_prefill_bf16_d128_kernel<extend> (+ gather, append)",
+                                            "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                            "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
 
 def main():

@@ -78,6 +78,16 @@ def serve_bytes(lens, H_q: int, H_kv: int, d: int, g: int, k: int, elem: int, n_
     return total
 
 
+def extend_flops(lens, n: int, H_q: int, d: int, g: int, k: int) -> int:
+    """Algorithmic FLOPs of one chunked append: 4*d per visible (new token, key) pair and
+    query head, for the n tokens at positions lens[b] .. lens[b]+n-1 of every sequence."""
+    total = 0
+    for t0 in lens:
+        for p in range(int(t0), int(t0) + n):
+            total += decode_keys(p, g, k)
+    return 4 * d * H_q * total
+
+
 def kv_cache_bytes(n_tokens: int, g: int, k: int, B: int, H: int, d: int, elem: int) -> tuple[int, int]:
     per_token = B * H * 2 * d * elem
     return per_token * (n_tokens // g + (k + 1) * g), per_token * n_tokens

@@ -392,8 +392,9 @@ class ServeCache(KVCache):
     def extend(self, q, k, v, out_dtype=None, scale: float | None = None):
         """Append n tokens to every sequence and return their outputs [B, H_q, n, d].
 
-        q: [B, H_q, n, d]; k, v: [B, H_kv, n, d].  Chunks longer than k_local*g + 1 are
-        split into consecutive cca_cache_extend calls (each advances `lens`).
+        q: [B, H_q, n, d]; k, v: [B, H_kv, n, d].  Chunks longer than k_local*g + 1 (rounded
+        down to a multiple of 256 when that is at least 256) are split into consecutive
+        cca_cache_extend calls (each advances `lens`).
         """
         B, H, d = self.shape_bhd
         n = q.shape[2]
@@ -403,12 +404,15 @@ class ServeCache(KVCache):
         _need(k, (B, H, n, d), self.dtype, "k")
         _need(v, (B, H, n, d), self.dtype, "v")
         out = torch.empty((B, self.H_q, n, d), dtype=out_dtype, device=q.device)
+        # at most k*g+1 tokens per call; above 256, whole 256-query tiles of the attention kernel
         piece = self.desc.k_local * self.desc.g + 1
+        if piece >= 256:
+            piece -= piece % 256
         for a in range(0, n, piece):
             e = min(n, a + piece)
             m = e - a
             qs, ks, vs = (x[:, :, a:e].contiguous() for x in (q, k, v))
-            os_ = torch.empty((B, self.H_q, m, d), dtype=out_dtype, device=q.device)
+            os_ = out if m == n else torch.empty((B, self.H_q, m, d), dtype=out_dtype, device=q.device)
             ws_bytes = _lib.cca_extend_workspace_bytes(ctypes.byref(self.desc), m)
             if self._ext_ws is None or self._ext_ws.numel() * 4 < ws_bytes:
                 self._ext_ws = torch.empty(((ws_bytes + 15) // 16) * 4, dtype=torch.float32, device=q.device)
@@ -417,7 +421,8 @@ class ServeCache(KVCache):
                                          _ptr(self._ext_ws), self._ext_ws.numel() * 4, scale, _stream()),
                    "cca_cache_extend")
             self.lens_host = [x + m for x in self.lens_host]   # the call advanced `lens` on the device
-            out[:, :, a:e] = os_
+            if m != n:
+                out[:, :, a:e] = os_
         return out
 
 
