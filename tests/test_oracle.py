@@ -19,3 +19,13 @@ from tests import serving_pins
 def test_serving_pin(pin):
     ok, detail = pin(oracle.cca_serving)
     assert ok, detail
+
+
+import oracle.cca_backward
+from tests import backward_pins
+
+
+@pytest.mark.parametrize("pin", backward_pins.ALL_BACKWARD_PINS, ids=lambda f: f.__name__)
+def test_backward_pin(pin):
+    ok, detail = pin(oracle.cca_backward)
+    assert ok, detail

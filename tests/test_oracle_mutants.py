@@ -128,3 +128,47 @@ def test_some_serving_pin_catches(name, monkeypatch):
         if not ok:
             failed.append(pin.__name__)
     assert failed, f"no serving pin caught mutant '{name}'"
+
+
+import oracle.cca_backward as bwd
+from tests import backward_pins
+
+
+def _softmax_backward_sign(p, dp):
+    p = np.asarray(p, np.float64)
+    dp = np.asarray(dp, np.float64)
+    return p * (p @ dp - dp)
+
+
+def _pool_backward_no_weight_grad(a, Kg, Vg, q_hat, dKc_j, dVc_j, scale):
+    return np.outer(a, dKc_j), np.outer(a, dVc_j), np.zeros_like(q_hat, dtype=np.float64)
+
+
+_orig_pool_backward = bwd.pool_backward_group
+
+
+def _pool_backward_no_query_grad(a, Kg, Vg, q_hat, dKc_j, dVc_j, scale):
+    dKg, dVg, _ = _orig_pool_backward(a, Kg, Vg, q_hat, dKc_j, dVc_j, scale)
+    return dKg, dVg, np.zeros_like(q_hat, dtype=np.float64)
+
+
+BACKWARD_MUTANTS = {
+    "softmax backward with the wrong sign": ("softmax_backward", _softmax_backward_sign),
+    "pooling weights treated as constants": ("pool_backward_group", _pool_backward_no_weight_grad),
+    "no gradient into the scoring query": ("pool_backward_group", _pool_backward_no_query_grad),
+}
+
+
+@pytest.mark.parametrize("name", list(BACKWARD_MUTANTS))
+def test_some_backward_pin_catches(name, monkeypatch):
+    attr, fn = BACKWARD_MUTANTS[name]
+    monkeypatch.setattr(bwd, attr, fn)
+    failed = []
+    for pin in backward_pins.ALL_BACKWARD_PINS:
+        try:
+            ok, _ = pin(bwd)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"no backward pin caught mutant '{name}'"
