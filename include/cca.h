@@ -134,6 +134,38 @@ int cca_attention_gqa(const void* q, const void* k, const void* v, const void* k
                       int dt, int out_dt, hipStream_t stream);
 
 /*
+ * Training ([CCA] Triton section: the fused operator serves training as well;
+ * the models are fine-tuned with it).  bf16 inputs, d = 128, one query head per
+ * key/value head; other dtypes or head dims give CCA_ERR_UNSUPPORTED.
+ *
+ * cca_prefill_lse: cca_prefill that also writes, for every query t, the
+ *   natural-log log-sum-exp of its scaled scores over its visible keys,
+ *   lse[t] = log sum_i exp(scale * key_i . Q[t])  (device float32 [B, H, L]),
+ *   which the backward pass uses to recompute the softmax weights.
+ *
+ * cca_backward: gradients of sum(out * dout) with respect to q, k, v, by the
+ *   chain rule through the attention softmax and through the pooling softmax
+ *   (core token j: Kc = a.K_group, Vc = a.V_group, a = softmax(scale q_hat.K_group),
+ *   so the gradients of Kc and Vc reach the group's keys and values and its
+ *   scoring query Q[j*g+g-1]).  The forward's rounding of the core tokens to
+ *   bf16 is treated as the identity.
+ *   q, k, v, kc, vc, out : the forward's inputs and results (bf16, as above);
+ *   lse   : device float32 [B, H, L] from cca_prefill_lse;
+ *   dout  : device bf16 [B, H, L, d], the gradient of the output;
+ *   dq, dk, dv : device float32 [B, H, L, d], written (every element);
+ *   workspace : device, >= cca_backward_workspace_bytes(B, H, L, d, g) bytes.
+ *   Limits and errors as for cca_prefill.
+ */
+int cca_prefill_lse(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse,
+                    int B, int H, int64_t L, int d, int g, int k_local, float scale,
+                    int dt, int out_dt, hipStream_t stream);
+size_t cca_backward_workspace_bytes(int B, int H, int64_t L, int d, int g);
+int cca_backward(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out,
+                 const float* lse, const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H, int64_t L, int d, int g, int k_local, float scale,
+                 int dt, hipStream_t stream);
+
+/*
  * Compressed KV cache for decode ([CCA] Triton section: the fused operator
  * serves decode with a KV cache holding core tokens plus local raw tokens;
  * compute/memory efficiency section, Fig. 3).  Plain-old-data descriptor;

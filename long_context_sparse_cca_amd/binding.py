@@ -71,6 +71,15 @@ EXPORTS = {
                                                                 ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                                 ctypes.c_int, ctypes.c_float, ctypes.c_int,
                                                                 ctypes.c_int, ctypes.c_void_p]),
+    "cca_prefill_lse": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_void_p]),
+    "cca_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                       ctypes.c_int]),
+    "cca_backward": (ctypes.c_int, [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                                             ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "cca_cache_ring_slots": (ctypes.c_int64, [ctypes.POINTER(CacheDesc)]),
     "cca_cache_load_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                + [ctypes.c_int64, ctypes.c_void_p]),
@@ -237,6 +246,65 @@ def attention(q, k, v, kc, vc, g: int, k_local: int, scale: float | None = None,
                                    k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream())
     _check(st, "cca_attention")
     return out
+
+
+def prefill_lse(q, k, v, g: int, k_local: int, scale: float | None = None, out_dtype=None):
+    """Forward for training: (out [B,H,L,d], lse [B,H,L] float32, kc, vc): cca_prefill_lse."""
+    lib = load_library()
+    B, H, Hkv, L, d = _heads(q, k, v)
+    if Hkv != H:
+        raise CCAError("the training path takes one query head per key/value head")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    m = L // g if g >= 1 else 0
+    kc = _core_buffer(B, H, m, d, q)
+    vc = _core_buffer(B, H, m, d, q)
+    out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, max(L, 1)), dtype=torch.float32, device=q.device)[:, :, :L]
+    _check(lib.cca_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), B, H, L, d, g,
+                               k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()),
+           "cca_prefill_lse")
+    return out, lse, kc, vc
+
+
+def backward(q, k, v, kc, vc, out, lse, dout, g: int, k_local: int, scale: float | None = None):
+    """Gradients (dq, dk, dv), float32 [B,H,L,d], of sum(out * dout): cca_backward."""
+    lib = load_library()
+    B, H, Hkv, L, d = _heads(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    m = L // g if g >= 1 else 0
+    _need(kc, (B, H, m, d), q.dtype, "kc")
+    _need(vc, (B, H, m, d), q.dtype, "vc")
+    _need(out, (B, H, L, d), q.dtype, "out")
+    _need(dout, (B, H, L, d), q.dtype, "dout")
+    if tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32 or not lse.is_cuda:
+        raise CCAError("lse must be a float32 device tensor [B, H, L]")
+    dq, dk, dv = (torch.empty((B, H, L, d), dtype=torch.float32, device=q.device) for _ in range(3))
+    ws_bytes = lib.cca_backward_workspace_bytes(B, H, L, d, g)
+    ws = torch.empty((max(ws_bytes, 16) + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    _check(lib.cca_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * 4, B, H, L, d, g, k_local, scale,
+                            _dtype_code(q.dtype), _stream()), "cca_backward")
+    return dq, dk, dv
+
+
+class CCAAttention(torch.autograd.Function):
+    """CCA prefill attention as an autograd function (bf16, d = 128): forward cca_prefill_lse,
+    backward cca_backward.  apply(q, k, v, g, k_local, scale=None) -> out [B,H,L,d]."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, k_local, scale=None):
+        out, lse, kc, vc = prefill_lse(q, k, v, g, k_local, scale)
+        ctx.save_for_backward(q, k, v, kc, vc, out, lse)
+        ctx.cfg = (g, k_local, scale)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, kc, vc, out, lse = ctx.saved_tensors
+        g, k_local, scale = ctx.cfg
+        dq, dk, dv = backward(q, k, v, kc, vc, out, lse, dout.to(q.dtype).contiguous(), g, k_local, scale)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
 
 
 class KVCache:

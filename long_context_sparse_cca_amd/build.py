@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcca.so")
-SOURCES = ["api.hip", "pool.hip", "prefill.hip", "prefill_bf16.hip", "decode.hip", "serve.hip", "extend.hip"]
+SOURCES = ["api.hip", "pool.hip", "prefill.hip", "prefill_bf16.hip", "decode.hip", "serve.hip", "extend.hip", "backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -42,7 +42,7 @@ def _compile(src: str, obj_dir: str) -> str:
 def build(verbose: bool = False) -> str:
     obj_dir = os.path.join(ROOT, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 7)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

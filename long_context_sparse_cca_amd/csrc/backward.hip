@@ -1,0 +1,606 @@
+// Backward pass of CCA prefill attention (bf16 inputs, head dim 128, float32 gradients).
+//
+// Method: the CCA write-up ("ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展"):
+// the fused operator serves training (Triton section); the forward pools each
+// group with its last query (global-aware pooling, core-token and core K/V
+// equations) and attends, in one softmax, to the core tokens before the raw
+// window and the raw keys of the window (locality-preserving module, global-local
+// fusion).  The gradients follow the chain rule through both softmaxes:
+//
+//   attention  p = softmax(scale k.q) over the visible keys, ds = p (dp - D),
+//              dp = dO.v, D = dO.O (= sum_i p_i dp_i);
+//              dQ += scale sum ds k;  dkey += scale ds q;  dval += p dO
+//   pooling    (core keys/values of group j: Kc = a.K_group, Vc = a.V_group,
+//              a = softmax(scale q_hat.K_group))
+//              dV_group += a dVc;  da = dKc.K + dVc.V;  dz = a (da - a.da);
+//              dK_group += a dKc + scale dz q_hat;  dQ[last row] += scale dz.K_group
+//
+// Launches:
+//   1. cca_bwd_prep_kernel     D[t] = dO[t].O[t]
+//   2. cca_bwd_dq_kernel       per 256-query tile: recompute scores and p from the
+//                              forward's log-sum-exp, dQ = scale (P o (dP - D)) K
+//   3. cca_bwd_dkdv_kernel     per 128-key tile (core tokens or raw keys): loop over
+//                              the query tiles that see it; dK, dV of raw keys go to
+//                              dk, dv, those of core tokens to dKc, dVc (workspace)
+//   4. cca_bwd_pool_kernel     per group: dKc, dVc through the pooling into dk, dv,
+//                              and into dq at the group's last row
+// The score and gradient products run on bf16 MFMA (32x32x16) with float32
+// accumulation; P and dS are rounded to bf16 as MFMA operands, as P is in the
+// forward.  Tiles are staged HBM -> LDS with global_load_lds and read with the
+// same 16-byte XOR swizzle and transpose reads as the forward kernel.
+#include "cca_internal.h"
+
+namespace cca {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;
+constexpr int kTileRows = 64;                       // rows per staged tile
+constexpr int kTileBytes = kTileRows * kRowBytes;   // 16 KB
+constexpr float kLn2 = 0.69314718055994531f;
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Operand read offsets inside a row-major swizzled tile (bytes, relative to the
+// first row of a 32-row sub-block).
+//   rows operand (A of X.Y^T with X rows from LDS): row l32, logical chunk 2*d16 + hf;
+//   transpose operand (A of X^T.P with X rows from LDS): the four 8-byte pieces
+//   that ds_read_b64_tr_b16 turns into rows 16u + 4*(G>>1) + 8r .. +3 at dims
+//   dt*32 + 16*(G&1) + lane%16, matching the register order of a 32x32 MFMA
+//   output used as the B operand.
+struct TileOffsets {
+  int rows[kD / 16];
+  int tr[2][kD / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int d16 = 0; d16 < kD / 16; ++d16) rows[d16] = l32 * kRowBytes + (((2 * d16 + hf) ^ swz(l32)) * 16);
+    const int s = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 4 * (grp >> 1) + 8 * r + (s >> 2);
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const int chunk = dt * 4 + 2 * (grp & 1) + ((s & 3) >> 1);
+        tr[r][dt] = row * kRowBytes + ((chunk ^ swz(row)) * 16) + (s & 1) * 8;
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Rows-operand MFMA chain: out = X_subblock(32 rows from LDS) . Y^T where Y's 32
+// rows sit in registers as B operands yop[d16].
+__device__ __forceinline__ f32x16_t rows_chain(const uint8_t* tile_sb, const TileOffsets& o, const uint4* yop) {
+  uint4 xa[kD / 16];
+#pragma unroll
+  for (int d16 = 0; d16 < kD / 16; ++d16) xa[d16] = *reinterpret_cast<const uint4*>(tile_sb + o.rows[d16]);
+  f32x16_t s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int d16 = 0; d16 < kD / 16; ++d16) s = mfma(xa[d16], yop[d16], s);
+  return s;
+}
+
+// Transpose-operand accumulation: acc[dt] += X_subblock^T (d x 32 rows from LDS) . W
+// where W [32 rows x 32 cols] is the fp32 32x32 MFMA output `w` (rounded to bf16).
+__device__ __forceinline__ void tr_accumulate(const uint8_t* tile_sb, const TileOffsets& o, const f32x16_t& w,
+                                              f32x16_t* acc) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x2_t pp[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pp[e] = bf16x2_t{(__bf16)w[8 * u + 2 * e], (__bf16)w[8 * u + 2 * e + 1]};
+    const uint4 pb = __builtin_bit_cast(uint4, pp);
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) {
+      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[0][dt]));
+      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[1][dt]));
+      const v4s_t both[2] = {lo, hi};
+      acc[dt] = mfma(__builtin_bit_cast(uint4, both), pb, acc[dt]);
+    }
+  }
+}
+
+// Fill a 64-row tile (rows base .. base+63 of a row-major [*, 128] bf16 array,
+// rows past `lim` repeat row `lim`) into LDS with the chunk swizzle.  nw waves
+// share the fill: wave w writes rows w*64/nw .. in groups of 4 rows per instruction.
+template <int NW>
+__device__ __forceinline__ void fill_tile(const bf16_t* src, int64_t base, int64_t lim, uint8_t* dst, int wave,
+                                          int lane) {
+  constexpr int ITERS = kTileRows / (4 * NW);
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    const int r = wave * (4 * ITERS) + i * 4 + (lane >> 4);
+    const int off = ((lane & 15) ^ swz(r)) * 16;
+    const int64_t gr = min(base + r, lim);
+    uint8_t* d = dst + (wave * (4 * ITERS) + i * 4) * kRowBytes;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)src +
+                                                                                      (size_t)gr * kRowBytes + off),
+                                     (__attribute__((address_space(3))) void*)d, 16, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. D[t] = dO[t] . O[t]  (16 lanes per row)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict__ dO,
+                                                           float* __restrict__ Dv, int64_t rows) {
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
+  const int c = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < rows) {
+    float a[8], b[8];
+    Elem<bf16_t>::chunk_to_f32(ld16(O + (size_t)row * kD + 8 * c), a);
+    Elem<bf16_t>::chunk_to_f32(ld16(dO + (size_t)row * kD + 8 * c), b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(a[e], b[e], s);
+  }
+  s = lane_group_sum<16>(s);
+  if (row < rows && c == 0) Dv[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dQ: 256 queries per workgroup (8 waves x 32), loop over the visible key tiles
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dQ, int BH, int L, int g,
+    int k_local, float scale, int ntiles) {
+  constexpr int kBM = 256, kBN = 64;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[2 * kTileBytes];
+  int bh, qtile;
+  map_block(BH * ntiles, ntiles, bh, qtile);
+  const int m = L / g;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int q0 = qtile * kBM;
+  const int q_last = min(q0 + kBM - 1, L - 1);
+  const int nc_wg = max(0, q_last / g - k_local);
+  const int rl_wg = max(0, q0 / g - k_local) * g;
+  const int n_core_tiles = (nc_wg + kBN - 1) / kBN;
+  const int n_tiles = n_core_tiles + (q_last - rl_wg + kBN) / kBN;
+
+  const int qa = q0 + wave * 32;
+  const bool wave_live = qa < L;
+  const int qb = min(qa + 31, L - 1);
+  const int cl_min = qa / g - k_local, cl_max = qb / g - k_local;
+  const int rl_min = max(0, cl_min) * g, rl_max = max(0, cl_max) * g;
+  const int q_lane = min(qa + l32, L - 1);
+  const int cl_lane = q_lane / g - k_local;
+  const int rl_lane = max(0, cl_lane) * g;
+  const int core_lo = (cl_lane > 0) ? 0 : -0x40000000;
+  const unsigned core_span = (unsigned)max(cl_lane - 1, 0);
+  const unsigned raw_span = (unsigned)(q_lane - rl_lane);
+
+  const size_t slice = (size_t)bh * L * kD;
+  const bf16_t* Ks = K + slice;
+  const bf16_t* Vs = V + slice;
+  const bf16_t* Kcs = Kc + (size_t)bh * m * kD;
+  const bf16_t* Vcs = Vc + (size_t)bh * m * kD;
+
+  // B operands of the score and dP chains: this lane's query / upstream-gradient row
+  uint4 qop[kD / 16], dop[kD / 16];
+#pragma unroll
+  for (int s = 0; s < kD / 16; ++s) {
+    qop[s] = ld16(Q + slice + (size_t)q_lane * kD + s * 16 + hf * 8);
+    dop[s] = ld16(dO + slice + (size_t)q_lane * kD + s * 16 + hf * 8);
+  }
+  const float sc = scale * kLog2e;
+  const float lse2 = lse[(size_t)bh * L + q_lane] * kLog2e;
+  const float Dq = Dv[(size_t)bh * L + q_lane];
+
+  TileOffsets off;
+  off.init(lane);
+  f32x16_t acc[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+
+  auto issue = [&](int it, uint8_t* buf) {
+    const bf16_t *ks, *vs;
+    int base, lim;
+    if (it < n_core_tiles) {
+      ks = Kcs; vs = Vcs; base = it * kBN; lim = m - 1;
+    } else {
+      ks = Ks; vs = Vs; base = rl_wg + (it - n_core_tiles) * kBN; lim = L - 1;
+    }
+    fill_tile<8>(ks, base, lim, buf, wave, lane);
+    fill_tile<8>(vs, base, lim, buf + kTileBytes, wave, lane);
+  };
+
+  auto compute = [&](const uint8_t* kt, const uint8_t* vt, int it) {
+    const bool core = it < n_core_tiles;
+    const int tbase = core ? it * kBN : rl_wg + (it - n_core_tiles) * kBN;
+    const int lo = core ? core_lo : rl_lane;
+    const unsigned span = core ? core_span : raw_span;
+#pragma unroll
+    for (int sb = 0; sb < kBN / 32; ++sb) {
+      const int kb = tbase + sb * 32;
+      int cls;
+      if (core) {
+        cls = (kb >= cl_max) ? 0 : ((kb + 32 <= cl_min) ? 1 : 2);
+      } else {
+        if (kb + 31 < rl_min || kb > qb) cls = 0;
+        else if (kb >= rl_max && kb + 31 <= qa) cls = 1;
+        else cls = 2;
+      }
+      if (cls == 0) continue;
+      const uint8_t* ksb = kt + sb * 32 * kRowBytes;
+      const uint8_t* vsb = vt + sb * 32 * kRowBytes;
+      f32x16_t s = rows_chain(ksb, off, qop);    // S^T: keys x queries
+      f32x16_t dp = rows_chain(vsb, off, dop);   // dP^T
+      if (cls == 2) {
+        const int k0 = kb + 4 * hf - lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool vis = (unsigned)(k0 + 8 * i + j) <= span;
+            s[4 * i + j] = vis ? s[4 * i + j] : -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[r], sc, -lse2));
+        dp[r] = p * (dp[r] - Dq);                 // dS^T
+      }
+      tr_accumulate(ksb, off, dp, acc);          // dQ^T += K^T dS^T
+    }
+  };
+
+  if (n_tiles > 0) issue(0, lds0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    if (it + 1 < n_tiles) issue(it + 1, lds1);
+    if (wave_live) compute(lds0, lds0 + kTileBytes, it);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    if (it + 2 < n_tiles) issue(it + 2, lds0);
+    if (wave_live) compute(lds1, lds1 + kTileBytes, it + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (!wave_live) return;
+  const int q_row = qa + l32;
+  if (q_row >= L) return;
+  float* o = dQ + slice + (size_t)q_row * kD;
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) =
+          make_float4(acc[dt][4 * i] * scale, acc[dt][4 * i + 1] * scale, acc[dt][4 * i + 2] * scale,
+                      acc[dt][4 * i + 3] * scale);
+}
+
+// ---------------------------------------------------------------------------
+// 3. dK, dV: 128 keys per workgroup (4 waves x 32, one wave per SIMD), loop over
+//    the 64-query tiles that see them
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void cca_bwd_dkdv_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dK, float* __restrict__ dV,
+    float* __restrict__ dKc, float* __restrict__ dVc, int BH, int L, int g, int k_local, float scale, int n_core_wg,
+    int n_wg) {
+  constexpr int kBK = 128;  // keys per workgroup
+  constexpr int kBufBytes = 2 * kTileBytes + 2 * kTileRows * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBufBytes];
+  // workgroups of a slice: core tiles first (the heavy ones), then raw tiles
+  const int bh = blockIdx.x / n_wg;
+  const int wi = blockIdx.x - bh * n_wg;
+  const bool core = wi < n_core_wg;
+  const int m = L / g;
+  const int key0 = core ? wi * kBK : (wi - n_core_wg) * kBK;
+  const int key_end = core ? m : L;        // keys of this kind
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int c0 = key0 + wave * 32;         // this wave's first key
+  const int c_last = min(key0 + kBK, key_end) - 1;
+
+  // query range [t_lo, t_hi] that can see any key of the workgroup
+  int t_lo, t_hi;
+  if (core) {
+    t_lo = (key0 + k_local + 1) * g;       // core j visible iff t >= (j + k + 1) g
+    t_hi = L - 1;
+  } else {
+    t_lo = key0;
+    t_hi = min(L - 1, (c_last / g + k_local + 1) * g - 1);
+  }
+  const int tq0 = (t_lo / kTileRows) * kTileRows;
+  const int n_qt = (t_lo <= t_hi) ? (t_hi - tq0) / kTileRows + 1 : 0;
+
+  const size_t slice = (size_t)bh * L * kD;
+  const bf16_t* Ks = core ? Kc + (size_t)bh * m * kD : K + slice;
+  const bf16_t* Vs = core ? Vc + (size_t)bh * m * kD : V + slice;
+  const bf16_t* Qs = Q + slice;
+  const bf16_t* dOs = dO + slice;
+  const int key_lane = min(c0 + l32, key_end - 1);
+  uint4 kop[kD / 16], vop[kD / 16];
+#pragma unroll
+  for (int s = 0; s < kD / 16; ++s) {
+    kop[s] = ld16(Ks + (size_t)key_lane * kD + s * 16 + hf * 8);
+    vop[s] = ld16(Vs + (size_t)key_lane * kD + s * 16 + hf * 8);
+  }
+  const float sc = scale * kLog2e;
+  TileOffsets off;
+  off.init(lane);
+  f32x16_t acck[kD / 32], accv[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acck[dt][r] = accv[dt][r] = 0.f;
+
+  // visibility of key c (this lane's column) to query t: core: c < t/g - k; raw: rl(t) <= c <= t
+  const bool wave_live = c0 < key_end;
+  const int c_hi = min(c0 + 31, key_end - 1);
+
+  auto issue = [&](int qt, uint8_t* buf) {
+    const int base = tq0 + qt * kTileRows;
+    fill_tile<4>(Qs, base, L - 1, buf, wave, lane);
+    fill_tile<4>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
+    // log-sum-exp (log2 units) and D of the tile's 64 queries
+    if (tid < 2 * kTileRows) {
+      const int r = tid & (kTileRows - 1);
+      const int t = min(base + r, L - 1);
+      float* dst = reinterpret_cast<float*>(buf + 2 * kTileBytes) + tid;
+      *dst = (tid < kTileRows) ? lse[(size_t)bh * L + t] * kLog2e : Dv[(size_t)bh * L + t];
+    }
+  };
+
+  auto compute = [&](const uint8_t* buf, int qt) {
+    const float* lse_t = reinterpret_cast<const float*>(buf + 2 * kTileBytes);
+    const float* d_t = lse_t + kTileRows;
+#pragma unroll
+    for (int sb = 0; sb < kTileRows / 32; ++sb) {
+      const int t0 = tq0 + qt * kTileRows + sb * 32;
+      const int t1 = min(t0 + 31, L - 1);
+      if (t0 >= L) continue;
+      int cls;   // 0: nothing visible, 1: everything visible, 2: mixed
+      if (core) {
+        const int nc_lo = max(0, t0 / g - k_local), nc_hi = max(0, t1 / g - k_local);
+        cls = (nc_hi <= c0) ? 0 : ((c_hi < nc_lo && t0 + 31 < L) ? 1 : 2);
+      } else {
+        const int rl_lo = max(0, t0 / g - k_local) * g, rl_hi = max(0, t1 / g - k_local) * g;
+        if (t1 < c0 || rl_lo > c_hi) cls = 0;
+        else if (t0 >= c_hi && rl_hi <= c0 && t0 + 31 < L) cls = 1;
+        else cls = 2;
+      }
+      if (cls == 0) continue;
+      const uint8_t* qsb = buf + sb * 32 * kRowBytes;
+      const uint8_t* dsb = buf + kTileBytes + sb * 32 * kRowBytes;
+      f32x16_t s = rows_chain(qsb, off, kop);    // S: queries (rows) x keys (cols)
+      f32x16_t dp = rows_chain(dsb, off, vop);   // dP
+      const int key = c0 + l32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 lv = *reinterpret_cast<const float4*>(lse_t + sb * 32 + 8 * i + 4 * hf);
+        const float4 dv = *reinterpret_cast<const float4*>(d_t + sb * 32 + 8 * i + 4 * hf);
+        const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dr[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * i + j;
+          float p = fast_exp2(fmaf(s[r], sc, -lr[j]));
+          if (cls == 2) {
+            const int t = t0 + 8 * i + 4 * hf + j;
+            bool vis;
+            if (core) {
+              vis = key < t / g - k_local;
+            } else {
+              vis = key <= t && key >= max(0, t / g - k_local) * g;
+            }
+            vis = vis && t < L && key <= c_hi;
+            p = vis ? p : 0.f;
+          }
+          s[r] = p;                               // P
+          dp[r] = p * (dp[r] - dr[j]);            // dS
+        }
+      }
+      tr_accumulate(dsb, off, s, accv);          // dV^T += dO^T P
+      tr_accumulate(qsb, off, dp, acck);         // dK^T += Q^T dS
+    }
+  };
+
+  if (n_qt > 0) issue(0, lds0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int qt = 0; qt < n_qt; qt += 2) {
+    if (qt + 1 < n_qt) issue(qt + 1, lds1);
+    if (wave_live) compute(lds0, qt);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (qt + 1 >= n_qt) break;
+    if (qt + 2 < n_qt) issue(qt + 2, lds0);
+    if (wave_live) compute(lds1, qt + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (!wave_live) return;
+  const int key = c0 + l32;
+  if (key >= key_end) return;
+  float* ok = core ? dKc + ((size_t)bh * m + key) * kD : dK + slice + (size_t)key * kD;
+  float* ov = core ? dVc + ((size_t)bh * m + key) * kD : dV + slice + (size_t)key * kD;
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4*>(ok + dt * 32 + 8 * i + 4 * hf) =
+          make_float4(acck[dt][4 * i] * scale, acck[dt][4 * i + 1] * scale, acck[dt][4 * i + 2] * scale,
+                      acck[dt][4 * i + 3] * scale);
+      *reinterpret_cast<float4*>(ov + dt * 32 + 8 * i + 4 * hf) =
+          make_float4(accv[dt][4 * i], accv[dt][4 * i + 1], accv[dt][4 * i + 2], accv[dt][4 * i + 3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. pooling backward: one wave per group
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                                          const bf16_t* __restrict__ V,
+                                                          const float* __restrict__ dKc,
+                                                          const float* __restrict__ dVc, float* __restrict__ dQ,
+                                                          float* __restrict__ dK, float* __restrict__ dV, int64_t L,
+                                                          int g, int64_t m, float scale) {
+  extern __shared__ float sm[];   // a[g], then da / dz[g]
+  float* a_l = sm;
+  float* z_l = sm + g;
+  const int64_t gid = blockIdx.x;
+  const int64_t bh = gid / m, j = gid - bh * m;
+  const int lane = threadIdx.x;
+  const size_t row0 = (size_t)bh * L + (size_t)j * g;        // first row of the group
+  const size_t rowq = row0 + g - 1;                           // its scoring query
+  const float* dkc = dKc + ((size_t)bh * m + j) * kD;
+  const float* dvc = dVc + ((size_t)bh * m + j) * kD;
+  // scoring pass: 4 lanes per row, 32 dims each (q_hat, dKc, dVc slices in registers)
+  const int rsub = lane >> 2, seg = lane & 3;
+  float qf[32], kcf[32], vcf[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) Elem<bf16_t>::chunk_to_f32(ld16(Q + rowq * kD + seg * 32 + c * 8), qf + c * 8);
+#pragma unroll
+  for (int e = 0; e < 32; e += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(dkc + seg * 32 + e);
+    const float4 y = *reinterpret_cast<const float4*>(dvc + seg * 32 + e);
+    kcf[e] = x.x; kcf[e + 1] = x.y; kcf[e + 2] = x.z; kcf[e + 3] = x.w;
+    vcf[e] = y.x; vcf[e + 1] = y.y; vcf[e + 2] = y.z; vcf[e + 3] = y.w;
+  }
+  const float sc = scale * kLog2e;
+  for (int r0 = 0; r0 < g; r0 += 16) {
+    const int r = r0 + rsub;
+    float s = 0.f, da = 0.f;
+    if (r < g) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float kf[8], vf[8];
+        Elem<bf16_t>::chunk_to_f32(ld16(K + (row0 + r) * kD + seg * 32 + c * 8), kf);
+        Elem<bf16_t>::chunk_to_f32(ld16(V + (row0 + r) * kD + seg * 32 + c * 8), vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s = fmaf(qf[c * 8 + e], kf[e], s);
+          da = fmaf(kcf[c * 8 + e], kf[e], fmaf(vcf[c * 8 + e], vf[e], da));
+        }
+      }
+    }
+    s = lane_group_sum<4>(s);
+    da = lane_group_sum<4>(da);
+    if (seg == 0 && r < g) {
+      a_l[r] = s * sc;
+      z_l[r] = da;
+    }
+  }
+  wave_lds_sync();
+  // softmax of the group scores, then dz = a (da - a.da)
+  float mx = -INFINITY;
+  for (int r = lane; r < g; r += kWave) mx = fmaxf(mx, a_l[r]);
+  mx = wave_max_xor(mx, 1, kWave);
+  float sum = 0.f;
+  for (int r = lane; r < g; r += kWave) sum += fast_exp2(a_l[r] - mx);
+  sum = wave_sum_xor(sum, 1, kWave);
+  const float inv = 1.0f / sum;
+  float ada = 0.f;
+  for (int r = lane; r < g; r += kWave) ada += fast_exp2(a_l[r] - mx) * inv * z_l[r];
+  ada = wave_sum_xor(ada, 1, kWave);
+  wave_lds_sync();
+  for (int r = lane; r < g; r += kWave) {
+    const float a = fast_exp2(a_l[r] - mx) * inv;
+    z_l[r] = a * (z_l[r] - ada);
+    a_l[r] = a;
+  }
+  wave_lds_sync();
+  // row updates: each lane owns 2 consecutive dims
+  const int col = lane * 2;
+  float q2[2], kc2[2], vc2[2], dq2[2] = {0.f, 0.f};
+  {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + rowq * kD + col);
+    q2[0] = __uint_as_float(w << 16);
+    q2[1] = __uint_as_float(w & 0xffff0000u);
+    kc2[0] = dkc[col]; kc2[1] = dkc[col + 1];
+    vc2[0] = dvc[col]; vc2[1] = dvc[col + 1];
+  }
+  for (int r = 0; r < g; ++r) {
+    const float a = a_l[r], dz = z_l[r];
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(K + (row0 + r) * kD + col);
+    const float k0 = __uint_as_float(kw << 16), k1 = __uint_as_float(kw & 0xffff0000u);
+    float2* pk = reinterpret_cast<float2*>(dK + (row0 + r) * kD + col);
+    float2* pv = reinterpret_cast<float2*>(dV + (row0 + r) * kD + col);
+    float2 xk = *pk, xv = *pv;
+    xk.x += a * kc2[0] + scale * dz * q2[0];
+    xk.y += a * kc2[1] + scale * dz * q2[1];
+    xv.x += a * vc2[0];
+    xv.y += a * vc2[1];
+    *pk = xk;
+    *pv = xv;
+    dq2[0] = fmaf(dz, k0, dq2[0]);
+    dq2[1] = fmaf(dz, k1, dq2[1]);
+  }
+  float2* pq = reinterpret_cast<float2*>(dQ + rowq * kD + col);
+  float2 xq = *pq;
+  xq.x += scale * dq2[0];
+  xq.y += scale * dq2[1];
+  *pq = xq;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int H, int64_t L, int d, int g) {
+  const size_t BH = (size_t)B * H;
+  const size_t m = (size_t)(L / g);
+  return (BH * (size_t)L + 2 * BH * m * (size_t)d) * sizeof(float);
+}
+
+hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                                     const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                                     float* dv, void* workspace, int BH, int64_t L, int g, int k_local, float scale,
+                                     hipStream_t stream) {
+  const int64_t m = L / g;
+  float* Dv = (float*)workspace;
+  float* dKc = Dv + (size_t)BH * L;
+  float* dVc = dKc + (size_t)BH * m * kD;
+  const int64_t rows = (int64_t)BH * L;
+  hipLaunchKernelGGL(cca_bwd_prep_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
+                     (const bf16_t*)out, (const bf16_t*)dout, Dv, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntiles = (int)((L + 255) / 256);
+  hipLaunchKernelGGL(cca_bwd_dq_kernel, dim3((unsigned)(BH * ntiles)), dim3(512), 0, stream, (const bf16_t*)q,
+                     (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, (const bf16_t*)dout,
+                     lse, (const float*)Dv, dq, BH, (int)L, g, k_local, scale, ntiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_core_wg = (int)((m + 127) / 128);
+  const int n_wg = n_core_wg + (int)((L + 127) / 128);
+  hipLaunchKernelGGL(cca_bwd_dkdv_kernel, dim3((unsigned)((int64_t)BH * n_wg)), dim3(256), 0, stream,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
+                     (const bf16_t*)dout, lse, (const float*)Dv, dk, dv, dKc, dVc, BH, (int)L, g, k_local, scale,
+                     n_core_wg, n_wg);
+  e = hipGetLastError();
+  if (e != hipSuccess || m == 0) return e;
+  hipLaunchKernelGGL(cca_bwd_pool_kernel, dim3((unsigned)((int64_t)BH * m)), dim3(64), (size_t)2 * g * sizeof(float),
+                     stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const float*)dKc,
+                     (const float*)dVc, dq, dk, dv, L, g, m, scale);
+  return hipGetLastError();
+}
+
+}  // namespace cca

@@ -32,9 +32,10 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
                                     int64_t L, int g, int k_local, float scale, hipStream_t stream);
 
 // bf16, head dim 128 fast path of the fused attention (prefill_bf16.hip).
+// lse (optional, float32 [BH][L]): natural-log log-sum-exp of each query's scaled scores.
 hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                     void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
-                                    float scale, hipStream_t stream);
+                                    float scale, hipStream_t stream, float* lse = nullptr);
 
 // Extend-mode attention (bf16 d=128 fast kernel or the generic one): q, out [B*H][n][d];
 // k, v [B*H_kv][ext.raw_rows][d]; kc, vc [B*H_kv][ext.core_rows][d].
@@ -76,6 +77,14 @@ size_t serve_workspace_bytes(const cca_cache_t* c, int H_q);
 hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream);
+
+// Backward pass, bf16, head dim 128 (backward.hip).  Workspace: D [BH][L], then
+// dKc and dVc [BH][L/g][d], all float32.
+size_t backward_workspace_bytes(int B, int H, int64_t L, int d, int g);
+hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                                     const void* out, const float* lse, const void* dout, float* dq, float* dk,
+                                     float* dv, void* workspace, int BH, int64_t L, int g, int k_local, float scale,
+                                     hipStream_t stream);
 
 // Chunked append of n tokens per sequence (extend.hip).
 size_t extend_workspace_bytes(const cca_cache_t* c, int n);

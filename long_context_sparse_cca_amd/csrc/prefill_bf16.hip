@@ -65,7 +65,7 @@ template <bool EXT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
-    int nq, int L, int g, int k_local, float scale, int ntiles, ExtendArgs ext) {
+    int nq, int L, int g, int k_local, float scale, int ntiles, ExtendArgs ext, float* __restrict__ lse) {
   // one array per buffer: the LDS-DMA fill of one buffer then provably does not
   // alias the operand reads of the other, so no wait is forced between them
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
@@ -332,9 +332,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   if (!wave_live) return;
   // ---- normalise and store: lane (query l32, half hf) holds O[q][dt*32 + 8i + 4hf + j]
-  const float inv = 1.0f / xhalf_sum(l_run);
+  const float l_tot = xhalf_sum(l_run);
+  const float inv = 1.0f / l_tot;
   const int q_row = qa + l32 - pos0;                     // row within the slice
   if (q_row >= nQ) return;
+  if (lse != nullptr && hf == 0) {
+    // natural-log log-sum-exp of the scaled scores: (m_run + log2 l) * ln 2
+    lse[(size_t)bh * nQ + q_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
   if (out_f32) {
     float* o = reinterpret_cast<float*>(Out) + slice + (size_t)q_row * kD;
 #pragma unroll
@@ -363,14 +368,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                     void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
-                                    float scale, hipStream_t stream) {
+                                    float scale, hipStream_t stream, float* lse) {
   const int ntiles = (int)((L + kBM - 1) / kBM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
   const ExtendArgs none{nullptr, 1, 0, 0, 0};
   hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel<false>, dim3((unsigned)nblocks), dim3(512), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out,
-                     out_f32, BH, nq, (int)L, g, k_local, scale, ntiles, none);
+                     out_f32, BH, nq, (int)L, g, k_local, scale, ntiles, none, lse);
   return hipGetLastError();
 }
 
@@ -382,7 +387,7 @@ hipError_t launch_extend_attention_bf16_d128(const void* q, const void* k, const
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel<true>, dim3((unsigned)nblocks), dim3(512), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out,
-                     out_f32, BH, nq, 0, g, k_local, scale, ntiles, ext);
+                     out_f32, BH, nq, 0, g, k_local, scale, ntiles, ext, (float*)nullptr);
   return hipGetLastError();
 }
 

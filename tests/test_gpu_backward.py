@@ -1,0 +1,97 @@
+"""Backward pass of CCA prefill (bf16, d = 128): HIP path vs the gradient oracle.
+
+Shapes span several 256-query and 128-key tiles with ragged tails, g not a power of
+two, g = 1 (causal attention), a window wider than the sequence, and core tiles seen by
+many query tiles.  The oracle recomputes the forward with core tokens stored in bf16
+(the forward's stored core tokens) and differentiates in fp64.
+Tolerance: the spec bf16 bound 2e-2, taken relative to the gradient's own scale
+(max-abs error <= 2e-2 * max(1, max|reference|)): the softmax weights and dS are
+rounded to bf16 as matrix-core operands (relative 2^-9 each), and D = dO.O uses the
+bf16-rounded forward output.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cca_backward
+from long_context_sparse_cca_amd import binding
+from long_context_sparse_cca_amd.synth import np_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x, device):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=torch.bfloat16).contiguous()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# (B, H, L, g, k, seed)
+BWD_CASES = [
+    (1, 2, 300, 16, 2, 70),
+    (1, 1, 700, 16, 4, 71),     # core tiles seen by several query tiles
+    (2, 1, 517, 7, 3, 72),      # g not a power of two, ragged tiles
+    (1, 1, 200, 1, 0, 73),      # g = 1: causal attention
+    (1, 1, 640, 16, 100, 74),   # window wider than the sequence
+    (1, 1, 1500, 32, 5, 75),    # many core tokens per key tile
+]
+
+
+def _id(c):
+    B, H, L, g, k, seed = c
+    return f"B{B}H{H}L{L}g{g}k{k}"
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=_id)
+def test_backward_matches_oracle(gpu, case):
+    B, H, L, g, k, seed = case
+    d = 128
+    _say(f"backward case {_id(case)} seed {seed}")
+    Q, K, V = np_inputs(B, H, L, d, "bf16", seed)
+    dO = np_inputs(B, H, L, d, "bf16", seed + 500)[0]
+    q, kk, v, do = (_dev(x, gpu) for x in (Q, K, V, dO))
+    scale = 1.0 / math.sqrt(d)
+    out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
+    dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
+    torch.cuda.synchronize()
+    # the training forward is the plain forward, plus the log-sum-exp
+    assert torch.equal(out, binding.prefill(q, kk, v, g, k, scale))
+    for b in range(B):
+        for h in range(H):
+            _, lse_ref = cca_backward.cca_forward_lse_slice(Q[b, h], K[b, h], V[b, h], g, k, scale, core_dtype="bf16")
+            e = np.abs(lse[b, h].cpu().numpy() - lse_ref).max()
+            assert e <= 1e-2, f"lse err {e:.3e}"
+    # gradients against the oracle, using the GPU's bf16 forward output for D = dO.O is not
+    # needed: the oracle is exact and the tolerance covers the bf16 rounding of O
+    want = cca_backward.cca_backward(Q, K, V, dO, g, k, scale, core_dtype="bf16")
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
+
+
+def test_autograd_function_matches_backward(gpu):
+    B, H, L, d, g, k = 1, 2, 400, 128, 16, 3
+    Q, K, V = np_inputs(B, H, L, d, "bf16", 80)
+    q, kk, v = (_dev(x, gpu).requires_grad_(True) for x in (Q, K, V))
+    out = binding.CCAAttention.apply(q, kk, v, g, k)
+    dO = _dev(np_inputs(B, H, L, d, "bf16", 81)[0], gpu)
+    out.backward(dO)
+    o2, lse, kc, vc = binding.prefill_lse(q.detach(), kk.detach(), v.detach(), g, k)
+    dq, dk, dv = binding.backward(q.detach(), kk.detach(), v.detach(), kc, vc, o2, lse, dO, g, k)
+    torch.cuda.synchronize()
+    assert torch.equal(q.grad, dq.to(torch.bfloat16)) and torch.equal(kk.grad, dk.to(torch.bfloat16))
+    assert torch.equal(v.grad, dv.to(torch.bfloat16))
+
+
+def test_backward_unsupported_shapes(gpu):
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(binding.CCAError):
+        binding.prefill_lse(q, q.clone(), q.clone(), 16, 1)
