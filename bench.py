@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the standard-attention comparison")
+    ap.add_argument("--no-training", action="store_true", help="skip the forward+backward measurement")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the serving decode measurement (per-sequence lengths, grouped-query heads)")
-    ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "copy"], default="all",
+    ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "training", "copy"], default="all",
                     help="profiling aid: run only one phase (the JSON line is then not the benchmark result); "
                          "'copy' runs a plain 1 GiB device copy whose counter readings calibrate FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
@@ -237,6 +238,42 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
                                             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
 
+def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int = 3):
+    """Forward with log-sum-exp (cca_prefill_lse) and backward (cca_backward) of one layer,
+    B=1, H=32, d=128, g=16, k=64, bf16, outside the timed steps."""
+    import torch
+
+    from long_context_sparse_cca_amd.synth import torch_inputs
+    q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, dev, seed=seed + 7, heavy_frac=HEAVY)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 8)
+    dout = torch.randn((1, H, L, D), generator=gen, device=dev).to(torch.bfloat16)
+    out, lse, kc, vc = binding.prefill_lse(q, k, v, G, KL)
+    binding.backward(q, k, v, kc, vc, out, lse, dout, G, KL)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    fw, bw = [], []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        out, lse, kc, vc = binding.prefill_lse(q, k, v, G, KL)
+        e[1].record(stream)
+        binding.backward(q, k, v, kc, vc, out, lse, dout, G, KL)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        fw.append(e[0].elapsed_time(e[1]))
+        bw.append(e[1].elapsed_time(e[2]))
+    fw_ms, bw_ms = sum(fw) / reps, sum(bw) / reps
+    fl = accounting.backward_flops(1, H, L, D, G, KL)
+    tf = fl / (bw_ms * 1e-3) / 1e12
+    return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL},
+            "forward_ms": fw_ms, "backward_ms": bw_ms, "backward_flops": fl,
+            "roofline": {"kernel": "cca_bwd_dq_kernel + cca_bwd_dkdv_kernel (+ prep, pooling backward)",
+                         "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16_TFLOPS,
+                         "per_unit": "10*d FLOPs per visible (query, key) pair"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -263,6 +300,10 @@ def main():
         dt = (time.perf_counter() - t0) / args.steps
         print(json.dumps({"phase": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "ms": dt * 1e3,
                           "gbs": 4 * n / dt / 1e9}), flush=True)
+        return
+    if args.phase == "training":
+        print(json.dumps({"phase": "training", "training": training_step(binding, accounting, dev, args.seed)}),
+              flush=True)
         return
     if args.phase == "serving":
         print(json.dumps({"phase": "serving",
@@ -404,6 +445,9 @@ def main():
         del cache, qs, ks, vs, k0, v0, kc0, vc0
         torch.cuda.empty_cache()
         res["serving_decode"] = serving_decode(binding, accounting, dev, args.seed)
+    if do_prefill and not args.no_training and args.phase == "all":
+        res["training"] = training_step(binding, accounting, dev, args.seed)
+        torch.cuda.empty_cache()
     if do_prefill and not args.no_dense and args.phase == "all":
         res["dense_comparison"] = dense_comparison(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_cpu_baseline and args.phase == "all":

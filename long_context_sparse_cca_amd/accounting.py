@@ -78,6 +78,13 @@ def serve_bytes(lens, H_q: int, H_kv: int, d: int, g: int, k: int, elem: int, n_
     return total
 
 
+def backward_flops(B: int, H: int, L: int, d: int, g: int, k: int) -> int:
+    """Algorithmic FLOPs of the attention backward: five products per visible (query, key)
+    pair given the forward's log-sum-exp (scores recomputed, dP, dV, dK, dQ), 2*d each."""
+    core, raw = attention_pairs(L, g, k)
+    return 10 * d * (core + raw) * B * H
+
+
 def extend_flops(lens, n: int, H_q: int, d: int, g: int, k: int) -> int:
     """Algorithmic FLOPs of one chunked append: 4*d per visible (new token, key) pair and
     query head, for the n tokens at positions lens[b] .. lens[b]+n-1 of every sequence."""

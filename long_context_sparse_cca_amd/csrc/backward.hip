@@ -16,12 +16,13 @@
 //              dK_group += a dKc + scale dz q_hat;  dQ[last row] += scale dz.K_group
 //
 // Launches:
-//   1. cca_bwd_prep_kernel     D[t] = dO[t].O[t]
+//   1. cca_bwd_prep_kernel     D[t] = dO[t].O[t]; the log-sum-exp in log2 units
 //   2. cca_bwd_dq_kernel       per 256-query tile: recompute scores and p from the
 //                              forward's log-sum-exp, dQ = scale (P o (dP - D)) K
-//   3. cca_bwd_dkdv_kernel     per 128-key tile (core tokens or raw keys): loop over
-//                              the query tiles that see it; dK, dV of raw keys go to
-//                              dk, dv, those of core tokens to dKc, dVc (workspace)
+//   3. cca_bwd_dkdv_kernel     per 256-key tile (core tokens or raw keys): loop over
+//                              the query tiles that see it; dV (one launch) and dK
+//                              (another) of raw keys go to dv, dk, those of core
+//                              tokens to dVc, dKc (workspace)
 //   4. cca_bwd_pool_kernel     per group: dKc, dVc through the pooling into dk, dv,
 //                              and into dq at the group's last row
 // The score and gradient products run on bf16 MFMA (32x32x16) with float32
@@ -135,7 +136,8 @@ __device__ __forceinline__ void fill_tile(const bf16_t* src, int64_t base, int64
 // 1. D[t] = dO[t] . O[t]  (16 lanes per row)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict__ dO,
-                                                           float* __restrict__ Dv, int64_t rows) {
+                                                           const float* __restrict__ lse, float* __restrict__ Dv,
+                                                           float* __restrict__ lse2, int64_t rows) {
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
   const int c = threadIdx.x & 15;
   float s = 0.f;
@@ -147,7 +149,10 @@ __global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restr
     for (int e = 0; e < 8; ++e) s = fmaf(a[e], b[e], s);
   }
   s = lane_group_sum<16>(s);
-  if (row < rows && c == 0) Dv[row] = s;
+  if (row < rows && c == 0) {
+    Dv[row] = s;
+    lse2[row] = lse[row] * kLog2e;   // log-sum-exp in log2 units, as the kernels use it
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dop[s] = ld16(dO + slice + (size_t)q_lane * kD + s * 16 + hf * 8);
   }
   const float sc = scale * kLog2e;
-  const float lse2 = lse[(size_t)bh * L + q_lane] * kLog2e;
+  const float lse2 = lse[(size_t)bh * L + q_lane];   // log2 units
   const float Dq = Dv[(size_t)bh * L + q_lane];
 
   TileOffsets off;
@@ -293,22 +298,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// 3. dK, dV: 128 keys per workgroup (4 waves x 32, one wave per SIMD), loop over
-//    the 64-query tiles that see them
+// 3. dV (MODE 0) and dK (MODE 1): 256 keys per workgroup (8 waves x 32, two waves
+//    per SIMD), loop over the 64-query tiles that see them.  The two gradients
+//    are separate launches so that each fits two waves per SIMD: dV needs the
+//    scores only, dK the scores and dP; both recompute the scores.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void cca_bwd_dkdv_kernel(
+template <int MODE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dK, float* __restrict__ dV,
-    float* __restrict__ dKc, float* __restrict__ dVc, int BH, int L, int g, int k_local, float scale, int n_core_wg,
-    int n_wg) {
-  constexpr int kBK = 128;  // keys per workgroup
+    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dKV,
+    float* __restrict__ dKVc, int BH, int L, int g, int k_local, float scale, int n_core_wg, int n_wg) {
+  constexpr int kBK = 256;  // keys per workgroup
   constexpr int kBufBytes = 2 * kTileBytes + 2 * kTileRows * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBufBytes];
-  // workgroups of a slice: core tiles first (the heavy ones), then raw tiles
-  const int bh = blockIdx.x / n_wg;
-  const int wi = blockIdx.x - bh * n_wg;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[kBufBytes];
+  // heaviest work first across all slices: workgroup index wi (core tiles from the
+  // first core token, which the most queries see, then raw tiles) is the slow index
+  const int wi = blockIdx.x / BH;
+  const int bh = blockIdx.x - wi * BH;
   const bool core = wi < n_core_wg;
   const int m = L / g;
   const int key0 = core ? wi * kBK : (wi - n_core_wg) * kBK;
@@ -338,35 +347,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bf16_t* Qs = Q + slice;
   const bf16_t* dOs = dO + slice;
   const int key_lane = min(c0 + l32, key_end - 1);
-  uint4 kop[kD / 16], vop[kD / 16];
+  uint4 kop[kD / 16], vop[MODE == 1 ? kD / 16 : 1];
 #pragma unroll
   for (int s = 0; s < kD / 16; ++s) {
     kop[s] = ld16(Ks + (size_t)key_lane * kD + s * 16 + hf * 8);
-    vop[s] = ld16(Vs + (size_t)key_lane * kD + s * 16 + hf * 8);
+    if constexpr (MODE == 1) vop[s] = ld16(Vs + (size_t)key_lane * kD + s * 16 + hf * 8);
   }
   const float sc = scale * kLog2e;
   TileOffsets off;
   off.init(lane);
-  f32x16_t acck[kD / 32], accv[kD / 32];
+  f32x16_t acc[kD / 32];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acck[dt][r] = accv[dt][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
-  // visibility of key c (this lane's column) to query t: core: c < t/g - k; raw: rl(t) <= c <= t
   const bool wave_live = c0 < key_end;
   const int c_hi = min(c0 + 31, key_end - 1);
 
   auto issue = [&](int qt, uint8_t* buf) {
     const int base = tq0 + qt * kTileRows;
-    fill_tile<4>(Qs, base, L - 1, buf, wave, lane);
-    fill_tile<4>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
-    // log-sum-exp (log2 units) and D of the tile's 64 queries
-    if (tid < 2 * kTileRows) {
-      const int r = tid & (kTileRows - 1);
-      const int t = min(base + r, L - 1);
-      float* dst = reinterpret_cast<float*>(buf + 2 * kTileBytes) + tid;
-      *dst = (tid < kTileRows) ? lse[(size_t)bh * L + t] * kLog2e : Dv[(size_t)bh * L + t];
+    fill_tile<8>(Qs, base, L - 1, buf, wave, lane);
+    fill_tile<8>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
+    // log-sum-exp (log2 units) and D of the tile's 64 queries: one 4-byte DMA per lane
+    if (wave < 2) {
+      const int t = min(base + lane, L - 1);
+      const float* src = (wave == 0 ? lse : Dv) + (size_t)bh * L + t;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(buf + 2 * kTileBytes +
+                                                                                  wave * kTileRows * 4),
+                                       4, 0, 0);
     }
   };
 
@@ -392,14 +402,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const uint8_t* qsb = buf + sb * 32 * kRowBytes;
       const uint8_t* dsb = buf + kTileBytes + sb * 32 * kRowBytes;
       f32x16_t s = rows_chain(qsb, off, kop);    // S: queries (rows) x keys (cols)
-      f32x16_t dp = rows_chain(dsb, off, vop);   // dP
+      f32x16_t dp;
+      if constexpr (MODE == 1) dp = rows_chain(dsb, off, vop);   // dP
       const int key = c0 + l32;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 lv = *reinterpret_cast<const float4*>(lse_t + sb * 32 + 8 * i + 4 * hf);
-        const float4 dv = *reinterpret_cast<const float4*>(d_t + sb * 32 + 8 * i + 4 * hf);
         const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
-        const float dr[4] = {dv.x, dv.y, dv.z, dv.w};
+        float dr[4];
+        if constexpr (MODE == 1) {
+          const float4 dv = *reinterpret_cast<const float4*>(d_t + sb * 32 + 8 * i + 4 * hf);
+          dr[0] = dv.x; dr[1] = dv.y; dr[2] = dv.z; dr[3] = dv.w;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * i + j;
@@ -415,44 +429,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             vis = vis && t < L && key <= c_hi;
             p = vis ? p : 0.f;
           }
-          s[r] = p;                               // P
-          dp[r] = p * (dp[r] - dr[j]);            // dS
+          if constexpr (MODE == 0) s[r] = p;                       // P
+          else dp[r] = p * (dp[r] - dr[j]);                        // dS
         }
       }
-      tr_accumulate(dsb, off, s, accv);          // dV^T += dO^T P
-      tr_accumulate(qsb, off, dp, acck);         // dK^T += Q^T dS
+      if constexpr (MODE == 0) tr_accumulate(dsb, off, s, acc);   // dV^T += dO^T P
+      else tr_accumulate(qsb, off, dp, acc);                      // dK^T += Q^T dS
     }
   };
 
+  // three buffers, two query tiles in flight ahead of the one being used (the query
+  // stream of a core tile is long and comes from beyond L2)
+  // vmcnt(4): waits until at most 4 of this wave's loads are outstanding.  A wave issues 4
+  // tile loads per tile (waves 0-1 one more, for the statistics), in order, and loads
+  // complete in order: the tile before the newest one has then landed.
+  constexpr int kW2 = 0x0F70 | 4;
   if (n_qt > 0) issue(0, lds0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (n_qt > 1) issue(1, lds1);
+  if (n_qt > 1) __builtin_amdgcn_s_waitcnt(kW2);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int qt = 0; qt < n_qt; qt += 2) {
-    if (qt + 1 < n_qt) issue(qt + 1, lds1);
+  for (int qt = 0; qt < n_qt; qt += 3) {
+    if (qt + 2 < n_qt) issue(qt + 2, lds2);
     if (wave_live) compute(lds0, qt);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (qt + 2 < n_qt) __builtin_amdgcn_s_waitcnt(kW2);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (qt + 1 >= n_qt) break;
-    if (qt + 2 < n_qt) issue(qt + 2, lds0);
+    if (qt + 3 < n_qt) issue(qt + 3, lds0);
     if (wave_live) compute(lds1, qt + 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (qt + 3 < n_qt) __builtin_amdgcn_s_waitcnt(kW2);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (qt + 2 >= n_qt) break;
+    if (qt + 4 < n_qt) issue(qt + 4, lds1);
+    if (wave_live) compute(lds2, qt + 2);
+    if (qt + 4 < n_qt) __builtin_amdgcn_s_waitcnt(kW2);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
   if (!wave_live) return;
   const int key = c0 + l32;
   if (key >= key_end) return;
-  float* ok = core ? dKc + ((size_t)bh * m + key) * kD : dK + slice + (size_t)key * kD;
-  float* ov = core ? dVc + ((size_t)bh * m + key) * kD : dV + slice + (size_t)key * kD;
+  float* o = core ? dKVc + ((size_t)bh * m + key) * kD : dKV + slice + (size_t)key * kD;
+  const float f = (MODE == 1) ? scale : 1.0f;
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<float4*>(ok + dt * 32 + 8 * i + 4 * hf) =
-          make_float4(acck[dt][4 * i] * scale, acck[dt][4 * i + 1] * scale, acck[dt][4 * i + 2] * scale,
-                      acck[dt][4 * i + 3] * scale);
-      *reinterpret_cast<float4*>(ov + dt * 32 + 8 * i + 4 * hf) =
-          make_float4(accv[dt][4 * i], accv[dt][4 * i + 1], accv[dt][4 * i + 2], accv[dt][4 * i + 3]);
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) =
+          make_float4(acc[dt][4 * i] * f, acc[dt][4 * i + 1] * f, acc[dt][4 * i + 2] * f, acc[dt][4 * i + 3] * f);
 }
 
 // ---------------------------------------------------------------------------
@@ -567,7 +593,7 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
 size_t backward_workspace_bytes(int B, int H, int64_t L, int d, int g) {
   const size_t BH = (size_t)B * H;
   const size_t m = (size_t)(L / g);
-  return (BH * (size_t)L + 2 * BH * m * (size_t)d) * sizeof(float);
+  return (2 * BH * (size_t)L + 2 * BH * m * (size_t)d) * sizeof(float);
 }
 
 hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
@@ -576,25 +602,32 @@ hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v
                                      hipStream_t stream) {
   const int64_t m = L / g;
   float* Dv = (float*)workspace;
-  float* dKc = Dv + (size_t)BH * L;
+  float* lse2 = Dv + (size_t)BH * L;
+  float* dKc = lse2 + (size_t)BH * L;
   float* dVc = dKc + (size_t)BH * m * kD;
   const int64_t rows = (int64_t)BH * L;
   hipLaunchKernelGGL(cca_bwd_prep_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
-                     (const bf16_t*)out, (const bf16_t*)dout, Dv, rows);
+                     (const bf16_t*)out, (const bf16_t*)dout, lse, Dv, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntiles = (int)((L + 255) / 256);
   hipLaunchKernelGGL(cca_bwd_dq_kernel, dim3((unsigned)(BH * ntiles)), dim3(512), 0, stream, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, (const bf16_t*)dout,
-                     lse, (const float*)Dv, dq, BH, (int)L, g, k_local, scale, ntiles);
+                     (const float*)lse2, (const float*)Dv, dq, BH, (int)L, g, k_local, scale, ntiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_core_wg = (int)((m + 127) / 128);
-  const int n_wg = n_core_wg + (int)((L + 127) / 128);
-  hipLaunchKernelGGL(cca_bwd_dkdv_kernel, dim3((unsigned)((int64_t)BH * n_wg)), dim3(256), 0, stream,
+  const int n_core_wg = (int)((m + 255) / 256);
+  const int n_wg = n_core_wg + (int)((L + 255) / 256);
+  hipLaunchKernelGGL(cca_bwd_dkdv_kernel<0>, dim3((unsigned)((int64_t)BH * n_wg)), dim3(512), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
-                     (const bf16_t*)dout, lse, (const float*)Dv, dk, dv, dKc, dVc, BH, (int)L, g, k_local, scale,
-                     n_core_wg, n_wg);
+                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dv, dVc, BH, (int)L, g, k_local, scale, n_core_wg,
+                     n_wg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cca_bwd_dkdv_kernel<1>, dim3((unsigned)((int64_t)BH * n_wg)), dim3(512), 0, stream,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
+                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dk, dKc, BH, (int)L, g, k_local, scale, n_core_wg,
+                     n_wg);
   e = hipGetLastError();
   if (e != hipSuccess || m == 0) return e;
   hipLaunchKernelGGL(cca_bwd_pool_kernel, dim3((unsigned)((int64_t)BH * m)), dim3(64), (size_t)2 * g * sizeof(float),

@@ -78,8 +78,8 @@ hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream);
 
-// Backward pass, bf16, head dim 128 (backward.hip).  Workspace: D [BH][L], then
-// dKc and dVc [BH][L/g][d], all float32.
+// Backward pass, bf16, head dim 128 (backward.hip).  Workspace: D [BH][L], the
+// log-sum-exp in log2 units [BH][L], then dKc and dVc [BH][L/g][d], all float32.
 size_t backward_workspace_bytes(int B, int H, int64_t L, int d, int g);
 hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                      const void* out, const float* lse, const void* dout, float* dq, float* dk,
