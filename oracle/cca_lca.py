@@ -1,0 +1,92 @@
+"""CPU fp64 oracle for the LCA-style pooling variant -- test infrastructure only.
+
+Source: "Latent-Condensed Transformer for Efficient Long Context Modeling"
+(gist.science), section 2 "Methodology": the context is split into groups; the
+importance of a token in its group is scored with the dot product of the
+group's MEAN query and the token's key; the content part of the representation
+is pooled with those weights (semantic condensation, weighted pooling); the
+positional part -- the RoPE key, which cannot be mixed -- is not pooled: the
+token with the highest importance is the group's anchor and its positional key
+is kept as is (positional anchoring, maximum selection); the most recent w
+tokens stay uncondensed (local context).  The attention over condensed groups
+plus the local window is the one of the CCA write-up ("ICML 2025 | 全局池化+局部保留，
+CCA-Attention为LLM长文本建模带来突破性进展", global-local fusion).
+
+Readings (the page describes the method in MLA's latent space; these kernels
+take per-head keys and values):
+  R18  the last d_rope dimensions of each key are its positional (RoPE) part,
+       the first d - d_rope its content part; values have no positional part;
+  R19  the mean query of group j is the mean of Q over the group's g positions;
+       the scores use the full key (content and positional dimensions), with the
+       attention scale;
+  R20  the anchor is the first position with the largest score; where several
+       scores are equal to within rounding, any of them is a valid anchor (tests
+       check the GPU's choice is such a maximum and compare the rest with the
+       oracle evaluated at that choice).
+Everything is float64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import cca_oracle as _o
+
+__all__ = ["group_mean_query", "lca_scores", "lca_pool", "lca_slice"]
+
+
+def group_mean_query(Q, j: int, g: int) -> np.ndarray:
+    """Mean of the group's g queries (R19)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    return Q[j * g:(j + 1) * g].sum(axis=0) / g
+
+
+def lca_scores(Q, K, g: int, scale: float) -> np.ndarray:
+    """Importance scores [m, g]: scale * mean query . key, per complete group."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    m = _o.n_core_groups(K.shape[0], g)
+    S = np.empty((m, g))
+    for j in range(m):
+        S[j] = scale * (K[j * g:(j + 1) * g] @ group_mean_query(Q, j, g))
+    return S
+
+
+def lca_pool(Q, K, V, g: int, scale: float, d_rope: int, anchors=None, core_dtype=None):
+    """(Kc [m,d], Vc [m,d], anchors [m]) of one slice.
+
+    Content dims of Kc and all of Vc: importance-weighted sums (softmax of the
+    scores); positional dims of Kc: the anchor token's key (argmax of the
+    scores, or the given `anchors`).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L, d = K.shape
+    dc = d - d_rope
+    S = lca_scores(Q, K, g, scale)
+    m = S.shape[0]
+    if anchors is None:
+        anchors = np.array([int(np.argmax(S[j])) for j in range(m)], dtype=np.int64)
+    Kc = np.empty((m, d))
+    Vc = np.empty((m, d))
+    for j in range(m):
+        a = _o.softmax(S[j])
+        rows = slice(j * g, (j + 1) * g)
+        Kc[j, :dc] = a @ K[rows, :dc]
+        Kc[j, dc:] = K[j * g + int(anchors[j]), dc:]
+        Vc[j] = a @ V[rows]
+    return _o.round_storage(Kc, core_dtype), _o.round_storage(Vc, core_dtype), np.asarray(anchors)
+
+
+def lca_slice(Q, K, V, g: int, k: int, scale: float, d_rope: int, anchors=None, core_dtype=None) -> np.ndarray:
+    """Output [L, d] of one slice: LCA core tokens, then CCA's unified attention."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L, d = Q.shape
+    Kc, Vc, _ = lca_pool(Q, K, V, g, scale, d_rope, anchors, core_dtype)
+    out = np.empty((L, d))
+    for t in range(L):
+        out[t] = _o.cca_row(Q[t], t, K, V, Kc, Vc, g, k, scale)
+    return out

@@ -1,0 +1,79 @@
+"""Pins for the LCA-style pooling oracle (oracle/cca_lca.py).
+
+Each pin takes the LCA module and returns (ok, detail).  References: a
+hand-derived closed form, reductions to the pinned CCA oracle (identical queries
+in a group make the mean query the last query; no positional dimensions make the
+core key the plain weighted sum), and structural facts (the positional part of a
+core key is one of the group's keys, the one with the largest score).  Page:
+"Latent-Condensed Transformer for Efficient Long Context Modeling", section 2.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle.cca_oracle as cca
+from long_context_sparse_cca_amd.synth import np_inputs
+
+
+def _err(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def pin_closed_form(lc):
+    """d = 2 (content dim 0, positional dim 1), g = 2, one group, scale 1.
+
+    Q rows (1, 0) and (3, 0): mean query (2, 0).  K rows (0, 5) and (x, -5) with
+    x = ln(3)/2: scores (0, 2x) = (0, ln 3), weights (1/4, 3/4); anchor = row 1.
+    Kc = (3x/4, -5): the content dim is pooled, the positional dim is the anchor's
+    (pooling it would give 5/4 - 15/4 = -2.5).  V rows (1, 2) and (3, 4): Vc = (5/2, 7/2).
+    """
+    x = math.log(3.0) / 2
+    Q = np.array([[1.0, 0.0], [3.0, 0.0]])
+    K = np.array([[0.0, 5.0], [x, -5.0]])
+    V = np.array([[1.0, 2.0], [3.0, 4.0]])
+    Kc, Vc, anc = lc.lca_pool(Q, K, V, 2, 1.0, 1)
+    e = max(_err(Kc, [[3 * x / 4, -5.0]]), _err(Vc, [[2.5, 3.5]]))
+    return e < 1e-12 and list(anc) == [1], f"max err {e:.3e}, anchors {list(anc)}"
+
+
+def pin_identical_queries_no_rope_is_cca_pooling(lc):
+    """Queries equal within each group and d_rope = 0: LCA pooling is CCA pooling."""
+    L, g, d = 48, 6, 8
+    Q, K, V = (x[0, 0].astype(np.float64) for x in np_inputs(1, 1, L, d, "f32", 21))
+    for j in range(L // g):
+        Q[j * g:(j + 1) * g] = Q[j * g + g - 1]
+    Kc, Vc, _ = lc.lca_pool(Q, K, V, g, 0.4, 0)
+    Kr, Vr, _ = cca.pool(Q, K, V, g, 0.4)
+    e = max(_err(Kc, Kr), _err(Vc, Vr))
+    return e < 1e-12, f"max err {e:.3e}"
+
+
+def pin_anchor_is_the_top_scored_key(lc):
+    """The positional dims of every core key are exactly those of the group's top-scored key."""
+    L, g, d, dr = 60, 5, 8, 3
+    Q, K, V = (x[0, 0].astype(np.float64) for x in np_inputs(1, 1, L, d, "f32", 22))
+    sc = 1.0 / math.sqrt(d)
+    Kc, _, anc = lc.lca_pool(Q, K, V, g, sc, dr)
+    for j in range(L // g):
+        qbar = Q[j * g:(j + 1) * g].mean(axis=0)
+        s = K[j * g:(j + 1) * g] @ qbar
+        top = int(np.argmax(s))
+        if int(anc[j]) != top or not np.array_equal(Kc[j, d - dr:], K[j * g + top, d - dr:]):
+            return False, f"group {j}"
+    return True, ""
+
+
+def pin_no_window_overlap_and_attention_is_cca(lc):
+    """With the same core tokens the attention is CCA's: g = 1 gives causal attention again."""
+    L, d = 30, 4
+    Q, K, V = (x[0, 0].astype(np.float64) for x in np_inputs(1, 1, L, d, "f32", 23))
+    sc = 0.5
+    out = lc.lca_slice(Q, K, V, 1, 2, sc, 2)   # groups of one token: the core token is the token itself
+    e = _err(out, cca.cca_slice(Q, K, V, 1, 2, sc))
+    return e < 1e-12, f"max err {e:.3e}"
+
+
+ALL_LCA_PINS = [pin_closed_form, pin_identical_queries_no_rope_is_cca_pooling, pin_anchor_is_the_top_scored_key,
+                pin_no_window_overlap_and_attention_is_cca]

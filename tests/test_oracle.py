@@ -29,3 +29,13 @@ from tests import backward_pins
 def test_backward_pin(pin):
     ok, detail = pin(oracle.cca_backward)
     assert ok, detail
+
+
+import oracle.cca_lca
+from tests import lca_pins
+
+
+@pytest.mark.parametrize("pin", lca_pins.ALL_LCA_PINS, ids=lambda f: f.__name__)
+def test_lca_pin(pin):
+    ok, detail = pin(oracle.cca_lca)
+    assert ok, detail

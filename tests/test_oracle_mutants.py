@@ -172,3 +172,50 @@ def test_some_backward_pin_catches(name, monkeypatch):
         if not ok:
             failed.append(pin.__name__)
     assert failed, f"no backward pin caught mutant '{name}'"
+
+
+import oracle.cca_lca as lca
+from tests import lca_pins
+
+
+def _last_query_instead_of_mean(Q, j, g):
+    return np.asarray(Q, np.float64)[j * g + g - 1]
+
+
+def _sum_instead_of_mean(Q, j, g):
+    return np.asarray(Q, np.float64)[j * g:(j + 1) * g].sum(axis=0)
+
+
+_orig_lca_pool = lca.lca_pool
+
+
+def _pooled_positional_dims(Q, K, V, g, scale, d_rope, anchors=None, core_dtype=None):
+    return _orig_lca_pool(Q, K, V, g, scale, 0, anchors, core_dtype)
+
+
+def _anchor_is_argmin(Q, K, V, g, scale, d_rope, anchors=None, core_dtype=None):
+    S = lca.lca_scores(Q, K, g, scale)
+    return _orig_lca_pool(Q, K, V, g, scale, d_rope, np.argmin(S, axis=1), core_dtype)
+
+
+LCA_MUTANTS = {
+    "importance from the last query": ("group_mean_query", _last_query_instead_of_mean),
+    "importance from the summed queries": ("group_mean_query", _sum_instead_of_mean),
+    "positional dims pooled": ("lca_pool", _pooled_positional_dims),
+    "anchor at the lowest score": ("lca_pool", _anchor_is_argmin),
+}
+
+
+@pytest.mark.parametrize("name", list(LCA_MUTANTS))
+def test_some_lca_pin_catches(name, monkeypatch):
+    attr, fn = LCA_MUTANTS[name]
+    monkeypatch.setattr(lca, attr, fn)
+    failed = []
+    for pin in lca_pins.ALL_LCA_PINS:
+        try:
+            ok, _ = pin(lca)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"no LCA pin caught mutant '{name}'"
