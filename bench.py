@@ -49,7 +49,9 @@ def parse():
     ap.add_argument("--no-training", action="store_true", help="skip the forward+backward measurement")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the serving decode measurement (per-sequence lengths, grouped-query heads)")
-    ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "training", "copy"], default="all",
+    ap.add_argument("--no-lca", action="store_true", help="skip the LCA-style variant measurement")
+    ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "training", "lca", "copy"],
+                    default="all",
                     help="profiling aid: run only one phase (the JSON line is then not the benchmark result); "
                          "'copy' runs a plain 1 GiB device copy whose counter readings calibrate FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
@@ -274,6 +276,39 @@ def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int 
                          "per_unit": "10*d FLOPs per visible (query, key) pair"}}
 
 
+def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int = 64, reps: int = 5):
+    """LCA-style condensation (cca_pool_kv_lca) and the prefill built on it (cca_prefill_lca),
+    B=1, H=32, d=128, g=16, k=64, bf16, last 64 dims of each key positional; outside the timed steps."""
+    import torch
+
+    from long_context_sparse_cca_amd.synth import torch_inputs
+    q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, dev, seed=seed + 9, heavy_frac=HEAVY)
+    binding.prefill_lca(q, k, v, G, KL, d_rope)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    tp, tf = [], []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        binding.pool_kv_lca(q, k, v, G, d_rope)
+        e[1].record(stream)
+        e[2].record(stream)
+        binding.prefill_lca(q, k, v, G, KL, d_rope)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        tp.append(e[0].elapsed_time(e[1]))
+        tf.append(e[2].elapsed_time(e[3]))
+    pool_ms, prefill_ms = sum(tp) / reps, sum(tf) / reps
+    byt = accounting.lca_pool_bytes(1, H, L, D, G, 2)
+    gbs = byt / (pool_ms * 1e-3) / 1e9
+    return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL, "d_rope": d_rope},
+            "pool_ms": pool_ms, "prefill_ms": prefill_ms, "prefill_tokens_per_s": L / (prefill_ms * 1e-3),
+            "pool_bytes": byt,
+            "roofline": {"kernel": "cca_pool_lca_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                         "per_unit": "(3*g + 2)*d*2 bytes per group"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -303,6 +338,10 @@ def main():
         return
     if args.phase == "training":
         print(json.dumps({"phase": "training", "training": training_step(binding, accounting, dev, args.seed)}),
+              flush=True)
+        return
+    if args.phase == "lca":
+        print(json.dumps({"phase": "lca", "lca_variant": lca_variant(binding, accounting, dev, args.seed)}),
               flush=True)
         return
     if args.phase == "serving":
@@ -447,6 +486,9 @@ def main():
         res["serving_decode"] = serving_decode(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_training and args.phase == "all":
         res["training"] = training_step(binding, accounting, dev, args.seed)
+        torch.cuda.empty_cache()
+    if do_prefill and not args.no_lca and args.phase == "all":
+        res["lca_variant"] = lca_variant(binding, accounting, dev, args.seed)
         torch.cuda.empty_cache()
     if do_prefill and not args.no_dense and args.phase == "all":
         res["dense_comparison"] = dense_comparison(binding, accounting, dev, args.seed)

@@ -134,6 +134,29 @@ int cca_attention_gqa(const void* q, const void* k, const void* v, const void* k
                       int dt, int out_dt, hipStream_t stream);
 
 /*
+ * LCA-style pooling variant ("Latent-Condensed Transformer for Efficient Long
+ * Context Modeling", section 2: importance from the mean query of the group,
+ * weighted pooling of the content part, positional anchoring of the RoPE part).
+ * Per group j: q_bar = mean of Q[j*g .. j*g+g-1]; s_i = scale * q_bar . K[j*g+i];
+ * a = softmax(s); the first d - d_rope dims of Kc[j] are sum_i a_i K[j*g+i], its
+ * last d_rope dims are those of K[j*g + anchor], anchor = the first i with the
+ * largest s_i; Vc[j] = sum_i a_i V[j*g+i].  The last d_rope dims of a key are
+ * taken to be its positional (RoPE) part; d_rope = 0 pools every dim.
+ *   anchors : optional device int32 [B, H, floor(L/g)], receives each anchor
+ *             (position within its group); may be NULL.
+ * cca_prefill_lca: this pooling followed by the attention of cca_prefill (the
+ * condensed groups in the role of the core tokens; raw local window as in CCA).
+ * Other arguments, limits and errors as for cca_pool_kv / cca_prefill;
+ * 0 <= d_rope <= d else CCA_ERR_INVALID.
+ */
+int cca_pool_kv_lca(const void* q, const void* k, const void* v, void* kc, void* vc, int32_t* anchors,
+                    int B, int H, int64_t L, int d, int g, int d_rope, float scale,
+                    int dt, hipStream_t stream);
+int cca_prefill_lca(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int32_t* anchors,
+                    int B, int H, int64_t L, int d, int g, int k_local, int d_rope, float scale,
+                    int dt, int out_dt, hipStream_t stream);
+
+/*
  * Training ([CCA] Triton section: the fused operator serves training as well;
  * the models are fine-tuned with it).  bf16 inputs, d = 128, one query head per
  * key/value head; other dtypes or head dims give CCA_ERR_UNSUPPORTED.

@@ -47,6 +47,13 @@ def pool_bytes(B: int, H: int, L: int, d: int, g: int, elem: int) -> int:
     return B * H * elem * d * (2 * m * g + m + 2 * m)
 
 
+def lca_pool_bytes(B: int, H: int, L: int, d: int, g: int, elem: int) -> int:
+    """HBM bytes of the LCA-style pooling pass: Q, K and V of complete groups read once
+    (the anchor's key row is a re-read of a row already fetched), condensed K/V out."""
+    m = L // g
+    return B * H * elem * d * (3 * m * g + 2 * m)
+
+
 def attention_min_bytes(B: int, H: int, L: int, d: int, g: int, elem: int, out_elem: int) -> int:
     """Compulsory HBM bytes of the fused attention: Q, K, V and core K/V read once, O written once."""
     m = L // g

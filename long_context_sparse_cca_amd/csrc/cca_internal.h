@@ -21,6 +21,11 @@ struct ExtendArgs {
   int64_t core_rows;   // rows per core K/V slice
 };
 
+// LCA-style pooling (pool_lca.hip): mean-query importance, the last d_rope dims of a
+// core key taken from the group's top-scored token; anchors (optional) receive its index.
+hipError_t launch_pool_lca(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
+                           int32_t* anchors, int BH, int64_t L, int g, int d_rope, float scale, hipStream_t stream);
+
 // Grouped-query attention: nq = H / H_kv query heads share each key/value head.
 // Query/output slices are (b, h) = b*H + h; key/value and core slices are
 // (b, h_kv) = b*H_kv + h_kv, and query slice s reads key/value slice s / nq.

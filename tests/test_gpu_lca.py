@@ -1,0 +1,153 @@
+"""LCA-style pooling variant on the GPU vs the CPU oracle (oracle/cca_lca.py).
+
+The anchor is an argmax, so the GPU's choice is checked first: its score (fp64,
+recomputed by the oracle) must equal the group's largest score to within the
+rounding of fp32 scores.  Condensed keys/values and the attention output are then
+compared with the oracle evaluated at the GPU's anchors.  The positional dims of
+a condensed key are copies of one key row, so they are compared bit for bit.
+Tolerances (max-abs) as for CCA: fp32 1e-4, bf16 2e-2, plus one storage rounding
+of the condensed tokens.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cca_lca, cca_oracle
+from long_context_sparse_cca_amd import binding
+from long_context_sparse_cca_amd.synth import np_inputs, torch_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+ULP = {"f32": 2.0 ** -22, "bf16": 2.0 ** -8}
+
+
+def _dev(x, dt, device):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=TDT[dt]).contiguous()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_anchors(S, anchors):
+    """Every anchor is a maximum of its group's scores (to fp32 rounding of the scores)."""
+    anchors = np.asarray(anchors, dtype=np.int64)
+    assert anchors.shape == (S.shape[0],)
+    assert np.all((anchors >= 0) & (anchors < S.shape[1])), "anchor outside its group"
+    best = S.max(axis=1)
+    picked = S[np.arange(S.shape[0]), anchors]
+    eps = 1e-5 * np.maximum(1.0, np.abs(S).max(axis=1))
+    assert np.all(picked >= best - eps), f"anchor not a maximum: gap {np.max(best - picked):.3e}"
+
+
+# (B, H, L, d, g, k, d_rope, dtype, seed)
+LCA_CASES = [
+    (1, 2, 256, 64, 16, 1, 32, "f32", 0),
+    (1, 2, 1000, 128, 16, 4, 64, "bf16", 1),     # several tiles, ragged tail
+    (2, 3, 517, 64, 7, 3, 16, "bf16", 2),        # g not a power of two
+    (1, 2, 640, 128, 16, 100, 0, "f32", 3),      # d_rope = 0: every dim pooled
+    (1, 1, 700, 128, 64, 2, 128, "bf16", 4),     # d_rope = d: whole key from the anchor
+    (1, 1, 300, 128, 100, 1, 64, "f32", 5),      # g > 64: scores over two passes of the wave
+    (1, 1, 15, 64, 16, 1, 32, "bf16", 6),        # L < g: nothing condensed
+]
+
+
+def _case_id(c):
+    B, H, L, d, g, k, r, dt, seed = c
+    return f"B{B}H{H}L{L}d{d}g{g}k{k}r{r}-{dt}"
+
+
+@pytest.mark.parametrize("case", LCA_CASES, ids=_case_id)
+def test_lca_matches_oracle(gpu, case):
+    B, H, L, d, g, k, d_rope, dt, seed = case
+    _say(f"lca case {_case_id(case)} seed {seed}")
+    Q, K, V = np_inputs(B, H, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    out, kc, vc, anchors = binding.prefill_lca(q, kk, v, g, k, d_rope, scale, out_dtype=torch.float32)
+    kc2, vc2, anchors2 = binding.pool_kv_lca(q, kk, v, g, d_rope, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(anchors, anchors2) and torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    m = L // g
+    dc = d - d_rope
+    for b in range(B):
+        for h in range(H):
+            Qs, Ks, Vs = (x[b, h].astype(np.float64) for x in (Q, K, V))
+            anc = anchors[b, h].cpu().numpy()
+            if m:
+                _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
+                Kc, Vc, _ = cca_lca.lca_pool(Qs, Ks, Vs, g, scale, d_rope, anchors=anc)
+                gk = kc[b, h].float().cpu().numpy()
+                gv = vc[b, h].float().cpu().numpy()
+                # positional dims: the anchor's key row, exactly
+                want_pos = Ks[np.arange(m) * g + anc.astype(np.int64), dc:]
+                assert np.array_equal(gk[:, dc:], want_pos), "positional dims differ from the anchor key"
+                for got, ref in ((gk[:, :dc], Kc[:, :dc]), (gv, Vc)):
+                    bound = TOL[dt] + ULP[dt] * np.abs(ref)
+                    assert np.all(np.abs(got - ref) <= bound), f"condensed err {np.abs(got - ref).max():.3e}"
+            want = cca_lca.lca_slice(Qs, Ks, Vs, g, k, scale, d_rope, anchors=anc if m else None, core_dtype=dt)
+            err = np.abs(out[b, h].cpu().numpy().astype(np.float64) - want).max()
+            assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e} at b={b} h={h}"
+
+
+def test_lca_equal_scores_take_first_position(gpu):
+    """Groups of identical keys score equally: the anchor is the group's first token."""
+    B, H, L, d, g = 1, 2, 256, 128, 16
+    Q, K, V = np_inputs(B, H, L, d, "bf16", 11)
+    K = np.repeat(K[:, :, ::g], g, axis=2)   # every key of a group equals the group's first key
+    q, kk, v = (_dev(x, "bf16", gpu) for x in (Q, K, V))
+    kc, vc, anchors = binding.pool_kv_lca(q, kk, v, g, 64)
+    torch.cuda.synchronize()
+    assert int(anchors.abs().max()) == 0
+    # equal scores: uniform weights, so the condensed key equals the shared key
+    assert torch.equal(kc, kk[:, :, ::g])
+
+
+def test_lca_invalid_rope_width(gpu):
+    Q, K, V = np_inputs(1, 1, 64, 64, "f32", 0)
+    q, kk, v = (_dev(x, "f32", gpu) for x in (Q, K, V))
+    for r in (-1, 65):
+        with pytest.raises(binding.CCAError):
+            binding.pool_kv_lca(q, kk, v, 16, r)
+
+
+def test_lca_full_size_sampled(gpu):
+    """32K tokens, 32 heads, d = 128, bf16: sampled groups and queries against the oracle."""
+    B, H, L, d, g, k, d_rope = 1, 32, 32768, 128, 16, 1, 64
+    _say(f"lca full size B{B} H{H} L{L}")
+    q, kk, v = torch_inputs(B, H, L, d, torch.bfloat16, gpu, seed=21)
+    scale = 1.0 / math.sqrt(d)
+    out, kc, vc, anchors = binding.prefill_lca(q, kk, v, g, k, d_rope, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    m = L // g
+    dc = d - d_rope
+    for h in rng.choice(H, size=3, replace=False):
+        Qs = q[0, h].double().cpu().numpy()
+        Ks = kk[0, h].double().cpu().numpy()
+        Vs = v[0, h].double().cpu().numpy()
+        anc = anchors[0, h].cpu().numpy()
+        groups = np.concatenate([[0, m - 1], rng.choice(m, size=30, replace=False)])
+        for j in groups:
+            rows = slice(j * g, (j + 1) * g)
+            S = cca_lca.lca_scores(Qs[rows], Ks[rows], g, scale)
+            _check_anchors(S, anc[j:j + 1])
+            Kc, Vc, _ = cca_lca.lca_pool(Qs[rows], Ks[rows], Vs[rows], g, scale, d_rope, anchors=anc[j:j + 1])
+            gk = kc[0, h, j].float().cpu().numpy()
+            gv = vc[0, h, j].float().cpu().numpy()
+            assert np.array_equal(gk[dc:], Ks[j * g + anc[j], dc:])
+            for got, ref in ((gk[:dc], Kc[0, :dc]), (gv, Vc[0])):
+                assert np.all(np.abs(got - ref) <= TOL["bf16"] + ULP["bf16"] * np.abs(ref))
+        # sampled query rows: the oracle's row with the GPU's condensed tokens (as stored)
+        gkc = kc[0, h].double().cpu().numpy()
+        gvc = vc[0, h].double().cpu().numpy()
+        for t in np.concatenate([[0, L - 1], rng.choice(L, size=20, replace=False)]):
+            want = cca_oracle.cca_row(Qs[t], int(t), Ks, Vs, gkc, gvc, g, k, scale)
+            err = np.abs(out[0, h, t].cpu().numpy().astype(np.float64) - want).max()
+            assert err <= TOL["bf16"], f"row {t} err {err:.3e}"
