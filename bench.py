@@ -40,8 +40,8 @@ HEAVY = 0.01
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -377,7 +377,7 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     pe = [ev() for _ in range(3)]
     de = [ev() for _ in range(2 * DEC_STEPS)]
-    t_pool, t_attn, t_dec, t_decstep = [], [], [], []
+    t_pool, t_attn, t_dec, t_decstep, dec_all = [], [], [], [], []
 
     def one_step(record: bool):
         if do_prefill:
@@ -401,7 +401,9 @@ def main():
             t_pool.append(pe[0].elapsed_time(pe[1]))
             t_attn.append(pe[1].elapsed_time(pe[2]))
         if do_decode:
-            d = sum(de[2 * s].elapsed_time(de[2 * s + 1]) for s in range(DEC_STEPS))
+            per = [de[2 * s].elapsed_time(de[2 * s + 1]) for s in range(DEC_STEPS)]
+            dec_all.extend(per)
+            d = sum(per)
             w = de[0].elapsed_time(de[2 * DEC_STEPS - 1])
             t_dec.append(d / DEC_STEPS)       # kernel time per step
             t_decstep.append(w / DEC_STEPS)   # step-to-step time, launch gaps included
@@ -417,6 +419,13 @@ def main():
     print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")  # noqa: E731
+
+    def median(xs):
+        if not xs:
+            return float("nan")
+        ys = sorted(xs)
+        h = len(ys) // 2
+        return ys[h] if len(ys) % 2 else 0.5 * (ys[h - 1] + ys[h])
     res = {
         "metric": METRIC,
         "value": None,
@@ -440,7 +449,7 @@ def main():
     }
     src_attn = source_hash("prefill.hip", "prefill_bf16.hip", "cca_device.h")
     if do_prefill:
-        ms_pool, ms_attn = mean(t_pool), mean(t_attn)
+        ms_pool, ms_attn = median(t_pool), median(t_attn)   # medians over the timed steps
         ms_prefill = ms_pool + ms_attn
         flops = accounting.prefill_flops(PREFILL_B, H, PREFILL_L, D, G, KL)
         pool_b = accounting.pool_bytes(PREFILL_B, H, PREFILL_L, D, G, 2)
@@ -448,6 +457,7 @@ def main():
         res["value"] = PREFILL_B * PREFILL_L / (ms_prefill * 1e-3)
         res["prefill"] = {
             "ms": ms_prefill, "pool_ms": ms_pool, "attention_ms": ms_attn,
+            "attention_ms_mean": mean(t_attn), "attention_ms_min": min(t_attn), "attention_ms_max": max(t_attn),
             "attention_tflops": tflops, "attention_flops": flops,
             "pool_gbs": pool_b / (ms_pool * 1e-3) / 1e9, "pool_bytes": pool_b,
             "pool_hbm_frac": pool_b / (ms_pool * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -468,10 +478,12 @@ def main():
         nchunks = cache.ws_bytes // (DEC_B * H * (D + 2) * 4)   # chunk count the library chose
         byt = [accounting.decode_bytes(DEC_B, H, D, DEC_L0 + s, G, KL, 2, nchunks) for s in range(DEC_STEPS)]
         mean_bytes = sum(byt) / len(byt)
-        us_dec = mean(t_dec) * 1e3
+        us_dec = median(t_dec) * 1e3
         gbs = mean_bytes / (us_dec * 1e-6) / 1e9
         res["decode"] = {
-            "us_per_step": mean(t_decstep) * 1e3, "kernel_us": us_dec, "chunks": nchunks,
+            "us_per_step": median(t_decstep) * 1e3, "us_per_step_mean": mean(t_decstep) * 1e3,
+            "kernel_us": us_dec, "kernel_us_mean": mean(t_dec) * 1e3, "kernel_us_p50_over_steps": median(dec_all) * 1e3,
+            "chunks": nchunks,
             "bytes_per_step": mean_bytes,
             "roofline": {"kernel": "cca_decode_kernel<bf16,128,append> + cca_decode_merge_kernel",
                          "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",

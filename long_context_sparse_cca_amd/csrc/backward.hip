@@ -329,14 +329,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int c0 = key0 + wave * 32;         // this wave's first key
   const int c_last = min(key0 + kBK, key_end) - 1;
 
+  // Visibility in query positions, so that the loops need no division by g:
+  //   core token j is seen by the queries t >= (j + k + 1) g,
+  //   raw key u by the queries u <= t <= (u / g + k + 1) g - 1.
+  auto core_first = [&](int j) { return (int)min((int64_t)L, ((int64_t)j + k_local + 1) * g); };
+  auto raw_last = [&](int u) { return (int)min((int64_t)L - 1, ((int64_t)(u / g) + k_local + 1) * g - 1); };
   // query range [t_lo, t_hi] that can see any key of the workgroup
   int t_lo, t_hi;
   if (core) {
-    t_lo = (key0 + k_local + 1) * g;       // core j visible iff t >= (j + k + 1) g
+    t_lo = core_first(key0);
     t_hi = L - 1;
   } else {
     t_lo = key0;
-    t_hi = min(L - 1, (c_last / g + k_local + 1) * g - 1);
+    t_hi = raw_last(c_last);
   }
   const int tq0 = (t_lo / kTileRows) * kTileRows;
   const int n_qt = (t_lo <= t_hi) ? (t_hi - tq0) / kTileRows + 1 : 0;
@@ -365,8 +370,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool wave_live = c0 < key_end;
   const int c_hi = min(c0 + 31, key_end - 1);
 
+  // per wave: a sub-block of queries [t0, t1] sees none of the keys c0..c_hi when t1 < w_none_below
+  // or t0 > w_none_above, and all of them when t0 >= w_all_from and t1 <= w_all_to
+  const int w_none_below = core ? core_first(c0) : c0;
+  const int w_none_above = core ? L - 1 : raw_last(c_hi);
+  const int w_all_from = core ? core_first(c_hi) : c_hi;
+  const int w_all_to = core ? L - 1 : raw_last(c0);
+  // per lane: this key is seen by the queries q_lo .. q_lo + q_span (none for a lane past the last key)
+  int q_lo;
+  unsigned q_span;
+  {
+    const int key = c0 + l32;
+    const int a = core ? core_first(key) : key;
+    const int b = core ? L - 1 : raw_last(key);
+    const bool ok = key <= c_hi && a <= b;
+    q_lo = ok ? a : -0x40000000;
+    q_span = ok ? (unsigned)(b - a) : 0u;
+  }
+
+  // query tiles from the last one down: the workgroups of a slice that run together
+  // then stream the same query tiles at about the same time (shared in L2)
+  auto tile_base = [&](int qt) { return tq0 + (n_qt - 1 - qt) * kTileRows; };
   auto issue = [&](int qt, uint8_t* buf) {
-    const int base = tq0 + qt * kTileRows;
+    const int base = tile_base(qt);
     fill_tile<8>(Qs, base, L - 1, buf, wave, lane);
     fill_tile<8>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
     // log-sum-exp (log2 units) and D of the tile's 64 queries: one 4-byte DMA per lane
@@ -385,26 +411,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float* d_t = lse_t + kTileRows;
 #pragma unroll
     for (int sb = 0; sb < kTileRows / 32; ++sb) {
-      const int t0 = tq0 + qt * kTileRows + sb * 32;
+      const int t0 = tile_base(qt) + sb * 32;
       const int t1 = min(t0 + 31, L - 1);
       if (t0 >= L) continue;
       int cls;   // 0: nothing visible, 1: everything visible, 2: mixed
-      if (core) {
-        const int nc_lo = max(0, t0 / g - k_local), nc_hi = max(0, t1 / g - k_local);
-        cls = (nc_hi <= c0) ? 0 : ((c_hi < nc_lo && t0 + 31 < L) ? 1 : 2);
-      } else {
-        const int rl_lo = max(0, t0 / g - k_local) * g, rl_hi = max(0, t1 / g - k_local) * g;
-        if (t1 < c0 || rl_lo > c_hi) cls = 0;
-        else if (t0 >= c_hi && rl_hi <= c0 && t0 + 31 < L) cls = 1;
-        else cls = 2;
-      }
+      if (t1 < w_none_below || t0 > w_none_above) cls = 0;
+      else if (t0 >= w_all_from && t1 <= w_all_to && t0 + 31 < L) cls = 1;
+      else cls = 2;
       if (cls == 0) continue;
       const uint8_t* qsb = buf + sb * 32 * kRowBytes;
       const uint8_t* dsb = buf + kTileBytes + sb * 32 * kRowBytes;
       f32x16_t s = rows_chain(qsb, off, kop);    // S: queries (rows) x keys (cols)
       f32x16_t dp;
       if constexpr (MODE == 1) dp = rows_chain(dsb, off, vop);   // dP
-      const int key = c0 + l32;
+      const int tq = t0 + 4 * hf - q_lo;   // query t0 + 8i + 4hf + j is visible iff (tq + 8i + j) <= q_span
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 lv = *reinterpret_cast<const float4*>(lse_t + sb * 32 + 8 * i + 4 * hf);
@@ -419,14 +439,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int r = 4 * i + j;
           float p = fast_exp2(fmaf(s[r], sc, -lr[j]));
           if (cls == 2) {
-            const int t = t0 + 8 * i + 4 * hf + j;
-            bool vis;
-            if (core) {
-              vis = key < t / g - k_local;
-            } else {
-              vis = key <= t && key >= max(0, t / g - k_local) * g;
-            }
-            vis = vis && t < L && key <= c_hi;
+            const bool vis = (unsigned)(tq + 8 * i + j) <= q_span;
             p = vis ? p : 0.f;
           }
           if constexpr (MODE == 0) s[r] = p;                       // P
