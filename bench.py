@@ -87,12 +87,27 @@ def cpu_baseline(q, k, v, out, seconds: float):
     import numpy as np
 
     import oracle
+    n_cpu = len(os.sched_getaffinity(0))
+    blas = "unknown"
+    limiter = None
     try:
         import threadpoolctl
-        threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+        limiter = threadpoolctl.threadpool_limits(limits=n_cpu)   # BLAS/OpenMP pools sized to the cores we may use
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        threads = sum(i.get("num_threads", 0) for i in info)
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info) or "none found"
     except Exception:  # noqa: BLE001
         threads = 1
     threads = threads or 1
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     scale = 1.0 / math.sqrt(D)
     Q = q[0, 0].float().cpu().numpy().astype(np.float64)
     K = k[0, 0].float().cpu().numpy().astype(np.float64)
@@ -115,6 +130,8 @@ def cpu_baseline(q, k, v, out, seconds: float):
     Kx, Vx, _ = oracle.pool(Q, K, V, G, scale)
     err_exact = max(float(np.abs(got[int(t)] - oracle.cca_row(Q[t], int(t), K, V, Kx, Vx, G, KL, scale)).max())
                     for t in rows[:min(n, 2000)])
+    if limiter is not None:
+        limiter.restore_original_limits()
     per_row = t_rows / n
     layer_s = H * PREFILL_B * (t_pool + PREFILL_L * per_row)
     return {
@@ -124,7 +141,9 @@ def cpu_baseline(q, k, v, out, seconds: float):
         "kind": "oracle",
         "sample": (f"head 0 of the prefill input: full pooling ({t_pool:.2f} s) + {n} uniformly drawn query rows "
                    f"({t_rows:.1f} s); extrapolated to all {H} heads x {PREFILL_L} rows"),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model,
+        "cpus_available": n_cpu,
+        "blas": blas,
         "parity_max_abs_err": err,
         "parity_rows": n,
         "err_vs_exact_core_tokens": err_exact,

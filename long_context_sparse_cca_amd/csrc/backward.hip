@@ -77,40 +77,47 @@ __device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f
                                                  0, 0, 0);
 }
 
-// Rows-operand MFMA chain: out = X_subblock(32 rows from LDS) . Y^T where Y's 32
-// rows sit in registers as B operands yop[d16].
-__device__ __forceinline__ f32x16_t rows_chain(const uint8_t* tile_sb, const TileOffsets& o, const uint4* yop) {
-  uint4 xa[kD / 16];
+// Transpose-operand accumulation acc[dt] += X_subblock^T (d x 32 rows from LDS) . W,
+// W [32 rows x 32 cols] the fp32 32x32 MFMA output `w` rounded to bf16, in two halves:
+// the transpose reads of half u (rows 16u .. 16u+15) are issued early (tr_read), the
+// MFMAs later (tr_mfma).
+struct TrHalf {
+  v4s_t r[2][kD / 32];
+};
+__device__ __forceinline__ void tr_read(const uint8_t* tile_sb, const TileOffsets& o, int u, TrHalf& t) {
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt) {
+    t.r[0][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[0][dt]));
+    t.r[1][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[1][dt]));
+  }
+}
+__device__ __forceinline__ void tr_mfma(const TrHalf& t, const f32x16_t& w, int u, f32x16_t* acc) {
+  bf16x2_t pp[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pp[e] = bf16x2_t{(__bf16)w[8 * u + 2 * e], (__bf16)w[8 * u + 2 * e + 1]};
+  const uint4 pb = __builtin_bit_cast(uint4, pp);
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt) {
+    const v4s_t both[2] = {t.r[0][dt], t.r[1][dt]};
+    acc[dt] = mfma(__builtin_bit_cast(uint4, both), pb, acc[dt]);
+  }
+}
+
+// Rows-operand chain out = X_subblock (32 rows from LDS) . Y^T, Y's 32 rows in registers
+// as B operands yop[d16]: the reads (rows_read) are issued before the MFMAs (rows_mfma).
+__device__ __forceinline__ void rows_read(const uint8_t* tile_sb, const TileOffsets& o, uint4* xa) {
 #pragma unroll
   for (int d16 = 0; d16 < kD / 16; ++d16) xa[d16] = *reinterpret_cast<const uint4*>(tile_sb + o.rows[d16]);
+}
+__device__ __forceinline__ f32x16_t rows_mfma(const uint4* xa, const uint4* yop) {
   f32x16_t s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
   for (int d16 = 0; d16 < kD / 16; ++d16) s = mfma(xa[d16], yop[d16], s);
   return s;
-}
-
-// Transpose-operand accumulation: acc[dt] += X_subblock^T (d x 32 rows from LDS) . W
-// where W [32 rows x 32 cols] is the fp32 32x32 MFMA output `w` (rounded to bf16).
-__device__ __forceinline__ void tr_accumulate(const uint8_t* tile_sb, const TileOffsets& o, const f32x16_t& w,
-                                              f32x16_t* acc) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    bf16x2_t pp[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pp[e] = bf16x2_t{(__bf16)w[8 * u + 2 * e], (__bf16)w[8 * u + 2 * e + 1]};
-    const uint4 pb = __builtin_bit_cast(uint4, pp);
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
-      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[0][dt]));
-      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[1][dt]));
-      const v4s_t both[2] = {lo, hi};
-      acc[dt] = mfma(__builtin_bit_cast(uint4, both), pb, acc[dt]);
-    }
-  }
 }
 
 // Fill a 64-row tile (rows base .. base+63 of a row-major [*, 128] bf16 array,
@@ -249,8 +256,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (cls == 0) continue;
       const uint8_t* ksb = kt + sb * 32 * kRowBytes;
       const uint8_t* vsb = vt + sb * 32 * kRowBytes;
-      f32x16_t s = rows_chain(ksb, off, qop);    // S^T: keys x queries
-      f32x16_t dp = rows_chain(vsb, off, dop);   // dP^T
+      // operand reads up front; score and dP chains at raised priority, the first half of the
+      // K^T transpose reads issued behind them so that their latency hides under dS
+      uint4 xa[kD / 16], ya[kD / 16];
+      rows_read(ksb, off, xa);
+      rows_read(vsb, off, ya);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      f32x16_t s = rows_mfma(xa, qop);           // S^T: keys x queries
+      f32x16_t dp = rows_mfma(ya, dop);          // dP^T
+      TrHalf th;
+      tr_read(ksb, off, 0, th);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       if (cls == 2) {
         const int k0 = kb + 4 * hf - lo;
 #pragma unroll
@@ -266,7 +284,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float p = fast_exp2(fmaf(s[r], sc, -lse2));
         dp[r] = p * (dp[r] - Dq);                 // dS^T
       }
-      tr_accumulate(ksb, off, dp, acc);          // dQ^T += K^T dS^T
+      tr_mfma(th, dp, 0, acc);                   // dQ^T += K^T dS^T
+      tr_read(ksb, off, 1, th);
+      tr_mfma(th, dp, 1, acc);
     }
   };
 
@@ -421,9 +441,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (cls == 0) continue;
       const uint8_t* qsb = buf + sb * 32 * kRowBytes;
       const uint8_t* dsb = buf + kTileBytes + sb * 32 * kRowBytes;
-      f32x16_t s = rows_chain(qsb, off, kop);    // S: queries (rows) x keys (cols)
+      uint4 xa[kD / 16], ya[MODE == 1 ? kD / 16 : 1];
+      rows_read(qsb, off, xa);
+      if constexpr (MODE == 1) rows_read(dsb, off, ya);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      f32x16_t s = rows_mfma(xa, kop);           // S: queries (rows) x keys (cols)
       f32x16_t dp;
-      if constexpr (MODE == 1) dp = rows_chain(dsb, off, vop);   // dP
+      if constexpr (MODE == 1) dp = rows_mfma(ya, vop);   // dP
+      TrHalf th0, th1;
+      tr_read(MODE == 0 ? dsb : qsb, off, 0, th0);
+      if constexpr (MODE == 0) tr_read(dsb, off, 1, th1);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       const int tq = t0 + 4 * hf - q_lo;   // query t0 + 8i + 4hf + j is visible iff (tq + 8i + j) <= q_span
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -446,8 +476,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           else dp[r] = p * (dp[r] - dr[j]);                        // dS
         }
       }
-      if constexpr (MODE == 0) tr_accumulate(dsb, off, s, acc);   // dV^T += dO^T P
-      else tr_accumulate(qsb, off, dp, acc);                      // dK^T += Q^T dS
+      if constexpr (MODE == 0) {                 // dV^T += dO^T P
+        tr_mfma(th0, s, 0, acc);
+        tr_mfma(th1, s, 1, acc);
+      } else {                                   // dK^T += Q^T dS
+        tr_mfma(th0, dp, 0, acc);
+        tr_read(qsb, off, 1, th1);
+        tr_mfma(th1, dp, 1, acc);
+      }
     }
   };
 

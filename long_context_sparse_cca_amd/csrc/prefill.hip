@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int bh, qtile;
   map_block(BH * ntiles, ntiles, bh, qtile);
+  if constexpr (EXT) bh = kv_major_slice(bh, BH, ext.Hq, nq);
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
