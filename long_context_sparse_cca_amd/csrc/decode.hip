@@ -130,7 +130,7 @@ struct DecodeWs {
 // With APPEND, wave 0 of chunk 0 also writes the new token into its ring slot and,
 // when the token completes a group, pools that group into the core array (the new
 // core token is not visible to this step, so nothing here reads it).
-template <typename T, int D, bool APPEND>
+template <typename T, int D, bool APPEND, bool STREAM>
 __global__ __launch_bounds__(256) void cca_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ core_k,
     T* __restrict__ core_v, T* __restrict__ ring_k, T* __restrict__ ring_v, DecodeWs ws, int64_t max_groups,
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
         kp = rk + (size_t)slot * D;
         vp = rv + (size_t)slot * D;
       }
-      kr[u] = ld16(kp + part * C::EPC);
-      vr[u] = ld16(vp + part * C::EPC);
+      kr[u] = ld16_kv<STREAM>(kp + part * C::EPC);
+      vr[u] = ld16_kv<STREAM>(vp + part * C::EPC);
     }
     float s[C::U];
 #pragma unroll
@@ -363,9 +363,17 @@ hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_ne
   ws.acc = (float*)workspace;
   ws.ml = ws.acc + (size_t)BH * nchunks * D;
   const size_t dyn_lds = APPEND ? (size_t)c->g * sizeof(float) : 0;
-  hipLaunchKernelGGL((cca_decode_kernel<T, D, APPEND>), dim3((unsigned)BH, nchunks), dim3(256), dyn_lds, stream,
-                     (const T*)q, (const T*)k_new, (const T*)v_new, (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k,
-                     (T*)c->ring_v, ws, c->max_groups, R, t, c->g, n_c, raw_lo, n_keys, chunk, nchunks, scale);
+  const bool stream_kv = BH * n_keys * D * (int64_t)sizeof(T) * 2 > kStreamBytes;
+  if (stream_kv)
+    hipLaunchKernelGGL((cca_decode_kernel<T, D, APPEND, true>), dim3((unsigned)BH, nchunks), dim3(256), dyn_lds,
+                       stream, (const T*)q, (const T*)k_new, (const T*)v_new, (T*)c->core_k, (T*)c->core_v,
+                       (T*)c->ring_k, (T*)c->ring_v, ws, c->max_groups, R, t, c->g, n_c, raw_lo, n_keys, chunk,
+                       nchunks, scale);
+  else
+    hipLaunchKernelGGL((cca_decode_kernel<T, D, APPEND, false>), dim3((unsigned)BH, nchunks), dim3(256), dyn_lds,
+                       stream, (const T*)q, (const T*)k_new, (const T*)v_new, (T*)c->core_k, (T*)c->core_v,
+                       (T*)c->ring_k, (T*)c->ring_v, ws, c->max_groups, R, t, c->g, n_c, raw_lo, n_keys, chunk,
+                       nchunks, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(64) void cca_pool_kernel(const T* __restrict__ Q, c
 // bf16, d = 128, g = 16: one wave per group, every load of the group issued up
 // front.  Lane (rq = lane/16, c = lane%16) owns the 16-byte column chunk c
 // (dims 8c..8c+7) of the rows rq, rq+4, rq+8, rq+12.
+template <bool STREAM>
 __global__ __launch_bounds__(256) void cca_pool_bf16_d128_g16_kernel(const bf16_t* __restrict__ Q,
                                                                    const bf16_t* __restrict__ K,
                                                                    const bf16_t* __restrict__ V,
@@ -51,8 +52,8 @@ __global__ __launch_bounds__(256) void cca_pool_bf16_d128_g16_kernel(const bf16_
   uint4 kr[4], vr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    kr[i] = ld16(kg + (size_t)(rq + 4 * i) * D + 8 * c);
-    vr[i] = ld16(vg + (size_t)(rq + 4 * i) * D + 8 * c);
+    kr[i] = ld16_kv<STREAM>(kg + (size_t)(rq + 4 * i) * D + 8 * c);
+    vr[i] = ld16_kv<STREAM>(vg + (size_t)(rq + 4 * i) * D + 8 * c);
   }
   float qf[8];
   Elem<bf16_t>::chunk_to_f32(ld16(qh + 8 * c), qf);
@@ -140,9 +141,15 @@ hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* 
     if (d == 128 && g == 16) {
       const int64_t m = L / 16, n = (int64_t)BHkv * m;
       if (n == 0) return hipSuccess;
-      hipLaunchKernelGGL(cca_pool_bf16_d128_g16_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
-                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, L, m, n, nq,
-                         scale);
+      // K and V are read once here; past the last-level cache they are streamed
+      if (n * 16 * 128 * 2 * 2 > kStreamBytes)
+        hipLaunchKernelGGL(cca_pool_bf16_d128_g16_kernel<true>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
+                           (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, L, m, n,
+                           nq, scale);
+      else
+        hipLaunchKernelGGL(cca_pool_bf16_d128_g16_kernel<false>, dim3((unsigned)((n + 3) / 4)), dim3(256), 0,
+                           stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)kc, (bf16_t*)vc, L,
+                           m, n, nq, scale);
       return hipGetLastError();
     }
     if (d == 128) return launch_pool_t<bf16_t, 128>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);

@@ -37,7 +37,7 @@ struct ServeCfg {
   static constexpr int KPI = NWAVE * KPW * U;         // key rows per workgroup iteration
 };
 
-template <typename T, int D, int RH>
+template <typename T, int D, int RH, bool STREAM>
 __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
     const int32_t* __restrict__ lens, int64_t max_len, const T* __restrict__ q, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ core_k, T* __restrict__ core_v, T* __restrict__ ring_k,
@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
         kp = rk + (size_t)slot * D;
         vp = rv + (size_t)slot * D;
       }
-      kr[u] = ld16(kp + part * C::EPC);
-      vr[u] = ld16(vp + part * C::EPC);
+      kr[u] = ld16_kv<STREAM>(kp + part * C::EPC);
+      vr[u] = ld16_kv<STREAM>(vp + part * C::EPC);
     }
     float s[C::U][RH];
     float vf[C::U][C::EPC];
@@ -259,10 +259,18 @@ hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, 
   float* ws_acc = (float*)workspace;
   float* ws_ml = ws_acc + (size_t)c->B * H_q * nchunks * D;
   const int64_t nblk = (int64_t)c->B * c->H * nhb;
-  hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH>), dim3((unsigned)nblk, nchunks), dim3(256),
-                     (size_t)c->g * sizeof(float), stream, lens, max_len, (const T*)q, (const T*)k, (const T*)v,
-                     (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k, (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb,
-                     c->max_groups, R, c->g, c->k_local, chunk, nchunks, scale);
+  // K/V bytes of the step if every sequence were max_len long (an upper bound)
+  const bool stream_kv = (int64_t)c->B * c->H * n_keys_max * D * (int64_t)sizeof(T) * 2 > kStreamBytes;
+  if (stream_kv)
+    hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH, true>), dim3((unsigned)nblk, nchunks), dim3(256),
+                       (size_t)c->g * sizeof(float), stream, lens, max_len, (const T*)q, (const T*)k, (const T*)v,
+                       (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k, (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb,
+                       c->max_groups, R, c->g, c->k_local, chunk, nchunks, scale);
+  else
+    hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH, false>), dim3((unsigned)nblk, nchunks), dim3(256),
+                       (size_t)c->g * sizeof(float), stream, lens, max_len, (const T*)q, (const T*)k, (const T*)v,
+                       (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k, (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb,
+                       c->max_groups, R, c->g, c->k_local, chunk, nchunks, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
