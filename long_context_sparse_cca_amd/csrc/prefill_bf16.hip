@@ -32,11 +32,11 @@ constexpr int kRowBytes = kD * 2;        // 256
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KB
 constexpr int kBufBytes = 2 * kTileBytes;    // K tile + V tile
 // Lazy rescaling: the reference point of the exponentials moves only when a row's
-// max exceeds it by more than this (log2 units).  The weights then stay <= 2^16,
-// so the fp32 row sums and accumulators cannot overflow unless the sum of |V| over
-// a row exceeds ~2^112; the final division by the row sum makes the result
-// independent of the reference point up to rounding.
-constexpr float kThreshold = 16.0f;
+// weights in a sub-block sum above kSumLimit (then to the row's running max).  The
+// weights thus stay <= 2^16, so the fp32 row sums and accumulators cannot overflow
+// unless the sum of |V| over a row exceeds ~2^112; the final division by the row sum
+// makes the result independent of the reference point up to rounding.
+constexpr float kSumLimit = 65536.0f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -278,12 +278,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
       }
 
-      float bmax = max3f(s[0], s[1], s[2]);
+      // Weights P^T (B operand) against the current reference point m_run.  The maximum of
+      // the sub-block is not computed up front: a lane whose 16 weights sum above 2^16 (some
+      // weight may exceed it, or the reference is still unset) makes the wave move the
+      // reference to the running maximum and recompute the weights (rare after the first
+      // sub-blocks).  Weights therefore stay <= 2^16, as with an explicit threshold check.
+      bf16x2_t pp[2][4];
+      float bsum;
+      auto weights = [&]() {
+        bsum = 0.f;
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) bmax = max3f(bmax, s[r], s[r + 1]);
-      bmax = fmaxf(bmax, s[15]);
-      bmax = xhalf_max(bmax) * sc;
-      if (__builtin_amdgcn_ballot_w64(bmax > m_run + kThreshold) != 0) {
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(s[8 * u + 2 * e], sc, -m_run));
+            const float p1 = fast_exp2(fmaf(s[8 * u + 2 * e + 1], sc, -m_run));
+            pp[u][e] = bf16x2_t{(__bf16)p0, (__bf16)p1};
+            bsum = __builtin_amdgcn_fdot2_f32_bf16(pp[u][e], ones, bsum, false);
+          }
+      };
+      weights();
+      if (__builtin_amdgcn_ballot_w64(bsum > kSumLimit) != 0) {
+        float bmax = max3f(s[0], s[1], s[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) bmax = max3f(bmax, s[r], s[r + 1]);
+        bmax = fmaxf(bmax, s[15]);
+        bmax = xhalf_max(bmax) * sc;
         const float m_new = fmaxf(m_run, bmax);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
@@ -292,20 +312,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        weights();
       }
+      l_run += bsum;
 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        // P^T (B operand): keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u .. 8u+7
-        bf16x2_t pp[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[8 * u + 2 * e], sc, -m_run));
-          const float p1 = fast_exp2(fmaf(s[8 * u + 2 * e + 1], sc, -m_run));
-          pp[e] = bf16x2_t{(__bf16)p0, (__bf16)p1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[e], ones, l_run, false);
-        }
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pp);
+        // P^T: keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u .. 8u+7
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pp[u]);
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
           const v4s_t both[2] = {vop[u][0][dt], vop[u][1][dt]};
