@@ -289,7 +289,7 @@ def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int 
     tf = fl / (bw_ms * 1e-3) / 1e12
     return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL},
             "forward_ms": fw_ms, "backward_ms": bw_ms, "backward_flops": fl,
-            "roofline": {"kernel": "cca_bwd_dq_kernel + cca_bwd_dkdv_kernel (+ prep, pooling backward)",
+            "roofline": {"kernel": "cca_bwd_dq_kernel + cca_bwd_dkdv16_kernel (+ prep, pooling backward)",
                          "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / PEAK_BF16_TFLOPS,
                          "per_unit": "10*d FLOPs per visible (query, key) pair"}}

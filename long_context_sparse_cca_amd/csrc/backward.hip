@@ -19,14 +19,13 @@
 //   1. cca_bwd_prep_kernel     D[t] = dO[t].O[t]; the log-sum-exp in log2 units
 //   2. cca_bwd_dq_kernel       per 256-query tile: recompute scores and p from the
 //                              forward's log-sum-exp, dQ = scale (P o (dP - D)) K
-//   3. cca_bwd_dkdv_kernel     per 256-key tile (core tokens or raw keys): loop over
-//                              the query tiles that see it; dV (one launch) and dK
-//                              (another) of raw keys go to dv, dk, those of core
-//                              tokens to dVc, dKc (workspace)
+//   3. cca_bwd_dkdv16_kernel   per 192-key tile (core tokens or raw keys): loop over
+//                              the query tiles that see it; dV and dK of raw keys go
+//                              to dv, dk, those of core tokens to dVc, dKc (workspace)
 //   4. cca_bwd_pool_kernel     per group: dKc, dVc through the pooling into dk, dv,
 //                              and into dq at the group's last row
-// The score and gradient products run on bf16 MFMA (32x32x16) with float32
-// accumulation; P and dS are rounded to bf16 as MFMA operands, as P is in the
+// The score and gradient products run on bf16 MFMA (32x32x16 for dQ, 16x16x32 for
+// dK and dV) with float32 accumulation; P and dS are rounded to bf16 as MFMA operands, as P is in the
 // forward.  Tiles are staged HBM -> LDS with global_load_lds and read with the
 // same 16-byte XOR swizzle and transpose reads as the forward kernel.
 #include "cca_internal.h"
@@ -318,35 +317,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// 3. dV (MODE 0) and dK (MODE 1): 256 keys per workgroup (8 waves x 32, two waves
-//    per SIMD), loop over the 64-query tiles that see them.  The two gradients
-//    are separate launches so that each fits two waves per SIMD: dV needs the
-//    scores only, dK the scores and dP; both recompute the scores.
+// 3. dK and dV: 192 keys per workgroup (12 waves x 16 keys, three waves per SIMD) on
+//    16x16x32 MFMAs, so that the scores and weights of a (query, key) pair are computed
+//    once for both gradients.  A workgroup loops over the 64-query tiles that see its
+//    keys (core token j: queries from (j+k+1) g; raw key u: queries u .. (u/g+k+1) g - 1),
+//    with Q, dO and the tile's statistics DMA'd into LDS, two tiles in flight.
+//    Lane l of a wave holds key l%16; with G = l/16, its score registers are the queries
+//    16b + 4G + i (b = 0, 1, i = 0..3) of a 32-query sub-block.  Those 8 values are
+//    exactly the B operand of the gradient MFMAs when their reduction index k = 8G + t
+//    stands for query 4G + t (t < 4) or 16 + 4G + t - 4 (t >= 4); the A operands (dO^T,
+//    Q^T) are read from the tiles in that query order with transpose reads.  At three
+//    waves per SIMD (168 registers each) the LDS operand traffic of the 16-key layout
+//    (64 bytes per MFMA cycle and wave) has enough waves to hide behind.
 // ---------------------------------------------------------------------------
-template <int MODE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_bwd_dkdv_kernel(
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+__global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) void cca_bwd_dkdv16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dKV,
-    float* __restrict__ dKVc, int BH, int L, int g, int k_local, float scale, int n_core_wg, int n_wg) {
-  constexpr int kBK = 256;  // keys per workgroup
+    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dK, float* __restrict__ dV,
+    float* __restrict__ dKc, float* __restrict__ dVc, int BH, int L, int g, int k_local, float scale, int n_core_wg) {
+  constexpr int kBK = 192;  // keys per workgroup
   constexpr int kBufBytes = 2 * kTileBytes + 2 * kTileRows * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[kBufBytes];
-  // heaviest work first across all slices: workgroup index wi (core tiles from the
-  // first core token, which the most queries see, then raw tiles) is the slow index
+  // heaviest work first across all slices (workgroup index wi is the slow index)
   const int wi = blockIdx.x / BH;
   const int bh = blockIdx.x - wi * BH;
   const bool core = wi < n_core_wg;
   const int m = L / g;
   const int key0 = core ? wi * kBK : (wi - n_core_wg) * kBK;
-  const int key_end = core ? m : L;        // keys of this kind
+  const int key_end = core ? m : L;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int c0 = key0 + wave * 32;         // this wave's first key
+  const int n16 = lane & 15, G = lane >> 4;
+  const int c0 = key0 + wave * 16;         // this wave's first key
   const int c_last = min(key0 + kBK, key_end) - 1;
 
   // Visibility in query positions, so that the loops need no division by g:
@@ -354,7 +364,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   //   raw key u by the queries u <= t <= (u / g + k + 1) g - 1.
   auto core_first = [&](int j) { return (int)min((int64_t)L, ((int64_t)j + k_local + 1) * g); };
   auto raw_last = [&](int u) { return (int)min((int64_t)L - 1, ((int64_t)(u / g) + k_local + 1) * g - 1); };
-  // query range [t_lo, t_hi] that can see any key of the workgroup
   int t_lo, t_hi;
   if (core) {
     t_lo = core_first(key0);
@@ -371,36 +380,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* Vs = core ? Vc + (size_t)bh * m * kD : V + slice;
   const bf16_t* Qs = Q + slice;
   const bf16_t* dOs = dO + slice;
-  const int key_lane = min(c0 + l32, key_end - 1);
-  uint4 kop[kD / 16], vop[MODE == 1 ? kD / 16 : 1];
+  // B operands of the score and dP products: dims 32kk + 8G .. +7 of this lane's key
+  const int key_lane = min(c0 + n16, key_end - 1);
+  uint4 kop[kD / 32], vop[kD / 32];
 #pragma unroll
-  for (int s = 0; s < kD / 16; ++s) {
-    kop[s] = ld16(Ks + (size_t)key_lane * kD + s * 16 + hf * 8);
-    if constexpr (MODE == 1) vop[s] = ld16(Vs + (size_t)key_lane * kD + s * 16 + hf * 8);
+  for (int kk = 0; kk < kD / 32; ++kk) {
+    kop[kk] = ld16(Ks + (size_t)key_lane * kD + kk * 32 + G * 8);
+    vop[kk] = ld16(Vs + (size_t)key_lane * kD + kk * 32 + G * 8);
   }
   const float sc = scale * kLog2e;
-  TileOffsets off;
-  off.init(lane);
-  f32x16_t acc[kD / 32];
+  // A-operand read offsets inside a sub-block (bytes): rows operand, row n16 (+16b),
+  // logical chunk 4kk + G; transpose operand, rows 4G + n16/4 (+16 for the second
+  // half), dims 16 blk + 4 (n16 % 4) .. +3
+  int roff[kD / 32];
 #pragma unroll
-  for (int dt = 0; dt < kD / 32; ++dt)
+  for (int kk = 0; kk < kD / 32; ++kk) roff[kk] = n16 * kRowBytes + (((4 * kk + G) ^ swz(n16)) * 16);
+  int toff[2][kD / 16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * h + 4 * G + (n16 >> 2);
+#pragma unroll
+    for (int blk = 0; blk < kD / 16; ++blk) {
+      const int chunk = 2 * blk + ((n16 & 3) >> 1);
+      toff[h][blk] = row * kRowBytes + ((chunk ^ swz(row)) * 16) + (n16 & 1) * 8;
+    }
+  }
+  f32x4_t acc_v[kD / 16], acc_k[kD / 16];
+#pragma unroll
+  for (int blk = 0; blk < kD / 16; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc_v[blk][i] = acc_k[blk][i] = 0.f;
 
   const bool wave_live = c0 < key_end;
-  const int c_hi = min(c0 + 31, key_end - 1);
-
-  // per wave: a sub-block of queries [t0, t1] sees none of the keys c0..c_hi when t1 < w_none_below
-  // or t0 > w_none_above, and all of them when t0 >= w_all_from and t1 <= w_all_to
+  const int c_hi = min(c0 + 15, key_end - 1);
   const int w_none_below = core ? core_first(c0) : c0;
   const int w_none_above = core ? L - 1 : raw_last(c_hi);
   const int w_all_from = core ? core_first(c_hi) : c_hi;
   const int w_all_to = core ? L - 1 : raw_last(c0);
-  // per lane: this key is seen by the queries q_lo .. q_lo + q_span (none for a lane past the last key)
   int q_lo;
   unsigned q_span;
   {
-    const int key = c0 + l32;
+    const int key = c0 + n16;
     const int a = core ? core_first(key) : key;
     const int b = core ? L - 1 : raw_last(key);
     const bool ok = key <= c_hi && a <= b;
@@ -408,20 +428,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     q_span = ok ? (unsigned)(b - a) : 0u;
   }
 
-  // query tiles from the last one down: the workgroups of a slice that run together
-  // then stream the same query tiles at about the same time (shared in L2)
+  // query tiles from the last one down (the workgroups of a slice that run together
+  // then stream the same tiles)
   auto tile_base = [&](int qt) { return tq0 + (n_qt - 1 - qt) * kTileRows; };
   auto issue = [&](int qt, uint8_t* buf) {
     const int base = tile_base(qt);
-    fill_tile<8>(Qs, base, L - 1, buf, wave, lane);
-    fill_tile<8>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
-    // log-sum-exp (log2 units) and D of the tile's 64 queries: one 4-byte DMA per lane
-    if (wave < 2) {
+    if (wave < 8) {
+      fill_tile<8>(Qs, base, L - 1, buf, wave, lane);
+      fill_tile<8>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
+    } else if (wave < 10) {
       const int t = min(base + lane, L - 1);
-      const float* src = (wave == 0 ? lse : Dv) + (size_t)bh * L + t;
+      const float* src = (wave == 8 ? lse : Dv) + (size_t)bh * L + t;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(buf + 2 * kTileBytes +
-                                                                                  wave * kTileRows * 4),
+                                                                                  (wave - 8) * kTileRows * 4),
                                        4, 0, 0);
     }
   };
@@ -441,93 +461,113 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (cls == 0) continue;
       const uint8_t* qsb = buf + sb * 32 * kRowBytes;
       const uint8_t* dsb = buf + kTileBytes + sb * 32 * kRowBytes;
-      uint4 xa[kD / 16], ya[MODE == 1 ? kD / 16 : 1];
-      rows_read(qsb, off, xa);
-      if constexpr (MODE == 1) rows_read(dsb, off, ya);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);
-      f32x16_t s = rows_mfma(xa, kop);           // S: queries (rows) x keys (cols)
-      f32x16_t dp;
-      if constexpr (MODE == 1) dp = rows_mfma(ya, vop);   // dP
-      TrHalf th0, th1;
-      tr_read(MODE == 0 ? dsb : qsb, off, 0, th0);
-      if constexpr (MODE == 0) tr_read(dsb, off, 1, th1);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-      const int tq = t0 + 4 * hf - q_lo;   // query t0 + 8i + 4hf + j is visible iff (tq + 8i + j) <= q_span
+      // scores S and dP for the two 16-query blocks (queries 16b + 4G + i in lane registers)
+      f32x4_t s[2], dp[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 lv = *reinterpret_cast<const float4*>(lse_t + sb * 32 + 8 * i + 4 * hf);
-        const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
-        float dr[4];
-        if constexpr (MODE == 1) {
-          const float4 dv = *reinterpret_cast<const float4*>(d_t + sb * 32 + 8 * i + 4 * hf);
-          dr[0] = dv.x; dr[1] = dv.y; dr[2] = dv.z; dr[3] = dv.w;
+      for (int b = 0; b < 2; ++b) {
+        uint4 xa[kD / 32], ya[kD / 32];
+#pragma unroll
+        for (int kk = 0; kk < kD / 32; ++kk) {
+          xa[kk] = *reinterpret_cast<const uint4*>(qsb + 16 * b * kRowBytes + roff[kk]);
+          ya[kk] = *reinterpret_cast<const uint4*>(dsb + 16 * b * kRowBytes + roff[kk]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * i + j;
-          float p = fast_exp2(fmaf(s[r], sc, -lr[j]));
-          if (cls == 2) {
-            const bool vis = (unsigned)(tq + 8 * i + j) <= q_span;
-            p = vis ? p : 0.f;
-          }
-          if constexpr (MODE == 0) s[r] = p;                       // P
-          else dp[r] = p * (dp[r] - dr[j]);                        // dS
+        for (int i = 0; i < 4; ++i) s[b][i] = dp[b][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < kD / 32; ++kk) s[b] = mfma16(xa[kk], kop[kk], s[b]);
+#pragma unroll
+        for (int kk = 0; kk < kD / 32; ++kk) dp[b] = mfma16(ya[kk], vop[kk], dp[b]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      // weights and dS; per-query statistics of the lane's 8 queries
+      float pw[8], dsw[8];
+      const int tq = t0 + 4 * G - q_lo;   // query t0 + 16b + 4G + i visible iff (tq + 16b + i) <= q_span
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float4 lv = *reinterpret_cast<const float4*>(lse_t + sb * 32 + 16 * b + 4 * G);
+        const float4 dv = *reinterpret_cast<const float4*>(d_t + sb * 32 + 16 * b + 4 * G);
+        const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
+        const float dr[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = fast_exp2(fmaf(s[b][i], sc, -lr[i]));
+          if (cls == 2) p = ((unsigned)(tq + 16 * b + i) <= q_span) ? p : 0.f;
+          pw[4 * b + i] = p;
+          dsw[4 * b + i] = p * (dp[b][i] - dr[i]);
         }
       }
-      if constexpr (MODE == 0) {                 // dV^T += dO^T P
-        tr_mfma(th0, s, 0, acc);
-        tr_mfma(th1, s, 1, acc);
-      } else {                                   // dK^T += Q^T dS
-        tr_mfma(th0, dp, 0, acc);
-        tr_read(qsb, off, 1, th1);
-        tr_mfma(th1, dp, 1, acc);
+      bf16x2_t pp[4], qq[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pp[e] = bf16x2_t{(__bf16)pw[2 * e], (__bf16)pw[2 * e + 1]};
+        qq[e] = bf16x2_t{(__bf16)dsw[2 * e], (__bf16)dsw[2 * e + 1]};
+      }
+      const uint4 pb = __builtin_bit_cast(uint4, pp);
+      const uint4 db = __builtin_bit_cast(uint4, qq);
+      // dV^T += dO^T P and dK^T += Q^T dS, 16 dims per MFMA
+#pragma unroll
+      for (int blk = 0; blk < kD / 16; ++blk) {
+        const v4s_t o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(dsb + toff[0][blk]));
+        const v4s_t o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(dsb + toff[1][blk]));
+        const v4s_t q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(qsb + toff[0][blk]));
+        const v4s_t q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(qsb + toff[1][blk]));
+        const v4s_t ob[2] = {o0, o1};
+        const v4s_t qb[2] = {q0, q1};
+        acc_v[blk] = mfma16(__builtin_bit_cast(uint4, ob), pb, acc_v[blk]);
+        acc_k[blk] = mfma16(__builtin_bit_cast(uint4, qb), db, acc_k[blk]);
       }
     }
   };
 
-  // three buffers, two query tiles in flight ahead of the one being used (the query
-  // stream of a core tile is long and comes from beyond L2)
-  // vmcnt(4): waits until at most 4 of this wave's loads are outstanding.  A wave issues 4
-  // tile loads per tile (waves 0-1 one more, for the statistics), in order, and loads
-  // complete in order: the tile before the newest one has then landed.
-  constexpr int kW2 = 0x0F70 | 4;
+  // the tile before the newest one has landed: waves 0-7 issue 4 loads per tile, waves 8-9 one
+  auto wait_older = [&]() {
+    if (wave < 8) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else __builtin_amdgcn_s_waitcnt(0x0F71);
+  };
   if (n_qt > 0) issue(0, lds0);
   if (n_qt > 1) issue(1, lds1);
-  if (n_qt > 1) __builtin_amdgcn_s_waitcnt(kW2);
+  if (n_qt > 1) wait_older();
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int qt = 0; qt < n_qt; qt += 3) {
     if (qt + 2 < n_qt) issue(qt + 2, lds2);
     if (wave_live) compute(lds0, qt);
-    if (qt + 2 < n_qt) __builtin_amdgcn_s_waitcnt(kW2);
+    if (qt + 2 < n_qt) wait_older();
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (qt + 1 >= n_qt) break;
     if (qt + 3 < n_qt) issue(qt + 3, lds0);
     if (wave_live) compute(lds1, qt + 1);
-    if (qt + 3 < n_qt) __builtin_amdgcn_s_waitcnt(kW2);
+    if (qt + 3 < n_qt) wait_older();
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (qt + 2 >= n_qt) break;
     if (qt + 4 < n_qt) issue(qt + 4, lds1);
     if (wave_live) compute(lds2, qt + 2);
-    if (qt + 4 < n_qt) __builtin_amdgcn_s_waitcnt(kW2);
+    if (qt + 4 < n_qt) wait_older();
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
   if (!wave_live) return;
-  const int key = c0 + l32;
+  const int key = c0 + n16;
   if (key >= key_end) return;
-  float* o = core ? dKVc + ((size_t)bh * m + key) * kD : dKV + slice + (size_t)key * kD;
-  const float f = (MODE == 1) ? scale : 1.0f;
+  float* ov = core ? dVc + ((size_t)bh * m + key) * kD : dV + slice + (size_t)key * kD;
+  float* ok = core ? dKc + ((size_t)bh * m + key) * kD : dK + slice + (size_t)key * kD;
+  // lane holds dims 16 blk + 4G + i of its key
 #pragma unroll
-  for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) =
-          make_float4(acc[dt][4 * i] * f, acc[dt][4 * i + 1] * f, acc[dt][4 * i + 2] * f, acc[dt][4 * i + 3] * f);
+  for (int blk = 0; blk < kD / 16; ++blk) {
+    *reinterpret_cast<float4*>(ov + 16 * blk + 4 * G) =
+        make_float4(acc_v[blk][0], acc_v[blk][1], acc_v[blk][2], acc_v[blk][3]);
+    *reinterpret_cast<float4*>(ok + 16 * blk + 4 * G) =
+        make_float4(acc_k[blk][0] * scale, acc_k[blk][1] * scale, acc_k[blk][2] * scale, acc_k[blk][3] * scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -665,18 +705,12 @@ hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v
                      (const float*)lse2, (const float*)Dv, dq, BH, (int)L, g, k_local, scale, ntiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_core_wg = (int)((m + 255) / 256);
-  const int n_wg = n_core_wg + (int)((L + 255) / 256);
-  hipLaunchKernelGGL(cca_bwd_dkdv_kernel<0>, dim3((unsigned)((int64_t)BH * n_wg)), dim3(512), 0, stream,
+  const int n_core_wg = (int)((m + 191) / 192);
+  const int n_wg = n_core_wg + (int)((L + 191) / 192);
+  hipLaunchKernelGGL(cca_bwd_dkdv16_kernel, dim3((unsigned)((int64_t)BH * n_wg)), dim3(768), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
-                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dv, dVc, BH, (int)L, g, k_local, scale, n_core_wg,
-                     n_wg);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(cca_bwd_dkdv_kernel<1>, dim3((unsigned)((int64_t)BH * n_wg)), dim3(512), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
-                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dk, dKc, BH, (int)L, g, k_local, scale, n_core_wg,
-                     n_wg);
+                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dk, dv, dKc, dVc, BH, (int)L, g,
+                     k_local, scale, n_core_wg);
   e = hipGetLastError();
   if (e != hipSuccess || m == 0) return e;
   hipLaunchKernelGGL(cca_bwd_pool_kernel, dim3((unsigned)((int64_t)BH * m)), dim3(64), (size_t)2 * g * sizeof(float),
