@@ -28,6 +28,14 @@ then the core part of dkey/dval (dKc, dVc) flows through the pooling:
 When the core tokens are stored rounded (`core_dtype`), the forward uses the
 rounded values and the derivative treats the rounding as the identity.
 
+Grouped-query attention (cca_backward_gqa; the forward of oracle/cca_serving.py,
+readings R14/R15: r = H / H_kv query heads share one key/value head, whose core
+tokens are pooled once with the mean over the r heads of the group's last-token
+query): the attention part runs per query head against its key/value head and
+the raw and core gradients of the r heads add up; the pooling backward runs once
+per key/value head with q_hat = that mean, and its gradient dq_hat reaches each
+of the r heads' last-row queries with weight 1/r.
+
 Everything is float64; loops are per query and per group so each step can be
 read against the formulas above.  Pinned by finite differences and, in the
 cases where CCA is plain causal attention, by torch's autograd of its
@@ -41,7 +49,7 @@ import numpy as np
 from . import cca_oracle as _o
 
 __all__ = ["softmax_backward", "pool_backward_group", "cca_backward_slice", "cca_backward",
-           "cca_forward_lse_slice"]
+           "cca_forward_lse_slice", "cca_backward_gqa"]
 
 
 def softmax_backward(p, dp):
@@ -139,3 +147,77 @@ def cca_backward(Q, K, V, dO, g: int, k: int, scale: float, core_dtype=None):
         for o, x in zip(outs, r):
             o[idx] = x
     return tuple(outs)
+
+
+def _attention_backward(Qh, K, V, Kc, Vc, dOh, g: int, k: int, scale: float):
+    """Attention part of the backward for one query head against given raw and core K/V:
+    (dQ [L,d], dK_raw [L,d], dV_raw [L,d], dKc [m,d], dVc [m,d])."""
+    L, d = Qh.shape
+    m = Kc.shape[0]
+    dQ = np.zeros((L, d))
+    dK = np.zeros((L, d))
+    dV = np.zeros((L, d))
+    dKc = np.zeros((m, d))
+    dVc = np.zeros((m, d))
+    for t in range(L):
+        n_c = _o.visible_core_count(t, g, k)
+        lo, hi = _o.raw_window(t, g, k)
+        keys = np.concatenate([Kc[:n_c], K[lo:hi + 1]])
+        vals = np.concatenate([Vc[:n_c], V[lo:hi + 1]])
+        p = _o.softmax(scale * (keys @ Qh[t]))
+        ds = softmax_backward(p, vals @ dOh[t])
+        dQ[t] = scale * (ds @ keys)
+        dkey = scale * np.outer(ds, Qh[t])
+        dval = np.outer(p, dOh[t])
+        dKc[:n_c] += dkey[:n_c]
+        dVc[:n_c] += dval[:n_c]
+        dK[lo:hi + 1] += dkey[n_c:]
+        dV[lo:hi + 1] += dval[n_c:]
+    return dQ, dK, dV, dKc, dVc
+
+
+def cca_backward_gqa(Q, K, V, dO, g: int, k: int, scale: float, core_dtype=None):
+    """(dQ [B,H,L,d], dK [B,H_kv,L,d], dV [B,H_kv,L,d]) of the grouped-query CCA prefill.
+
+    Q, dO: [B, H, L, d]; K, V: [B, H_kv, L, d], H a multiple of H_kv.  Query head h
+    reads key/value head h // r (R15); each key/value head's core tokens are pooled
+    once with the mean last-token query of its r heads (R14).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, H, L, d = Q.shape
+    Hkv = K.shape[1]
+    if H % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    r = H // Hkv
+    m = _o.n_core_groups(L, g)
+    dQ = np.zeros(Q.shape)
+    dK = np.zeros(K.shape)
+    dV = np.zeros(V.shape)
+    for b in range(B):
+        for hk in range(Hkv):
+            heads = range(hk * r, (hk + 1) * r)
+            q_mean = Q[b, hk * r:(hk + 1) * r].sum(axis=0) / r
+            Kc, Vc, A = _o.pool(q_mean, K[b, hk], V[b, hk], g, scale, core_dtype)
+            dKc = np.zeros((m, d))
+            dVc = np.zeros((m, d))
+            for h in heads:
+                gq, gk, gv, gkc, gvc = _attention_backward(Q[b, h], K[b, hk], V[b, hk], Kc, Vc, dO[b, h], g, k,
+                                                           scale)
+                dQ[b, h] += gq
+                dK[b, hk] += gk
+                dV[b, hk] += gv
+                dKc += gkc
+                dVc += gvc
+            for j in range(m):
+                rows = slice(j * g, (j + 1) * g)
+                row = _o.group_query_row(j, g)
+                dKg, dVg, dqh = pool_backward_group(A[j], K[b, hk, rows], V[b, hk, rows], q_mean[row], dKc[j],
+                                                    dVc[j], scale)
+                dK[b, hk, rows] += dKg
+                dV[b, hk, rows] += dVg
+                for h in heads:
+                    dQ[b, h, row] += dqh / r
+    return dQ, dK, dV

@@ -84,5 +84,35 @@ def pin_lse_matches_library_logsumexp(b):
     return e < 1e-12, f"max err {e:.3e}"
 
 
+def pin_gqa_finite_differences(b):
+    """Grouped-query gradients (r = 2 and r = 3 query heads per key/value head) against central
+    differences of the grouped-query forward of oracle/cca_serving.py."""
+    import oracle.cca_serving as serving
+    worst = 0.0
+    for (H, Hkv, L, g, k, d, seed) in [(4, 2, 9, 3, 1, 2, 11), (3, 1, 8, 2, 1, 2, 12)]:
+        Q = np_inputs(1, H, L, d, "f32", seed)[0].astype(np.float64)
+        K, V = (x[:, :Hkv].astype(np.float64) for x in np_inputs(1, H, L, d, "f32", seed + 1)[1:])
+        W = np.random.default_rng(seed + 70).standard_normal((1, H, L, d))
+        sc = 0.6
+        dQ, dK, dV = b.cca_backward_gqa(Q, K, V, W, g, k, sc)
+
+        def loss():
+            return float(np.sum(serving.cca_gqa(Q, K, V, g, k, sc) * W))
+
+        h = 1e-6
+        for X, dX in ((Q, dQ), (K, dK), (V, dV)):
+            num = np.zeros_like(X)
+            for idx in np.ndindex(*X.shape):
+                x0 = X[idx]
+                X[idx] = x0 + h
+                fp = loss()
+                X[idx] = x0 - h
+                fm = loss()
+                X[idx] = x0
+                num[idx] = (fp - fm) / (2 * h)
+            worst = max(worst, _err(num, dX))
+    return worst < 1e-7, f"max err {worst:.3e}"
+
+
 ALL_BACKWARD_PINS = [pin_finite_differences, pin_causal_special_cases_match_autograd,
-                     pin_lse_matches_library_logsumexp]
+                     pin_lse_matches_library_logsumexp, pin_gqa_finite_differences]

@@ -152,7 +152,48 @@ def _pool_backward_no_query_grad(a, Kg, Vg, q_hat, dKc_j, dVc_j, scale):
     return dKg, dVg, np.zeros_like(q_hat, dtype=np.float64)
 
 
+_orig_attention_backward = bwd._attention_backward
+
+
+def _attention_only_dq(Q, K, V, dO, g, k, scale, core_dtype=None):
+    """dQ of the attention part alone (no pooling backward), per query head."""
+    import oracle.cca_serving as serving
+    Q, K, V, dO = (np.asarray(x, np.float64) for x in (Q, K, V, dO))
+    B, H, L, d = Q.shape
+    r = H // K.shape[1]
+    out = np.zeros_like(Q)
+    for b in range(B):
+        for h in range(H):
+            hk = h // r
+            Kc, Vc, _ = serving.pool_gqa(Q[b, hk * r:(hk + 1) * r], K[b, hk], V[b, hk], g, scale, core_dtype)
+            out[b, h] = _orig_attention_backward(Q[b, h], K[b, hk], V[b, hk], Kc, Vc, dO[b, h], g, k, scale)[0]
+    return out
+
+
+def _gqa_dq_hat_to_first_head(Q, K, V, dO, g, k, scale, core_dtype=None):
+    """Grouped-query backward whose pooling gradient dq_hat reaches only the first query head of a group."""
+    dQ, dK, dV = _orig_gqa_backward(Q, K, V, dO, g, k, scale, core_dtype)
+    H = dQ.shape[1]
+    r = H // np.asarray(K).shape[1]
+    dq_pool = dQ - _attention_only_dq(Q, K, V, dO, g, k, scale, core_dtype)
+    for h in range(H):
+        if h % r:
+            dQ[:, h] -= dq_pool[:, h]
+            dQ[:, h - h % r] += dq_pool[:, h]
+    return dQ, dK, dV
+
+
+def _core_key_grads_doubled(Qh, K, V, Kc, Vc, dOh, g, k, scale):
+    """Attention backward (grouped-query path) with the core-key gradients doubled."""
+    dQ, dK, dV, dKc, dVc = _orig_attention_backward(Qh, K, V, Kc, Vc, dOh, g, k, scale)
+    return dQ, dK, dV, dKc * 2.0, dVc
+
+
+_orig_gqa_backward = bwd.cca_backward_gqa
+
 BACKWARD_MUTANTS = {
+    "grouped-query dq_hat to the first head only": ("cca_backward_gqa", _gqa_dq_hat_to_first_head),
+    "core-key gradients doubled (grouped-query path)": ("_attention_backward", _core_key_grads_doubled),
     "softmax backward with the wrong sign": ("softmax_backward", _softmax_backward_sign),
     "pooling weights treated as constants": ("pool_backward_group", _pool_backward_no_weight_grad),
     "no gradient into the scoring query": ("pool_backward_group", _pool_backward_no_query_grad),
