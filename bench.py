@@ -259,13 +259,16 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
                                             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
 
-def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int = 3):
+def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int = 3, H_kv: int = H):
     """Forward with log-sum-exp (cca_prefill_lse) and backward (cca_backward) of one layer,
-    B=1, H=32, d=128, g=16, k=64, bf16, outside the timed steps."""
+    B=1, H=32 (H_kv key/value heads), d=128, g=16, k=64, bf16, outside the timed steps."""
     import torch
 
     from long_context_sparse_cca_amd.synth import torch_inputs
     q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, dev, seed=seed + 7, heavy_frac=HEAVY)
+    if H_kv != H:
+        k = k[:, :H_kv].contiguous()
+        v = v[:, :H_kv].contiguous()
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed + 8)
     dout = torch.randn((1, H, L, D), generator=gen, device=dev).to(torch.bfloat16)
@@ -287,7 +290,7 @@ def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int 
     fw_ms, bw_ms = sum(fw) / reps, sum(bw) / reps
     fl = accounting.backward_flops(1, H, L, D, G, KL)
     tf = fl / (bw_ms * 1e-3) / 1e12
-    return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL},
+    return {"config": {"B": 1, "H": H, "H_kv": H_kv, "d": D, "L": L, "g": G, "k_local": KL},
             "forward_ms": fw_ms, "backward_ms": bw_ms, "backward_flops": fl,
             "roofline": {"kernel": "cca_bwd_dq_kernel + cca_bwd_dkdv16_kernel (+ prep, pooling backward)",
                          "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -356,8 +359,8 @@ def main():
                           "gbs": 4 * n / dt / 1e9}), flush=True)
         return
     if args.phase == "training":
-        print(json.dumps({"phase": "training", "training": training_step(binding, accounting, dev, args.seed)}),
-              flush=True)
+        print(json.dumps({"phase": "training", "training": training_step(binding, accounting, dev, args.seed),
+                          "training_gqa": training_step(binding, accounting, dev, args.seed, H_kv=8)}), flush=True)
         return
     if args.phase == "lca":
         print(json.dumps({"phase": "lca", "lca_variant": lca_variant(binding, accounting, dev, args.seed)}),
@@ -517,6 +520,8 @@ def main():
         res["serving_decode"] = serving_decode(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_training and args.phase == "all":
         res["training"] = training_step(binding, accounting, dev, args.seed)
+        torch.cuda.empty_cache()
+        res["training_gqa"] = training_step(binding, accounting, dev, args.seed, H_kv=8)
         torch.cuda.empty_cache()
     if do_prefill and not args.no_lca and args.phase == "all":
         res["lca_variant"] = lca_variant(binding, accounting, dev, args.seed)

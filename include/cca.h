@@ -189,6 +189,24 @@ int cca_backward(const void* q, const void* k, const void* v, const void* kc, co
                  int dt, hipStream_t stream);
 
 /*
+ * Training with grouped-query attention (readings as for cca_prefill_gqa: the r = H/H_kv
+ * query heads h*r .. h*r+r-1 read key/value head h, whose core tokens are pooled once with
+ * the mean over those heads of the group's last-token query).  The gradient of that mean
+ * reaches each of the r queries with weight 1/r; the key/value gradients sum over the r
+ * heads.  k, v, kc, vc, dk, dv have H_kv heads ([B, H_kv, ...]); q, out, lse, dout, dq
+ * have H.  cca_prefill_lse / cca_backward are these with H_kv = H.  Errors as for
+ * cca_prefill_gqa; bf16 and d = 128 only (else CCA_ERR_UNSUPPORTED).
+ */
+int cca_prefill_lse_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse,
+                        int B, int H, int H_kv, int64_t L, int d, int g, int k_local, float scale,
+                        int dt, int out_dt, hipStream_t stream);
+size_t cca_backward_gqa_workspace_bytes(int B, int H, int H_kv, int64_t L, int d, int g);
+int cca_backward_gqa(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int H_kv, int64_t L, int d, int g, int k_local,
+                     float scale, int dt, hipStream_t stream);
+
+/*
  * Compressed KV cache for decode ([CCA] Triton section: the fused operator
  * serves decode with a KV cache holding core tokens plus local raw tokens;
  * compute/memory efficiency section, Fig. 3).  Plain-old-data descriptor;

@@ -80,6 +80,16 @@ EXPORTS = {
     "cca_backward": (ctypes.c_int, [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                                              ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                              ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "cca_prefill_lse_gqa": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                                  ctypes.c_int, ctypes.c_void_p]),
+    "cca_backward_gqa_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                                           ctypes.c_int, ctypes.c_int]),
+    "cca_backward_gqa": (ctypes.c_int, [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                                                 ctypes.c_int, ctypes.c_void_p]),
     "cca_pool_kv_lca": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                               ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
@@ -291,48 +301,65 @@ def prefill_lca(q, k, v, g: int, k_local: int, d_rope: int, scale: float | None 
 
 
 def prefill_lse(q, k, v, g: int, k_local: int, scale: float | None = None, out_dtype=None):
-    """Forward for training: (out [B,H,L,d], lse [B,H,L] float32, kc, vc): cca_prefill_lse."""
+    """Forward for training: (out [B,H,L,d], lse [B,H,L] float32, kc, vc [B,H_kv,L//g,d]).
+
+    q [B,H,L,d], k, v [B,H_kv,L,d]: cca_prefill_lse, or cca_prefill_lse_gqa when H_kv < H.
+    """
     lib = load_library()
     B, H, Hkv, L, d = _heads(q, k, v)
-    if Hkv != H:
-        raise CCAError("the training path takes one query head per key/value head")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     m = L // g if g >= 1 else 0
-    kc = _core_buffer(B, H, m, d, q)
-    vc = _core_buffer(B, H, m, d, q)
+    kc = _core_buffer(B, Hkv, m, d, q)
+    vc = _core_buffer(B, Hkv, m, d, q)
     out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, H, max(L, 1)), dtype=torch.float32, device=q.device)[:, :, :L]
-    _check(lib.cca_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), B, H, L, d, g,
-                               k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()),
-           "cca_prefill_lse")
+    if Hkv == H:
+        st = lib.cca_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), B, H, L, d, g,
+                                 k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream())
+    else:
+        st = lib.cca_prefill_lse_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), B, H, Hkv,
+                                     L, d, g, k_local, scale, _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                     _stream())
+    _check(st, "cca_prefill_lse")
     return out, lse, kc, vc
 
 
 def backward(q, k, v, kc, vc, out, lse, dout, g: int, k_local: int, scale: float | None = None):
-    """Gradients (dq, dk, dv), float32 [B,H,L,d], of sum(out * dout): cca_backward."""
+    """Gradients of sum(out * dout): dq float32 [B,H,L,d], dk, dv float32 [B,H_kv,L,d].
+
+    cca_backward, or cca_backward_gqa when k, v have fewer heads than q.
+    """
     lib = load_library()
     B, H, Hkv, L, d = _heads(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     m = L // g if g >= 1 else 0
-    _need(kc, (B, H, m, d), q.dtype, "kc")
-    _need(vc, (B, H, m, d), q.dtype, "vc")
+    _need(kc, (B, Hkv, m, d), q.dtype, "kc")
+    _need(vc, (B, Hkv, m, d), q.dtype, "vc")
     _need(out, (B, H, L, d), q.dtype, "out")
     _need(dout, (B, H, L, d), q.dtype, "dout")
     if tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32 or not lse.is_cuda:
         raise CCAError("lse must be a float32 device tensor [B, H, L]")
-    dq, dk, dv = (torch.empty((B, H, L, d), dtype=torch.float32, device=q.device) for _ in range(3))
-    ws_bytes = lib.cca_backward_workspace_bytes(B, H, L, d, g)
+    dq = torch.empty((B, H, L, d), dtype=torch.float32, device=q.device)
+    dk, dv = (torch.empty((B, Hkv, L, d), dtype=torch.float32, device=q.device) for _ in range(2))
+    ws_bytes = lib.cca_backward_gqa_workspace_bytes(B, H, Hkv, L, d, g)
     ws = torch.empty((max(ws_bytes, 16) + 15) // 16 * 4, dtype=torch.float32, device=q.device)
-    _check(lib.cca_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), _ptr(dout),
-                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * 4, B, H, L, d, g, k_local, scale,
-                            _dtype_code(q.dtype), _stream()), "cca_backward")
+    if Hkv == H:
+        st = lib.cca_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), _ptr(dout),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * 4, B, H, L, d, g, k_local, scale,
+                              _dtype_code(q.dtype), _stream())
+    else:
+        st = lib.cca_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(lse), _ptr(dout),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * 4, B, H, Hkv, L, d, g,
+                                  k_local, scale, _dtype_code(q.dtype), _stream())
+    _check(st, "cca_backward")
     return dq, dk, dv
 
 
 class CCAAttention(torch.autograd.Function):
-    """CCA prefill attention as an autograd function (bf16, d = 128): forward cca_prefill_lse,
-    backward cca_backward.  apply(q, k, v, g, k_local, scale=None) -> out [B,H,L,d]."""
+    """CCA prefill attention as an autograd function (bf16, d = 128; k, v may have fewer heads
+    than q): forward cca_prefill_lse, backward cca_backward.
+    apply(q, k, v, g, k_local, scale=None) -> out [B,H,L,d]."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, k_local, scale=None):

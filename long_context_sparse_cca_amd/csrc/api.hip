@@ -118,30 +118,40 @@ int cca_attention(const void* q, const void* k, const void* v, const void* kc, c
   return cca_attention_gqa(q, k, v, kc, vc, out, B, H, H, L, d, g, k_local, scale, dt, out_dt, stream);
 }
 
-int cca_prefill_lse(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse, int B,
-                    int H, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
-  int s = check_prefill(q, k, v, kc, vc, out, B, H, H, L, d, g, k_local, scale, dt, out_dt);
+int cca_prefill_lse_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse,
+                        int B, int H, int H_kv, int64_t L, int d, int g, int k_local, float scale, int dt,
+                        int out_dt, hipStream_t stream) {
+  int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, out_dt);
   if (s != CCA_OK) return s;
   if (dt != CCA_BF16 || d != 128) return CCA_ERR_UNSUPPORTED;
   if (L > 0 && (lse == nullptr || ((uintptr_t)lse & 3u) != 0)) return CCA_ERR_INVALID;
   if (L == 0) return CCA_OK;
-  const int BH = B * H;
-  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, BH, L, g, 1, scale, stream);
+  const int nq = H / H_kv;
+  hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, B * H_kv, L, g, nq, scale, stream);
   if (e != hipSuccess) return CCA_ERR_HIP;
-  return hip_status(cca::launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_dt == CCA_F32, BH, 1, L, g, k_local,
+  return hip_status(cca::launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, nq, L, g, k_local,
                                                   scale, stream, lse));
 }
 
-size_t cca_backward_workspace_bytes(int B, int H, int64_t L, int d, int g) {
-  if (B < 1 || H < 1 || L < 0 || g < 1 || (d != 64 && d != 128)) return 0;
-  return cca::backward_workspace_bytes(B, H, L, d, g);
+int cca_prefill_lse(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse, int B,
+                    int H, int64_t L, int d, int g, int k_local, float scale, int dt, int out_dt, hipStream_t stream) {
+  return cca_prefill_lse_gqa(q, k, v, kc, vc, out, lse, B, H, H, L, d, g, k_local, scale, dt, out_dt, stream);
 }
 
-int cca_backward(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out,
-                 const float* lse, const void* dout, float* dq, float* dk, float* dv, void* workspace,
-                 size_t workspace_bytes, int B, int H, int64_t L, int d, int g, int k_local, float scale, int dt,
-                 hipStream_t stream) {
-  int s = check_prefill(q, k, v, kc, vc, out, B, H, H, L, d, g, k_local, scale, dt, dt);
+size_t cca_backward_gqa_workspace_bytes(int B, int H, int H_kv, int64_t L, int d, int g) {
+  if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || L < 0 || g < 1 || (d != 64 && d != 128)) return 0;
+  return cca::backward_workspace_bytes(B, H, H_kv, L, d, g);
+}
+
+size_t cca_backward_workspace_bytes(int B, int H, int64_t L, int d, int g) {
+  return cca_backward_gqa_workspace_bytes(B, H, H, L, d, g);
+}
+
+int cca_backward_gqa(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int H_kv, int64_t L, int d, int g, int k_local,
+                     float scale, int dt, hipStream_t stream) {
+  int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, dt);
   if (s != CCA_OK) return s;
   if (dt != CCA_BF16 || d != 128) return CCA_ERR_UNSUPPORTED;
   if (L == 0) return CCA_OK;
@@ -149,9 +159,17 @@ int cca_backward(const void* q, const void* k, const void* v, const void* kc, co
       lse == nullptr || ((uintptr_t)lse & 3u) != 0)
     return CCA_ERR_INVALID;
   if ((int64_t)B * H * ((L + 127) / 128 + L / g / 128 + 1) >= INT32_MAX) return CCA_ERR_INVALID;
-  if (workspace_bytes < cca_backward_workspace_bytes(B, H, L, d, g)) return CCA_ERR_WORKSPACE;
-  return hip_status(cca::launch_backward_bf16_d128(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, B * H, L,
-                                                   g, k_local, scale, stream));
+  if (workspace_bytes < cca_backward_gqa_workspace_bytes(B, H, H_kv, L, d, g)) return CCA_ERR_WORKSPACE;
+  return hip_status(cca::launch_backward_bf16_d128(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, B * H,
+                                                   H / H_kv, L, g, k_local, scale, stream));
+}
+
+int cca_backward(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out,
+                 const float* lse, const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H, int64_t L, int d, int g, int k_local, float scale, int dt,
+                 hipStream_t stream) {
+  return cca_backward_gqa(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, H, L, d, g,
+                          k_local, scale, dt, stream);
 }
 
 int cca_pool_kv_lca(const void* q, const void* k, const void* v, void* kc, void* vc, int32_t* anchors, int B, int H,

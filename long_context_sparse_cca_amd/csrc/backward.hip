@@ -167,8 +167,8 @@ __global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restr
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dQ, int BH, int L, int g,
-    int k_local, float scale, int ntiles) {
+    const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dQ, int BH, int nq, int L,
+    int g, int k_local, float scale, int ntiles) {
   constexpr int kBM = 256, kBN = 64;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[2 * kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[2 * kTileBytes];
@@ -199,11 +199,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const unsigned core_span = (unsigned)max(cl_lane - 1, 0);
   const unsigned raw_span = (unsigned)(q_lane - rl_lane);
 
-  const size_t slice = (size_t)bh * L * kD;
-  const bf16_t* Ks = K + slice;
-  const bf16_t* Vs = V + slice;
-  const bf16_t* Kcs = Kc + (size_t)bh * m * kD;
-  const bf16_t* Vcs = Vc + (size_t)bh * m * kD;
+  const size_t slice = (size_t)bh * L * kD;              // query / dQ slice
+  const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
+  const bf16_t* Ks = K + (size_t)bkv * L * kD;
+  const bf16_t* Vs = V + (size_t)bkv * L * kD;
+  const bf16_t* Kcs = Kc + (size_t)bkv * m * kD;
+  const bf16_t* Vcs = Vc + (size_t)bkv * m * kD;
 
   // B operands of the score and dP chains: this lane's query / upstream-gradient row
   uint4 qop[kD / 16], dop[kD / 16];
@@ -339,15 +340,16 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dK, float* __restrict__ dV,
-    float* __restrict__ dKc, float* __restrict__ dVc, int BH, int L, int g, int k_local, float scale, int n_core_wg) {
+    float* __restrict__ dKc, float* __restrict__ dVc, int BHkv, int nq, int L, int g, int k_local, float scale,
+    int n_core_wg) {
   constexpr int kBK = 192;  // keys per workgroup
   constexpr int kBufBytes = 2 * kTileBytes + 2 * kTileRows * 4;
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds2[kBufBytes];
   // heaviest work first across all slices (workgroup index wi is the slow index)
-  const int wi = blockIdx.x / BH;
-  const int bh = blockIdx.x - wi * BH;
+  const int wi = blockIdx.x / BHkv;
+  const int bkv = blockIdx.x - wi * BHkv;   // key/value slice
   const bool core = wi < n_core_wg;
   const int m = L / g;
   const int key0 = core ? wi * kBK : (wi - n_core_wg) * kBK;
@@ -374,12 +376,14 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
   const int tq0 = (t_lo / kTileRows) * kTileRows;
   const int n_qt = (t_lo <= t_hi) ? (t_hi - tq0) / kTileRows + 1 : 0;
+  // the nq query heads that read this key/value slice each see the same query tiles:
+  // iteration it covers tile it % n_qt of head it / n_qt
+  const int n_it = n_qt * nq;
 
-  const size_t slice = (size_t)bh * L * kD;
-  const bf16_t* Ks = core ? Kc + (size_t)bh * m * kD : K + slice;
-  const bf16_t* Vs = core ? Vc + (size_t)bh * m * kD : V + slice;
-  const bf16_t* Qs = Q + slice;
-  const bf16_t* dOs = dO + slice;
+  const size_t slice = (size_t)bkv * L * kD;              // key/value (and dK/dV) slice
+  const bf16_t* Ks = core ? Kc + (size_t)bkv * m * kD : K + slice;
+  const bf16_t* Vs = core ? Vc + (size_t)bkv * m * kD : V + slice;
+  const size_t qslice0 = (size_t)bkv * nq;                // first query slice that reads it
   // B operands of the score and dP products: dims 32kk + 8G .. +7 of this lane's key
   const int key_lane = min(c0 + n16, key_end - 1);
   uint4 kop[kD / 32], vop[kD / 32];
@@ -430,15 +434,16 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
   // query tiles from the last one down (the workgroups of a slice that run together
   // then stream the same tiles)
-  auto tile_base = [&](int qt) { return tq0 + (n_qt - 1 - qt) * kTileRows; };
-  auto issue = [&](int qt, uint8_t* buf) {
-    const int base = tile_base(qt);
+  auto tile_base = [&](int it) { return tq0 + (n_qt - 1 - it % n_qt) * kTileRows; };
+  auto issue = [&](int it, uint8_t* buf) {
+    const int base = tile_base(it);
+    const size_t qs = qslice0 + it / n_qt;                // query slice of this iteration
     if (wave < 8) {
-      fill_tile<8>(Qs, base, L - 1, buf, wave, lane);
-      fill_tile<8>(dOs, base, L - 1, buf + kTileBytes, wave, lane);
+      fill_tile<8>(Q + qs * L * kD, base, L - 1, buf, wave, lane);
+      fill_tile<8>(dO + qs * L * kD, base, L - 1, buf + kTileBytes, wave, lane);
     } else if (wave < 10) {
       const int t = min(base + lane, L - 1);
-      const float* src = (wave == 8 ? lse : Dv) + (size_t)bh * L + t;
+      const float* src = (wave == 8 ? lse : Dv) + qs * L + t;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(buf + 2 * kTileBytes +
                                                                                   (wave - 8) * kTileRows * 4),
@@ -531,35 +536,35 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (wave < 8) __builtin_amdgcn_s_waitcnt(0x0F74);
     else __builtin_amdgcn_s_waitcnt(0x0F71);
   };
-  if (n_qt > 0) issue(0, lds0);
-  if (n_qt > 1) issue(1, lds1);
-  if (n_qt > 1) wait_older();
+  if (n_it > 0) issue(0, lds0);
+  if (n_it > 1) issue(1, lds1);
+  if (n_it > 1) wait_older();
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int qt = 0; qt < n_qt; qt += 3) {
-    if (qt + 2 < n_qt) issue(qt + 2, lds2);
+  for (int qt = 0; qt < n_it; qt += 3) {
+    if (qt + 2 < n_it) issue(qt + 2, lds2);
     if (wave_live) compute(lds0, qt);
-    if (qt + 2 < n_qt) wait_older();
+    if (qt + 2 < n_it) wait_older();
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (qt + 1 >= n_qt) break;
-    if (qt + 3 < n_qt) issue(qt + 3, lds0);
+    if (qt + 1 >= n_it) break;
+    if (qt + 3 < n_it) issue(qt + 3, lds0);
     if (wave_live) compute(lds1, qt + 1);
-    if (qt + 3 < n_qt) wait_older();
+    if (qt + 3 < n_it) wait_older();
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (qt + 2 >= n_qt) break;
-    if (qt + 4 < n_qt) issue(qt + 4, lds1);
+    if (qt + 2 >= n_it) break;
+    if (qt + 4 < n_it) issue(qt + 4, lds1);
     if (wave_live) compute(lds2, qt + 2);
-    if (qt + 4 < n_qt) wait_older();
+    if (qt + 4 < n_it) wait_older();
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
   if (!wave_live) return;
   const int key = c0 + n16;
   if (key >= key_end) return;
-  float* ov = core ? dVc + ((size_t)bh * m + key) * kD : dV + slice + (size_t)key * kD;
-  float* ok = core ? dKc + ((size_t)bh * m + key) * kD : dK + slice + (size_t)key * kD;
+  float* ov = core ? dVc + ((size_t)bkv * m + key) * kD : dV + slice + (size_t)key * kD;
+  float* ok = core ? dKc + ((size_t)bkv * m + key) * kD : dK + slice + (size_t)key * kD;
   // lane holds dims 16 blk + 4G + i of its key
 #pragma unroll
   for (int blk = 0; blk < kD / 16; ++blk) {
@@ -578,22 +583,38 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
                                                           const float* __restrict__ dKc,
                                                           const float* __restrict__ dVc, float* __restrict__ dQ,
                                                           float* __restrict__ dK, float* __restrict__ dV, int64_t L,
-                                                          int g, int64_t m, float scale) {
+                                                          int g, int64_t m, int nq, float scale) {
   extern __shared__ float sm[];   // a[g], then da / dz[g]
   float* a_l = sm;
   float* z_l = sm + g;
   const int64_t gid = blockIdx.x;
-  const int64_t bh = gid / m, j = gid - bh * m;
+  const int64_t bkv = gid / m, j = gid - bkv * m;           // key/value slice, group
   const int lane = threadIdx.x;
-  const size_t row0 = (size_t)bh * L + (size_t)j * g;        // first row of the group
-  const size_t rowq = row0 + g - 1;                           // its scoring query
-  const float* dkc = dKc + ((size_t)bh * m + j) * kD;
-  const float* dvc = dVc + ((size_t)bh * m + j) * kD;
+  const size_t row0 = (size_t)bkv * L + (size_t)j * g;       // first row of the group
+  // its scoring query: row j*g+g-1 of each of the nq query slices bkv*nq .. (their mean)
+  const size_t qrow0 = ((size_t)bkv * nq * L + (size_t)j * g + g - 1) * kD;
+  const size_t qstride = (size_t)L * kD;
+  const float inv_nq = 1.0f / (float)nq;
+  const float* dkc = dKc + ((size_t)bkv * m + j) * kD;
+  const float* dvc = dVc + ((size_t)bkv * m + j) * kD;
   // scoring pass: 4 lanes per row, 32 dims each (q_hat, dKc, dVc slices in registers)
   const int rsub = lane >> 2, seg = lane & 3;
   float qf[32], kcf[32], vcf[32];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) Elem<bf16_t>::chunk_to_f32(ld16(Q + rowq * kD + seg * 32 + c * 8), qf + c * 8);
+  for (int c = 0; c < 4; ++c) Elem<bf16_t>::chunk_to_f32(ld16(Q + qrow0 + seg * 32 + c * 8), qf + c * 8);
+  if (nq > 1) {
+    for (int h = 1; h < nq; ++h) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float f[8];
+        Elem<bf16_t>::chunk_to_f32(ld16(Q + qrow0 + h * qstride + seg * 32 + c * 8), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[c * 8 + e] += f[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) qf[e] *= inv_nq;
+  }
 #pragma unroll
   for (int e = 0; e < 32; e += 4) {
     const float4 x = *reinterpret_cast<const float4*>(dkc + seg * 32 + e);
@@ -646,11 +667,17 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
   wave_lds_sync();
   // row updates: each lane owns 2 consecutive dims
   const int col = lane * 2;
-  float q2[2], kc2[2], vc2[2], dq2[2] = {0.f, 0.f};
+  float q2[2] = {0.f, 0.f}, kc2[2], vc2[2], dq2[2] = {0.f, 0.f};
   {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + rowq * kD + col);
-    q2[0] = __uint_as_float(w << 16);
-    q2[1] = __uint_as_float(w & 0xffff0000u);
+    for (int h = 0; h < nq; ++h) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + qrow0 + h * qstride + col);
+      q2[0] += __uint_as_float(w << 16);
+      q2[1] += __uint_as_float(w & 0xffff0000u);
+    }
+    if (nq > 1) {
+      q2[0] *= inv_nq;
+      q2[1] *= inv_nq;
+    }
     kc2[0] = dkc[col]; kc2[1] = dkc[col + 1];
     vc2[0] = dvc[col]; vc2[1] = dvc[col + 1];
   }
@@ -670,30 +697,34 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
     dq2[0] = fmaf(dz, k0, dq2[0]);
     dq2[1] = fmaf(dz, k1, dq2[1]);
   }
-  float2* pq = reinterpret_cast<float2*>(dQ + rowq * kD + col);
-  float2 xq = *pq;
-  xq.x += scale * dq2[0];
-  xq.y += scale * dq2[1];
-  *pq = xq;
+  // d q_hat reaches each of the nq scoring queries with weight 1/nq
+  for (int h = 0; h < nq; ++h) {
+    float2* pq = reinterpret_cast<float2*>(dQ + qrow0 + h * qstride + col);
+    float2 xq = *pq;
+    xq.x += scale * inv_nq * dq2[0];
+    xq.y += scale * inv_nq * dq2[1];
+    *pq = xq;
+  }
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int H, int64_t L, int d, int g) {
-  const size_t BH = (size_t)B * H;
+size_t backward_workspace_bytes(int B, int H, int H_kv, int64_t L, int d, int g) {
+  const size_t BH = (size_t)B * H, BHkv = (size_t)B * H_kv;
   const size_t m = (size_t)(L / g);
-  return (2 * BH * (size_t)L + 2 * BH * m * (size_t)d) * sizeof(float);
+  return (2 * BH * (size_t)L + 2 * BHkv * m * (size_t)d) * sizeof(float);
 }
 
 hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                      const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                                     float* dv, void* workspace, int BH, int64_t L, int g, int k_local, float scale,
-                                     hipStream_t stream) {
+                                     float* dv, void* workspace, int BH, int nq, int64_t L, int g, int k_local,
+                                     float scale, hipStream_t stream) {
   const int64_t m = L / g;
+  const int BHkv = BH / nq;
   float* Dv = (float*)workspace;
   float* lse2 = Dv + (size_t)BH * L;
   float* dKc = lse2 + (size_t)BH * L;
-  float* dVc = dKc + (size_t)BH * m * kD;
+  float* dVc = dKc + (size_t)BHkv * m * kD;
   const int64_t rows = (int64_t)BH * L;
   hipLaunchKernelGGL(cca_bwd_prep_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
                      (const bf16_t*)out, (const bf16_t*)dout, lse, Dv, lse2, rows);
@@ -702,20 +733,20 @@ hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v
   const int ntiles = (int)((L + 255) / 256);
   hipLaunchKernelGGL(cca_bwd_dq_kernel, dim3((unsigned)(BH * ntiles)), dim3(512), 0, stream, (const bf16_t*)q,
                      (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, (const bf16_t*)dout,
-                     (const float*)lse2, (const float*)Dv, dq, BH, (int)L, g, k_local, scale, ntiles);
+                     (const float*)lse2, (const float*)Dv, dq, BH, nq, (int)L, g, k_local, scale, ntiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_core_wg = (int)((m + 191) / 192);
   const int n_wg = n_core_wg + (int)((L + 191) / 192);
-  hipLaunchKernelGGL(cca_bwd_dkdv16_kernel, dim3((unsigned)((int64_t)BH * n_wg)), dim3(768), 0, stream,
+  hipLaunchKernelGGL(cca_bwd_dkdv16_kernel, dim3((unsigned)((int64_t)BHkv * n_wg)), dim3(768), 0, stream,
                      (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
-                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dk, dv, dKc, dVc, BH, (int)L, g,
-                     k_local, scale, n_core_wg);
+                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dk, dv, dKc, dVc, BHkv, nq, (int)L,
+                     g, k_local, scale, n_core_wg);
   e = hipGetLastError();
   if (e != hipSuccess || m == 0) return e;
-  hipLaunchKernelGGL(cca_bwd_pool_kernel, dim3((unsigned)((int64_t)BH * m)), dim3(64), (size_t)2 * g * sizeof(float),
-                     stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const float*)dKc,
-                     (const float*)dVc, dq, dk, dv, L, g, m, scale);
+  hipLaunchKernelGGL(cca_bwd_pool_kernel, dim3((unsigned)((int64_t)BHkv * m)), dim3(64),
+                     (size_t)2 * g * sizeof(float), stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                     (const float*)dKc, (const float*)dVc, dq, dk, dv, L, g, m, nq, scale);
   return hipGetLastError();
 }
 

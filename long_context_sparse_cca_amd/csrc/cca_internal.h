@@ -83,13 +83,14 @@ hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream);
 
-// Backward pass, bf16, head dim 128 (backward.hip).  Workspace: D [BH][L], the
-// log-sum-exp in log2 units [BH][L], then dKc and dVc [BH][L/g][d], all float32.
-size_t backward_workspace_bytes(int B, int H, int64_t L, int d, int g);
+// Backward pass, bf16, head dim 128 (backward.hip); BH query slices, nq query heads per
+// key/value head.  Workspace: D [BH][L], the log-sum-exp in log2 units [BH][L], then dKc
+// and dVc [BH/nq][L/g][d], all float32.
+size_t backward_workspace_bytes(int B, int H, int H_kv, int64_t L, int d, int g);
 hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                      const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                                     float* dv, void* workspace, int BH, int64_t L, int g, int k_local, float scale,
-                                     hipStream_t stream);
+                                     float* dv, void* workspace, int BH, int nq, int64_t L, int g, int k_local,
+                                     float scale, hipStream_t stream);
 
 // Chunked append of n tokens per sequence (extend.hip).
 size_t extend_workspace_bytes(const cca_cache_t* c, int n);

@@ -95,3 +95,56 @@ def test_backward_unsupported_shapes(gpu):
     q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=gpu)
     with pytest.raises(binding.CCAError):
         binding.prefill_lse(q, q.clone(), q.clone(), 16, 1)
+
+
+# grouped-query training: (B, H, H_kv, L, g, k, seed)
+GQA_BWD_CASES = [
+    (1, 4, 2, 300, 16, 2, 90),    # r = 2
+    (1, 4, 1, 520, 16, 3, 91),    # multi-query (r = 4), ragged tiles
+    (2, 8, 2, 260, 7, 1, 92),     # r = 4, g not a power of two
+]
+
+
+def _gid(c):
+    B, H, Hkv, L, g, k, seed = c
+    return f"B{B}H{H}Hkv{Hkv}L{L}g{g}k{k}"
+
+
+@pytest.mark.parametrize("case", GQA_BWD_CASES, ids=_gid)
+def test_gqa_backward_matches_oracle(gpu, case):
+    B, H, Hkv, L, g, k, seed = case
+    d = 128
+    _say(f"gqa backward case {_gid(case)} seed {seed}")
+    Q = np_inputs(B, H, L, d, "bf16", seed)[0]
+    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, "bf16", seed + 1)[1:])
+    dO = np_inputs(B, H, L, d, "bf16", seed + 500)[0]
+    q, kk, v, do = (_dev(x, gpu) for x in (Q, K, V, dO))
+    scale = 1.0 / math.sqrt(d)
+    out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
+    dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
+    torch.cuda.synchronize()
+    assert tuple(dk.shape) == (B, Hkv, L, d) and tuple(kc.shape) == (B, Hkv, L // g, d)
+    assert torch.equal(out, binding.prefill(q, kk, v, g, k, scale))
+    want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype="bf16")
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
+
+
+def test_gqa_autograd_function(gpu):
+    B, H, Hkv, L, d, g, k = 1, 4, 2, 300, 128, 16, 2
+    Q = np_inputs(B, H, L, d, "bf16", 95)[0]
+    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, "bf16", 96)[1:])
+    q, kk, v = (_dev(x, gpu).requires_grad_(True) for x in (Q, K, V))
+    out = binding.CCAAttention.apply(q, kk, v, g, k)
+    dO = _dev(np_inputs(B, H, L, d, "bf16", 97)[0], gpu)
+    out.backward(dO)
+    torch.cuda.synchronize()
+    assert tuple(kk.grad.shape) == (B, Hkv, L, d) and tuple(q.grad.shape) == (B, H, L, d)
+    o2, lse, kc, vc = binding.prefill_lse(q.detach(), kk.detach(), v.detach(), g, k)
+    dq, dk, dv = binding.backward(q.detach(), kk.detach(), v.detach(), kc, vc, o2, lse, dO, g, k)
+    torch.cuda.synchronize()
+    assert torch.equal(q.grad, dq.to(torch.bfloat16)) and torch.equal(kk.grad, dk.to(torch.bfloat16))
+    assert torch.equal(v.grad, dv.to(torch.bfloat16))
