@@ -155,6 +155,19 @@ int cca_pool_kv_lca(const void* q, const void* k, const void* v, void* kc, void*
 int cca_prefill_lca(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, int32_t* anchors,
                     int B, int H, int64_t L, int d, int g, int k_local, int d_rope, float scale,
                     int dt, int out_dt, hipStream_t stream);
+/*
+ * Grouped-query form: k, v, kc, vc, anchors have H_kv heads; the importance query of a
+ * group of key/value head h is the mean over the group's g positions and over the r =
+ * H/H_kv query heads h*r .. h*r+r-1 that read it (the mean-over-heads reading of
+ * cca_pool_kv_gqa with the LCA page's mean over the group).  cca_pool_kv_lca /
+ * cca_prefill_lca are these with H_kv = H.  H % H_kv != 0 gives CCA_ERR_INVALID.
+ */
+int cca_pool_kv_lca_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, int32_t* anchors,
+                        int B, int H, int H_kv, int64_t L, int d, int g, int d_rope, float scale,
+                        int dt, hipStream_t stream);
+int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, void* out,
+                        int32_t* anchors, int B, int H, int H_kv, int64_t L, int d, int g, int k_local,
+                        int d_rope, float scale, int dt, int out_dt, hipStream_t stream);
 
 /*
  * Training ([CCA] Triton section: the fused operator serves training as well;

@@ -97,6 +97,14 @@ EXPORTS = {
                                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                               ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                               ctypes.c_void_p]),
+    "cca_pool_kv_lca_gqa": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                                  ctypes.c_void_p]),
+    "cca_prefill_lca_gqa": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "cca_cache_ring_slots": (ctypes.c_int64, [ctypes.POINTER(CacheDesc)]),
     "cca_cache_load_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                + [ctypes.c_int64, ctypes.c_void_p]),
@@ -266,37 +274,35 @@ def attention(q, k, v, kc, vc, g: int, k_local: int, scale: float | None = None,
 
 
 def pool_kv_lca(q, k, v, g: int, d_rope: int, scale: float | None = None):
-    """LCA-style condensed keys/values and anchors: (kc, vc [B,H,L//g,d], anchors int32 [B,H,L//g])."""
+    """LCA-style condensed keys/values and anchors of q [B,H,L,d], k, v [B,H_kv,L,d]:
+    (kc, vc [B,H_kv,L//g,d], anchors int32 [B,H_kv,L//g]); cca_pool_kv_lca_gqa."""
     lib = load_library()
     B, H, Hkv, L, d = _heads(q, k, v)
-    if Hkv != H:
-        raise CCAError("the LCA-style path takes one query head per key/value head")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     m = L // g if g >= 1 else 0
-    kc = _core_buffer(B, H, m, d, q)
-    vc = _core_buffer(B, H, m, d, q)
-    anchors = torch.empty((B, H, max(m, 1)), dtype=torch.int32, device=q.device)[:, :, :m]
-    _check(lib.cca_pool_kv_lca(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(anchors), B, H, L, d, g, d_rope,
-                               scale, _dtype_code(q.dtype), _stream()), "cca_pool_kv_lca")
+    kc = _core_buffer(B, Hkv, m, d, q)
+    vc = _core_buffer(B, Hkv, m, d, q)
+    anchors = torch.empty((B, Hkv, max(m, 1)), dtype=torch.int32, device=q.device)[:, :, :m]
+    _check(lib.cca_pool_kv_lca_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(anchors), B, H, Hkv, L, d, g,
+                                   d_rope, scale, _dtype_code(q.dtype), _stream()), "cca_pool_kv_lca")
     return kc, vc, anchors
 
 
 def prefill_lca(q, k, v, g: int, k_local: int, d_rope: int, scale: float | None = None, out_dtype=None):
-    """LCA-style prefill: (out [B,H,L,d], kc, vc, anchors int32 [B,H,L//g]): cca_prefill_lca."""
+    """LCA-style prefill of q [B,H,L,d], k, v [B,H_kv,L,d]: (out [B,H,L,d], kc, vc [B,H_kv,L//g,d],
+    anchors int32 [B,H_kv,L//g]); cca_prefill_lca_gqa."""
     lib = load_library()
     B, H, Hkv, L, d = _heads(q, k, v)
-    if Hkv != H:
-        raise CCAError("the LCA-style path takes one query head per key/value head")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     m = L // g if g >= 1 else 0
-    kc = _core_buffer(B, H, m, d, q)
-    vc = _core_buffer(B, H, m, d, q)
-    anchors = torch.empty((B, H, max(m, 1)), dtype=torch.int32, device=q.device)[:, :, :m]
+    kc = _core_buffer(B, Hkv, m, d, q)
+    vc = _core_buffer(B, Hkv, m, d, q)
+    anchors = torch.empty((B, Hkv, max(m, 1)), dtype=torch.int32, device=q.device)[:, :, :m]
     out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
-    _check(lib.cca_prefill_lca(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(anchors), B, H, L, d,
-                               g, k_local, d_rope, scale, _dtype_code(q.dtype), _dtype_code(out_dtype), _stream()),
-           "cca_prefill_lca")
+    _check(lib.cca_prefill_lca_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), _ptr(anchors), B, H, Hkv,
+                                   L, d, g, k_local, d_rope, scale, _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                   _stream()), "cca_prefill_lca")
     return out, kc, vc, anchors
 
 

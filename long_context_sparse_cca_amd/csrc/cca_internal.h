@@ -21,10 +21,12 @@ struct ExtendArgs {
   int64_t core_rows;   // rows per core K/V slice
 };
 
-// LCA-style pooling (pool_lca.hip): mean-query importance, the last d_rope dims of a
-// core key taken from the group's top-scored token; anchors (optional) receive its index.
+// LCA-style pooling (pool_lca.hip): mean-query importance (over the group and the nq query
+// heads of a key/value head), the last d_rope dims of a core key taken from the group's
+// top-scored token; anchors (optional) receive its index.
 hipError_t launch_pool_lca(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
-                           int32_t* anchors, int BH, int64_t L, int g, int d_rope, float scale, hipStream_t stream);
+                           int32_t* anchors, int BHkv, int64_t L, int g, int nq, int d_rope, float scale,
+                           hipStream_t stream);
 
 // Grouped-query attention: nq = H / H_kv query heads share each key/value head.
 // Query/output slices are (b, h) = b*H + h; key/value and core slices are

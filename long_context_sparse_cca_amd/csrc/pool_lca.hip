@@ -9,8 +9,8 @@
 // a key are its positional part; values are pooled entirely.  The condensed
 // groups then take the place of CCA's core tokens in the unified attention.
 //
-// One wave per group, HBM-bound: the group's g query rows, key rows and value rows
-// are each read once.
+// One wave per group, HBM-bound: the group's g query rows (of each of the nq query
+// heads that share the key/value head), key rows and value rows are each read once.
 #include "cca_internal.h"
 
 namespace cca {
@@ -37,7 +37,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void cca_pool_lca_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                           const T* __restrict__ V, T* __restrict__ Kc,
                                                           T* __restrict__ Vc, int32_t* __restrict__ anchors,
-                                                          int64_t L, int g, int64_t m, int d_rope, float scale) {
+                                                          int64_t L, int g, int64_t m, int nq, int d_rope,
+                                                          float scale) {
   extern __shared__ float sm[];   // mean query [D], then scores [g]
   float* qbar = sm;
   float* w = sm + D;
@@ -47,23 +48,27 @@ __global__ __launch_bounds__(64) void cca_pool_lca_kernel(const T* __restrict__ 
   constexpr int SEG = D / LPR;
   constexpr int SEGC = SEG / EPC;
   const int64_t gid = blockIdx.x;
-  const int64_t bh = gid / m, j = gid - bh * m;
+  const int64_t bh = gid / m, j = gid - bh * m;   // key/value slice, group
   const int lane = threadIdx.x;
   const size_t row0 = ((size_t)bh * L + (size_t)j * g) * D;
   const int col = lane * CPL;
 
-  // ---- mean query of the group: each lane sums its columns over the g rows
+  // ---- mean query of the group: each lane sums its columns over the g rows of each of
+  // the nq query slices bh*nq .. that read this key/value slice
   {
     float s[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) s[e] = 0.f;
-    for (int r = 0; r < g; ++r) {
-      float f[CPL];
-      load_cols<T, D>(Q + row0 + (size_t)r * D + col, f);
+    for (int h = 0; h < nq; ++h) {
+      const T* qg = Q + (((size_t)bh * nq + h) * L + (size_t)j * g) * D;
+      for (int r = 0; r < g; ++r) {
+        float f[CPL];
+        load_cols<T, D>(qg + (size_t)r * D + col, f);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) s[e] += f[e];
+        for (int e = 0; e < CPL; ++e) s[e] += f[e];
+      }
     }
-    const float inv_g = 1.0f / (float)g;
+    const float inv_g = 1.0f / ((float)g * (float)nq);
 #pragma unroll
     for (int e = 0; e < CPL; ++e) qbar[col + e] = s[e] * inv_g;
   }
@@ -139,26 +144,28 @@ __global__ __launch_bounds__(64) void cca_pool_lca_kernel(const T* __restrict__ 
 }
 
 template <typename T, int D>
-hipError_t launch_t(const void* q, const void* k, const void* v, void* kc, void* vc, int32_t* anchors, int BH,
-                    int64_t L, int g, int d_rope, float scale, hipStream_t stream) {
+hipError_t launch_t(const void* q, const void* k, const void* v, void* kc, void* vc, int32_t* anchors, int BHkv,
+                    int64_t L, int g, int nq, int d_rope, float scale, hipStream_t stream) {
   const int64_t m = L / g;
-  const int64_t n = (int64_t)BH * m;
+  const int64_t n = (int64_t)BHkv * m;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL((cca_pool_lca_kernel<T, D>), dim3((unsigned)n), dim3(64), (size_t)(D + g) * sizeof(float),
-                     stream, (const T*)q, (const T*)k, (const T*)v, (T*)kc, (T*)vc, anchors, L, g, m, d_rope, scale);
+                     stream, (const T*)q, (const T*)k, (const T*)v, (T*)kc, (T*)vc, anchors, L, g, m, nq, d_rope,
+                     scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_pool_lca(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
-                           int32_t* anchors, int BH, int64_t L, int g, int d_rope, float scale, hipStream_t stream) {
+                           int32_t* anchors, int BHkv, int64_t L, int g, int nq, int d_rope, float scale,
+                           hipStream_t stream) {
   if (dt == CCA_BF16) {
-    if (d == 128) return launch_t<bf16_t, 128>(q, k, v, kc, vc, anchors, BH, L, g, d_rope, scale, stream);
-    return launch_t<bf16_t, 64>(q, k, v, kc, vc, anchors, BH, L, g, d_rope, scale, stream);
+    if (d == 128) return launch_t<bf16_t, 128>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
+    return launch_t<bf16_t, 64>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
   }
-  if (d == 128) return launch_t<float, 128>(q, k, v, kc, vc, anchors, BH, L, g, d_rope, scale, stream);
-  return launch_t<float, 64>(q, k, v, kc, vc, anchors, BH, L, g, d_rope, scale, stream);
+  if (d == 128) return launch_t<float, 128>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
+  return launch_t<float, 64>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
 }
 
 }  // namespace cca

@@ -23,6 +23,12 @@ take per-head keys and values):
        scores are equal to within rounding, any of them is a valid anchor (tests
        check the GPU's choice is such a maximum and compare the rest with the
        oracle evaluated at that choice).
+  R21  with grouped-query heads (r = H / H_kv query heads sharing a key/value
+       head, as in oracle/cca_serving.py's R14/R15), a key/value head is condensed
+       once; its group importance query is the mean over the group's g positions
+       and over the r query heads (R14's mean over heads with R19's mean over the
+       group), and each query head attends to its key/value head's condensed
+       tokens and raw window.
 Everything is float64.
 """
 
@@ -32,7 +38,7 @@ import numpy as np
 
 from . import cca_oracle as _o
 
-__all__ = ["group_mean_query", "lca_scores", "lca_pool", "lca_slice"]
+__all__ = ["group_mean_query", "lca_scores", "lca_pool", "lca_slice", "lca_gqa"]
 
 
 def group_mean_query(Q, j: int, g: int) -> np.ndarray:
@@ -90,3 +96,34 @@ def lca_slice(Q, K, V, g: int, k: int, scale: float, d_rope: int, anchors=None, 
     for t in range(L):
         out[t] = _o.cca_row(Q[t], t, K, V, Kc, Vc, g, k, scale)
     return out
+
+
+def lca_gqa(Q, K, V, g: int, k: int, scale: float, d_rope: int, anchors=None, core_dtype=None):
+    """Grouped-query LCA-style prefill (R21): (out [B,H,L,d], Kc, Vc [B,H_kv,m,d], anchors [B,H_kv,m]).
+
+    Q: [B, H, L, d]; K, V: [B, H_kv, L, d].  `anchors`, if given, fixes the anchor of
+    every condensed token (the tests pass the GPU's choice, R20).
+    """
+    from . import cca_serving as _s
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, L, d = Q.shape
+    Hkv = K.shape[1]
+    if H % Hkv != 0:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    r = H // Hkv
+    m = _o.n_core_groups(L, g)
+    out = np.empty((B, H, L, d))
+    Kc = np.empty((B, Hkv, m, d))
+    Vc = np.empty((B, Hkv, m, d))
+    anc = np.empty((B, Hkv, m), dtype=np.int64)
+    for b in range(B):
+        for hk in range(Hkv):
+            q_mean = Q[b, hk * r:(hk + 1) * r].sum(axis=0) / r       # mean over the r heads, per position
+            a_in = None if anchors is None else np.asarray(anchors)[b, hk]
+            Kc[b, hk], Vc[b, hk], anc[b, hk] = lca_pool(q_mean, K[b, hk], V[b, hk], g, scale, d_rope, a_in,
+                                                        core_dtype)
+            for h in range(hk * r, (hk + 1) * r):
+                out[b, h] = _s.attend_with_core(Q[b, h], K[b, hk], V[b, hk], Kc[b, hk], Vc[b, hk], g, k, scale)
+    return out, Kc, Vc, anc

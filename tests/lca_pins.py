@@ -75,5 +75,40 @@ def pin_no_window_overlap_and_attention_is_cca(lc):
     return e < 1e-12, f"max err {e:.3e}"
 
 
-ALL_LCA_PINS = [pin_closed_form, pin_identical_queries_no_rope_is_cca_pooling, pin_anchor_is_the_top_scored_key,
+def pin_gqa_closed_form(lc):
+    """Grouped-query closed form (R21): d = 2 (content dim 0, positional dim 1), g = 2, r = 2, scale 1.
+
+    Head 0 queries (1, 0), (3, 0); head 1 queries (-1, 0), (1, 0): the mean over heads and
+    positions is (1, 0).  K rows (0, 5), (ln 3, -5): scores (0, ln 3), weights (1/4, 3/4),
+    anchor 1; Kc = (3 ln 3 / 4, -5), Vc = (5/2, 7/2) from V rows (1, 2), (3, 4).  (Head 0 alone
+    would give weights (1/10, 9/10); the sum over heads and positions (1/82, 81/82).)
+    """
+    x = math.log(3.0)
+    Q = np.array([[[[1.0, 0.0], [3.0, 0.0]], [[-1.0, 0.0], [1.0, 0.0]]]])
+    K = np.array([[[[0.0, 5.0], [x, -5.0]]]])
+    V = np.array([[[[1.0, 2.0], [3.0, 4.0]]]])
+    _, Kc, Vc, anc = lc.lca_gqa(Q, K, V, 2, 1, 1.0, 1)
+    e = max(_err(Kc[0, 0], [[3 * x / 4, -5.0]]), _err(Vc[0, 0], [[2.5, 3.5]]))
+    return e < 1e-12 and int(anc[0, 0, 0]) == 1, f"max err {e:.3e}, anchor {anc[0, 0, 0]}"
+
+
+def pin_gqa_identical_heads_is_per_head(lc):
+    """Identical query heads sharing a key/value head give the one-head condensation and outputs."""
+    H, Hkv, L, g, d, dr = 4, 2, 40, 5, 6, 2
+    Q1 = np_inputs(1, 2, L, d, "f32", 24)[0].astype(np.float64)
+    Q = np.repeat(Q1, 2, axis=1)                       # heads 2j, 2j+1 both equal Q1[:, j]
+    K, V = (x.astype(np.float64) for x in np_inputs(1, Hkv, L, d, "f32", 25)[1:])
+    sc = 0.45
+    out, Kc, Vc, _ = lc.lca_gqa(Q, K, V, g, 2, sc, dr)
+    worst = 0.0
+    for hk in range(Hkv):
+        Kr, Vr, _ = lc.lca_pool(Q1[0, hk], K[0, hk], V[0, hk], g, sc, dr)
+        ref = lc.lca_slice(Q1[0, hk], K[0, hk], V[0, hk], g, 2, sc, dr)
+        worst = max(worst, _err(Kc[0, hk], Kr), _err(Vc[0, hk], Vr), _err(out[0, 2 * hk], ref),
+                    _err(out[0, 2 * hk + 1], ref))
+    return worst < 1e-12, f"max err {worst:.3e}"
+
+
+ALL_LCA_PINS = [pin_gqa_closed_form, pin_gqa_identical_heads_is_per_head,
+                pin_closed_form, pin_identical_queries_no_rope_is_cca_pooling, pin_anchor_is_the_top_scored_key,
                 pin_no_window_overlap_and_attention_is_cca]

@@ -151,3 +151,51 @@ def test_lca_full_size_sampled(gpu):
             want = cca_oracle.cca_row(Qs[t], int(t), Ks, Vs, gkc, gvc, g, k, scale)
             err = np.abs(out[0, h, t].cpu().numpy().astype(np.float64) - want).max()
             assert err <= TOL["bf16"], f"row {t} err {err:.3e}"
+
+
+# grouped-query LCA-style prefill: (B, H, H_kv, L, d, g, k, d_rope, dtype, seed)
+LCA_GQA_CASES = [
+    (1, 4, 2, 600, 128, 16, 2, 64, "bf16", 30),
+    (2, 4, 1, 333, 64, 7, 3, 16, "f32", 31),    # multi-query, g not a power of two
+    (1, 8, 2, 520, 128, 16, 1, 0, "bf16", 32),  # r = 4, every dim pooled
+]
+
+
+def _gqa_id(c):
+    B, H, Hkv, L, d, g, k, r, dt, seed = c
+    return f"B{B}H{H}Hkv{Hkv}L{L}d{d}g{g}k{k}r{r}-{dt}"
+
+
+@pytest.mark.parametrize("case", LCA_GQA_CASES, ids=_gqa_id)
+def test_lca_gqa_matches_oracle(gpu, case):
+    B, H, Hkv, L, d, g, k, d_rope, dt, seed = case
+    _say(f"lca gqa case {_gqa_id(case)} seed {seed}")
+    Q = np_inputs(B, H, L, d, dt, seed)[0]
+    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, dt, seed + 1)[1:])
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    out, kc, vc, anchors = binding.prefill_lca(q, kk, v, g, k, d_rope, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert tuple(kc.shape) == (B, Hkv, L // g, d) and tuple(anchors.shape) == (B, Hkv, L // g)
+    r = H // Hkv
+    m = L // g
+    anc = anchors.cpu().numpy()
+    for b in range(B):
+        for hk in range(Hkv):
+            q_mean = Q[b, hk * r:(hk + 1) * r].astype(np.float64).mean(axis=0)
+            _check_anchors(cca_lca.lca_scores(q_mean, K[b, hk].astype(np.float64), g, scale), anc[b, hk])
+    want, Kc, Vc, _ = cca_lca.lca_gqa(Q, K, V, g, k, scale, d_rope, anchors=anc, core_dtype=dt)
+    dc = d - d_rope
+    gk = kc.float().cpu().numpy()
+    gv = vc.float().cpu().numpy()
+    if m:
+        Kx, Vx, _ = (np.asarray(x) for x in cca_lca.lca_gqa(Q, K, V, g, k, scale, d_rope, anchors=anc)[1:])
+        for got, ref in ((gk[..., :dc], Kx[..., :dc]), (gv, Vx)):
+            bound = TOL[dt] + ULP[dt] * np.abs(ref)
+            assert np.all(np.abs(got - ref) <= bound), f"condensed err {np.abs(got - ref).max():.3e}"
+        for b in range(B):
+            for hk in range(Hkv):
+                rows = np.arange(m) * g + anc[b, hk].astype(np.int64)
+                assert np.array_equal(gk[b, hk, :, dc:], K[b, hk, rows, dc:].astype(np.float32))
+    err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+    assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"

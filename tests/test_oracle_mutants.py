@@ -239,7 +239,36 @@ def _anchor_is_argmin(Q, K, V, g, scale, d_rope, anchors=None, core_dtype=None):
     return _orig_lca_pool(Q, K, V, g, scale, d_rope, np.argmin(S, axis=1), core_dtype)
 
 
+_orig_lca_gqa = lca.lca_gqa
+
+
+def _lca_gqa_first_head_only(Q, K, V, g, k, scale, d_rope, anchors=None, core_dtype=None):
+    """Grouped-query condensation scored with the first query head of each group of heads only."""
+    Q = np.asarray(Q, np.float64).copy()
+    r = Q.shape[1] // np.asarray(K).shape[1]
+    Qs = Q.copy()
+    for h in range(Q.shape[1]):
+        Qs[:, h] = Q[:, h - h % r]
+    _, Kc, Vc, anc = _orig_lca_gqa(Qs, K, V, g, k, scale, d_rope, anchors, core_dtype)
+    out = _orig_lca_gqa(Q, K, V, g, k, scale, d_rope, anc, core_dtype)[0]
+    return out, Kc, Vc, anc
+
+
+def _lca_gqa_sum_over_heads(Q, K, V, g, k, scale, d_rope, anchors=None, core_dtype=None):
+    """Grouped-query condensation scored with the sum (not the mean) over the query heads."""
+    Q = np.asarray(Q, np.float64)
+    r = Q.shape[1] // np.asarray(K).shape[1]
+    Qs = Q.copy()
+    for h in range(Q.shape[1]):
+        base = h - h % r
+        Qs[:, h] = Q[:, base:base + r].sum(axis=1)
+    _, Kc, Vc, anc = _orig_lca_gqa(Qs, K, V, g, k, scale, d_rope, anchors, core_dtype)
+    return _orig_lca_gqa(Q, K, V, g, k, scale, d_rope, anc, core_dtype)[0], Kc, Vc, anc
+
+
 LCA_MUTANTS = {
+    "grouped-query importance from the first head": ("lca_gqa", _lca_gqa_first_head_only),
+    "grouped-query importance from the summed heads": ("lca_gqa", _lca_gqa_sum_over_heads),
     "importance from the last query": ("group_mean_query", _last_query_instead_of_mean),
     "importance from the summed queries": ("group_mean_query", _sum_instead_of_mean),
     "positional dims pooled": ("lca_pool", _pooled_positional_dims),
