@@ -323,12 +323,43 @@ def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int 
     pool_ms, prefill_ms = sum(tp) / reps, sum(tf) / reps
     byt = accounting.lca_pool_bytes(1, H, L, D, G, 2)
     gbs = byt / (pool_ms * 1e-3) / 1e9
+    del q, k, v
+    torch.cuda.empty_cache()
+
+    # decode with the LCA-style cache: B=8 sequences at context 131072, 64 steps (4 condensations)
+    steps = 64
+    dq, dk, dv = torch_inputs(DEC_B, H, DEC_L0 + steps, D, torch.bfloat16, dev, seed=seed + 10, heavy_frac=HEAVY)
+    pre = [x[:, :, :DEC_L0].contiguous() for x in (dq, dk, dv)]
+    _, kc, vc, _ = binding.prefill_lca(*pre, G, KL, d_rope)
+    cache = binding.LCACache(DEC_B, H, D, G, KL, max_tokens=DEC_L0 + steps, d_rope=d_rope, dtype=torch.bfloat16,
+                             device=dev)
+    cache.load_prefill(*pre, kc, vc)
+    del pre, kc, vc
+    xs = [x[:, :, DEC_L0:].permute(2, 0, 1, 3).contiguous() for x in (dq, dk, dv)]
+    del dq, dk, dv
+    out = torch.empty((DEC_B, H, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for s_ in range(steps):
+        cache.append_decode(xs[0][s_], xs[1][s_], xs[2][s_], out=out)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+    nchunks = cache.ws_bytes // (DEC_B * H * (D + 2) * 4)
+    dbytes = sum(accounting.decode_bytes(DEC_B, H, D, DEC_L0 + s_, G, KL, 2, nchunks) for s_ in range(steps)) / steps
+    dgbs = dbytes / (dec_us * 1e-6) / 1e9
     return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL, "d_rope": d_rope},
             "pool_ms": pool_ms, "prefill_ms": prefill_ms, "prefill_tokens_per_s": L / (prefill_ms * 1e-3),
             "pool_bytes": byt,
             "roofline": {"kernel": "cca_pool_lca_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                         "per_unit": "(3*g + 2)*d*2 bytes per group"}}
+                         "per_unit": "(3*g + 2)*d*2 bytes per group"},
+            "decode": {"config": {"B": DEC_B, "H": H, "context": DEC_L0, "steps": steps},
+                       "us_per_step": dec_us, "bytes_per_step": dbytes,
+                       "roofline": {"kernel": "cca_decode_kernel<bf16,128,lca append> + cca_decode_merge_kernel",
+                                    "bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": dgbs / PEAK_HBM_GBS}}}
 
 
 def main():

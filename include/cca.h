@@ -310,6 +310,29 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
                             float scale, hipStream_t stream);
 
 /*
+ * LCA-style decode cache ("Latent-Condensed Transformer for Efficient Long Context
+ * Modeling", section 2, inference flow: a group is condensed as soon as its last token
+ * arrives, with the mean-query importance and positional anchoring of cca_pool_kv_lca;
+ * the attention is that of cca_cache_append_decode, over the condensed tokens and the
+ * raw ring).  The same cca_cache_t holds the condensed tokens in core_k/core_v.
+ *   qsum  : device float32 [B, H, d], caller-owned: the running sum of the queries of
+ *           each sequence's current (incomplete) group, in token order.  Zero for an
+ *           empty cache; cca_cache_load_prefill_lca sets it from the prefill's last
+ *           partial group; the append call adds the new query and, when the group
+ *           completes, condenses it with the mean (sum / g) and zeroes the sum.
+ *   d_rope: 0 <= d_rope <= d, the positional dims (as for cca_pool_kv_lca).
+ * cca_cache_load_prefill_lca: cca_cache_load_prefill (kc, vc from cca_prefill_lca of
+ *   the same prefix) plus qsum from q [B, H, L, d].
+ * cca_cache_append_decode_lca: as cca_cache_append_decode, with the LCA-style
+ *   condensation; workspace as cca_decode_workspace_bytes.  Errors as for those calls.
+ */
+int cca_cache_load_prefill_lca(cca_cache_t* c, float* qsum, const void* q, const void* k, const void* v,
+                               const void* kc, const void* vc, int64_t L, hipStream_t stream);
+int cca_cache_append_decode_lca(cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k,
+                                const void* v, void* out, int out_dt, void* workspace,
+                                size_t workspace_bytes, float scale, hipStream_t stream);
+
+/*
  * Serving decode step: every sequence of the batch at its own length, and
  * grouped-query attention (see the GQA reading above cca_pool_kv_gqa).  The
  * cache descriptor is the same; its H is the number of key/value heads and its

@@ -105,6 +105,11 @@ EXPORTS = {
                                                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                                   ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "cca_cache_load_prefill_lca": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 6 +
+                                   [ctypes.c_int64, ctypes.c_void_p]),
+    "cca_cache_append_decode_lca": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int] +
+                                    [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                             ctypes.c_float, ctypes.c_void_p]),
     "cca_cache_ring_slots": (ctypes.c_int64, [ctypes.POINTER(CacheDesc)]),
     "cca_cache_load_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                + [ctypes.c_int64, ctypes.c_void_p]),
@@ -456,6 +461,48 @@ class KVCache:
         _need(out, (B, H, d), out_dtype, "out")
         _check(_lib.cca_decode_step(ctypes.byref(self.desc), _ptr(q), _ptr(out), _dtype_code(out_dtype),
                                     _ptr(self.workspace), self.ws_bytes, scale, _stream()), "cca_decode_step")
+        return out
+
+
+class LCACache(KVCache):
+    """LCA-style decode cache: condensed tokens (mean-query importance, positional dims from
+    the top-scored token) plus the raw ring, and `qsum` (float32 [B,H,d]), the running sum
+    of the current group's queries."""
+
+    def __init__(self, B: int, H: int, d: int, g: int, k_local: int, max_tokens: int, d_rope: int,
+                 dtype=torch.bfloat16, device="cuda"):
+        super().__init__(B, H, d, g, k_local, max_tokens, dtype, device)
+        self.d_rope = int(d_rope)
+        self.qsum = torch.zeros((B, H, d), dtype=torch.float32, device=device)
+
+    def load_prefill(self, q, k, v, kc, vc):
+        """Seed the empty cache after an LCA-style prefill of L = k.shape[2] tokens (kc, vc from prefill_lca)."""
+        B, H, d = self.shape_bhd
+        L = k.shape[2]
+        m = L // self.desc.g
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, (B, H, L, d), self.dtype, name)
+        _need(kc, (B, H, m, d), self.dtype, "kc")
+        _need(vc, (B, H, m, d), self.dtype, "vc")
+        _check(_lib.cca_cache_load_prefill_lca(ctypes.byref(self.desc), _ptr(self.qsum), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(kc), _ptr(vc), L, _stream()), "cca_cache_load_prefill_lca")
+
+    def append(self, q, k, v, scale: float | None = None):
+        raise CCAError("an LCA-style cache appends with append_decode")
+
+    def append_decode(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
+        """Append one token (condensing a completed group) and return its attention output [B,H,d]."""
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, (B, H, d), self.dtype, name)
+        if out is None:
+            out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+        _need(out, (B, H, d), out_dtype, "out")
+        _check(_lib.cca_cache_append_decode_lca(ctypes.byref(self.desc), _ptr(self.qsum), self.d_rope, _ptr(q), _ptr(k),
+                                                _ptr(v), _ptr(out), _dtype_code(out_dtype), _ptr(self.workspace),
+                                                self.ws_bytes, scale, _stream()), "cca_cache_append_decode_lca")
         return out
 
 

@@ -282,6 +282,37 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
   return CCA_OK;
 }
 
+int cca_cache_load_prefill_lca(cca_cache_t* c, float* qsum, const void* q, const void* k, const void* v,
+                               const void* kc, const void* vc, int64_t L, hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (qsum == nullptr || !aligned16(qsum) || !aligned16(q)) return CCA_ERR_INVALID;
+  s = cca_cache_load_prefill(c, k, v, kc, vc, L, stream);
+  if (s != CCA_OK) return s;
+  return hip_status(cca::launch_qsum_seed(c, q, qsum, L, stream));
+}
+
+int cca_cache_append_decode_lca(cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k, const void* v,
+                                void* out, int out_dt, void* workspace, size_t workspace_bytes, float scale,
+                                hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
+  if (d_rope < 0 || d_rope > c->d) return CCA_ERR_INVALID;
+  if (qsum == nullptr || !aligned16(qsum) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(workspace) || !isfinite(scale))
+    return CCA_ERR_INVALID;
+  const int64_t t = c->n_tokens;
+  if ((t + 1) / c->g > c->max_groups) return CCA_ERR_CAPACITY;
+  if (workspace_bytes < cca_decode_workspace_bytes(c)) return CCA_ERR_WORKSPACE;
+  hipError_t e = cca::launch_append_decode_lca(c, qsum, d_rope, q, k, v, out, out_dt == CCA_F32, workspace, scale,
+                                               stream);
+  if (e != hipSuccess) return CCA_ERR_HIP;
+  c->n_tokens = t + 1;
+  c->n_pooled = (t + 1) / c->g;
+  return CCA_OK;
+}
+
 size_t cca_serve_workspace_bytes(const cca_cache_t* c, int H_q) {
   if (c == nullptr || c->B < 1 || c->H < 1 || (c->d != 64 && c->d != 128) || c->g < 1 || c->k_local < 0 ||
       c->max_groups < 1 || H_q < 1 || H_q % c->H != 0)

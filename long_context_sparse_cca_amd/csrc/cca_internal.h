@@ -68,6 +68,12 @@ hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out
 // Append (ring write + in-place pooling) and decode of the new token in one launch.
 hipError_t launch_append_decode(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
                                 int out_f32, void* workspace, float scale, hipStream_t stream);
+// LCA-style cache (decode.hip): qsum [B*H][d] float32 holds the running sum of the
+// current group's queries; a completed group is condensed with their mean.
+hipError_t launch_append_decode_lca(const cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k,
+                                    const void* v, void* out, int out_f32, void* workspace, float scale,
+                                    hipStream_t stream);
+hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, hipStream_t stream);
 
 // Log-sum-exp combination of per-chunk decode partials (workspace layout: acc
 // [nslices][nchunks][d] floats, then ml [nslices][nchunks][2]) into out [nslices][d].

@@ -16,6 +16,7 @@
 #include <algorithm>
 
 #include "cca_internal.h"
+#include "lca_group.h"
 #include "pool_group.h"
 
 namespace cca {
@@ -129,13 +130,17 @@ struct DecodeWs {
 // partial softmax state; cca_decode_merge_kernel combines the chunks of a slice.
 // With APPEND, wave 0 of chunk 0 also writes the new token into its ring slot and,
 // when the token completes a group, pools that group into the core array (the new
-// core token is not visible to this step, so nothing here reads it).
-template <typename T, int D, bool APPEND, bool STREAM>
+// core token is not visible to this step, so nothing here reads it).  APPEND = 1
+// pools as CCA does (the last query scores the group); APPEND = 2 condenses the
+// LCA way: qsum [B*H, D] (float32) holds the running sum of the current group's
+// queries, the completed group is scored with their mean, and its positional dims
+// (the last d_rope) come from the top-scored token.
+template <typename T, int D, int APPEND, bool STREAM>
 __global__ __launch_bounds__(256) void cca_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ core_k,
     T* __restrict__ core_v, T* __restrict__ ring_k, T* __restrict__ ring_v, DecodeWs ws, int64_t max_groups,
     int64_t R, int64_t t, int g, int64_t n_c, int64_t raw_lo, int64_t n_keys, int64_t chunk, int nchunks,
-    float scale) {
+    float scale, float* __restrict__ qsum, int d_rope) {
   using C = DecodeCfg<T, D>;
   __shared__ float red[C::NWAVE][D + 2];
   extern __shared__ float pool_lds[];
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
   const int64_t end = min(n_keys, start + chunk);
   const T* qrow = q + (size_t)bh * D;
 
-  if constexpr (APPEND) {
+  if constexpr (APPEND != 0) {
     if (ci == 0 && wave == 0) {
       const T* kt = k_new + (size_t)bh * D;
       const T* vt = v_new + (size_t)bh * D;
@@ -161,12 +166,42 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
         st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bh * R + slot) * D) + lane,
              ld16(reinterpret_cast<const uint4*>(vt) + lane));
       }
-      if ((t + 1) % g == 0) {
-        const int64_t beta = t / g;
-        const int64_t first = slot - (g - 1);
-        pool_group_wave<T, D>(qrow, 0, 1, ring_k + ((size_t)bh * R + first) * D, ring_v + ((size_t)bh * R + first) * D,
-                              kt, vt, g, scale, core_k + ((size_t)bh * max_groups + beta) * D,
-                              core_v + ((size_t)bh * max_groups + beta) * D, pool_lds);
+      if constexpr (APPEND == 1) {
+        if ((t + 1) % g == 0) {
+          const int64_t beta = t / g;
+          const int64_t first = slot - (g - 1);
+          pool_group_wave<T, D>(qrow, 0, 1, ring_k + ((size_t)bh * R + first) * D,
+                                ring_v + ((size_t)bh * R + first) * D, kt, vt, g, scale,
+                                core_k + ((size_t)bh * max_groups + beta) * D,
+                                core_v + ((size_t)bh * max_groups + beta) * D, pool_lds);
+        }
+      } else {
+        // running sum of the group's queries (in token order, as the prefill sums them)
+        constexpr int CPL = D / kWave;
+        const int col = lane * CPL;
+        float qf[CPL], qs[CPL];
+        lca_load_cols<T, D>(qrow + col, qf);
+        float* qsum_row = qsum + (size_t)bh * D + col;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) qs[e] = qsum_row[e] + qf[e];
+        if ((t + 1) % g == 0) {
+          const float inv_g = 1.0f / ((float)g * 1.0f);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            pool_lds[col + e] = qs[e] * inv_g;
+            qsum_row[e] = 0.f;
+          }
+          wave_lds_sync();
+          const int64_t beta = t / g;
+          const int64_t first = slot - (g - 1);
+          lca_condense_wave<T, D>(pool_lds, ring_k + ((size_t)bh * R + first) * D,
+                                  ring_v + ((size_t)bh * R + first) * D, kt, vt, g, scale, d_rope,
+                                  core_k + ((size_t)bh * max_groups + beta) * D,
+                                  core_v + ((size_t)bh * max_groups + beta) * D, pool_lds + D, nullptr);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) qsum_row[e] = qs[e];
+        }
       }
     }
   }
@@ -200,7 +235,7 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
       if (nn < n_c) {
         kp = ck + (size_t)nn * D;
         vp = cv + (size_t)nn * D;
-      } else if (APPEND && nn == n_keys - 1) {
+      } else if (APPEND != 0 && nn == n_keys - 1) {
         kp = k_new + (size_t)bh * D;   // the token appended by this very launch
         vp = v_new + (size_t)bh * D;
       } else {
@@ -347,9 +382,9 @@ __global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __res
   }
 }
 
-template <typename T, int D, bool APPEND>
+template <typename T, int D, int APPEND>
 hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_new, const void* v_new, void* out,
-                           int out_f32, void* workspace, float scale, hipStream_t stream) {
+                           int out_f32, void* workspace, float scale, float* qsum, int d_rope, hipStream_t stream) {
   const int64_t BH = (int64_t)c->B * c->H;
   const int64_t R = (int64_t)(c->k_local + 1) * c->g;
   const int64_t t = APPEND ? c->n_tokens : c->n_tokens - 1;   // position of the query
@@ -362,18 +397,20 @@ hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_ne
   DecodeWs ws;
   ws.acc = (float*)workspace;
   ws.ml = ws.acc + (size_t)BH * nchunks * D;
-  const size_t dyn_lds = APPEND ? (size_t)c->g * sizeof(float) : 0;
+  // pooling scratch: g scores (CCA); the mean query and g scores (LCA-style)
+  const size_t dyn_lds = APPEND == 1 ? (size_t)c->g * sizeof(float)
+                                     : (APPEND == 2 ? (size_t)(D + c->g) * sizeof(float) : 0);
   const bool stream_kv = BH * n_keys * D * (int64_t)sizeof(T) * 2 > kStreamBytes;
   if (stream_kv)
     hipLaunchKernelGGL((cca_decode_kernel<T, D, APPEND, true>), dim3((unsigned)BH, nchunks), dim3(256), dyn_lds,
                        stream, (const T*)q, (const T*)k_new, (const T*)v_new, (T*)c->core_k, (T*)c->core_v,
                        (T*)c->ring_k, (T*)c->ring_v, ws, c->max_groups, R, t, c->g, n_c, raw_lo, n_keys, chunk,
-                       nchunks, scale);
+                       nchunks, scale, qsum, d_rope);
   else
     hipLaunchKernelGGL((cca_decode_kernel<T, D, APPEND, false>), dim3((unsigned)BH, nchunks), dim3(256), dyn_lds,
                        stream, (const T*)q, (const T*)k_new, (const T*)v_new, (T*)c->core_k, (T*)c->core_v,
                        (T*)c->ring_k, (T*)c->ring_v, ws, c->max_groups, R, t, c->g, n_c, raw_lo, n_keys, chunk,
-                       nchunks, scale);
+                       nchunks, scale, qsum, d_rope);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
@@ -382,15 +419,48 @@ hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_ne
   return hipGetLastError();
 }
 
-template <bool APPEND>
+template <int APPEND>
 hipError_t launch_decode_any(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
-                             int out_f32, void* workspace, float scale, hipStream_t stream) {
+                             int out_f32, void* workspace, float scale, float* qsum, int d_rope,
+                             hipStream_t stream) {
   if (c->dt == CCA_BF16) {
-    if (c->d == 128) return launch_decode_t<bf16_t, 128, APPEND>(c, q, k, v, out, out_f32, workspace, scale, stream);
-    return launch_decode_t<bf16_t, 64, APPEND>(c, q, k, v, out, out_f32, workspace, scale, stream);
+    if (c->d == 128)
+      return launch_decode_t<bf16_t, 128, APPEND>(c, q, k, v, out, out_f32, workspace, scale, qsum, d_rope, stream);
+    return launch_decode_t<bf16_t, 64, APPEND>(c, q, k, v, out, out_f32, workspace, scale, qsum, d_rope, stream);
   }
-  if (c->d == 128) return launch_decode_t<float, 128, APPEND>(c, q, k, v, out, 1, workspace, scale, stream);
-  return launch_decode_t<float, 64, APPEND>(c, q, k, v, out, 1, workspace, scale, stream);
+  if (c->d == 128)
+    return launch_decode_t<float, 128, APPEND>(c, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
+  return launch_decode_t<float, 64, APPEND>(c, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
+}
+
+// Running sums of the queries of each slice's trailing partial group (rows m*g .. L-1)
+// of a prefill, to seed the LCA-style cache: one wave per slice, D/64 columns per lane.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void cca_qsum_seed_kernel(const T* __restrict__ q, float* __restrict__ qsum,
+                                                           int64_t L, int64_t row0) {
+  constexpr int CPL = D / kWave;
+  const int64_t bh = blockIdx.x;
+  const int col = threadIdx.x * CPL;
+  float s[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s[e] = 0.f;
+  for (int64_t r = row0; r < L; ++r) {
+    float f[CPL];
+    lca_load_cols<T, D>(q + ((size_t)bh * L + r) * D + col, f);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) s[e] += f[e];
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) qsum[(size_t)bh * D + col + e] = s[e];
+}
+
+template <typename T, int D>
+hipError_t launch_qsum_seed_t(const cca_cache_t* c, const void* q, float* qsum, int64_t L, hipStream_t stream) {
+  const int64_t BH = (int64_t)c->B * c->H;
+  const int64_t row0 = L / c->g * c->g;
+  hipLaunchKernelGGL((cca_qsum_seed_kernel<T, D>), dim3((unsigned)BH), dim3(64), 0, stream, (const T*)q, qsum, L,
+                     row0);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -451,12 +521,27 @@ hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, v
 
 hipError_t launch_decode(const cca_cache_t* c, const void* q, void* out, int out_f32, void* workspace, float scale,
                          hipStream_t stream) {
-  return launch_decode_any<false>(c, q, nullptr, nullptr, out, out_f32, workspace, scale, stream);
+  return launch_decode_any<0>(c, q, nullptr, nullptr, out, out_f32, workspace, scale, nullptr, 0, stream);
 }
 
 hipError_t launch_append_decode(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
                                 int out_f32, void* workspace, float scale, hipStream_t stream) {
-  return launch_decode_any<true>(c, q, k, v, out, out_f32, workspace, scale, stream);
+  return launch_decode_any<1>(c, q, k, v, out, out_f32, workspace, scale, nullptr, 0, stream);
+}
+
+hipError_t launch_append_decode_lca(const cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k,
+                                    const void* v, void* out, int out_f32, void* workspace, float scale,
+                                    hipStream_t stream) {
+  return launch_decode_any<2>(c, q, k, v, out, out_f32, workspace, scale, qsum, d_rope, stream);
+}
+
+hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, hipStream_t stream) {
+  if (c->dt == CCA_BF16) {
+    if (c->d == 128) return launch_qsum_seed_t<bf16_t, 128>(c, q, qsum, L, stream);
+    return launch_qsum_seed_t<bf16_t, 64>(c, q, qsum, L, stream);
+  }
+  if (c->d == 128) return launch_qsum_seed_t<float, 128>(c, q, qsum, L, stream);
+  return launch_qsum_seed_t<float, 64>(c, q, qsum, L, stream);
 }
 
 }  // namespace cca

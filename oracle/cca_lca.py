@@ -38,7 +38,7 @@ import numpy as np
 
 from . import cca_oracle as _o
 
-__all__ = ["group_mean_query", "lca_scores", "lca_pool", "lca_slice", "lca_gqa"]
+__all__ = ["group_mean_query", "lca_scores", "lca_pool", "lca_slice", "lca_gqa", "lca_decode_stream"]
 
 
 def group_mean_query(Q, j: int, g: int) -> np.ndarray:
@@ -127,3 +127,44 @@ def lca_gqa(Q, K, V, g: int, k: int, scale: float, d_rope: int, anchors=None, co
             for h in range(hk * r, (hk + 1) * r):
                 out[b, h] = _s.attend_with_core(Q[b, h], K[b, hk], V[b, hk], Kc[b, hk], Vc[b, hk], g, k, scale)
     return out, Kc, Vc, anc
+
+
+def lca_decode_stream(Q, K, V, L0: int, g: int, k: int, scale: float, d_rope: int, anchors=None, core_dtype=None):
+    """Outputs [L - L0, d] of tokens L0 .. L-1 appended one by one after a prefill of L0 tokens.
+
+    The inference flow of the page (section 2): a group is condensed as soon as its last
+    token has arrived, from the queries, keys and values of its g tokens (mean query,
+    weighted content, anchored positional part); the token then attends to the condensed
+    groups before its window and to the raw window, as in the prefill.  `anchors`, if
+    given, fixes each group's anchor (the tests pass the GPU's choice).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L, d = Q.shape
+    dc = d - d_rope
+    Kc, Vc = [], []
+
+    def condense(j):
+        s = lca_scores(Q[j * g:(j + 1) * g], K[j * g:(j + 1) * g], g, scale)[0]
+        a = _o.softmax(s)
+        anc = int(np.argmax(s)) if anchors is None else int(np.asarray(anchors)[j])
+        kc = np.empty(d)
+        kc[:dc] = a @ K[j * g:(j + 1) * g, :dc]
+        kc[dc:] = K[j * g + anc, dc:]
+        vc = a @ V[j * g:(j + 1) * g]
+        Kc.append(_o.round_storage(kc, core_dtype))
+        Vc.append(_o.round_storage(vc, core_dtype))
+
+    for j in range(L0 // g):          # the prefill's condensed groups
+        condense(j)
+    out = np.empty((L - L0, d))
+    for t in range(L0, L):
+        if (t + 1) % g == 0:          # the token completes its group
+            condense(t // g)
+        n_c = _o.visible_core_count(t, g, k)
+        lo, hi = _o.raw_window(t, g, k)
+        keys = np.concatenate([np.array(Kc[:n_c]).reshape(n_c, d), K[lo:hi + 1]])
+        vals = np.concatenate([np.array(Vc[:n_c]).reshape(n_c, d), V[lo:hi + 1]])
+        out[t - L0] = _o.softmax(scale * (keys @ Q[t])) @ vals
+    return out

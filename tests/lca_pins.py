@@ -109,6 +109,17 @@ def pin_gqa_identical_heads_is_per_head(lc):
     return worst < 1e-12, f"max err {worst:.3e}"
 
 
-ALL_LCA_PINS = [pin_gqa_closed_form, pin_gqa_identical_heads_is_per_head,
+def pin_decode_stream_is_prefill_rows(lc):
+    """Condensing each group as its last token arrives gives the prefill rows of the appended tokens."""
+    L0, L, g, k, d, dr = 13, 41, 4, 1, 6, 2
+    Q, K, V = (x[0, 0].astype(np.float64) for x in np_inputs(1, 1, L, d, "f32", 26))
+    sc = 0.5
+    got = lc.lca_decode_stream(Q, K, V, L0, g, k, sc, dr)
+    want = lc.lca_slice(Q, K, V, g, k, sc, dr)[L0:]
+    e = _err(got, want)
+    return e < 1e-12, f"max err {e:.3e}"
+
+
+ALL_LCA_PINS = [pin_decode_stream_is_prefill_rows, pin_gqa_closed_form, pin_gqa_identical_heads_is_per_head,
                 pin_closed_form, pin_identical_queries_no_rope_is_cca_pooling, pin_anchor_is_the_top_scored_key,
                 pin_no_window_overlap_and_attention_is_cca]

@@ -81,7 +81,8 @@ def test_lca_matches_oracle(gpu, case):
             Qs, Ks, Vs = (x[b, h].astype(np.float64) for x in (Q, K, V))
             anc = anchors[b, h].cpu().numpy()
             if m:
-                _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
+                if d_rope:
+                    _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
                 Kc, Vc, _ = cca_lca.lca_pool(Qs, Ks, Vs, g, scale, d_rope, anchors=anc)
                 gk = kc[b, h].float().cpu().numpy()
                 gv = vc[b, h].float().cpu().numpy()
@@ -199,3 +200,81 @@ def test_lca_gqa_matches_oracle(gpu, case):
                 assert np.array_equal(gk[b, hk, :, dc:], K[b, hk, rows, dc:].astype(np.float32))
     err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
     assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
+
+
+def _anchors_from_core(gk, K, g, d_rope):
+    """Anchor of each condensed key: the group row whose positional dims it carries (exact copies)."""
+    m, d = gk.shape
+    dc = d - d_rope
+    anc = np.zeros(m, dtype=np.int64)
+    if d_rope == 0:
+        return anc
+    for j in range(m):
+        hits = [i for i in range(g) if np.array_equal(gk[j, dc:], K[j * g + i, dc:])]
+        assert hits, f"condensed key {j}: positional dims match no key of its group"
+        anc[j] = hits[0]
+    return anc
+
+
+# LCA-style decode: (B, H, d, L0, steps, g, k, d_rope, dtype, seed)
+LCA_DECODE_CASES = [
+    (2, 2, 128, 300, 40, 16, 2, 64, "bf16", 40),   # prefix ends inside a group (qsum seeded with 12 queries)
+    (1, 2, 64, 64, 37, 8, 1, 16, "f32", 41),       # prefix on a group boundary
+    (1, 1, 128, 5, 60, 16, 1, 0, "bf16", 42),      # short prefix, every dim pooled
+]
+
+
+def _dec_id(c):
+    B, H, d, L0, S, g, k, r, dt, seed = c
+    return f"B{B}H{H}d{d}L0{L0}S{S}g{g}k{k}r{r}-{dt}"
+
+
+@pytest.mark.parametrize("case", LCA_DECODE_CASES, ids=_dec_id)
+def test_lca_decode_matches_oracle(gpu, case):
+    B, H, d, L0, S, g, k, d_rope, dt, seed = case
+    _say(f"lca decode case {_dec_id(case)} seed {seed}")
+    L = L0 + S
+    Q, K, V = np_inputs(B, H, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    cache = binding.LCACache(B, H, d, g, k, max_tokens=L, d_rope=d_rope, dtype=TDT[dt], device=gpu)
+    _, kc0, vc0, _ = binding.prefill_lca(q[:, :, :L0].contiguous(), kk[:, :, :L0].contiguous(),
+                                         v[:, :, :L0].contiguous(), g, k, d_rope, scale)
+    cache.load_prefill(q[:, :, :L0].contiguous(), kk[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc0, vc0)
+    outs = []
+    for t in range(L0, L):
+        outs.append(cache.append_decode(q[:, :, t].contiguous(), kk[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                                        out_dtype=torch.float32, scale=scale))
+    torch.cuda.synchronize()
+    got = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)   # [B, H, S, d]
+    m = L // g
+    assert cache.n_tokens == L
+    for b in range(B):
+        for h in range(H):
+            Qs, Ks, Vs = (x[b, h].astype(np.float64) for x in (Q, K, V))
+            gk = cache.core_k[b, h, :m].float().cpu().numpy()
+            gv = cache.core_v[b, h, :m].float().cpu().numpy()
+            anc = _anchors_from_core(gk, Ks, g, d_rope)
+            if m:
+                if d_rope:
+                    _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
+                Kc, Vc, _ = cca_lca.lca_pool(Qs, Ks, Vs, g, scale, d_rope, anchors=anc)
+                dc = d - d_rope
+                for x, ref in ((gk[:, :dc], Kc[:, :dc]), (gv, Vc)):
+                    bound = TOL[dt] + ULP[dt] * np.abs(ref)
+                    assert np.all(np.abs(x - ref) <= bound), f"condensed err {np.abs(x - ref).max():.3e}"
+            want = cca_lca.lca_decode_stream(Qs, Ks, Vs, L0, g, k, scale, d_rope, anchors=anc, core_dtype=dt)
+            err = np.abs(got[b, h] - want).max()
+            assert np.isfinite(err) and err <= TOL[dt], f"b={b} h={h}: max abs err {err:.3e}"
+    # the running query sum restarts with every group: it now holds the last partial group
+    part = L % g
+    want_qsum = Q[:, :, L - part:L].astype(np.float64).sum(axis=2) if part else np.zeros((B, H, d))
+    assert np.abs(cache.qsum.cpu().numpy() - want_qsum).max() <= 1e-3
+
+
+def test_lca_decode_invalid_rope_width(gpu):
+    cache = binding.LCACache(1, 1, 64, 8, 1, max_tokens=32, d_rope=65, dtype=torch.float32, device=gpu)
+    x = torch.zeros((1, 1, 64), dtype=torch.float32, device=gpu)
+    with pytest.raises(binding.CCAError):
+        cache.append_decode(x, x, x)
+    assert cache.n_tokens == 0
