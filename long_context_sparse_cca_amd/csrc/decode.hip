@@ -8,11 +8,15 @@
 // section); the core token becomes visible once the group has left the
 // window (locality-preserving module, group-aligned window).
 //
-//   cca_cache_load_kernel   : seed the cache from a prefill (core tokens + raw tail)
+//   cca_copy_rows_kernel    : seed the cache from a prefill (core tokens + raw tail)
 //   cca_append_kernel       : write the newest k,v into its ring slot; pool a completed group
 //   cca_decode_kernel       : one chunk of the visible keys per workgroup -> (m, l, acc[d]);
-//                             optionally also performs the append of the new token
+//                             optionally also performs the append of the new token, with
+//                             CCA pooling or the LCA-style condensation ("Latent-Condensed
+//                             Transformer for Efficient Long Context Modeling", section 2,
+//                             inference flow) of a completed group
 //   cca_decode_merge_kernel : log-sum-exp combination of the chunk states -> out[d]
+//   cca_qsum_seed_kernel    : running query sums of the trailing partial group (LCA-style cache)
 #include <algorithm>
 
 #include "cca_internal.h"
