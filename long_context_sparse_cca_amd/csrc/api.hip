@@ -43,7 +43,7 @@ const char* cca_status_string(int status) {
     case CCA_OK: return "ok";
     case CCA_ERR_INVALID: return "invalid argument";
     case CCA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
-    case CCA_ERR_WORKSPACE: return "decode workspace too small";
+    case CCA_ERR_WORKSPACE: return "workspace too small";
     case CCA_ERR_HIP: return "HIP kernel launch failed";
     case CCA_ERR_CAPACITY: return "cache capacity exceeded";
     default: return "unknown status";
@@ -287,9 +287,14 @@ int cca_cache_load_prefill_lca(cca_cache_t* c, float* qsum, const void* q, const
   int s = check_cache(c);
   if (s != CCA_OK) return s;
   if (qsum == nullptr || !aligned16(qsum) || !aligned16(q)) return CCA_ERR_INVALID;
-  s = cca_cache_load_prefill(c, k, v, kc, vc, L, stream);
-  if (s != CCA_OK) return s;
-  return hip_status(cca::launch_qsum_seed(c, q, qsum, L, stream));
+  // validate as cca_cache_load_prefill does before enqueueing anything, so that the
+  // descriptor changes only once all of the seeding is enqueued
+  if (c->n_tokens != 0 || L < 1 || !aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
+  const int64_t m = L / c->g;
+  if (m > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
+  if (m > c->max_groups) return CCA_ERR_CAPACITY;
+  if (cca::launch_qsum_seed(c, q, qsum, L, stream) != hipSuccess) return CCA_ERR_HIP;
+  return cca_cache_load_prefill(c, k, v, kc, vc, L, stream);
 }
 
 int cca_cache_append_decode_lca(cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k, const void* v,
