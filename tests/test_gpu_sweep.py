@@ -1,0 +1,258 @@
+"""Seeded random sweeps of the HIP entry points against the oracle.
+
+The hand-picked cases of the other GPU tests aim at known edges; these draw shapes at
+random (fixed seeds, so a failure names a reproducible case): sequence lengths from 1
+to ~1300 (ragged against every tile size), group sizes from 1 to 64 including primes,
+windows from 0 to 64 groups, head dims 64 and 128, fp32 and bf16, 1 to 4 query heads
+per key/value head, per-sequence lengths in the serving cache (some empty), chunked
+appends up to the largest allowed chunk, and the backward pass.  Tolerances as for the
+other parity tests: max-abs 1e-4 (fp32), 2e-2 (bf16), gradients 2e-2 of their scale.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cca_backward, cca_lca, cca_serving
+from long_context_sparse_cca_amd import binding
+from long_context_sparse_cca_amd.synth import np_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+GROUPS = [1, 2, 3, 5, 8, 13, 16, 17, 32, 64]
+WINDOWS = [0, 1, 2, 3, 7, 64]
+
+
+def _dev(x, dt, device):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=TDT[dt]).contiguous()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _inputs(B, H, Hkv, L, d, dt, seed):
+    Q = np_inputs(B, H, L, d, dt, seed)[0]
+    K, V = np_inputs(B, Hkv, L, d, dt, seed + 1000)[1:]
+    return Q, K, V
+
+
+def _prefill_cases(n=20, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        g = int(rng.choice(GROUPS))
+        k = int(rng.choice(WINDOWS))
+        # half the lengths log-uniform (many below one tile), half uniform up to 1300
+        L = int(np.exp(rng.uniform(0, np.log(1300)))) if i % 2 else int(rng.integers(1, 1300))
+        L = max(1, min(L, 4000 // (B * Hkv * r)))
+        cases.append((B, Hkv * r, Hkv, L, d, g, k, dt, 500 + i))
+    return cases
+
+
+def _pid(c):
+    B, H, Hkv, L, d, g, k, dt, seed = c
+    return f"B{B}H{H}kv{Hkv}L{L}d{d}g{g}k{k}-{dt}-s{seed}"
+
+
+@pytest.mark.parametrize("case", _prefill_cases(), ids=_pid)
+def test_prefill_sweep(gpu, case):
+    B, H, Hkv, L, d, g, k, dt, seed = case
+    _say(f"prefill sweep {_pid(case)}")
+    Q, K, V = _inputs(B, H, Hkv, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    out = binding.prefill(q, kk, v, g, k, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = cca_serving.cca_gqa(Q, K, V, g, k, scale, core_dtype=dt)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+    assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
+
+
+def _serve_cases(n=6, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        g = int(rng.choice([2, 5, 8, 16]))
+        k = int(rng.choice([0, 1, 3, 8]))
+        lens = [int(x) if rng.uniform() > 0.2 else 0 for x in rng.integers(1, 400, size=B)]
+        T = int(rng.integers(5, 26))
+        cases.append((B, Hkv * r, Hkv, d, g, k, dt, lens, T, 600 + i))
+    return cases
+
+
+def _sid(c):
+    B, Hq, Hkv, d, g, k, dt, lens, T, seed = c
+    return f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}-{dt}-L{'_'.join(map(str, lens))}-T{T}-s{seed}"
+
+
+def _serve_setup(B, Hq, Hkv, d, g, k, dt, lens0, total, seed, device):
+    Q, K, V = _inputs(B, Hq, Hkv, total, d, dt, seed)
+    cache = binding.ServeCache(B, Hq, Hkv, d, g, k, total + g, dtype=TDT[dt], device=device)
+    scale = 1.0 / math.sqrt(d)
+    for b, L in enumerate(lens0):
+        if L:
+            qb, kb, vb = (_dev(x[b:b + 1, :, :L], dt, device) for x in (Q, K, V))
+            _, kc, vc = binding.prefill(qb, kb, vb, g, k, scale, return_core=True)
+            cache.load_sequence(b, kb, vb, kc, vc)
+    return Q, K, V, cache, scale
+
+
+@pytest.mark.parametrize("case", _serve_cases(), ids=_sid)
+def test_serve_sweep(gpu, case):
+    B, Hq, Hkv, d, g, k, dt, lens0, T, seed = case
+    _say(f"serve sweep {_sid(case)}")
+    Q, K, V, cache, scale = _serve_setup(B, Hq, Hkv, d, g, k, dt, lens0, max(lens0) + T, seed, gpu)
+    outs = []
+    for i in range(T):
+        q, kk, v = (_dev(np.stack([x[b, :, lens0[b] + i] for b in range(B)]), dt, gpu) for x in (Q, K, V))
+        outs.append(cache.step(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy())
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == [L + T for L in lens0]
+    got = np.stack(outs, axis=2)
+    for b in range(B):
+        want = cca_serving.serve_rows(Q[b], K[b], V[b], [lens0[b] + i for i in range(T)], g, k, scale,
+                                      core_dtype=dt)
+        err = np.abs(got[b] - want).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+
+
+def _extend_cases(n=4, seed=99):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        g = int(rng.choice([4, 8, 16]))
+        k = int(rng.choice([1, 2, 4]))
+        lens = [int(x) for x in rng.integers(0, 300, size=B)]
+        chunks = [int(x) for x in rng.integers(1, k * g + 2, size=3)]   # up to the largest allowed chunk
+        cases.append((B, Hkv * r, Hkv, d, g, k, dt, lens, chunks, 700 + i))
+    return cases
+
+
+def _eid(c):
+    B, Hq, Hkv, d, g, k, dt, lens, chunks, seed = c
+    return f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}-{dt}-L{'_'.join(map(str, lens))}-n{'_'.join(map(str, chunks))}-s{seed}"
+
+
+@pytest.mark.parametrize("case", _extend_cases(), ids=_eid)
+def test_extend_sweep(gpu, case):
+    B, Hq, Hkv, d, g, k, dt, lens0, chunks, seed = case
+    _say(f"extend sweep {_eid(case)}")
+    total = max(lens0) + sum(chunks)
+    Q, K, V, cache, scale = _serve_setup(B, Hq, Hkv, d, g, k, dt, lens0, total, seed, gpu)
+    pos = list(lens0)
+    got = {b: [] for b in range(B)}
+    rows = {b: [] for b in range(B)}
+    for n in chunks:
+        q, kk, v = (_dev(np.stack([x[b, :, pos[b]:pos[b] + n] for b in range(B)]), dt, gpu) for x in (Q, K, V))
+        out = cache.extend(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy()
+        for b in range(B):
+            got[b].append(out[b])
+            rows[b].extend(range(pos[b], pos[b] + n))
+            pos[b] += n
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == pos
+    for b in range(B):
+        want = cca_serving.serve_rows(Q[b], K[b], V[b], rows[b], g, k, scale, core_dtype=dt)
+        err = np.abs(np.concatenate(got[b], axis=1) - want).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+
+
+def _backward_cases(n=4, seed=123):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 3, 8, 16, 17]))
+        k = int(rng.choice([0, 1, 2, 5]))
+        L = int(rng.integers(40, 700))
+        cases.append((1, Hkv * r, Hkv, L, g, k, 800 + i))
+    return cases
+
+
+def _bid(c):
+    B, H, Hkv, L, g, k, seed = c
+    return f"B{B}H{H}kv{Hkv}L{L}g{g}k{k}-s{seed}"
+
+
+@pytest.mark.parametrize("case", _backward_cases(), ids=_bid)
+def test_backward_sweep(gpu, case):
+    B, H, Hkv, L, g, k, seed = case
+    d = 128
+    _say(f"backward sweep {_bid(case)}")
+    Q, K, V = _inputs(B, H, Hkv, L, d, "bf16", seed)
+    dO = np_inputs(B, H, L, d, "bf16", seed + 2000)[0]
+    q, kk, v, do = (_dev(x, "bf16", gpu) for x in (Q, K, V, dO))
+    scale = 1.0 / math.sqrt(d)
+    out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
+    dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
+    torch.cuda.synchronize()
+    want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype="bf16")
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
+
+
+def _lca_cases(n=4, seed=321):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        g = int(rng.choice([2, 5, 16, 33]))
+        k = int(rng.choice([0, 1, 3]))
+        d_rope = int(rng.choice([0, 8, d // 2, d]))
+        L = int(rng.integers(1, 900))
+        cases.append((1, Hkv * r, Hkv, L, d, g, k, d_rope, dt, 900 + i))
+    return cases
+
+
+def _lid(c):
+    B, H, Hkv, L, d, g, k, r, dt, seed = c
+    return f"B{B}H{H}kv{Hkv}L{L}d{d}g{g}k{k}rope{r}-{dt}-s{seed}"
+
+
+@pytest.mark.parametrize("case", _lca_cases(), ids=_lid)
+def test_lca_sweep(gpu, case):
+    B, H, Hkv, L, d, g, k, d_rope, dt, seed = case
+    _say(f"lca sweep {_lid(case)}")
+    Q, K, V = _inputs(B, H, Hkv, L, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    out, kc, vc, anchors = binding.prefill_lca(q, kk, v, g, k, d_rope, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    anc = anchors.cpu().numpy()
+    r = H // Hkv
+    if L // g and d_rope:
+        for hk in range(Hkv):
+            q_mean = Q[0, hk * r:(hk + 1) * r].astype(np.float64).mean(axis=0)
+            S = cca_lca.lca_scores(q_mean, K[0, hk].astype(np.float64), g, scale)
+            picked = S[np.arange(S.shape[0]), anc[0, hk]]
+            assert np.all(picked >= S.max(axis=1) - 1e-5 * np.maximum(1.0, np.abs(S).max(axis=1)))
+    want = cca_lca.lca_gqa(Q, K, V, g, k, scale, d_rope, anchors=anc if L // g else None, core_dtype=dt)[0]
+    err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+    assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
