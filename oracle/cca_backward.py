@@ -49,7 +49,7 @@ import numpy as np
 from . import cca_oracle as _o
 
 __all__ = ["softmax_backward", "pool_backward_group", "cca_backward_slice", "cca_backward",
-           "cca_forward_lse_slice", "cca_backward_gqa"]
+           "cca_forward_lse_slice", "cca_backward_gqa", "cca_backward_sampled_slice"]
 
 
 def softmax_backward(p, dp):
@@ -221,3 +221,102 @@ def cca_backward_gqa(Q, K, V, dO, g: int, k: int, scale: float, core_dtype=None)
                 for h in heads:
                     dQ[b, h, row] += dqh / r
     return dQ, dK, dV
+
+
+def cca_backward_sampled_slice(Q, K, V, dO, g: int, k: int, scale: float, rows, keys, core_dtype=None):
+    """(dQ[rows], dK[keys], dV[keys]) of one key/value slice, for sizes where the full backward is too slow.
+
+    Q, dO: [L, d] (one query head) or [r, L, d] (the r query heads that share K, V [L, d],
+    readings R14/R15: the core tokens are pooled with their mean last-token query); dQ is
+    then [r, len(rows), d].  The same chain rule as cca_backward_slice / cca_backward_gqa,
+    organised per requested entry: every query's log-sum-exp and D = dO . O, then
+      dKc[j], dVc[j] (core token j) as sums over the queries (of every head) that see it,
+      the pooling backward of each group a requested key or row belongs to,
+      dK[u], dV[u] of a raw key as sums over the queries whose window holds it, plus the
+      pooling part when u lies in a complete group,
+      dQ[t] over t's visible keys, plus (1/r) d q_hat when t is the last row of a complete group.
+    """
+    single = np.asarray(Q).ndim == 2
+    Qh = np.asarray(Q, dtype=np.float64).reshape((-1,) + np.asarray(Q).shape[-2:])
+    dOh = np.asarray(dO, dtype=np.float64).reshape(Qh.shape)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    r, L, d = Qh.shape
+    m = _o.n_core_groups(L, g)
+    q_mean = Qh.sum(axis=0) / r
+    Kc, Vc, A = _o.pool(q_mean, K, V, g, scale, core_dtype)
+    # forward output and log-sum-exp of every query, one query group at a time (the group's
+    # rows share the core tokens and the window start; the causal end hides later raw keys)
+    lse = np.empty((r, L))
+    Dq = np.empty((r, L))
+    for h in range(r):
+        out = np.empty((L, d))
+        for beta in range((L + g - 1) // g):
+            t0, t1 = beta * g, min(L, beta * g + g)
+            n_c = _o.visible_core_count(t0, g, k)
+            lo, _ = _o.raw_window(t0, g, k)
+            keys_b = np.concatenate([Kc[:n_c], K[lo:t1]])
+            vals_b = np.concatenate([Vc[:n_c], V[lo:t1]])
+            z = scale * (Qh[h, t0:t1] @ keys_b.T)
+            hidden = np.arange(lo, t1)[None, :] > np.arange(t0, t1)[:, None]
+            z[:, n_c:][hidden] = -np.inf
+            mx = z.max(axis=1, keepdims=True)
+            e = np.exp(z - mx)
+            lse[h, t0:t1] = mx[:, 0] + np.log(e.sum(axis=1))
+            out[t0:t1] = (e / e.sum(axis=1, keepdims=True)) @ vals_b
+        Dq[h] = np.einsum("td,td->t", dOh[h], out)
+    t_all = np.arange(L)
+
+    core_cache = {}
+
+    def core_grads(j):
+        # queries that see core token j: n_c(t) > j, i.e. t >= (j + k + 1) g
+        if j not in core_cache:
+            ts = t_all[t_all >= (j + k + 1) * g]
+            dkc = np.zeros(d)
+            dvc = np.zeros(d)
+            for h in range(r):
+                p = np.exp(scale * (Qh[h, ts] @ Kc[j]) - lse[h, ts])
+                ds = p * (dOh[h, ts] @ Vc[j] - Dq[h, ts])
+                dkc += scale * (ds @ Qh[h, ts])
+                dvc += p @ dOh[h, ts]
+            core_cache[j] = (dkc, dvc)
+        return core_cache[j]
+
+    pool_cache = {}
+
+    def pool_grads(j):
+        if j not in pool_cache:
+            dkc, dvc = core_grads(j)
+            rg = slice(j * g, (j + 1) * g)
+            pool_cache[j] = pool_backward_group(A[j], K[rg], V[rg], q_mean[_o.group_query_row(j, g)], dkc, dvc,
+                                                scale)
+        return pool_cache[j]
+
+    dQ = np.zeros((r, len(rows), d))
+    for i, t in enumerate(rows):
+        n_c = _o.visible_core_count(t, g, k)
+        lo, hi = _o.raw_window(t, g, k)
+        keys_t = np.concatenate([Kc[:n_c], K[lo:hi + 1]])
+        vals_t = np.concatenate([Vc[:n_c], V[lo:hi + 1]])
+        for h in range(r):
+            p = np.exp(scale * (keys_t @ Qh[h, t]) - lse[h, t])
+            ds = p * (vals_t @ dOh[h, t] - Dq[h, t])
+            dQ[h, i] = scale * (ds @ keys_t)
+            if t % g == g - 1 and t // g < m:
+                dQ[h, i] += pool_grads(t // g)[2] / r
+    dK = np.zeros((len(keys), d))
+    dV = np.zeros((len(keys), d))
+    for i, u in enumerate(keys):
+        # queries whose raw window holds u: u <= t <= (u // g + k + 1) g - 1
+        ts = t_all[(t_all >= u) & (t_all <= min(L - 1, (u // g + k + 1) * g - 1))]
+        for h in range(r):
+            p = np.exp(scale * (Qh[h, ts] @ K[u]) - lse[h, ts])
+            ds = p * (dOh[h, ts] @ V[u] - Dq[h, ts])
+            dK[i] += scale * (ds @ Qh[h, ts])
+            dV[i] += p @ dOh[h, ts]
+        if u // g < m:
+            dKg, dVg, _ = pool_grads(u // g)
+            dK[i] += dKg[u % g]
+            dV[i] += dVg[u % g]
+    return (dQ[0] if single else dQ), dK, dV

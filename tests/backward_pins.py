@@ -114,5 +114,30 @@ def pin_gqa_finite_differences(b):
     return worst < 1e-7, f"max err {worst:.3e}"
 
 
+def pin_sampled_entries_match_full_backward(b):
+    """The per-entry form (used at full sizes on sampled rows and keys) gives the entries of the
+    full backward, core-token, raw-window and group-last rows included."""
+    worst = 0.0
+    for (L, g, k, d, seed) in [(50, 4, 2, 5, 13), (37, 3, 0, 4, 14), (64, 8, 1, 6, 15)]:
+        Q, K, V = (x[0, 0].astype(np.float64) for x in np_inputs(1, 1, L, d, "f32", seed))
+        W = np.random.default_rng(seed + 80).standard_normal((L, d))
+        sc = 0.6
+        fQ, fK, fV = b.cca_backward_slice(Q, K, V, W, g, k, sc)
+        rows = list(range(L))
+        sQ, sK, sV = b.cca_backward_sampled_slice(Q, K, V, W, g, k, sc, rows, rows)
+        worst = max(worst, _err(sQ, fQ), _err(sK, fK), _err(sV, fV))
+    # grouped-query: r = 3 query heads over one key/value head
+    L, g, k, d = 40, 4, 1, 4
+    Q = np_inputs(1, 3, L, d, "f32", 16)[0].astype(np.float64)
+    K, V = (x[:, :1].astype(np.float64) for x in np_inputs(1, 3, L, d, "f32", 17)[1:])
+    W = np.random.default_rng(18).standard_normal((1, 3, L, d))
+    fQ, fK, fV = b.cca_backward_gqa(Q, K, V, W, g, k, 0.6)
+    rows = list(range(L))
+    sQ, sK, sV = b.cca_backward_sampled_slice(Q[0], K[0, 0], V[0, 0], W[0], g, k, 0.6, rows, rows)
+    worst = max(worst, _err(sQ, fQ[0]), _err(sK, fK[0, 0]), _err(sV, fV[0, 0]))
+    return worst < 1e-10, f"max err {worst:.3e}"
+
+
 ALL_BACKWARD_PINS = [pin_finite_differences, pin_causal_special_cases_match_autograd,
-                     pin_lse_matches_library_logsumexp, pin_gqa_finite_differences]
+                     pin_lse_matches_library_logsumexp, pin_gqa_finite_differences,
+                     pin_sampled_entries_match_full_backward]

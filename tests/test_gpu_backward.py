@@ -148,3 +148,45 @@ def test_gqa_autograd_function(gpu):
     torch.cuda.synchronize()
     assert torch.equal(q.grad, dq.to(torch.bfloat16)) and torch.equal(kk.grad, dk.to(torch.bfloat16))
     assert torch.equal(v.grad, dv.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("Hkv", [32, 8], ids=["mha", "gqa8"])
+def test_backward_fullsize_32k_sampled(gpu, Hkv):
+    """L = 32768, H = 32, d = 128, g = 16, k = 64, bf16 (the 32K prefill layer), full backward on
+    the GPU; one query head's sampled dQ rows and its key/value head's sampled dK/dV keys
+    (core-token groups, window edges, group-last rows) against the per-entry oracle."""
+    from long_context_sparse_cca_amd.synth import torch_inputs
+    H, L, d, g, k = 32, 32768, 128, 16, 64
+    _say(f"backward full size L={L} H={H} H_kv={Hkv}")
+    q, kk, v = torch_inputs(1, H, L, d, torch.bfloat16, gpu, seed=31, heavy_frac=0.01)
+    if Hkv != H:
+        kk, v = kk[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(32)
+    do = torch.randn((1, H, L, d), generator=gen, device=gpu).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
+    dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
+    torch.cuda.synchronize()
+    r = H // Hkv
+    h = 5                        # query head; its key/value head is h // r
+    hk = h // r
+    rng = np.random.default_rng(7)
+    rows = sorted({0, 1, g - 1, g, k * g - 1, k * g, (k + 1) * g - 1, L // 2 - 1, L - g - 1, L - 1,
+                   *rng.integers(0, L, size=16).tolist()})
+    keys = sorted({0, g - 1, g, k * g, L // 2, L - g, L - 1, *rng.integers(0, L, size=16).tolist()})
+    heads = range(hk * r, (hk + 1) * r)
+    Qh = np.stack([q[0, i].double().cpu().numpy() for i in heads])
+    dOh = np.stack([do[0, i].double().cpu().numpy() for i in heads])
+    Kk = kk[0, hk].double().cpu().numpy()
+    Vk = v[0, hk].double().cpu().numpy()
+    wq, wk, wv = cca_backward.cca_backward_sampled_slice(Qh, Kk, Vk, dOh, g, k, scale, rows, keys,
+                                                         core_dtype="bf16")
+    got_q = np.stack([dq[0, i, rows].cpu().numpy() for i in heads])
+    got_k = dk[0, hk, keys].cpu().numpy()
+    got_v = dv[0, hk, keys].cpu().numpy()
+    for name, got, ref in (("dq", got_q, wq), ("dk", got_k, wk), ("dv", got_v, wv)):
+        err = np.abs(got.astype(np.float64) - ref).max()
+        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
