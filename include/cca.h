@@ -171,8 +171,9 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
 
 /*
  * Training ([CCA] Triton section: the fused operator serves training as well;
- * the models are fine-tuned with it).  bf16 inputs, d = 128, one query head per
- * key/value head; other dtypes or head dims give CCA_ERR_UNSUPPORTED.
+ * the models are fine-tuned with it).  bf16 or float32 inputs, d = 64 or 128,
+ * one query head per key/value head.  bf16 at d = 128 runs on the matrix cores;
+ * the other combinations run a plain float32 vector path, correct but far slower.
  *
  * cca_prefill_lse: cca_prefill that also writes, for every query t, the
  *   natural-log log-sum-exp of its scaled scores over its visible keys,
@@ -185,12 +186,14 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
  *   so the gradients of Kc and Vc reach the group's keys and values and its
  *   scoring query Q[j*g+g-1]).  The forward's rounding of the core tokens to
  *   bf16 is treated as the identity.
- *   q, k, v, kc, vc, out : the forward's inputs and results (bf16, as above);
+ *   q, k, v, kc, vc, out : the forward's inputs and results, all of type dt
+ *           (out_dt of the forward must equal dt);
  *   lse   : device float32 [B, H, L] from cca_prefill_lse;
- *   dout  : device bf16 [B, H, L, d], the gradient of the output;
+ *   dout  : device [B, H, L, d] of type dt, the gradient of the output;
  *   dq, dk, dv : device float32 [B, H, L, d], written (every element);
  *   workspace : device, >= cca_backward_workspace_bytes(B, H, L, d, g) bytes.
- *   Limits and errors as for cca_prefill.
+ *   Limits and errors as for cca_prefill; outside bf16 at d = 128 also
+ *   B*H*(L + L/g + 1) < 2^26 (one 64-lane wave per row and per key).
  */
 int cca_prefill_lse(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse,
                     int B, int H, int64_t L, int d, int g, int k_local, float scale,
@@ -208,7 +211,7 @@ int cca_backward(const void* q, const void* k, const void* v, const void* kc, co
  * reaches each of the r queries with weight 1/r; the key/value gradients sum over the r
  * heads.  k, v, kc, vc, dk, dv have H_kv heads ([B, H_kv, ...]); q, out, lse, dout, dq
  * have H.  cca_prefill_lse / cca_backward are these with H_kv = H.  Errors as for
- * cca_prefill_gqa; bf16 and d = 128 only (else CCA_ERR_UNSUPPORTED).
+ * cca_prefill_gqa.
  */
 int cca_prefill_lse_gqa(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse,
                         int B, int H, int H_kv, int64_t L, int d, int g, int k_local, float scale,

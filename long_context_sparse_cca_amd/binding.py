@@ -368,8 +368,8 @@ def backward(q, k, v, kc, vc, out, lse, dout, g: int, k_local: int, scale: float
 
 
 class CCAAttention(torch.autograd.Function):
-    """CCA prefill attention as an autograd function (bf16, d = 128; k, v may have fewer heads
-    than q): forward cca_prefill_lse, backward cca_backward.
+    """CCA prefill attention as an autograd function (bf16 or float32, d = 64 or 128; k, v may
+    have fewer heads than q): forward cca_prefill_lse, backward cca_backward.
     apply(q, k, v, g, k_local, scale=None) -> out [B,H,L,d]."""
 
     @staticmethod

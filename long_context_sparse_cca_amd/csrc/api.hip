@@ -123,14 +123,13 @@ int cca_prefill_lse_gqa(const void* q, const void* k, const void* v, void* kc, v
                         int out_dt, hipStream_t stream) {
   int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, out_dt);
   if (s != CCA_OK) return s;
-  if (dt != CCA_BF16 || d != 128) return CCA_ERR_UNSUPPORTED;
   if (L > 0 && (lse == nullptr || ((uintptr_t)lse & 3u) != 0)) return CCA_ERR_INVALID;
   if (L == 0) return CCA_OK;
   const int nq = H / H_kv;
   hipError_t e = cca::launch_pool(dt, d, q, k, v, kc, vc, B * H_kv, L, g, nq, scale, stream);
   if (e != hipSuccess) return CCA_ERR_HIP;
-  return hip_status(cca::launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, nq, L, g, k_local,
-                                                  scale, stream, lse));
+  return hip_status(cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, nq, L, g,
+                                                  k_local, scale, stream, lse));
 }
 
 int cca_prefill_lse(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse, int B,
@@ -153,15 +152,20 @@ int cca_backward_gqa(const void* q, const void* k, const void* v, const void* kc
                      float scale, int dt, hipStream_t stream) {
   int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, dt);
   if (s != CCA_OK) return s;
-  if (dt != CCA_BF16 || d != 128) return CCA_ERR_UNSUPPORTED;
   if (L == 0) return CCA_OK;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       lse == nullptr || ((uintptr_t)lse & 3u) != 0)
     return CCA_ERR_INVALID;
-  if ((int64_t)B * H * ((L + 127) / 128 + L / g / 128 + 1) >= INT32_MAX) return CCA_ERR_INVALID;
+  const bool fast = dt == CCA_BF16 && d == 128;
+  if (fast && (int64_t)B * H * ((L + 127) / 128 + L / g / 128 + 1) >= INT32_MAX) return CCA_ERR_INVALID;
+  // the other shapes launch one 64-lane wave per query row and per key
+  if (!fast && (int64_t)B * H * (L + L / g + 1) * 64 >= (int64_t)UINT32_MAX) return CCA_ERR_INVALID;
   if (workspace_bytes < cca_backward_gqa_workspace_bytes(B, H, H_kv, L, d, g)) return CCA_ERR_WORKSPACE;
-  return hip_status(cca::launch_backward_bf16_d128(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, B * H,
-                                                   H / H_kv, L, g, k_local, scale, stream));
+  if (fast)
+    return hip_status(cca::launch_backward_bf16_d128(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, B * H,
+                                                     H / H_kv, L, g, k_local, scale, stream));
+  return hip_status(cca::launch_backward_generic(dt, d, q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace,
+                                                 B * H, H / H_kv, L, g, k_local, scale, stream));
 }
 
 int cca_backward(const void* q, const void* k, const void* v, const void* kc, const void* vc, const void* out,

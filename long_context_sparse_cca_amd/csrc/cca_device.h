@@ -44,6 +44,7 @@ template <> struct Elem<bf16_t> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ __forceinline__ static float load1(const bf16_t* p) { return bf16_bits_to_f32(p->bits); }
   __device__ __forceinline__ static void store1(bf16_t* p, float v) { p->bits = f32_to_bf16_bits(v); }
 };
 
@@ -56,6 +57,7 @@ template <> struct Elem<float> {
     f[2] = __uint_as_float(c.z);
     f[3] = __uint_as_float(c.w);
   }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
   __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
 };
 

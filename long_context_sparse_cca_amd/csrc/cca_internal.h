@@ -34,9 +34,11 @@ hipError_t launch_pool_lca(int dt, int d, const void* q, const void* k, const vo
 hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
                        int BHkv, int64_t L, int g, int nq, float scale, hipStream_t stream);
 
+// lse (optional, float32 [BH][L]): each query's natural-log log-sum-exp of its scaled scores.
 hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v,
                                     const void* kc, const void* vc, void* out, int out_f32, int BH, int nq,
-                                    int64_t L, int g, int k_local, float scale, hipStream_t stream);
+                                    int64_t L, int g, int k_local, float scale, hipStream_t stream,
+                                    float* lse = nullptr);
 
 // bf16, head dim 128 fast path of the fused attention (prefill_bf16.hip).
 // lse (optional, float32 [BH][L]): natural-log log-sum-exp of each query's scaled scores.
@@ -99,6 +101,14 @@ hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v
                                      const void* out, const float* lse, const void* dout, float* dq, float* dk,
                                      float* dv, void* workspace, int BH, int nq, int64_t L, int g, int k_local,
                                      float scale, hipStream_t stream);
+
+// Backward pass for the other shapes (backward_generic.hip): float32 inputs at head dim
+// 64 or 128, bf16 at head dim 64; same arguments, gradients and workspace layout as above,
+// out and dout in the input type.
+hipError_t launch_backward_generic(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
+                                   const void* vc, const void* out, const float* lse, const void* dout, float* dq,
+                                   float* dk, float* dv, void* workspace, int BH, int nq, int64_t L, int g,
+                                   int k_local, float scale, hipStream_t stream);
 
 // Chunked append of n tokens per sequence (extend.hip).
 size_t extend_workspace_bytes(const cca_cache_t* c, int n);

@@ -69,7 +69,8 @@ template <typename T, int D, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ Kc, const T* __restrict__ Vc, void* __restrict__ Out, int out_f32,
-    int BH, int nq, int64_t L, int g, int k_local, float scale, int ntiles, ExtendArgs ext) {
+    int BH, int nq, int64_t L, int g, int k_local, float scale, int ntiles, ExtendArgs ext,
+    float* __restrict__ lse) {
   using C = PrefillCfg<T, D>;
   __shared__ __attribute__((aligned(16))) T lds_k[2][C::LDS_K];
   __shared__ __attribute__((aligned(16))) T lds_v[2][C::LDS_V];
@@ -347,6 +348,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float inv = 1.0f / l_tot;
   const int64_t q_row = qa + l32 - pos0;                 // row within the slice
   if (q_row >= nQ) return;
+  if (lse != nullptr && hf == 0) {
+    // natural-log log-sum-exp of the scaled scores: (m_run + log2 l) * ln 2
+    lse[(size_t)bh * nQ + q_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
   if (out_f32) {
     float* o = reinterpret_cast<float*>(Out) + ((size_t)bh * nQ + q_row) * D;
 #pragma unroll
@@ -380,7 +385,7 @@ namespace {
 template <typename T, int D>
 hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                             void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local, float scale,
-                            hipStream_t stream) {
+                            hipStream_t stream, float* lse = nullptr) {
   using C = PrefillCfg<T, D>;
   const int ntiles = (int)((L + C::BM - 1) / C::BM);
   const int64_t nblocks = (int64_t)BH * ntiles;
@@ -388,7 +393,7 @@ hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const v
   const ExtendArgs none{nullptr, 1, 0, 0, 0};
   hipLaunchKernelGGL((cca_prefill_kernel<T, D, false>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq, L, g,
-                     k_local, scale, ntiles, none);
+                     k_local, scale, ntiles, none, lse);
   return hipGetLastError();
 }
 
@@ -402,7 +407,7 @@ hipError_t launch_extend_t(const void* q, const void* k, const void* v, const vo
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL((cca_prefill_kernel<T, D, true>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq,
-                     (int64_t)0, g, k_local, scale, ntiles, ext);
+                     (int64_t)0, g, k_local, scale, ntiles, ext, (float*)nullptr);
   return hipGetLastError();
 }
 
@@ -410,14 +415,15 @@ hipError_t launch_extend_t(const void* q, const void* k, const void* v, const vo
 
 hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                     const void* vc, void* out, int out_f32, int BH, int nq, int64_t L, int g,
-                                    int k_local, float scale, hipStream_t stream) {
+                                    int k_local, float scale, hipStream_t stream, float* lse) {
   if (dt == CCA_BF16) {
     if (d == 128)
-      return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream);
-    return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream);
+      return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
+    return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
   }
-  if (d == 128) return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream);
-  return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream);
+  if (d == 128)
+    return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream, lse);
+  return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream, lse);
 }
 
 hipError_t launch_extend_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,

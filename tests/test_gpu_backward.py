@@ -1,4 +1,5 @@
-"""Backward pass of CCA prefill (bf16, d = 128): HIP path vs the gradient oracle.
+"""Backward pass of CCA prefill: HIP path vs the gradient oracle (bf16 d = 128 on the
+matrix cores; float32 inputs and d = 64 on the vector path, further down).
 
 Shapes span several 256-query and 128-key tiles with ragged tails, g not a power of
 two, g = 1 (causal attention), a window wider than the sequence, and core tiles seen by
@@ -92,9 +93,84 @@ def test_autograd_function_matches_backward(gpu):
 
 
 def test_backward_unsupported_shapes(gpu):
-    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=gpu)
+    q = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device=gpu)
     with pytest.raises(binding.CCAError):
         binding.prefill_lse(q, q.clone(), q.clone(), 16, 1)
+
+
+# The vector path: float32 inputs at d = 64 and 128, bf16 at d = 64.
+# (dtype, d, B, H, H_kv, L, g, k, seed)
+GEN_CASES = [
+    ("f32", 64, 1, 2, 2, 256, 16, 1, 110),    # the small float32 layer (B=1, H=2, d=64, L=256, g=16, k=1)
+    ("f32", 64, 2, 1, 1, 517, 7, 3, 111),     # g not a power of two, ragged tail
+    ("f32", 64, 1, 1, 1, 200, 1, 0, 112),     # g = 1: causal attention
+    ("f32", 64, 1, 1, 1, 640, 16, 100, 113),  # window wider than the sequence
+    ("f32", 64, 1, 4, 2, 300, 16, 2, 114),    # grouped-query, r = 2
+    ("f32", 128, 1, 1, 1, 700, 16, 4, 115),
+    ("f32", 128, 2, 8, 2, 260, 7, 1, 116),    # grouped-query, r = 4
+    ("bf16", 64, 1, 2, 2, 300, 16, 2, 117),
+    ("bf16", 64, 1, 4, 1, 520, 16, 3, 118),   # multi-query
+    ("f32", 64, 1, 1, 1, 15, 16, 1, 119),     # shorter than one group: no core tokens
+]
+
+
+def _gen_id(c):
+    dt, d, B, H, Hkv, L, g, k, seed = c
+    return f"{dt}d{d}B{B}H{H}Hkv{Hkv}L{L}g{g}k{k}"
+
+
+@pytest.mark.parametrize("case", GEN_CASES, ids=_gen_id)
+def test_generic_backward_matches_oracle(gpu, case):
+    """Gradients of the float32 vector path against the fp64 oracle.  Float32 inputs:
+    every product and sum in float32 (relative rounding ~1e-7 per step over at most a few
+    thousand terms), so the bound is 1e-4 * max(1, max|reference|) and the oracle's core
+    tokens are unrounded.  bf16 inputs: the core tokens and the output the gradients read
+    are bf16, so the bf16 bound 2e-2 applies, with the oracle's core tokens in bf16."""
+    dt, d, B, H, Hkv, L, g, k, seed = case
+    _say(f"generic backward case {_gen_id(case)} seed {seed}")
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    Q = np_inputs(B, H, L, d, dt, seed)[0]
+    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, dt, seed + 1)[1:])
+    dO = np_inputs(B, H, L, d, dt, seed + 500)[0]
+    q, kk, v, do = (torch.from_numpy(np.ascontiguousarray(x)).to(device=gpu, dtype=tdt) for x in (Q, K, V, dO))
+    scale = 1.0 / math.sqrt(d)
+    out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
+    dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, binding.prefill(q, kk, v, g, k, scale))
+    core = "bf16" if dt == "bf16" else None
+    tol = 1e-4 if dt == "f32" else 2e-2
+    if Hkv == H:
+        for b in range(B):
+            for h in range(H):
+                _, lse_ref = cca_backward.cca_forward_lse_slice(Q[b, h], K[b, h], V[b, h], g, k, scale,
+                                                                core_dtype=core)
+                e = np.abs(lse[b, h].cpu().numpy() - lse_ref).max() if L else 0.0
+                assert e <= (1e-4 if dt == "f32" else 1e-2), f"lse err {e:.3e}"
+        want = cca_backward.cca_backward(Q, K, V, dO, g, k, scale, core_dtype=core)
+    else:
+        want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype=core)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+        bound = tol * max(1.0, np.abs(ref).max())
+        _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
+
+
+def test_generic_autograd_function(gpu):
+    """The autograd function on float32 inputs at d = 64 routes through the vector path."""
+    B, H, Hkv, L, d, g, k = 1, 4, 2, 260, 64, 16, 2
+    Q = np_inputs(B, H, L, d, "f32", 120)[0]
+    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, "f32", 121)[1:])
+    q, kk, v = (torch.from_numpy(np.ascontiguousarray(x)).to(gpu).requires_grad_(True) for x in (Q, K, V))
+    out = binding.CCAAttention.apply(q, kk, v, g, k)
+    dO = torch.from_numpy(np.ascontiguousarray(np_inputs(B, H, L, d, "f32", 122)[0])).to(gpu)
+    out.backward(dO)
+    torch.cuda.synchronize()
+    o2, lse, kc, vc = binding.prefill_lse(q.detach(), kk.detach(), v.detach(), g, k)
+    dq, dk, dv = binding.backward(q.detach(), kk.detach(), v.detach(), kc, vc, o2, lse, dO, g, k)
+    torch.cuda.synchronize()
+    assert torch.equal(q.grad, dq) and torch.equal(kk.grad, dk) and torch.equal(v.grad, dv)
 
 
 # grouped-query training: (B, H, H_kv, L, g, k, seed)
