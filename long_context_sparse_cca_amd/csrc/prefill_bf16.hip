@@ -286,7 +286,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       bf16x2_t pp[2][4];
       float bsum;
       auto weights = [&]() {
-        bsum = 0.f;
+        // two partial row sums (one per 16-key half) halve the dependent dot2 chain
+        float h0 = 0.f, h1 = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -294,11 +295,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float p0 = fast_exp2(fmaf(s[8 * u + 2 * e], sc, -m_run));
             const float p1 = fast_exp2(fmaf(s[8 * u + 2 * e + 1], sc, -m_run));
             pp[u][e] = bf16x2_t{(__bf16)p0, (__bf16)p1};
-            bsum = __builtin_amdgcn_fdot2_f32_bf16(pp[u][e], ones, bsum, false);
+            if (u == 0) h0 = __builtin_amdgcn_fdot2_f32_bf16(pp[u][e], ones, h0, false);
+            else h1 = __builtin_amdgcn_fdot2_f32_bf16(pp[u][e], ones, h1, false);
           }
+        bsum = h0 + h1;
       };
       weights();
       if (__builtin_amdgcn_ballot_w64(bsum > kSumLimit) != 0) {
+        // an empty asm with a memory clobber keeps the compiler from hoisting the maximum's
+        // arithmetic above the (rarely taken) branch
+        asm volatile("" ::: "memory");
         float bmax = max3f(s[0], s[1], s[2]);
 #pragma unroll
         for (int r = 3; r < 15; r += 2) bmax = max3f(bmax, s[r], s[r + 1]);
