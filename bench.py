@@ -349,6 +349,9 @@ def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int 
     nchunks = cache.ws_bytes // (DEC_B * H * (D + 2) * 4)
     dbytes = sum(accounting.decode_bytes(DEC_B, H, D, DEC_L0 + s_, G, KL, 2, nchunks) for s_ in range(steps)) / steps
     dgbs = dbytes / (dec_us * 1e-6) / 1e9
+    del cache, xs
+    torch.cuda.empty_cache()
+    serving = lca_serving(binding, accounting, dev, seed, d_rope)
     return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL, "d_rope": d_rope},
             "pool_ms": pool_ms, "prefill_ms": prefill_ms, "prefill_tokens_per_s": L / (prefill_ms * 1e-3),
             "pool_bytes": byt,
@@ -359,7 +362,54 @@ def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int 
                        "us_per_step": dec_us, "bytes_per_step": dbytes,
                        "roofline": {"kernel": "cca_decode_kernel<bf16,128,lca append> + cca_decode_merge_kernel",
                                     "bound": "hbm", "achieved": dgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                    "frac": dgbs / PEAK_HBM_GBS}}}
+                                    "frac": dgbs / PEAK_HBM_GBS}},
+            "serving": serving}
+
+
+def lca_serving(binding, accounting, dev, seed, d_rope: int, steps: int = 64):
+    """Serving steps with the LCA-style cache (cca_cache_append_decode_varlen_lca), on the workload of
+    serving_decode: B=8 sequences at lengths 65536 + 9362*b, H_q=32 over H_kv=8, d=128, g=16, k=64, bf16."""
+    import torch
+
+    from long_context_sparse_cca_amd.synth import torch_inputs
+    B, Hq, Hkv = 8, 32, 8
+    lens0 = [65536 + 9362 * b for b in range(B)]
+    cache = binding.LCAServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + G, d_rope, dtype=torch.bfloat16,
+                                  device=dev)
+    for b, L in enumerate(lens0):
+        q, _, _ = torch_inputs(1, Hq, L, D, torch.bfloat16, dev, seed=seed + 60 + b, heavy_frac=HEAVY)
+        _, k, v = torch_inputs(1, Hkv, L, D, torch.bfloat16, dev, seed=seed + 80 + b, heavy_frac=HEAVY)
+        kc, vc, _ = binding.pool_kv_lca(q, k, v, G, d_rope)
+        cache.load_sequence(b, q, k, v, kc, vc)
+        del q, k, v, kc, vc
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 90)
+    qs = torch.randn((steps, B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    ks = torch.randn((steps, B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    vs = torch.randn((steps, B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    lens_at = []
+    for s in range(steps):
+        lens_at.append(list(cache.lens_host))
+        ev[2 * s].record(stream)
+        cache.step(qs[s], ks[s], vs[s], out=out)
+        ev[2 * s + 1].record(stream)
+    torch.cuda.synchronize()
+    warm = 8
+    us = [ev[2 * s].elapsed_time(ev[2 * s + 1]) * 1e3 for s in range(warm, steps)]
+    nchunks = cache.serve_ws_bytes // (B * Hq * (D + 2) * 4)
+    byt = [accounting.serve_bytes(lens_at[s], Hq, Hkv, D, G, KL, 2, nchunks) for s in range(warm, steps)]
+    us_mean = sum(us) / len(us)
+    gbs = sum(byt) / len(byt) / (us_mean * 1e-6) / 1e9
+    return {"config": {"B": B, "H_q": Hq, "H_kv": Hkv, "d": D, "g": G, "k_local": KL, "d_rope": d_rope,
+                       "lengths": lens0, "steps_timed": steps - warm},
+            "us_per_step": us_mean, "bytes_per_step": sum(byt) / len(byt),
+            "roofline": {"kernel": "cca_serve_decode_kernel<bf16,128,4,lca> + cca_decode_merge_kernel",
+                         "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS}}
 
 
 def main():

@@ -369,6 +369,38 @@ int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t 
                                    void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
 
 /*
+ * Serving with the LCA-style condensation ("Latent-Condensed Transformer for
+ * Efficient Long Context Modeling", sections 2 and 3: mean-query importance,
+ * positional dims from the top-scored token, grouped-query heads):
+ * cca_cache_append_decode_varlen, except that the group a token completes is
+ * condensed as by cca_pool_kv_lca_gqa.  Its importance query is the mean of the
+ * group's g queries over the r = H_q / c->H query heads that share each
+ * key/value head.
+ *   qsum   : device float32 [B, c->H, d], caller-owned.  Per sequence and
+ *            key/value head, it is the running sum of the queries of the current
+ *            (incomplete) group, over its tokens and the r query heads.  It is
+ *            zero for an empty sequence.  cca_cache_load_prefill_lca_gqa, run on a
+ *            one-sequence view of the cache, seeds it for that sequence.  Each
+ *            call adds the new token's r queries.  When the token completes the
+ *            group, the call condenses the group with sum / (g*r) and zeroes the
+ *            sum.  A sequence whose length is out of range is left as is.
+ *   d_rope : 0 <= d_rope <= d, as for cca_pool_kv_lca.
+ * Other arguments, workspace and errors are as for
+ * cca_cache_append_decode_varlen.
+ *
+ * cca_cache_load_prefill_lca_gqa: cca_cache_load_prefill (kc, vc from
+ *   cca_prefill_lca_gqa of the same prefix) plus qsum from q [B, H_q, L, d];
+ *   H_q is a multiple of c->H.  cca_cache_load_prefill_lca is this call with
+ *   H_q = c->H.
+ */
+int cca_cache_append_decode_varlen_lca(const cca_cache_t* c, float* qsum, int d_rope, int32_t* lens,
+                                       int64_t max_len, int H_q, const void* q, const void* k, const void* v,
+                                       void* out, int out_dt, void* workspace, size_t workspace_bytes,
+                                       float scale, hipStream_t stream);
+int cca_cache_load_prefill_lca_gqa(cca_cache_t* c, float* qsum, int H_q, const void* q, const void* k,
+                                   const void* v, const void* kc, const void* vc, int64_t L, hipStream_t stream);
+
+/*
  * Chunked append: n new tokens for every sequence in one call (chunked prefill
  * into an existing cache, several draft tokens, ...), with per-sequence lengths
  * and grouped-query heads as in cca_cache_append_decode_varlen.  Returns the

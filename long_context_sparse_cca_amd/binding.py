@@ -125,6 +125,13 @@ EXPORTS = {
                                                       ctypes.c_int] + [ctypes.c_void_p] * 4
                                        + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float,
                                           ctypes.c_void_p]),
+    "cca_cache_append_decode_varlen_lca": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int,
+                                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+                                           + [ctypes.c_void_p] * 4
+                                           + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float,
+                                              ctypes.c_void_p]),
+    "cca_cache_load_prefill_lca_gqa": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int]
+                                       + [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p]),
     "cca_extend_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int]),
     "cca_cache_extend": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_int] + [ctypes.c_void_p] * 4
@@ -614,6 +621,70 @@ class ServeCache(KVCache):
             if m != n:
                 out[:, :, a:e] = os_
         return out
+
+
+class LCAServeCache(ServeCache):
+    """Serving cache with the LCA-style condensation: per-sequence lengths, grouped-query heads,
+    groups condensed with the mean of their queries over positions and the query heads that
+    share a key/value head, positional dims (the last d_rope) from the top-scored token.
+    `qsum` (float32 [B, H_kv, d]) holds each sequence's running sum of its current group's
+    queries.  Chunked appends are not provided for this cache."""
+
+    def __init__(self, B: int, H_q: int, H_kv: int, d: int, g: int, k_local: int, max_tokens: int, d_rope: int,
+                 dtype=torch.bfloat16, device="cuda"):
+        super().__init__(B, H_q, H_kv, d, g, k_local, max_tokens, dtype, device)
+        self.d_rope = int(d_rope)
+        self.qsum = torch.zeros((B, H_kv, d), dtype=torch.float32, device=device)
+
+    def load_sequence(self, b: int, q, k, v, kc, vc):
+        """Seed sequence b (empty) after an LCA-style prefill of L_b = k.shape[2] tokens.
+
+        q: [1, H_q, L_b, d]; k, v: [1, H_kv, L_b, d]; kc, vc: [1, H_kv, L_b // g, d] (from
+        `prefill_lca`).  cca_cache_load_prefill_lca_gqa on a one-sequence view of the cache.
+        """
+        _, H, d = self.shape_bhd
+        L = k.shape[2]
+        m = L // self.desc.g
+        _need(q, (1, self.H_q, L, d), self.dtype, "q")
+        _need(k, (1, H, L, d), self.dtype, "k")
+        _need(v, (1, H, L, d), self.dtype, "v")
+        _need(kc, (1, H, m, d), self.dtype, "kc")
+        _need(vc, (1, H, m, d), self.dtype, "vc")
+        if self.lens_host[b] != 0:
+            raise CCAError(f"sequence {b} is not empty")
+        desc = self._seq_desc(b)
+        qsum_b = self.qsum[b]
+        _check(_lib.cca_cache_load_prefill_lca_gqa(ctypes.byref(desc), _ptr(qsum_b), self.H_q, _ptr(q), _ptr(k),
+                                                   _ptr(v), _ptr(kc), _ptr(vc), L, _stream()),
+               "cca_cache_load_prefill_lca_gqa")
+        self.lens_host[b] = L
+        self.lens[b] = L
+
+    def step(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
+        """Append one token to every sequence and return its outputs [B, H_q, d].
+
+        q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen_lca (advances `lens`).
+        """
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        _need(q, (B, self.H_q, d), self.dtype, "q")
+        _need(k, (B, H, d), self.dtype, "k")
+        _need(v, (B, H, d), self.dtype, "v")
+        if out is None:
+            out = torch.empty((B, self.H_q, d), dtype=out_dtype, device=q.device)
+        _need(out, (B, self.H_q, d), out_dtype, "out")
+        max_len = max(self.lens_host)
+        _check(_lib.cca_cache_append_decode_varlen_lca(ctypes.byref(self.desc), _ptr(self.qsum), self.d_rope,
+                                                       _ptr(self.lens), max_len, self.H_q, _ptr(q), _ptr(k), _ptr(v),
+                                                       _ptr(out), _dtype_code(out_dtype), _ptr(self.serve_ws),
+                                                       self.serve_ws_bytes, scale, _stream()),
+               "cca_cache_append_decode_varlen_lca")
+        self.lens_host = [x + 1 for x in self.lens_host]
+        return out
+
+    def extend(self, q, k, v, out_dtype=None, scale: float | None = None):
+        raise CCAError("chunked appends are not provided for the LCA-style serving cache; use step")
 
 
 def cache_append(cache: KVCache, q, k, v, scale=None):

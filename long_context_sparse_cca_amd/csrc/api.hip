@@ -286,19 +286,26 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
   return CCA_OK;
 }
 
-int cca_cache_load_prefill_lca(cca_cache_t* c, float* qsum, const void* q, const void* k, const void* v,
-                               const void* kc, const void* vc, int64_t L, hipStream_t stream) {
+int cca_cache_load_prefill_lca_gqa(cca_cache_t* c, float* qsum, int H_q, const void* q, const void* k,
+                                   const void* v, const void* kc, const void* vc, int64_t L, hipStream_t stream) {
   int s = check_cache(c);
   if (s != CCA_OK) return s;
   if (qsum == nullptr || !aligned16(qsum) || !aligned16(q)) return CCA_ERR_INVALID;
+  if (H_q < 1 || H_q % c->H != 0) return CCA_ERR_INVALID;
   // validate as cca_cache_load_prefill does before enqueueing anything, so that the
   // descriptor changes only once all of the seeding is enqueued
   if (c->n_tokens != 0 || L < 1 || !aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
   const int64_t m = L / c->g;
   if (m > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   if (m > c->max_groups) return CCA_ERR_CAPACITY;
-  if (cca::launch_qsum_seed(c, q, qsum, L, stream) != hipSuccess) return CCA_ERR_HIP;
+  if (cca::launch_qsum_seed(c, q, qsum, L, H_q / c->H, stream) != hipSuccess) return CCA_ERR_HIP;
   return cca_cache_load_prefill(c, k, v, kc, vc, L, stream);
+}
+
+int cca_cache_load_prefill_lca(cca_cache_t* c, float* qsum, const void* q, const void* k, const void* v,
+                               const void* kc, const void* vc, int64_t L, hipStream_t stream) {
+  if (c == nullptr) return CCA_ERR_INVALID;
+  return cca_cache_load_prefill_lca_gqa(c, qsum, c->H, q, k, v, kc, vc, L, stream);
 }
 
 int cca_cache_append_decode_lca(cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k, const void* v,
@@ -329,9 +336,9 @@ size_t cca_serve_workspace_bytes(const cca_cache_t* c, int H_q) {
   return cca::serve_workspace_bytes(c, H_q);
 }
 
-int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
-                                   const void* q, const void* k, const void* v, void* out, int out_dt,
-                                   void* workspace, size_t workspace_bytes, float scale, hipStream_t stream) {
+static int append_decode_varlen(const cca_cache_t* c, float* qsum, int d_rope, int32_t* lens, int64_t max_len,
+                                int H_q, const void* q, const void* k, const void* v, void* out, int out_dt,
+                                void* workspace, size_t workspace_bytes, float scale, hipStream_t stream) {
   int s = check_cache(c);
   if (s != CCA_OK) return s;
   if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
@@ -343,7 +350,23 @@ int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t 
   if ((max_len + 1) / c->g > c->max_groups) return CCA_ERR_CAPACITY;
   if (workspace_bytes < cca_serve_workspace_bytes(c, H_q)) return CCA_ERR_WORKSPACE;
   return hip_status(cca::launch_serve_append_decode(c, lens, max_len, H_q, q, k, v, out, out_dt == CCA_F32,
-                                                    workspace, scale, stream));
+                                                    workspace, scale, stream, qsum, d_rope));
+}
+
+int cca_cache_append_decode_varlen(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
+                                   const void* q, const void* k, const void* v, void* out, int out_dt,
+                                   void* workspace, size_t workspace_bytes, float scale, hipStream_t stream) {
+  return append_decode_varlen(c, nullptr, 0, lens, max_len, H_q, q, k, v, out, out_dt, workspace, workspace_bytes,
+                              scale, stream);
+}
+
+int cca_cache_append_decode_varlen_lca(const cca_cache_t* c, float* qsum, int d_rope, int32_t* lens,
+                                       int64_t max_len, int H_q, const void* q, const void* k, const void* v,
+                                       void* out, int out_dt, void* workspace, size_t workspace_bytes, float scale,
+                                       hipStream_t stream) {
+  if (c == nullptr || qsum == nullptr || !aligned16(qsum) || d_rope < 0 || d_rope > c->d) return CCA_ERR_INVALID;
+  return append_decode_varlen(c, qsum, d_rope, lens, max_len, H_q, q, k, v, out, out_dt, workspace, workspace_bytes,
+                              scale, stream);
 }
 
 size_t cca_extend_workspace_bytes(const cca_cache_t* c, int n) {

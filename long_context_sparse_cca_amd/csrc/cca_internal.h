@@ -75,7 +75,9 @@ hipError_t launch_append_decode(const cca_cache_t* c, const void* q, const void*
 hipError_t launch_append_decode_lca(const cca_cache_t* c, float* qsum, int d_rope, const void* q, const void* k,
                                     const void* v, void* out, int out_f32, void* workspace, float scale,
                                     hipStream_t stream);
-hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, hipStream_t stream);
+// q [B*c->H*nq][L][d]: nq query heads per cached head; qsum sums over them.
+hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, int nq,
+                            hipStream_t stream);
 
 // Log-sum-exp combination of per-chunk decode partials (workspace layout: acc
 // [nslices][nchunks][d] floats, then ml [nslices][nchunks][2]) into out [nslices][d].
@@ -89,9 +91,12 @@ hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, v
 // (device), H_q = nq * c->H query heads (grouped-query attention), append fused.
 int serve_num_chunks(const cca_cache_t* c, int H_q, int64_t max_len);
 size_t serve_workspace_bytes(const cca_cache_t* c, int H_q);
+// qsum (optional, float32 [B*c->H][d]): the LCA-style cache's running query sums; with it
+// a completed group is condensed the LCA way (d_rope positional dims) instead of pooled.
 hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
-                                      void* workspace, float scale, hipStream_t stream);
+                                      void* workspace, float scale, hipStream_t stream, float* qsum = nullptr,
+                                      int d_rope = 0);
 
 // Backward pass, bf16, head dim 128 (backward.hip); BH query slices, nq query heads per
 // key/value head.  Workspace: D [BH][L], the log-sum-exp in log2 units [BH][L], then dKc

@@ -438,10 +438,12 @@ hipError_t launch_decode_any(const cca_cache_t* c, const void* q, const void* k,
 }
 
 // Running sums of the queries of each slice's trailing partial group (rows m*g .. L-1)
-// of a prefill, to seed the LCA-style cache: one wave per slice, D/64 columns per lane.
+// of a prefill, over the nq query slices bh*nq .. that share cached slice bh, to seed the
+// LCA-style cache: one wave per cached slice, D/64 columns per lane; token by token,
+// each token's heads first (the order in which decode steps add them).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void cca_qsum_seed_kernel(const T* __restrict__ q, float* __restrict__ qsum,
-                                                           int64_t L, int64_t row0) {
+                                                           int64_t L, int64_t row0, int nq) {
   constexpr int CPL = D / kWave;
   const int64_t bh = blockIdx.x;
   const int col = threadIdx.x * CPL;
@@ -449,21 +451,29 @@ __global__ __launch_bounds__(64) void cca_qsum_seed_kernel(const T* __restrict__
 #pragma unroll
   for (int e = 0; e < CPL; ++e) s[e] = 0.f;
   for (int64_t r = row0; r < L; ++r) {
-    float f[CPL];
-    lca_load_cols<T, D>(q + ((size_t)bh * L + r) * D + col, f);
+    float t[CPL];
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) s[e] += f[e];
+    for (int e = 0; e < CPL; ++e) t[e] = 0.f;
+    for (int h = 0; h < nq; ++h) {
+      float f[CPL];
+      lca_load_cols<T, D>(q + (((size_t)bh * nq + h) * L + r) * D + col, f);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) t[e] += f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) s[e] += t[e];
   }
 #pragma unroll
   for (int e = 0; e < CPL; ++e) qsum[(size_t)bh * D + col + e] = s[e];
 }
 
 template <typename T, int D>
-hipError_t launch_qsum_seed_t(const cca_cache_t* c, const void* q, float* qsum, int64_t L, hipStream_t stream) {
+hipError_t launch_qsum_seed_t(const cca_cache_t* c, const void* q, float* qsum, int64_t L, int nq,
+                              hipStream_t stream) {
   const int64_t BH = (int64_t)c->B * c->H;
   const int64_t row0 = L / c->g * c->g;
   hipLaunchKernelGGL((cca_qsum_seed_kernel<T, D>), dim3((unsigned)BH), dim3(64), 0, stream, (const T*)q, qsum, L,
-                     row0);
+                     row0, nq);
   return hipGetLastError();
 }
 
@@ -539,13 +549,14 @@ hipError_t launch_append_decode_lca(const cca_cache_t* c, float* qsum, int d_rop
   return launch_decode_any<2>(c, q, k, v, out, out_f32, workspace, scale, qsum, d_rope, stream);
 }
 
-hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, hipStream_t stream) {
+hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, int nq,
+                            hipStream_t stream) {
   if (c->dt == CCA_BF16) {
-    if (c->d == 128) return launch_qsum_seed_t<bf16_t, 128>(c, q, qsum, L, stream);
-    return launch_qsum_seed_t<bf16_t, 64>(c, q, qsum, L, stream);
+    if (c->d == 128) return launch_qsum_seed_t<bf16_t, 128>(c, q, qsum, L, nq, stream);
+    return launch_qsum_seed_t<bf16_t, 64>(c, q, qsum, L, nq, stream);
   }
-  if (c->d == 128) return launch_qsum_seed_t<float, 128>(c, q, qsum, L, stream);
-  return launch_qsum_seed_t<float, 64>(c, q, qsum, L, stream);
+  if (c->d == 128) return launch_qsum_seed_t<float, 128>(c, q, qsum, L, nq, stream);
+  return launch_qsum_seed_t<float, 64>(c, q, qsum, L, nq, stream);
 }
 
 }  // namespace cca

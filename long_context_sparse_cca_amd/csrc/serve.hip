@@ -13,6 +13,12 @@
 // Efficient Long Context Modeling", section 2, which its section 3 extends to
 // grouped-query attention).
 //
+// LCA-style cache (LCA): a group is condensed instead, with the mean of all its queries
+// (its g tokens times the query heads sharing the key/value head; "Latent-Condensed
+// Transformer for Efficient Long Context Modeling", sections 2 and 3) as importance and
+// the top-scored token's positional dims (lca_group.h).  The running sum of the current
+// group's queries lives in qsum [B*H_kv][D] between calls.
+//
 // One workgroup = (sequence b, key/value head, block of RH query heads, chunk of
 // the key index space).  Every key/value row is loaded once per workgroup and
 // scored against all RH query heads, so grouped-query attention reads the cache
@@ -21,6 +27,7 @@
 #include <algorithm>
 
 #include "cca_internal.h"
+#include "lca_group.h"
 #include "pool_group.h"
 
 namespace cca {
@@ -37,12 +44,13 @@ struct ServeCfg {
   static constexpr int KPI = NWAVE * KPW * U;         // key rows per workgroup iteration
 };
 
-template <typename T, int D, int RH, bool STREAM>
+template <typename T, int D, int RH, bool STREAM, bool LCA>
 __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
     const int32_t* __restrict__ lens, int64_t max_len, const T* __restrict__ q, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ core_k, T* __restrict__ core_v, T* __restrict__ ring_k,
     T* __restrict__ ring_v, float* __restrict__ ws_acc, float* __restrict__ ws_ml, int Hkv, int nq, int nhb,
-    int64_t max_groups, int64_t R, int g, int k_local, int64_t chunk, int nchunks, float scale) {
+    int64_t max_groups, int64_t R, int g, int k_local, int64_t chunk, int nchunks, float scale,
+    float* __restrict__ qsum, int d_rope) {
   using C = ServeCfg<T, D, RH>;
   __shared__ float red[C::NWAVE][RH][D + 2];
   extern __shared__ float pool_lds[];
@@ -73,7 +81,41 @@ __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
       st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + lane,
            ld16(reinterpret_cast<const uint4*>(vt) + lane));
     }
-    if ((t + 1) % g == 0) {
+    if constexpr (LCA) {
+      // running sum of the group's queries: this token's, over the nq query heads
+      constexpr int CPL = D / kWave;
+      const int col = lane * CPL;
+      float qs[CPL];
+      float* qsum_row = qsum + (size_t)bkv * D + col;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) qs[e] = 0.f;
+      for (int h = 0; h < nq; ++h) {
+        float qf[CPL];
+        lca_load_cols<T, D>(q + ((size_t)b * Hq + (size_t)hk * nq + h) * D + col, qf);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) qs[e] += qf[e];
+      }
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) qs[e] += qsum_row[e];
+      if ((t + 1) % g == 0) {
+        const float inv = 1.0f / ((float)g * (float)nq);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          pool_lds[col + e] = qs[e] * inv;
+          qsum_row[e] = 0.f;
+        }
+        wave_lds_sync();
+        const int64_t beta = t / g;
+        const int64_t first = slot - (g - 1);
+        lca_condense_wave<T, D>(pool_lds, ring_k + ((size_t)bkv * R + first) * D,
+                                ring_v + ((size_t)bkv * R + first) * D, kt, vt, g, scale, d_rope,
+                                core_k + ((size_t)bkv * max_groups + beta) * D,
+                                core_v + ((size_t)bkv * max_groups + beta) * D, pool_lds + D, nullptr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) qsum_row[e] = qs[e];
+      }
+    } else if ((t + 1) % g == 0) {
       // the group occupies slots slot-g+1 .. slot (R is a multiple of g); its last row is the new token
       const int64_t beta = t / g;
       const int64_t first = slot - (g - 1);
@@ -241,10 +283,21 @@ int heads_per_block(int nq) {
   return 1;
 }
 
+template <typename T, int D, int RH, bool STREAM, bool LCA>
+void launch_serve_kernel(dim3 grid, size_t lds, hipStream_t stream, const cca_cache_t* c, int32_t* lens,
+                         int64_t max_len, const void* q, const void* k, const void* v, float* ws_acc, float* ws_ml,
+                         int nq, int nhb, int64_t R, int64_t chunk, int nchunks, float scale, float* qsum,
+                         int d_rope) {
+  hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH, STREAM, LCA>), grid, dim3(256), lds, stream, lens, max_len,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k,
+                     (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb, c->max_groups, R, c->g, c->k_local, chunk, nchunks,
+                     scale, qsum, d_rope);
+}
+
 template <typename T, int D, int RH>
 hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, const void* q,
                           const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
-                          hipStream_t stream) {
+                          float* qsum, int d_rope, hipStream_t stream) {
   const int nq = H_q / c->H;
   const int nhb = nq / RH;
   const int64_t R = (int64_t)(c->k_local + 1) * c->g;
@@ -261,16 +314,25 @@ hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, 
   const int64_t nblk = (int64_t)c->B * c->H * nhb;
   // K/V bytes of the step if every sequence were max_len long (an upper bound)
   const bool stream_kv = (int64_t)c->B * c->H * n_keys_max * D * (int64_t)sizeof(T) * 2 > kStreamBytes;
-  if (stream_kv)
-    hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH, true>), dim3((unsigned)nblk, nchunks), dim3(256),
-                       (size_t)c->g * sizeof(float), stream, lens, max_len, (const T*)q, (const T*)k, (const T*)v,
-                       (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k, (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb,
-                       c->max_groups, R, c->g, c->k_local, chunk, nchunks, scale);
-  else
-    hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH, false>), dim3((unsigned)nblk, nchunks), dim3(256),
-                       (size_t)c->g * sizeof(float), stream, lens, max_len, (const T*)q, (const T*)k, (const T*)v,
-                       (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k, (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb,
-                       c->max_groups, R, c->g, c->k_local, chunk, nchunks, scale);
+  const dim3 grid((unsigned)nblk, nchunks);
+  // pooling scratch: g scores (CCA); the mean query and g scores (LCA-style)
+  const bool lca = qsum != nullptr;
+  const size_t lds = (size_t)(lca ? D + c->g : c->g) * sizeof(float);
+  if (lca) {
+    if (stream_kv)
+      launch_serve_kernel<T, D, RH, true, true>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq, nhb,
+                                                R, chunk, nchunks, scale, qsum, d_rope);
+    else
+      launch_serve_kernel<T, D, RH, false, true>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq,
+                                                 nhb, R, chunk, nchunks, scale, qsum, d_rope);
+  } else {
+    if (stream_kv)
+      launch_serve_kernel<T, D, RH, true, false>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq,
+                                                 nhb, R, chunk, nchunks, scale, nullptr, 0);
+    else
+      launch_serve_kernel<T, D, RH, false, false>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq,
+                                                  nhb, R, chunk, nchunks, scale, nullptr, 0);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
@@ -280,13 +342,17 @@ hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, 
 
 template <typename T, int D>
 hipError_t launch_serve_d(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, const void* q,
-                          const void* k, const void* v, void* out, int out_f32, void* ws, float scale,
-                          hipStream_t stream) {
+                          const void* k, const void* v, void* out, int out_f32, void* ws, float scale, float* qsum,
+                          int d_rope, hipStream_t stream) {
   switch (heads_per_block(H_q / c->H)) {
-    case 8: return launch_serve_t<T, D, 8>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
-    case 4: return launch_serve_t<T, D, 4>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
-    case 2: return launch_serve_t<T, D, 2>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
-    default: return launch_serve_t<T, D, 1>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, stream);
+    case 8:
+      return launch_serve_t<T, D, 8>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, qsum, d_rope, stream);
+    case 4:
+      return launch_serve_t<T, D, 4>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, qsum, d_rope, stream);
+    case 2:
+      return launch_serve_t<T, D, 2>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, qsum, d_rope, stream);
+    default:
+      return launch_serve_t<T, D, 1>(c, lens, max_len, H_q, q, k, v, out, out_f32, ws, scale, qsum, d_rope, stream);
   }
 }
 
@@ -312,15 +378,17 @@ size_t serve_workspace_bytes(const cca_cache_t* c, int H_q) {
 
 hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
-                                      void* workspace, float scale, hipStream_t stream) {
+                                      void* workspace, float scale, hipStream_t stream, float* qsum, int d_rope) {
   if (c->dt == CCA_BF16) {
     if (c->d == 128)
-      return launch_serve_d<bf16_t, 128>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, stream);
-    return launch_serve_d<bf16_t, 64>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, stream);
+      return launch_serve_d<bf16_t, 128>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, qsum, d_rope,
+                                         stream);
+    return launch_serve_d<bf16_t, 64>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, qsum, d_rope,
+                                      stream);
   }
   if (c->d == 128)
-    return launch_serve_d<float, 128>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, stream);
-  return launch_serve_d<float, 64>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, stream);
+    return launch_serve_d<float, 128>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
+  return launch_serve_d<float, 64>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
 }
 
 }  // namespace cca

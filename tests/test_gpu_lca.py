@@ -278,3 +278,112 @@ def test_lca_decode_invalid_rope_width(gpu):
     with pytest.raises(binding.CCAError):
         cache.append_decode(x, x, x)
     assert cache.n_tokens == 0
+
+
+# LCA-style serving (per-sequence lengths, grouped-query heads):
+# (B, H_q, H_kv, d, g, k, d_rope, dtype, initial lengths, steps, seed)
+LCA_SERVE_CASES = [
+    (3, 4, 2, 128, 16, 2, 64, "bf16", [100, 37, 0], 40, 50),   # r = 2, one empty sequence
+    (2, 6, 2, 64, 5, 3, 16, "f32", [0, 23], 30, 51),           # r = 3, g not a power of two
+    (2, 8, 1, 128, 16, 4, 0, "bf16", [300, 129], 24, 52),      # multi-query, every dim pooled
+    (4, 2, 2, 64, 16, 1, 64, "f32", [37, 0, 16, 15], 24, 53),  # r = 1, whole key from the anchor
+]
+
+
+def _srv_id(c):
+    B, Hq, Hkv, d, g, k, r, dt, lens, T, seed = c
+    return f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}r{r}-{dt}-L{'_'.join(map(str, lens))}-T{T}"
+
+
+def _lca_serve_setup(case, device):
+    B, Hq, Hkv, d, g, k, d_rope, dt, lens0, T, seed = case
+    total = max(lens0) + T
+    Q = np_inputs(B, Hq, total, d, dt, seed)[0]
+    _, K, V = np_inputs(B, Hkv, total, d, dt, seed + 1000)
+    scale = 1.0 / math.sqrt(d)
+    cache = binding.LCAServeCache(B, Hq, Hkv, d, g, k, total + g, d_rope, dtype=TDT[dt], device=device)
+    for b, L in enumerate(lens0):
+        if L == 0:
+            continue
+        qb, kb, vb = (_dev(x[b:b + 1, :, :L], dt, device) for x in (Q, K, V))
+        _, kc, vc, _ = binding.prefill_lca(qb, kb, vb, g, k, d_rope, scale)
+        cache.load_sequence(b, qb, kb, vb, kc, vc)
+    return Q, K, V, cache, scale
+
+
+def _step_inputs(Q, K, V, pos, dt, device):
+    B = len(pos)
+    return tuple(_dev(np.stack([X[b, :, pos[b]] for b in range(B)]), dt, device) for X in (Q, K, V))
+
+
+@pytest.mark.parametrize("case", LCA_SERVE_CASES, ids=_srv_id)
+def test_lca_serve_steps_match_oracle(gpu, case):
+    """Every step's outputs are the LCA-style prefill rows of each sequence at its position
+    (grouped-query form, oracle at the GPU's anchors); the condensed tokens and the running
+    query sums match too."""
+    B, Hq, Hkv, d, g, k, d_rope, dt, lens0, T, seed = case
+    _say(f"lca serve case {_srv_id(case)} seed {seed}")
+    Q, K, V, cache, scale = _lca_serve_setup(case, gpu)
+    outs = []
+    for i in range(T):
+        q, kk, v = _step_inputs(Q, K, V, [L + i for L in lens0], dt, gpu)
+        outs.append(cache.step(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy())
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == [L + T for L in lens0]
+    got = np.stack(outs, axis=2).astype(np.float64)   # [B, H_q, T, d]
+    r = Hq // Hkv
+    dc = d - d_rope
+    for b in range(B):
+        n = lens0[b] + T
+        m = n // g
+        Qb, Kb, Vb = (x[b, :, :n].astype(np.float64) for x in (Q, K, V))
+        anc = np.zeros((Hkv, m), dtype=np.int64)
+        gks, gvs = [], []
+        for hk in range(Hkv):
+            gk = cache.core_k[b, hk, :m].float().cpu().numpy()
+            gks.append(gk)
+            gvs.append(cache.core_v[b, hk, :m].float().cpu().numpy())
+            anc[hk] = _anchors_from_core(gk, Kb[hk], g, d_rope)
+            if m and d_rope:
+                q_mean = Qb[hk * r:(hk + 1) * r].mean(axis=0)
+                _check_anchors(cca_lca.lca_scores(q_mean, Kb[hk], g, scale), anc[hk])
+        out, Kc, Vc, _ = cca_lca.lca_gqa(Qb[None], Kb[None], Vb[None], g, k, scale, d_rope, anchors=anc[None],
+                                         core_dtype=dt)
+        if m:
+            for hk in range(Hkv):
+                for x, ref in ((gks[hk][:, :dc], Kc[0, hk][:, :dc]), (gvs[hk], Vc[0, hk])):
+                    bound = TOL[dt] + ULP[dt] * np.abs(ref)
+                    assert np.all(np.abs(x - ref) <= bound), f"condensed err {np.abs(x - ref).max():.3e}"
+        want = out[0][:, lens0[b]:n]
+        err = np.abs(got[b] - want).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+        # the running sums hold the current partial group, over its positions and the r heads
+        part = n % g
+        for hk in range(Hkv):
+            want_qsum = Qb[hk * r:(hk + 1) * r, n - part:n].sum(axis=(0, 1)) if part else np.zeros(d)
+            assert np.abs(cache.qsum[b, hk].cpu().numpy() - want_qsum).max() <= 1e-3
+
+
+def test_lca_serve_out_of_range_length_leaves_state(gpu):
+    """A device length beyond max_len gives NaN outputs and leaves that sequence's cache and sums."""
+    case = (2, 4, 2, 128, 16, 2, 64, "bf16", [60, 70], 1, 54)
+    B, Hq, Hkv, d, g, k, d_rope, dt, lens0, T, seed = case
+    Q, K, V, cache, scale = _lca_serve_setup(case, gpu)
+    cache.lens[1] = 10 ** 6          # the host still believes 70 (max_len = 70)
+    ring_before = cache.ring_k[1].clone()
+    qsum_before = cache.qsum[1].clone()
+    q, kk, v = _step_inputs(Q, K, V, lens0, dt, gpu)
+    out = cache.step(q, kk, v, out_dtype=torch.float32, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
+    assert torch.equal(cache.ring_k[1], ring_before) and torch.equal(cache.qsum[1], qsum_before)
+    assert cache.lens.cpu().tolist() == [lens0[0] + 1, 10 ** 6]
+
+
+def test_lca_serve_invalid_rope_width(gpu):
+    cache = binding.LCAServeCache(1, 2, 1, 64, 8, 1, 32, d_rope=65, dtype=torch.float32, device=gpu)
+    q = torch.zeros((1, 2, 64), dtype=torch.float32, device=gpu)
+    x = torch.zeros((1, 1, 64), dtype=torch.float32, device=gpu)
+    with pytest.raises(binding.CCAError):
+        cache.step(q, x, x)
+    assert cache.lens.cpu().tolist() == [0]
