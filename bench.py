@@ -374,8 +374,9 @@ def lca_serving(binding, accounting, dev, seed, d_rope: int, steps: int = 64):
     from long_context_sparse_cca_amd.synth import torch_inputs
     B, Hq, Hkv = 8, 32, 8
     lens0 = [65536 + 9362 * b for b in range(B)]
-    cache = binding.LCAServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + G, d_rope, dtype=torch.bfloat16,
-                                  device=dev)
+    n_ext, chunks = 1024, 3
+    cache = binding.LCAServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + chunks * n_ext + G, d_rope,
+                                  dtype=torch.bfloat16, device=dev)
     for b, L in enumerate(lens0):
         q, _, _ = torch_inputs(1, Hq, L, D, torch.bfloat16, dev, seed=seed + 60 + b, heavy_frac=HEAVY)
         _, k, v = torch_inputs(1, Hkv, L, D, torch.bfloat16, dev, seed=seed + 80 + b, heavy_frac=HEAVY)
@@ -404,12 +405,35 @@ def lca_serving(binding, accounting, dev, seed, d_rope: int, steps: int = 64):
     byt = [accounting.serve_bytes(lens_at[s], Hq, Hkv, D, G, KL, 2, nchunks) for s in range(warm, steps)]
     us_mean = sum(us) / len(us)
     gbs = sum(byt) / len(byt) / (us_mean * 1e-6) / 1e9
+    # chunked append: 1024 new tokens for every sequence per call
+    qe = torch.randn((B, Hq, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
+    ke = torch.randn((B, Hkv, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
+    ve = torch.randn((B, Hkv, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
+    cache.extend(qe, ke, ve)   # first call sizes the staging workspace
+    torch.cuda.synchronize()
+    ext_ms, ext_fl = [], []
+    for _ in range(chunks - 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lens_now = list(cache.lens_host)
+        e0.record(stream)
+        cache.extend(qe, ke, ve)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ext_ms.append(e0.elapsed_time(e1))
+        ext_fl.append(accounting.extend_flops(lens_now, n_ext, Hq, D, G, KL))
+    ms = sum(ext_ms) / len(ext_ms)
+    tf = sum(ext_fl) / len(ext_fl) / (ms * 1e-3) / 1e12
     return {"config": {"B": B, "H_q": Hq, "H_kv": Hkv, "d": D, "g": G, "k_local": KL, "d_rope": d_rope,
                        "lengths": lens0, "steps_timed": steps - warm},
             "us_per_step": us_mean, "bytes_per_step": sum(byt) / len(byt),
             "roofline": {"kernel": "cca_serve_decode_kernel<bf16,128,4,lca> + cca_decode_merge_kernel",
                          "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS}}
+                         "frac": gbs / PEAK_HBM_GBS},
+            "chunked_append": {"tokens_per_sequence": n_ext, "ms_per_call": ms,
+                               "tokens_per_s": B * n_ext / (ms * 1e-3), "flops_per_call": sum(ext_fl) / len(ext_fl),
+                               "roofline": {"kernel": "cca_prefill_bf16_d128_kernel<extend> (+ gather, lca append)",
+                                            "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                            "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
 
 def main():

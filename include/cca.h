@@ -431,6 +431,19 @@ int cca_cache_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H
                      void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
 
 /*
+ * Chunked append for the LCA-style serving cache: cca_cache_extend, except that every
+ * group the chunk completes is condensed as by cca_cache_append_decode_varlen_lca.  The
+ * mean query covers the group's tokens and the r query heads.  Queries of its tokens
+ * before the chunk come from qsum; the others come from q.  Afterwards qsum holds,
+ * per sequence and key/value head, the sum of the queries of the trailing incomplete
+ * group.  qsum and d_rope are as for cca_cache_append_decode_varlen_lca.  Everything
+ * else is as for cca_cache_extend.
+ */
+int cca_cache_extend_lca(const cca_cache_t* c, float* qsum, int d_rope, int32_t* lens, int64_t max_len,
+                         int H_q, int n, const void* q, const void* k, const void* v, void* out, int out_dt,
+                         void* workspace, size_t workspace_bytes, float scale, hipStream_t stream);
+
+/*
  * KV-cache accounting ([CCA] compute/memory efficiency, Fig. 3: the cache
  * holds core plus local tokens instead of every token).  Host-only integer
  * arithmetic, no device work.  After n_tokens tokens with group size g and

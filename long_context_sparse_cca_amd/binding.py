@@ -132,6 +132,10 @@ EXPORTS = {
                                               ctypes.c_void_p]),
     "cca_cache_load_prefill_lca_gqa": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int]
                                        + [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p]),
+    "cca_cache_extend_lca": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+                             + [ctypes.c_void_p] * 4
+                             + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
     "cca_extend_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int]),
     "cca_cache_extend": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_int] + [ctypes.c_void_p] * 4
@@ -586,6 +590,12 @@ class ServeCache(KVCache):
         self.lens_host = [x + 1 for x in self.lens_host]   # the call advanced `lens` on the device
         return out
 
+    def _extend_call(self, m, qs, ks, vs, os_, out_dtype, scale):
+        _check(_lib.cca_cache_extend(ctypes.byref(self.desc), _ptr(self.lens), max(self.lens_host), self.H_q, m,
+                                     _ptr(qs), _ptr(ks), _ptr(vs), _ptr(os_), _dtype_code(out_dtype),
+                                     _ptr(self._ext_ws), self._ext_ws.numel() * 4, scale, _stream()),
+               "cca_cache_extend")
+
     def extend(self, q, k, v, out_dtype=None, scale: float | None = None):
         """Append n tokens to every sequence and return their outputs [B, H_q, n, d].
 
@@ -613,10 +623,7 @@ class ServeCache(KVCache):
             ws_bytes = _lib.cca_extend_workspace_bytes(ctypes.byref(self.desc), m)
             if self._ext_ws is None or self._ext_ws.numel() * 4 < ws_bytes:
                 self._ext_ws = torch.empty(((ws_bytes + 15) // 16) * 4, dtype=torch.float32, device=q.device)
-            _check(_lib.cca_cache_extend(ctypes.byref(self.desc), _ptr(self.lens), max(self.lens_host), self.H_q, m,
-                                         _ptr(qs), _ptr(ks), _ptr(vs), _ptr(os_), _dtype_code(out_dtype),
-                                         _ptr(self._ext_ws), self._ext_ws.numel() * 4, scale, _stream()),
-                   "cca_cache_extend")
+            self._extend_call(m, qs, ks, vs, os_, out_dtype, scale)
             self.lens_host = [x + m for x in self.lens_host]   # the call advanced `lens` on the device
             if m != n:
                 out[:, :, a:e] = os_
@@ -628,7 +635,8 @@ class LCAServeCache(ServeCache):
     groups condensed with the mean of their queries over positions and the query heads that
     share a key/value head, positional dims (the last d_rope) from the top-scored token.
     `qsum` (float32 [B, H_kv, d]) holds each sequence's running sum of its current group's
-    queries.  Chunked appends are not provided for this cache."""
+    queries.  `step` and `extend` (cca_cache_append_decode_varlen_lca, cca_cache_extend_lca)
+    work as for ServeCache."""
 
     def __init__(self, B: int, H_q: int, H_kv: int, d: int, g: int, k_local: int, max_tokens: int, d_rope: int,
                  dtype=torch.bfloat16, device="cuda"):
@@ -683,8 +691,12 @@ class LCAServeCache(ServeCache):
         self.lens_host = [x + 1 for x in self.lens_host]
         return out
 
-    def extend(self, q, k, v, out_dtype=None, scale: float | None = None):
-        raise CCAError("chunked appends are not provided for the LCA-style serving cache; use step")
+    def _extend_call(self, m, qs, ks, vs, os_, out_dtype, scale):
+        _check(_lib.cca_cache_extend_lca(ctypes.byref(self.desc), _ptr(self.qsum), self.d_rope, _ptr(self.lens),
+                                         max(self.lens_host), self.H_q, m, _ptr(qs), _ptr(ks), _ptr(vs), _ptr(os_),
+                                         _dtype_code(out_dtype), _ptr(self._ext_ws), self._ext_ws.numel() * 4, scale,
+                                         _stream()),
+               "cca_cache_extend_lca")
 
 
 def cache_append(cache: KVCache, q, k, v, scale=None):

@@ -376,9 +376,9 @@ size_t cca_extend_workspace_bytes(const cca_cache_t* c, int n) {
   return cca::extend_workspace_bytes(c, n);
 }
 
-int cca_cache_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
-                     const void* k, const void* v, void* out, int out_dt, void* workspace, size_t workspace_bytes,
-                     float scale, hipStream_t stream) {
+static int cache_extend(const cca_cache_t* c, float* qsum, int d_rope, int32_t* lens, int64_t max_len, int H_q, int n,
+                        const void* q, const void* k, const void* v, void* out, int out_dt, void* workspace,
+                        size_t workspace_bytes, float scale, hipStream_t stream) {
   int s = check_cache(c);
   if (s != CCA_OK) return s;
   if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
@@ -393,7 +393,22 @@ int cca_cache_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H
   if ((int64_t)c->B * H_q * ((n + 127) / 128) >= INT32_MAX) return CCA_ERR_INVALID;
   if (workspace_bytes < cca_extend_workspace_bytes(c, n)) return CCA_ERR_WORKSPACE;
   return hip_status(cca::launch_extend(c, lens, max_len, H_q, n, q, k, v, out, out_dt == CCA_F32, workspace, scale,
-                                       stream));
+                                       stream, qsum, d_rope));
+}
+
+int cca_cache_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
+                     const void* k, const void* v, void* out, int out_dt, void* workspace, size_t workspace_bytes,
+                     float scale, hipStream_t stream) {
+  return cache_extend(c, nullptr, 0, lens, max_len, H_q, n, q, k, v, out, out_dt, workspace, workspace_bytes, scale,
+                      stream);
+}
+
+int cca_cache_extend_lca(const cca_cache_t* c, float* qsum, int d_rope, int32_t* lens, int64_t max_len, int H_q,
+                         int n, const void* q, const void* k, const void* v, void* out, int out_dt, void* workspace,
+                         size_t workspace_bytes, float scale, hipStream_t stream) {
+  if (c == nullptr || qsum == nullptr || !aligned16(qsum) || d_rope < 0 || d_rope > c->d) return CCA_ERR_INVALID;
+  return cache_extend(c, qsum, d_rope, lens, max_len, H_q, n, q, k, v, out, out_dt, workspace, workspace_bytes, scale,
+                      stream);
 }
 
 int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt, int64_t* resident_bytes,

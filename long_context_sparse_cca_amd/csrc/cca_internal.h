@@ -115,10 +115,12 @@ hipError_t launch_backward_generic(int dt, int d, const void* q, const void* k, 
                                    float* dk, float* dv, void* workspace, int BH, int nq, int64_t L, int g,
                                    int k_local, float scale, hipStream_t stream);
 
-// Chunked append of n tokens per sequence (extend.hip).
+// Chunked append of n tokens per sequence (extend.hip); qsum (optional): the LCA-style
+// cache's running query sums, as for launch_serve_append_decode.
 size_t extend_workspace_bytes(const cca_cache_t* c, int n);
 hipError_t launch_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
                          const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
-                         hipStream_t stream);
+                         hipStream_t stream, float* qsum = nullptr,
+                         int d_rope = 0);
 
 }  // namespace cca

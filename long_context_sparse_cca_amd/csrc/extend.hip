@@ -19,6 +19,12 @@
 //   3. append: the chunk's keys/values go to their ring slots, every group the chunk
 //      completes is pooled into its core slot (mean query over the query heads that
 //      share the key/value head), and the sequence length advances by n.
+// LCA-style cache: launch 3 condenses a completed group instead (mean of the group's
+// queries over its positions and the query heads sharing the key/value head, positional
+// dims from the top-scored token; "Latent-Condensed Transformer for Efficient Long Context
+// Modeling", sections 2 and 3), taking the queries of the group's tokens before the chunk
+// from the running sum qsum; a fourth launch then leaves in qsum the sum of the chunk's
+// trailing incomplete group.
 // With n <= k*g + 1 no token of the chunk can see a core token pooled from the same
 // chunk (the earliest group it completes becomes visible k*g+1 positions after the
 // chunk's first token), so pooling can follow the attention.  Launch 3 overwrites
@@ -26,6 +32,7 @@
 #include <algorithm>
 
 #include "cca_internal.h"
+#include "lca_group.h"
 #include "pool_group.h"
 
 namespace cca {
@@ -72,14 +79,34 @@ __global__ __launch_bounds__(256) void cca_extend_gather_kernel(const int32_t* _
   st16(reinterpret_cast<uint4*>(sv + dst) + c, ld16(reinterpret_cast<const uint4*>(srcv) + c));
 }
 
-// One wave per new token: its ring slot, and the pooling of the group it completes.
+// Sum over the nq query heads h*nq .. of chunk row `row` for this lane's D/64 columns,
+// added to s (q_chunk [B*Hq][n][D], head slices of sequence b).
 template <typename T, int D>
+__device__ __forceinline__ void add_query_row(const T* __restrict__ q_chunk, int64_t b, int Hq, int hk, int nq,
+                                              int n, int64_t row, int col, float* s) {
+  constexpr int CPL = D / kWave;
+  float t[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) t[e] = 0.f;
+  for (int h = 0; h < nq; ++h) {
+    float f[CPL];
+    lca_load_cols<T, D>(q_chunk + (((size_t)b * Hq + (size_t)hk * nq + h) * n + row) * D + col, f);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) t[e] += f[e];
+  }
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s[e] += t[e];
+}
+
+// One wave per new token: its ring slot, and the pooling (LCA: condensation) of the group
+// it completes.
+template <typename T, int D, bool LCA>
 __global__ __launch_bounds__(256) void cca_extend_append_kernel(
     int32_t* __restrict__ lens, const int32_t* __restrict__ pos_ws, const T* __restrict__ q_chunk,
     const T* __restrict__ k_chunk, const T* __restrict__ v_chunk, const T* __restrict__ sk,
     const T* __restrict__ sv, T* __restrict__ ring_k, T* __restrict__ ring_v, T* __restrict__ core_k,
     T* __restrict__ core_v, int Hkv, int nq, int n, int64_t R, int64_t max_groups, int g, int k_local,
-    int64_t raw_rows, float scale) {
+    int64_t raw_rows, float scale, const float* __restrict__ qsum, int d_rope) {
   extern __shared__ float w_lds[];
   const int64_t bkv = blockIdx.x;
   const int64_t b = bkv / Hkv;
@@ -109,15 +136,68 @@ __global__ __launch_bounds__(256) void cca_extend_append_kernel(
   const size_t first = ((size_t)bkv * raw_rows + (p - g + 1 - raw0)) * D;
   const size_t last = ((size_t)bkv * raw_rows + (p - raw0)) * D;
   const int Hq = Hkv * nq;
-  pool_group_wave<T, D>(q_chunk + (((size_t)b * Hq + (size_t)hk * nq) * n + i) * D, (int64_t)n * D, nq, sk + first,
-                        sv + first, sk + last, sv + last, g, scale, core_k + ((size_t)bkv * max_groups + beta) * D,
-                        core_v + ((size_t)bkv * max_groups + beta) * D, w_lds + wave * g);
+  if constexpr (LCA) {
+    // the group's queries: chunk rows i-g+1 .. i, or the running sum of its tokens before
+    // the chunk followed by rows 0 .. i (token order, heads first, as the decode steps add them)
+    constexpr int CPL = D / kWave;
+    const int col = lane * CPL;
+    float s[CPL];
+    int64_t r0 = (int64_t)i - g + 1;
+    if (r0 < 0) {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s[e] = qsum[(size_t)bkv * D + col + e];
+      r0 = 0;
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s[e] = 0.f;
+    }
+    for (int64_t r = r0; r <= i; ++r) add_query_row<T, D>(q_chunk, b, Hq, hk, nq, n, r, col, s);
+    float* qbar = w_lds + wave * (D + g);
+    const float inv = 1.0f / ((float)g * (float)nq);
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) qbar[col + e] = s[e] * inv;
+    wave_lds_sync();
+    lca_condense_wave<T, D>(qbar, sk + first, sv + first, sk + last, sv + last, g, scale, d_rope,
+                            core_k + ((size_t)bkv * max_groups + beta) * D,
+                            core_v + ((size_t)bkv * max_groups + beta) * D, qbar + D, nullptr);
+  } else {
+    pool_group_wave<T, D>(q_chunk + (((size_t)b * Hq + (size_t)hk * nq) * n + i) * D, (int64_t)n * D, nq,
+                          sk + first, sv + first, sk + last, sv + last, g, scale,
+                          core_k + ((size_t)bkv * max_groups + beta) * D,
+                          core_v + ((size_t)bkv * max_groups + beta) * D, w_lds + wave * g);
+  }
+}
+
+// LCA-style cache, after the append launch (which read the sums at the chunk's start): one
+// wave per key/value slice leaves in qsum the sum of the queries of the trailing incomplete
+// group -- the chunk's rows after its last completed group, plus the previous sum when the
+// chunk completes no group.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void cca_extend_qsum_kernel(const int32_t* __restrict__ pos_ws,
+                                                            const T* __restrict__ q_chunk, float* __restrict__ qsum,
+                                                            int Hkv, int nq, int n, int g) {
+  constexpr int CPL = D / kWave;
+  const int64_t bkv = blockIdx.x;
+  const int64_t b = bkv / Hkv;
+  const int hk = (int)(bkv - b * Hkv);
+  const int64_t t = pos_ws[b];
+  if (t < 0) return;
+  const int col = threadIdx.x * CPL;
+  const int64_t end = t + n;
+  const bool completes = end / g > t / g;
+  float s[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) s[e] = completes ? 0.f : qsum[(size_t)bkv * D + col + e];
+  const int64_t r0 = completes ? end / g * g - t : 0;
+  for (int64_t r = r0; r < n; ++r) add_query_row<T, D>(q_chunk, b, Hkv * nq, hk, nq, n, r, col, s);
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) qsum[(size_t)bkv * D + col + e] = s[e];
 }
 
 template <typename T, int D>
 hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
                            const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
-                           hipStream_t stream) {
+                           float* qsum, int d_rope, hipStream_t stream) {
   const int64_t R = (int64_t)(c->k_local + 1) * c->g;
   const int64_t raw_rows = R + n;
   const int64_t BHkv = (int64_t)c->B * c->H;
@@ -136,10 +216,23 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
   e = launch_extend_attention(c->dt, D, q, sk, sv, c->core_k, c->core_v, out, out_f32, c->B * H_q, nq, c->g,
                               c->k_local, scale, ext, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((cca_extend_append_kernel<T, D>), dim3((unsigned)BHkv, (unsigned)((n + 3) / 4)), dim3(256),
-                     (size_t)4 * c->g * sizeof(float), stream, lens, pos_ws, (const T*)q, (const T*)k, (const T*)v,
-                     (const T*)sk, (const T*)sv, (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k, (T*)c->core_v, c->H, nq,
-                     n, R, c->max_groups, c->g, c->k_local, raw_rows, scale);
+  const dim3 agrid((unsigned)BHkv, (unsigned)((n + 3) / 4));
+  if (qsum == nullptr) {
+    hipLaunchKernelGGL((cca_extend_append_kernel<T, D, false>), agrid, dim3(256), (size_t)4 * c->g * sizeof(float),
+                       stream, lens, pos_ws, (const T*)q, (const T*)k, (const T*)v, (const T*)sk, (const T*)sv,
+                       (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k, (T*)c->core_v, c->H, nq, n, R, c->max_groups,
+                       c->g, c->k_local, raw_rows, scale, (const float*)nullptr, 0);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((cca_extend_append_kernel<T, D, true>), agrid, dim3(256),
+                     (size_t)4 * (D + c->g) * sizeof(float), stream, lens, pos_ws, (const T*)q, (const T*)k,
+                     (const T*)v, (const T*)sk, (const T*)sv, (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k,
+                     (T*)c->core_v, c->H, nq, n, R, c->max_groups, c->g, c->k_local, raw_rows, scale,
+                     (const float*)qsum, d_rope);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((cca_extend_qsum_kernel<T, D>), dim3((unsigned)BHkv), dim3(64), 0, stream,
+                     (const int32_t*)pos_ws, (const T*)q, qsum, c->H, nq, n, c->g);
   return hipGetLastError();
 }
 
@@ -153,15 +246,19 @@ size_t extend_workspace_bytes(const cca_cache_t* c, int n) {
 
 hipError_t launch_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
                          const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
-                         hipStream_t stream) {
+                         hipStream_t stream, float* qsum, int d_rope) {
   if (c->dt == CCA_BF16) {
     if (c->d == 128)
-      return launch_extend_t<bf16_t, 128>(c, lens, max_len, H_q, n, q, k, v, out, out_f32, workspace, scale, stream);
-    return launch_extend_t<bf16_t, 64>(c, lens, max_len, H_q, n, q, k, v, out, out_f32, workspace, scale, stream);
+      return launch_extend_t<bf16_t, 128>(c, lens, max_len, H_q, n, q, k, v, out, out_f32, workspace, scale, qsum,
+                                          d_rope, stream);
+    return launch_extend_t<bf16_t, 64>(c, lens, max_len, H_q, n, q, k, v, out, out_f32, workspace, scale, qsum,
+                                       d_rope, stream);
   }
   if (c->d == 128)
-    return launch_extend_t<float, 128>(c, lens, max_len, H_q, n, q, k, v, out, 1, workspace, scale, stream);
-  return launch_extend_t<float, 64>(c, lens, max_len, H_q, n, q, k, v, out, 1, workspace, scale, stream);
+    return launch_extend_t<float, 128>(c, lens, max_len, H_q, n, q, k, v, out, 1, workspace, scale, qsum, d_rope,
+                                       stream);
+  return launch_extend_t<float, 64>(c, lens, max_len, H_q, n, q, k, v, out, 1, workspace, scale, qsum, d_rope,
+                                    stream);
 }
 
 }  // namespace cca

@@ -387,3 +387,72 @@ def test_lca_serve_invalid_rope_width(gpu):
     with pytest.raises(binding.CCAError):
         cache.step(q, x, x)
     assert cache.lens.cpu().tolist() == [0]
+
+
+# LCA-style chunked append: (B, H_q, H_kv, d, g, k, d_rope, dtype, initial lengths, chunk sizes, seed)
+LCA_EXTEND_CASES = [
+    (2, 4, 2, 128, 16, 2, 64, "bf16", [100, 37], [1, 5, 17, 33, 40], 60),   # 40 > k*g+1: split by the binding
+    (2, 8, 2, 128, 16, 4, 32, "bf16", [0, 300], [65, 64, 3], 61),          # chunked prefill from empty
+    (1, 3, 1, 64, 5, 3, 16, "f32", [0], [16, 16, 16, 1, 7], 62),           # r = 3, g = 5, k*g+1 = 16
+    (2, 6, 3, 64, 16, 1, 0, "f32", [20, 3], [17, 2, 17], 63),              # every dim pooled
+]
+
+
+def _ext_id(c):
+    B, Hq, Hkv, d, g, k, r, dt, lens, chunks, seed = c
+    return f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}r{r}-{dt}-L{'_'.join(map(str, lens))}-n{'_'.join(map(str, chunks))}"
+
+
+@pytest.mark.parametrize("case", LCA_EXTEND_CASES, ids=_ext_id)
+def test_lca_extend_chunks_match_oracle(gpu, case):
+    """Chunks (and three single steps after them) give the LCA-style grouped-query prefill rows
+    at their positions; condensed tokens and running sums as for the single-step path."""
+    B, Hq, Hkv, d, g, k, d_rope, dt, lens0, chunks, seed = case
+    _say(f"lca extend case {_ext_id(case)} seed {seed}")
+    T = sum(chunks) + 3
+    Q, K, V, cache, scale = _lca_serve_setup((B, Hq, Hkv, d, g, k, d_rope, dt, lens0, T, seed), gpu)
+    pos = list(lens0)
+    got = {b: [] for b in range(B)}
+    for n in chunks:
+        q, kk, v = (_dev(np.stack([X[b, :, pos[b]:pos[b] + n] for b in range(B)]), dt, gpu) for X in (Q, K, V))
+        out = cache.extend(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy()
+        for b in range(B):
+            got[b].append(out[b])
+            pos[b] += n
+    for _ in range(3):
+        q, kk, v = _step_inputs(Q, K, V, pos, dt, gpu)
+        out = cache.step(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy()
+        for b in range(B):
+            got[b].append(out[b][:, None, :])
+            pos[b] += 1
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == pos
+    r = Hq // Hkv
+    dc = d - d_rope
+    for b in range(B):
+        n_tot = pos[b]
+        m = n_tot // g
+        Qb, Kb, Vb = (x[b, :, :n_tot].astype(np.float64) for x in (Q, K, V))
+        anc = np.zeros((Hkv, m), dtype=np.int64)
+        gks, gvs = [], []
+        for hk in range(Hkv):
+            gk = cache.core_k[b, hk, :m].float().cpu().numpy()
+            gks.append(gk)
+            gvs.append(cache.core_v[b, hk, :m].float().cpu().numpy())
+            anc[hk] = _anchors_from_core(gk, Kb[hk], g, d_rope)
+            if m and d_rope:
+                _check_anchors(cca_lca.lca_scores(Qb[hk * r:(hk + 1) * r].mean(axis=0), Kb[hk], g, scale), anc[hk])
+        out, Kc, Vc, _ = cca_lca.lca_gqa(Qb[None], Kb[None], Vb[None], g, k, scale, d_rope, anchors=anc[None],
+                                         core_dtype=dt)
+        if m:
+            for hk in range(Hkv):
+                for x, ref in ((gks[hk][:, :dc], Kc[0, hk][:, :dc]), (gvs[hk], Vc[0, hk])):
+                    bound = TOL[dt] + ULP[dt] * np.abs(ref)
+                    assert np.all(np.abs(x - ref) <= bound), f"condensed err {np.abs(x - ref).max():.3e}"
+        g_b = np.concatenate(got[b], axis=1).astype(np.float64)
+        err = np.abs(g_b - out[0][:, lens0[b]:n_tot]).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+        part = n_tot % g
+        for hk in range(Hkv):
+            want_qsum = Qb[hk * r:(hk + 1) * r, n_tot - part:n_tot].sum(axis=(0, 1)) if part else np.zeros(d)
+            assert np.abs(cache.qsum[b, hk].cpu().numpy() - want_qsum).max() <= 1e-3
