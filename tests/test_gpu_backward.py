@@ -5,7 +5,7 @@ Shapes span several 256-query and 128-key tiles with ragged tails, g not a power
 two, g = 1 (causal attention), a window wider than the sequence, and core tiles seen by
 many query tiles.  The oracle recomputes the forward with core tokens stored in bf16
 (the forward's stored core tokens) and differentiates in fp64.
-Tolerance: the spec bf16 bound 2e-2, taken relative to the gradient's own scale
+Tolerance: the bf16 bound 2e-2, taken relative to the gradient's own scale
 (max-abs error <= 2e-2 * max(1, max|reference|)): the softmax weights and dS are
 rounded to bf16 as matrix-core operands (relative 2^-9 each), and D = dO.O uses the
 bf16-rounded forward output.
