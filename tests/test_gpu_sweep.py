@@ -5,7 +5,8 @@ random (fixed seeds, so a failure names a reproducible case): sequence lengths f
 to ~1300 (ragged against every tile size), group sizes from 1 to 64 including primes,
 windows from 0 to 64 groups, head dims 64 and 128, fp32 and bf16, 1 to 4 query heads
 per key/value head, per-sequence lengths in the serving cache (some empty), chunked
-appends up to the largest allowed chunk, and the backward pass.  Tolerances as for the
+appends up to the largest allowed chunk, the LCA-style serving cache (steps and chunks
+mixed), and the backward pass (matrix-core and vector paths).  Tolerances as for the
 other parity tests: max-abs 1e-4 (fp32), 2e-2 (bf16), gradients 2e-2 of their scale.
 """
 import math
@@ -256,3 +257,121 @@ def test_lca_sweep(gpu, case):
     want = cca_lca.lca_gqa(Q, K, V, g, k, scale, d_rope, anchors=anc if L // g else None, core_dtype=dt)[0]
     err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
     assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
+
+
+def _lca_serve_cases(n=4, seed=55):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 3]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        g = int(rng.choice([2, 5, 8, 16]))
+        k = int(rng.choice([0, 1, 3]))
+        d_rope = int(rng.choice([0, 8, d // 2, d]))
+        lens = [int(x) if rng.uniform() > 0.25 else 0 for x in rng.integers(1, 300, size=B)]
+        # a mix of chunked appends (n <= k*g + 1) and single steps
+        ops = [int(rng.integers(1, k * g + 2)) if rng.uniform() < 0.5 else 1 for _ in range(int(rng.integers(3, 8)))]
+        cases.append((B, Hkv * r, Hkv, d, g, k, d_rope, dt, lens, ops, 950 + i))
+    return cases
+
+
+def _lsid(c):
+    B, Hq, Hkv, d, g, k, r, dt, lens, ops, seed = c
+    return (f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}rope{r}-{dt}-L{'_'.join(map(str, lens))}"
+            f"-ops{'_'.join(map(str, ops))}-s{seed}")
+
+
+def _anchor_rows(gk, K, g, d_rope):
+    m, d = gk.shape
+    anc = np.zeros(m, dtype=np.int64)
+    if d_rope == 0:
+        return anc
+    for j in range(m):
+        hits = [i for i in range(g) if np.array_equal(gk[j, d - d_rope:], K[j * g + i, d - d_rope:])]
+        assert hits, f"condensed key {j}: positional dims match no key of its group"
+        anc[j] = hits[0]
+    return anc
+
+
+@pytest.mark.parametrize("case", _lca_serve_cases(), ids=_lsid)
+def test_lca_serve_sweep(gpu, case):
+    """LCA-style serving cache: chunked appends (op n > 1, or n = 1 through the chunk path when
+    drawn as a chunk) and single steps, every row against the LCA-style prefill rows."""
+    B, Hq, Hkv, d, g, k, d_rope, dt, lens0, ops, seed = case
+    _say(f"lca serve sweep {_lsid(case)}")
+    total = max(lens0) + sum(ops)
+    Q, K, V = _inputs(B, Hq, Hkv, total, d, dt, seed)
+    scale = 1.0 / math.sqrt(d)
+    cache = binding.LCAServeCache(B, Hq, Hkv, d, g, k, total + g, d_rope, dtype=TDT[dt], device=gpu)
+    for b, L in enumerate(lens0):
+        if L:
+            qb, kb, vb = (_dev(x[b:b + 1, :, :L], dt, gpu) for x in (Q, K, V))
+            _, kc, vc, _ = binding.prefill_lca(qb, kb, vb, g, k, d_rope, scale)
+            cache.load_sequence(b, qb, kb, vb, kc, vc)
+    pos = list(lens0)
+    got = {b: [] for b in range(B)}
+    for j, n in enumerate(ops):
+        if n == 1 and j % 2:
+            q, kk, v = (_dev(np.stack([x[b, :, pos[b]] for b in range(B)]), dt, gpu) for x in (Q, K, V))
+            out = cache.step(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy()[:, :, None, :]
+        else:
+            q, kk, v = (_dev(np.stack([x[b, :, pos[b]:pos[b] + n] for b in range(B)]), dt, gpu) for x in (Q, K, V))
+            out = cache.extend(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy()
+        for b in range(B):
+            got[b].append(out[b])
+            pos[b] += n
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == pos
+    for b in range(B):
+        n_tot = pos[b]
+        m = n_tot // g
+        Qb, Kb, Vb = (x[b, :, :n_tot].astype(np.float64) for x in (Q, K, V))
+        anc = np.stack([_anchor_rows(cache.core_k[b, hk, :m].float().cpu().numpy(), Kb[hk], g, d_rope)
+                        for hk in range(Hkv)])
+        want = cca_lca.lca_gqa(Qb[None], Kb[None], Vb[None], g, k, scale, d_rope, anchors=anc[None],
+                               core_dtype=dt)[0][0][:, lens0[b]:n_tot]
+        err = np.abs(np.concatenate(got[b], axis=1) - want).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+
+
+def _generic_backward_cases(n=4, seed=131):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt, d = [("f32", 64), ("f32", 128), ("bf16", 64)][int(rng.integers(0, 3))]
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 3]))
+        g = int(rng.choice([1, 3, 8, 16, 17]))
+        k = int(rng.choice([0, 1, 2, 5]))
+        L = int(rng.integers(1, 500))
+        cases.append((dt, d, Hkv * r, Hkv, L, g, k, 1300 + i))
+    return cases
+
+
+def _gbid(c):
+    dt, d, H, Hkv, L, g, k, seed = c
+    return f"{dt}d{d}H{H}kv{Hkv}L{L}g{g}k{k}-s{seed}"
+
+
+@pytest.mark.parametrize("case", _generic_backward_cases(), ids=_gbid)
+def test_generic_backward_sweep(gpu, case):
+    """Backward pass on the vector path (float32 inputs, head dim 64) at random shapes."""
+    dt, d, H, Hkv, L, g, k, seed = case
+    _say(f"generic backward sweep {_gbid(case)}")
+    Q, K, V = _inputs(1, H, Hkv, L, d, dt, seed)
+    dO = np_inputs(1, H, L, d, dt, seed + 2000)[0]
+    q, kk, v, do = (_dev(x, dt, gpu) for x in (Q, K, V, dO))
+    scale = 1.0 / math.sqrt(d)
+    out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
+    dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
+    torch.cuda.synchronize()
+    core = "bf16" if dt == "bf16" else None
+    tol = 1e-4 if dt == "f32" else 2e-2
+    want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype=core)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
+        bound = tol * max(1.0, np.abs(ref).max())
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
