@@ -28,6 +28,7 @@ DECODE_CASES = [
     (2, 2, 128, 5, 3, 0, 90, "f32", 2),      # empty cache: every token appended
     (1, 2, 128, 16, 64, 1500, 1600, "bf16", 3),  # window of 1024 raw tokens, ring wraps
     (1, 1, 64, 1, 4, 20, 60, "bf16", 4),     # g = 1: pooling every step
+    (1, 1, 128, 512, 1, 1000, 1100, "bf16", 5),  # groups of 512 pooled in place from the ring
 ]
 
 

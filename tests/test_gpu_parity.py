@@ -46,6 +46,8 @@ PREFILL_CASES = [
     (1, 1, 300, 128, 64, 2, "f32", 8),     # g = 64
     (1, 1, 2100, 128, 32, 5, "bf16", 9),   # core tiles with masked sub-blocks in the middle
     (1, 1, 410, 64, 3, 11, "f32", 10),
+    (1, 1, 5000, 128, 1024, 2, "bf16", 11),  # large groups: 4 core tokens of 1024 rows each
+    (1, 1, 9000, 64, 4096, 0, "f32", 12),    # the largest group size the library takes
 ]
 
 
