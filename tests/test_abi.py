@@ -89,3 +89,42 @@ def test_benchmark_pair_count_matches_oracle(L, g, k):
     assert accounting.kv_cache_bytes(L, g, k, 2, 3, 64, 2) == oracle.kv_cache_bytes(L, g, k, 2, 3, 64, 2)
     assert sum(accounting.attention_pairs(L, g, k)) == sum(
         accounting.decode_keys(t, g, k) for t in range(L))
+
+
+def test_validation_of_training_lca_and_serving_calls(lib):
+    """Host-side validation of the training, LCA-style and serving entry points (no launch)."""
+    P = ctypes.c_void_p(256)          # a 16-byte aligned stand-in that is never dereferenced
+    NULL = None
+    # training: head counts that do not divide, an unbuilt head dim, a short workspace
+    assert lib.cca_prefill_lse_gqa(P, P, P, P, P, P, P, 1, 4, 3, 64, 128, 16, 1, 0.1, 1, 1, NULL) == -1
+    assert lib.cca_backward_gqa(P, P, P, P, P, P, P, P, P, P, P, P, 1 << 30, 1, 2, 2, 64, 96, 16, 1, 0.1, 1,
+                                NULL) == -2
+    need = lib.cca_backward_gqa_workspace_bytes(1, 4, 2, 640, 128, 16)
+    assert need == (2 * 4 * 640 + 2 * 2 * (640 // 16) * 128) * 4
+    assert lib.cca_backward_gqa(P, P, P, P, P, P, P, P, P, P, P, P, need - 1, 1, 4, 2, 640, 128, 16, 1, 0.1, 1,
+                                NULL) == -3
+    assert lib.cca_backward_gqa_workspace_bytes(1, 4, 3, 640, 128, 16) == 0
+    # LCA-style: positional width outside [0, d]
+    assert lib.cca_pool_kv_lca(P, P, P, P, P, NULL, 1, 1, 64, 128, 16, 129, 0.1, 1, NULL) == -1
+    assert lib.cca_pool_kv_lca(P, P, P, P, P, NULL, 1, 1, 64, 128, 16, -1, 0.1, 1, NULL) == -1
+    # LCA-style serving: running sums missing, positional width, head multiple, chunk size
+    d = binding.CacheDesc(256, 256, 256, 256, 2, 2, 128, 16, 2, 1, 64, 0, 0)
+    assert lib.cca_cache_append_decode_varlen_lca(ctypes.byref(d), NULL, 64, P, 10, 4, P, P, P, P, 1, P, 1 << 30,
+                                                  0.1, NULL) == -1
+    assert lib.cca_cache_append_decode_varlen_lca(ctypes.byref(d), P, 129, P, 10, 4, P, P, P, P, 1, P, 1 << 30,
+                                                  0.1, NULL) == -1
+    assert lib.cca_cache_append_decode_varlen_lca(ctypes.byref(d), P, 64, P, 10, 3, P, P, P, P, 1, P, 1 << 30,
+                                                  0.1, NULL) == -1
+    assert lib.cca_cache_extend_lca(ctypes.byref(d), P, 64, P, 10, 4, 2 * 16 + 2, P, P, P, P, 1, P, 1 << 30, 0.1,
+                                    NULL) == -1
+    assert lib.cca_cache_extend_lca(ctypes.byref(d), NULL, 64, P, 10, 4, 4, P, P, P, P, 1, P, 1 << 30, 0.1,
+                                    NULL) == -1
+    # capacity: 64 core slots hold 1024 tokens; a step at position 1023 completes group 63, 1039 needs slot 64
+    assert lib.cca_cache_append_decode_varlen(ctypes.byref(d), P, 1040, 4, P, P, P, P, 1, P, 1 << 30, 0.1,
+                                              NULL) == -5
+    assert lib.cca_cache_load_prefill_lca_gqa(ctypes.byref(d), P, 3, P, P, P, P, P, 100, NULL) == -1
+    # a short serving workspace
+    ws = lib.cca_serve_workspace_bytes(ctypes.byref(d), 4)
+    assert ws > 0 and lib.cca_serve_workspace_bytes(ctypes.byref(d), 3) == 0
+    assert lib.cca_cache_append_decode_varlen(ctypes.byref(d), P, 100, 4, P, P, P, P, 1, P, ws - 1, 0.1,
+                                              NULL) == -3
