@@ -199,8 +199,8 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
     B, Hq, Hkv = 8, 32, 8
     lens0 = [65536 + 9362 * b for b in range(B)]
     n_ext, chunks = 1024, 3
-    cache = binding.ServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + chunks * n_ext + G, dtype=torch.bfloat16,
-                               device=dev)
+    cache = binding.ServeCache(B, Hq, Hkv, D, G, KL, max(lens0) + steps + 32 + chunks * n_ext + G,
+                               dtype=torch.bfloat16, device=dev)
     for b, L in enumerate(lens0):
         q, _, _ = torch_inputs(1, Hq, L, D, torch.bfloat16, dev, seed=seed + 10 + b, heavy_frac=HEAVY)
         _, k, v = torch_inputs(1, Hkv, L, D, torch.bfloat16, dev, seed=seed + 30 + b, heavy_frac=HEAVY)
@@ -229,6 +229,20 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
     byt = [accounting.serve_bytes(lens_at[s], Hq, Hkv, D, G, KL, 2, nchunks) for s in range(warm, steps)]
     us_mean = sum(us) / len(us)
     gbs = sum(byt) / len(byt) / (us_mean * 1e-6) / 1e9
+    # the same step captured once in a HIP graph (work split bounded by the length after the replays)
+    g_steps = 32
+    gr = cache.graph(max(cache.lens_host) + g_steps)
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for s in range(4):
+        gr.step(qs[s], ks[s], vs[s])
+    torch.cuda.synchronize()
+    gev[0].record(stream)
+    for s in range(4, g_steps):   # replays alone (the static inputs hold the last token copied in)
+        gr.graph.replay()
+    gev[1].record(stream)
+    torch.cuda.synchronize()
+    cache.lens_host = [x + g_steps - 4 for x in cache.lens_host]
+    graph_us = gev[0].elapsed_time(gev[1]) / (g_steps - 4) * 1e3
     # chunked append: 1024 new tokens for every sequence per call (four 256-query tiles; one call takes up to k*g+1)
     qe = torch.randn((B, Hq, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
     ke = torch.randn((B, Hkv, n_ext, D), generator=gen, device=dev).to(torch.bfloat16)
@@ -252,6 +266,8 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
             "us_per_step": us_mean, "bytes_per_step": sum(byt) / len(byt),
             "roofline": {"kernel": "cca_serve_decode_kernel<bf16,128,4> + cca_decode_merge_kernel", "bound": "hbm",
                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS},
+            "graph_replay": {"us_per_step": graph_us, "steps_timed": g_steps - 4,
+                             "note": "the step captured once in a HIP graph and replayed back to back"},
             "chunked_append": {"tokens_per_sequence": n_ext, "ms_per_call": ms,
                                "tokens_per_s": B * n_ext / (ms * 1e-3), "flops_per_call": sum(ext_fl) / len(ext_fl),
                                "roofline": {"kernel": "cca_prefill_bf16_d128_kernel<extend> (+ gather, append)",

@@ -568,10 +568,17 @@ class ServeCache(KVCache):
         self.lens_host[b] = L
         self.lens[b] = L
 
-    def step(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
+    def _step_call(self, q, k, v, out, out_dtype, max_len, scale):
+        _check(_lib.cca_cache_append_decode_varlen(ctypes.byref(self.desc), _ptr(self.lens), max_len, self.H_q,
+                                                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(out_dtype),
+                                                   _ptr(self.serve_ws), self.serve_ws_bytes, scale, _stream()),
+               "cca_cache_append_decode_varlen")
+
+    def step(self, q, k, v, out_dtype=None, out=None, scale: float | None = None, max_len: int | None = None):
         """Append one token to every sequence and return its outputs [B, H_q, d].
 
         q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen (which also advances `lens`).
+        `max_len` (default: the longest sequence) bounds every length and sets the work split.
         """
         B, H, d = self.shape_bhd
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -582,13 +589,17 @@ class ServeCache(KVCache):
         if out is None:
             out = torch.empty((B, self.H_q, d), dtype=out_dtype, device=q.device)
         _need(out, (B, self.H_q, d), out_dtype, "out")
-        max_len = max(self.lens_host)
-        _check(_lib.cca_cache_append_decode_varlen(ctypes.byref(self.desc), _ptr(self.lens), max_len, self.H_q,
-                                                   _ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(out_dtype),
-                                                   _ptr(self.serve_ws), self.serve_ws_bytes, scale, _stream()),
-               "cca_cache_append_decode_varlen")
+        bound = max(self.lens_host)
+        max_len = bound if max_len is None else int(max_len)
+        if max_len < bound:
+            raise CCAError("max_len is below a sequence length")
+        self._step_call(q, k, v, out, out_dtype, max_len, scale)
         self.lens_host = [x + 1 for x in self.lens_host]   # the call advanced `lens` on the device
         return out
+
+    def graph(self, max_len: int, out_dtype=None, scale: float | None = None):
+        """A serving step captured in a HIP graph (see ServeGraph)."""
+        return ServeGraph(self, max_len, out_dtype, scale)
 
     def _extend_call(self, m, qs, ks, vs, os_, out_dtype, scale):
         _check(_lib.cca_cache_extend(ctypes.byref(self.desc), _ptr(self.lens), max(self.lens_host), self.H_q, m,
@@ -668,28 +679,12 @@ class LCAServeCache(ServeCache):
         self.lens_host[b] = L
         self.lens[b] = L
 
-    def step(self, q, k, v, out_dtype=None, out=None, scale: float | None = None):
-        """Append one token to every sequence and return its outputs [B, H_q, d].
-
-        q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen_lca (advances `lens`).
-        """
-        B, H, d = self.shape_bhd
-        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-        out_dtype = self.dtype if out_dtype is None else out_dtype
-        _need(q, (B, self.H_q, d), self.dtype, "q")
-        _need(k, (B, H, d), self.dtype, "k")
-        _need(v, (B, H, d), self.dtype, "v")
-        if out is None:
-            out = torch.empty((B, self.H_q, d), dtype=out_dtype, device=q.device)
-        _need(out, (B, self.H_q, d), out_dtype, "out")
-        max_len = max(self.lens_host)
+    def _step_call(self, q, k, v, out, out_dtype, max_len, scale):
         _check(_lib.cca_cache_append_decode_varlen_lca(ctypes.byref(self.desc), _ptr(self.qsum), self.d_rope,
                                                        _ptr(self.lens), max_len, self.H_q, _ptr(q), _ptr(k), _ptr(v),
                                                        _ptr(out), _dtype_code(out_dtype), _ptr(self.serve_ws),
                                                        self.serve_ws_bytes, scale, _stream()),
                "cca_cache_append_decode_varlen_lca")
-        self.lens_host = [x + 1 for x in self.lens_host]
-        return out
 
     def _extend_call(self, m, qs, ks, vs, os_, out_dtype, scale):
         _check(_lib.cca_cache_extend_lca(ctypes.byref(self.desc), _ptr(self.qsum), self.d_rope, _ptr(self.lens),
@@ -697,6 +692,45 @@ class LCAServeCache(ServeCache):
                                          _dtype_code(out_dtype), _ptr(self._ext_ws), self._ext_ws.numel() * 4, scale,
                                          _stream()),
                "cca_cache_extend_lca")
+
+
+class ServeGraph:
+    """One serving decode step of a ServeCache (or LCAServeCache) captured in a HIP graph.
+
+    The step keeps every length on the device and allocates nothing, so it can be captured
+    once and replayed per token.  The capture fixes the host-side work-split bound `max_len`:
+    every replay must leave each sequence at most that long.  A sequence that has outgrown
+    it gets NaN outputs and is not advanced, as in the plain call.  Write the token's q, k, v
+    into `self.q`, `self.k`, `self.v` (or pass them to `step`), replay, and read `self.out`.
+    """
+
+    def __init__(self, cache: ServeCache, max_len: int, out_dtype=None, scale: float | None = None):
+        B, H, d = cache.shape_bhd
+        if max(cache.lens_host) > max_len:
+            raise CCAError("max_len is below a sequence length")
+        self.cache = cache
+        self.max_len = int(max_len)
+        self.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        self.out_dtype = cache.dtype if out_dtype is None else out_dtype
+        dev = cache.core_k.device
+        self.q = torch.zeros((B, cache.H_q, d), dtype=cache.dtype, device=dev)
+        self.k = torch.zeros((B, H, d), dtype=cache.dtype, device=dev)
+        self.v = torch.zeros((B, H, d), dtype=cache.dtype, device=dev)
+        self.out = torch.empty((B, cache.H_q, d), dtype=self.out_dtype, device=dev)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            # capture only: nothing runs, so the cache and the lengths are untouched here
+            cache._step_call(self.q, self.k, self.v, self.out, self.out_dtype, self.max_len, self.scale)
+
+    def step(self, q=None, k=None, v=None):
+        """Copy the token's inputs in (if given), replay the step and return `self.out`."""
+        for dst, src in ((self.q, q), (self.k, k), (self.v, v)):
+            if src is not None:
+                dst.copy_(src)
+        self.graph.replay()
+        self.cache.lens_host = [x + 1 if x <= self.max_len else x for x in self.cache.lens_host]
+        return self.out
 
 
 def cache_append(cache: KVCache, q, k, v, scale=None):

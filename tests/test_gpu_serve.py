@@ -138,3 +138,49 @@ def test_serve_capacity_error(gpu):
         cache.step(*step)                            # position 47 completes group 2: a third core slot
     # the failed call changed nothing on the host side
     assert cache.lens_host == [47]
+
+
+@pytest.mark.parametrize("lca", [False, True], ids=["cca", "lca"])
+def test_serve_graph_replay_matches_eager(gpu, lca):
+    """A serving step captured in a HIP graph and replayed once per token gives bit-identical
+    outputs, caches and lengths to the eager calls with the same work-split bound.  Eager
+    work and synchronisations run between the replays, and every replay is checked."""
+    B, Hq, Hkv, d, g, k, dt, lens0, T, seed = (3, 4, 2, 128, 16, 2, "bf16", [100, 37, 0], 40, 38)
+    bound = max(lens0) + T
+    total = bound + 1
+    Q, _, _ = np_inputs(B, Hq, total, d, dt, seed)
+    _, K, V = np_inputs(B, Hkv, total, d, dt, seed + 1000)
+    scale = 1.0 / math.sqrt(d)
+
+    def make():
+        if lca:
+            c = binding.LCAServeCache(B, Hq, Hkv, d, g, k, total + g, 64, dtype=TDT[dt], device=gpu)
+        else:
+            c = binding.ServeCache(B, Hq, Hkv, d, g, k, total + g, dtype=TDT[dt], device=gpu)
+        for b, L in enumerate(lens0):
+            if L:
+                qb, kb, vb = (_dev(x[b:b + 1, :, :L], dt, gpu) for x in (Q, K, V))
+                if lca:
+                    _, kc, vc, _ = binding.prefill_lca(qb, kb, vb, g, k, 64, scale)
+                    c.load_sequence(b, qb, kb, vb, kc, vc)
+                else:
+                    _, kc, vc = binding.prefill(qb, kb, vb, g, k, scale, return_core=True)
+                    c.load_sequence(b, kb, vb, kc, vc)
+        return c
+
+    eager, graphed = make(), make()
+    torch.cuda.synchronize()
+    gr = graphed.graph(bound, out_dtype=torch.float32, scale=scale)
+    assert graphed.lens.cpu().tolist() == lens0          # capturing ran nothing
+    for i in range(T):
+        q = _dev(np.stack([Q[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
+        kk = _dev(np.stack([K[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
+        v = _dev(np.stack([V[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
+        want = eager.step(q, kk, v, out_dtype=torch.float32, scale=scale, max_len=bound)
+        got = gr.step(q, kk, v)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), f"step {i}: replay differs from the eager call"
+    assert graphed.lens.cpu().tolist() == eager.lens.cpu().tolist() == [L + T for L in lens0]
+    assert graphed.lens_host == eager.lens_host
+    for name in ("core_k", "core_v", "ring_k", "ring_v") + (("qsum",) if lca else ()):
+        assert torch.equal(getattr(graphed, name), getattr(eager, name)), name
