@@ -174,3 +174,42 @@ def test_attention_entry_matches_prefill(gpu):
     b = binding.attention(q, kk, v, kc2, vc2, 16, 3, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(kc, kc2) and torch.equal(vc, vc2) and torch.equal(a, b)
+
+
+def _extreme_inputs(kind, L, d, dt, seed):
+    """Score ranges far from N(0,1): 'sharp' scales Q by 8 and K by 4 (scores with standard
+    deviation 32: nearly one-hot softmaxes); 'ramp' adds a component shared by every query
+    whose key weight grows with the position, so the running maximum rises at almost every
+    key sub-block (the rescaling path of the online softmax)."""
+    Q, K, V = np_inputs(1, 1, L, d, "f32", seed)
+    if kind == "sharp":
+        Q, K = Q * 8.0, K * 4.0
+    else:
+        u = np.ones(d, dtype=np.float32) / np.sqrt(d)
+        Q = Q + 6.0 * u
+        K = K + (np.arange(L, dtype=np.float32)[:, None] * (40.0 / L)) * u
+    if dt == "bf16":
+        Q, K, V = (torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).float().numpy() for x in (Q, K, V))
+    return Q, K, V
+
+
+@pytest.mark.parametrize("case", [("sharp", 700, 128, 16, 2, "bf16"), ("sharp", 500, 64, 8, 3, "f32"),
+                                  ("ramp", 1000, 128, 16, 4, "bf16"), ("ramp", 600, 64, 5, 2, "f32")],
+                         ids=lambda c: f"{c[0]}-L{c[1]}d{c[2]}g{c[3]}k{c[4]}-{c[5]}")
+def test_prefill_extreme_score_ranges(gpu, case):
+    kind, L, d, g, k, dt = case
+    _say(f"extreme-score prefill {case}")
+    Q, K, V = _extreme_inputs(kind, L, d, dt, 15)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    out = binding.prefill(q, kk, v, g, k, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, scale, core_dtype=dt)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - want).max()
+    # Large scores are ill-conditioned in float32: a score carries a rounding error of about
+    # sqrt(d) * 2^-24 * sum_i |q_i k_i| * scale, a weight the same relative error, and the
+    # output at most twice the largest of them times max|V|.  Added to the usual bound.
+    Q0, K0 = np.abs(Q[0, 0].astype(np.float64)), np.abs(K[0, 0].astype(np.float64))
+    ds = math.sqrt(d) * 2.0 ** -24 * (Q0 @ K0.T).max() * scale
+    tol = TOL[dt] + 2.0 * ds * np.abs(V).max()
+    assert np.isfinite(err) and err <= tol, f"max abs err {err:.3e} > {tol:.3e}"
