@@ -51,7 +51,7 @@ typedef enum {
   CCA_OK = 0,
   CCA_ERR_INVALID = -1,     /* null pointer, misaligned pointer, bad size or count */
   CCA_ERR_UNSUPPORTED = -2, /* head dim not 64/128, dtype combination not built */
-  CCA_ERR_WORKSPACE = -3,   /* decode workspace smaller than cca_decode_workspace_bytes() */
+  CCA_ERR_WORKSPACE = -3,   /* workspace smaller than the matching *_workspace_bytes() */
   CCA_ERR_HIP = -4,         /* a kernel launch failed */
   CCA_ERR_CAPACITY = -5     /* the cache has no room for another token */
 } cca_status_t;
