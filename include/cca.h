@@ -58,7 +58,8 @@ typedef enum {
 
 typedef enum {
   CCA_F32 = 0,  /* IEEE float32 */
-  CCA_BF16 = 1  /* bfloat16 (upper half of a float32; conversions round to nearest even) */
+  CCA_BF16 = 1, /* bfloat16 (upper half of a float32; conversions round to nearest even) */
+  CCA_F16 = 2   /* IEEE binary16 (conversions round to nearest even; overflow gives infinity) */
 } cca_dtype_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -87,9 +88,10 @@ int cca_pool_kv(const void* q, const void* k, const void* v, void* kc, void* vc,
  *             them, e.g. to seed a decode cache with cca_cache_load_prefill).
  *             May be NULL when floor(L/g) == 0.
  *   out     : device, [B, H, L, d] of dtype out_dt, written.  out_dt is CCA_F32
- *             or equal to dt.  Accumulation is float32; for dt = CCA_BF16 the
- *             QK^T and PV products run on bf16 matrix cores with the softmax
- *             weights rounded to bf16, for dt = CCA_F32 on float32 matrix cores.
+ *             or equal to dt.  Accumulation is float32; for dt = CCA_BF16 or
+ *             CCA_F16 the QK^T and PV products run on matrix cores of that type
+ *             with the softmax weights rounded to it, for dt = CCA_F32 on
+ *             float32 matrix cores.
  *   k_local >= 0 (any value >= floor((L-1)/g) gives plain causal attention);
  *   L <= INT32_MAX; B*H*ceil(L/128) and B*H*floor(L/g) below INT32_MAX.
  */
@@ -171,7 +173,7 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
 
 /*
  * Training ([CCA] Triton section: the fused operator serves training as well;
- * the models are fine-tuned with it).  bf16 or float32 inputs, d = 64 or 128,
+ * the models are fine-tuned with it).  bf16, binary16 or float32 inputs, d = 64 or 128,
  * one query head per key/value head.  bf16 at d = 128 runs on the matrix cores;
  * the other combinations run a plain float32 vector path, correct but far slower.
  *
@@ -185,7 +187,7 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
  *   (core token j: Kc = a.K_group, Vc = a.V_group, a = softmax(scale q_hat.K_group),
  *   so the gradients of Kc and Vc reach the group's keys and values and its
  *   scoring query Q[j*g+g-1]).  The forward's rounding of the core tokens to
- *   bf16 is treated as the identity.
+ *   a 16-bit dt is treated as the identity.
  *   q, k, v, kc, vc, out : the forward's inputs and results, all of type dt
  *           (out_dt of the forward must equal dt);
  *   lse   : device float32 [B, H, L] from cca_prefill_lse;

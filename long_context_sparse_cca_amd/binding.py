@@ -18,9 +18,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcca.so")
 
-CCA_F32, CCA_BF16 = 0, 1
-_DT = {torch.float32: CCA_F32, torch.bfloat16: CCA_BF16}
-_TORCH_DT = {CCA_F32: torch.float32, CCA_BF16: torch.bfloat16}
+CCA_F32, CCA_BF16, CCA_F16 = 0, 1, 2
+_DT = {torch.float32: CCA_F32, torch.bfloat16: CCA_BF16, torch.float16: CCA_F16}
+_TORCH_DT = {CCA_F32: torch.float32, CCA_BF16: torch.bfloat16, CCA_F16: torch.float16}
 
 _lib = None
 
@@ -379,7 +379,7 @@ def backward(q, k, v, kc, vc, out, lse, dout, g: int, k_local: int, scale: float
 
 
 class CCAAttention(torch.autograd.Function):
-    """CCA prefill attention as an autograd function (bf16 or float32, d = 64 or 128; k, v may
+    """CCA prefill attention as an autograd function (bf16, binary16 or float32, d = 64 or 128; k, v may
     have fewer heads than q): forward cca_prefill_lse, backward cca_backward.
     apply(q, k, v, g, k_local, scale=None) -> out [B,H,L,d]."""
 

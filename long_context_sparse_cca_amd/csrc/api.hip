@@ -12,7 +12,7 @@ constexpr int kMaxGroup = 4096;  // pooling keeps one float score per group row 
 bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 
 int check_shape(int B, int H, int64_t L, int d, int g, int dt) {
-  if (dt != CCA_F32 && dt != CCA_BF16) return CCA_ERR_UNSUPPORTED;
+  if (dt != CCA_F32 && dt != CCA_BF16 && dt != CCA_F16) return CCA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CCA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || L < 0 || g < 1 || g > kMaxGroup) return CCA_ERR_INVALID;
   if ((int64_t)B * H > (int64_t)1 << 24) return CCA_ERR_INVALID;
@@ -414,8 +414,8 @@ int cca_cache_extend_lca(const cca_cache_t* c, float* qsum, int d_rope, int32_t*
 int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt, int64_t* resident_bytes,
                        int64_t* full_bytes) {
   if (n_tokens < 0 || g < 1 || k_local < 0 || B < 1 || H < 1 || d < 1) return CCA_ERR_INVALID;
-  if (dt != CCA_F32 && dt != CCA_BF16) return CCA_ERR_UNSUPPORTED;
-  const int64_t per_token = (int64_t)B * H * 2 * d * (dt == CCA_BF16 ? 2 : 4);
+  if (dt != CCA_F32 && dt != CCA_BF16 && dt != CCA_F16) return CCA_ERR_UNSUPPORTED;
+  const int64_t per_token = (int64_t)B * H * 2 * d * cca::dtype_bytes(dt);
   if (resident_bytes) *resident_bytes = per_token * (n_tokens / g + (int64_t)(k_local + 1) * g);
   if (full_bytes) *full_bytes = per_token * n_tokens;
   return CCA_OK;

@@ -32,10 +32,8 @@ __device__ __forceinline__ void load_dims(const T* p, float* f) {
       Elem<T>::chunk_to_f32(ld16(p), f);
     } else {
       const uint2 w = *reinterpret_cast<const uint2*>(p);
-      f[0] = __uint_as_float(w.x << 16);
-      f[1] = __uint_as_float(w.x & 0xffff0000u);
-      f[2] = __uint_as_float(w.y << 16);
-      f[3] = __uint_as_float(w.y & 0xffff0000u);
+      Elem<T>::pair_to_f32(w.x, f);
+      Elem<T>::pair_to_f32(w.y, f + 2);
     }
   } else {
 #pragma unroll
@@ -311,18 +309,10 @@ hipError_t launch_backward_generic(int dt, int d, const void* q, const void* k, 
                                    const void* vc, const void* out, const float* lse, const void* dout, float* dq,
                                    float* dk, float* dv, void* workspace, int BH, int nq, int64_t L, int g,
                                    int k_local, float scale, hipStream_t stream) {
-  if (dt == CCA_BF16) {
-    if (d == 128)
-      return launch_t<bf16_t, 128>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq, L, g, k_local,
-                                   scale, stream);
-    return launch_t<bf16_t, 64>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq, L, g, k_local,
-                                scale, stream);
-  }
-  if (d == 128)
-    return launch_t<float, 128>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq, L, g, k_local,
-                                scale, stream);
-  return launch_t<float, 64>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq, L, g, k_local, scale,
-                             stream);
+  return dispatch_td(dt, d, [&](auto t, auto dd) {
+    return launch_t<decltype(t), decltype(dd)::value>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq,
+                                                      L, g, k_local, scale, stream);
+  });
 }
 
 }  // namespace cca

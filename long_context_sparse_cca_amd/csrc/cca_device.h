@@ -30,6 +30,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// IEEE binary16 is stored as its 16-bit pattern; arithmetic happens in float32.
+struct f16_t {
+  uint16_t bits;
+};
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// Round-to-nearest-even float32 -> binary16 bits (overflow gives infinity).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+}
+
 // Element traits: loads of 16-byte chunks and conversion to float.
 template <typename T> struct Elem;
 
@@ -46,6 +63,34 @@ template <> struct Elem<bf16_t> {
   }
   __device__ __forceinline__ static float load1(const bf16_t* p) { return bf16_bits_to_f32(p->bits); }
   __device__ __forceinline__ static void store1(bf16_t* p, float v) { p->bits = f32_to_bf16_bits(v); }
+  // 16-bit types: one element from its bits, two from a 32-bit word, two packed into one
+  __device__ __forceinline__ static float bits_to_f32(uint32_t h) { return bf16_bits_to_f32(h); }
+  __device__ __forceinline__ static void pair_to_f32(uint32_t w, float* f) {
+    f[0] = __uint_as_float(w << 16);
+    f[1] = __uint_as_float(w & 0xffff0000u);
+  }
+  __device__ __forceinline__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  static constexpr uint16_t kNaNBits = 0x7fc0;
+};
+
+template <> struct Elem<f16_t> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerChunk = 8;
+  __device__ __forceinline__ static void chunk_to_f32(const uint4& c, float* f) {
+    const f16x8_t h = __builtin_bit_cast(f16x8_t, c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+  }
+  __device__ __forceinline__ static float load1(const f16_t* p) { return f16_bits_to_f32(p->bits); }
+  __device__ __forceinline__ static void store1(f16_t* p, float v) { p->bits = f32_to_f16_bits(v); }
+  __device__ __forceinline__ static float bits_to_f32(uint32_t h) { return f16_bits_to_f32(h); }
+  __device__ __forceinline__ static void pair_to_f32(uint32_t w, float* f) {
+    const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+    f[0] = (float)h[0];
+    f[1] = (float)h[1];
+  }
+  __device__ __forceinline__ static uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+  static constexpr uint16_t kNaNBits = 0x7e00;
 };
 
 template <> struct Elem<float> {

@@ -1,10 +1,32 @@
 // Internal launch interface between the C ABI (api.hip) and the kernel files.
 #pragma once
 
+#include <type_traits>
+
 #include "cca_device.h"
 #include "cca.h"
 
 namespace cca {
+
+// Calls fn(T{}, std::integral_constant<int, D>{}) with the element type T of cca_dtype_t
+// dt (bf16_t, f16_t or float) and the head dim D (64 or 128; validated by the caller).
+template <typename Fn>
+hipError_t dispatch_td(int dt, int d, Fn&& fn) {
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  if (dt == CCA_BF16) return d == 128 ? fn(bf16_t{}, D128{}) : fn(bf16_t{}, D64{});
+  if (dt == CCA_F16) return d == 128 ? fn(f16_t{}, D128{}) : fn(f16_t{}, D64{});
+  return d == 128 ? fn(float{}, D128{}) : fn(float{}, D64{});
+}
+
+// Output encoding of the decode merge: 0 float32, 1 bf16, 2 binary16.
+inline int out_mode(int out_f32, int dt) {
+  if (out_f32) return 0;
+  return dt == CCA_BF16 ? 1 : (dt == CCA_F16 ? 2 : 0);
+}
+
+// Bytes per element of a cca_dtype_t.
+inline int dtype_bytes(int dt) { return dt == CCA_F32 ? 4 : 2; }
 
 // Each launcher enqueues its kernels on `stream` and returns the launch status.
 // Arguments have been validated by the caller (api.hip).
@@ -83,7 +105,7 @@ hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, in
 // [nslices][nchunks][d] floats, then ml [nslices][nchunks][2]) into out [nslices][d].
 // With lens non-null, lens[b] (b = slice / slices_per_seq) is then advanced by one
 // when it lies in [0, max_len].
-hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_bf16,
+hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_mode,
                                int64_t nslices, int nchunks, int32_t* lens, int slices_per_seq, int64_t max_len,
                                hipStream_t stream);
 

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __restrict__ ws_acc,
                                                               const float* __restrict__ ws_ml, void* __restrict__ out,
-                                                              int out_bf16, int nchunks, int32_t* __restrict__ lens,
+                                                              int out_mode, int nchunks, int32_t* __restrict__ lens,
                                                               int slices_per_seq, int64_t max_len) {
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
@@ -376,7 +376,8 @@ __global__ __launch_bounds__(64) void cca_decode_merge_kernel(const float* __res
 #pragma unroll
   for (int e = 0; e < CPL; ++e) {
     const size_t o = (size_t)bh * D + lane * CPL + e;
-    if (out_bf16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(a[e] * inv);
+    if (out_mode == 1) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(a[e] * inv);
+    else if (out_mode == 2) reinterpret_cast<uint16_t*>(out)[o] = f32_to_f16_bits(a[e] * inv);
     else reinterpret_cast<float*>(out)[o] = a[e] * inv;
   }
   if (lens != nullptr && lane == 0 && bh % slices_per_seq == 0) {
@@ -417,9 +418,8 @@ hipError_t launch_decode_t(const cca_cache_t* c, const void* q, const void* k_ne
                        nchunks, scale, qsum, d_rope);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
   hipLaunchKernelGGL((cca_decode_merge_kernel<D>), dim3((unsigned)BH), dim3(64), 0, stream, ws.acc, ws.ml, out,
-                     out_bf16, nchunks, (int32_t*)nullptr, 1, (int64_t)0);
+                     out_mode(out_f32, c->dt), nchunks, (int32_t*)nullptr, 1, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -427,14 +427,11 @@ template <int APPEND>
 hipError_t launch_decode_any(const cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
                              int out_f32, void* workspace, float scale, float* qsum, int d_rope,
                              hipStream_t stream) {
-  if (c->dt == CCA_BF16) {
-    if (c->d == 128)
-      return launch_decode_t<bf16_t, 128, APPEND>(c, q, k, v, out, out_f32, workspace, scale, qsum, d_rope, stream);
-    return launch_decode_t<bf16_t, 64, APPEND>(c, q, k, v, out, out_f32, workspace, scale, qsum, d_rope, stream);
-  }
-  if (c->d == 128)
-    return launch_decode_t<float, 128, APPEND>(c, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
-  return launch_decode_t<float, 64, APPEND>(c, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
+  return dispatch_td(c->dt, c->d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    return launch_decode_t<T, decltype(dd)::value, APPEND>(c, q, k, v, out, sizeof(T) == 4 ? 1 : out_f32, workspace,
+                                                           scale, qsum, d_rope, stream);
+  });
 }
 
 // Running sums of the queries of each slice's trailing partial group (rows m*g .. L-1)
@@ -500,8 +497,7 @@ size_t decode_workspace_bytes(const cca_cache_t* c) {
 hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc, const void* vc,
                              int64_t L, hipStream_t stream) {
   const int64_t BH = (int64_t)c->B * c->H;
-  const int esz = (c->dt == CCA_BF16) ? 2 : 4;
-  const int cpr = c->d * esz / 16;
+  const int cpr = c->d * dtype_bytes(c->dt) / 16;
   const int64_t m = L / c->g;
   const int64_t R = (int64_t)(c->k_local + 1) * c->g;
   hipError_t e = copy_rows(kc, c->core_k, vc, c->core_v, BH, m, cpr, m, 0, c->max_groups, 0, INT64_MAX, stream);
@@ -512,24 +508,21 @@ hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v,
 
 hipError_t launch_cache_append(const cca_cache_t* c, const void* q, const void* k, const void* v, float scale,
                                hipStream_t stream) {
-  if (c->dt == CCA_BF16) {
-    if (c->d == 128) return launch_append_t<bf16_t, 128>(c, q, k, v, scale, stream);
-    return launch_append_t<bf16_t, 64>(c, q, k, v, scale, stream);
-  }
-  if (c->d == 128) return launch_append_t<float, 128>(c, q, k, v, scale, stream);
-  return launch_append_t<float, 64>(c, q, k, v, scale, stream);
+  return dispatch_td(c->dt, c->d, [&](auto t, auto dd) {
+    return launch_append_t<decltype(t), decltype(dd)::value>(c, q, k, v, scale, stream);
+  });
 }
 
-hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_bf16,
+hipError_t launch_decode_merge(int d, const float* ws_acc, const float* ws_ml, void* out, int out_mode,
                                int64_t nslices, int nchunks, int32_t* lens, int slices_per_seq, int64_t max_len,
                                hipStream_t stream) {
   if (nslices == 0) return hipSuccess;
   if (d == 128)
     hipLaunchKernelGGL((cca_decode_merge_kernel<128>), dim3((unsigned)nslices), dim3(64), 0, stream, ws_acc, ws_ml,
-                       out, out_bf16, nchunks, lens, slices_per_seq, max_len);
+                       out, out_mode, nchunks, lens, slices_per_seq, max_len);
   else
     hipLaunchKernelGGL((cca_decode_merge_kernel<64>), dim3((unsigned)nslices), dim3(64), 0, stream, ws_acc, ws_ml,
-                       out, out_bf16, nchunks, lens, slices_per_seq, max_len);
+                       out, out_mode, nchunks, lens, slices_per_seq, max_len);
   return hipGetLastError();
 }
 
@@ -551,12 +544,9 @@ hipError_t launch_append_decode_lca(const cca_cache_t* c, float* qsum, int d_rop
 
 hipError_t launch_qsum_seed(const cca_cache_t* c, const void* q, float* qsum, int64_t L, int nq,
                             hipStream_t stream) {
-  if (c->dt == CCA_BF16) {
-    if (c->d == 128) return launch_qsum_seed_t<bf16_t, 128>(c, q, qsum, L, nq, stream);
-    return launch_qsum_seed_t<bf16_t, 64>(c, q, qsum, L, nq, stream);
-  }
-  if (c->d == 128) return launch_qsum_seed_t<float, 128>(c, q, qsum, L, nq, stream);
-  return launch_qsum_seed_t<float, 64>(c, q, qsum, L, nq, stream);
+  return dispatch_td(c->dt, c->d, [&](auto t, auto dd) {
+    return launch_qsum_seed_t<decltype(t), decltype(dd)::value>(c, q, qsum, L, nq, stream);
+  });
 }
 
 }  // namespace cca

@@ -240,25 +240,19 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
 
 size_t extend_workspace_bytes(const cca_cache_t* c, int n) {
   const size_t R = (size_t)(c->k_local + 1) * c->g;
-  const size_t esz = (c->dt == CCA_BF16) ? 2 : 4;
+  const size_t esz = (size_t)dtype_bytes(c->dt);
   return pos_bytes(c->B) + 2 * (size_t)c->B * c->H * (R + (size_t)n) * c->d * esz;
 }
 
 hipError_t launch_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,
                          const void* k, const void* v, void* out, int out_f32, void* workspace, float scale,
                          hipStream_t stream, float* qsum, int d_rope) {
-  if (c->dt == CCA_BF16) {
-    if (c->d == 128)
-      return launch_extend_t<bf16_t, 128>(c, lens, max_len, H_q, n, q, k, v, out, out_f32, workspace, scale, qsum,
-                                          d_rope, stream);
-    return launch_extend_t<bf16_t, 64>(c, lens, max_len, H_q, n, q, k, v, out, out_f32, workspace, scale, qsum,
-                                       d_rope, stream);
-  }
-  if (c->d == 128)
-    return launch_extend_t<float, 128>(c, lens, max_len, H_q, n, q, k, v, out, 1, workspace, scale, qsum, d_rope,
-                                       stream);
-  return launch_extend_t<float, 64>(c, lens, max_len, H_q, n, q, k, v, out, 1, workspace, scale, qsum, d_rope,
-                                    stream);
+  return dispatch_td(c->dt, c->d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    return launch_extend_t<T, decltype(dd)::value>(c, lens, max_len, H_q, n, q, k, v, out,
+                                                   sizeof(T) == 4 ? 1 : out_f32, workspace, scale, qsum, d_rope,
+                                                   stream);
+  });
 }
 
 }  // namespace cca

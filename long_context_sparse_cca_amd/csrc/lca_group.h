@@ -20,11 +20,9 @@ __device__ __forceinline__ void lca_load_cols(const T* p, float* f) {
   constexpr int CPL = D / kWave;   // columns per lane: 1 or 2
   if constexpr (sizeof(T) == 2) {
     if constexpr (CPL == 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-      f[0] = __uint_as_float(w << 16);
-      f[1] = __uint_as_float(w & 0xffff0000u);
+      Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(p), f);
     } else {
-      f[0] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[0]);
+      f[0] = Elem<T>::bits_to_f32(reinterpret_cast<const uint16_t*>(p)[0]);
     }
   } else {
 #pragma unroll

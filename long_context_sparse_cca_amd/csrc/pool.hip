@@ -152,11 +152,10 @@ hipError_t launch_pool(int dt, int d, const void* q, const void* k, const void* 
                            m, n, nq, scale);
       return hipGetLastError();
     }
-    if (d == 128) return launch_pool_t<bf16_t, 128>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
-    return launch_pool_t<bf16_t, 64>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
   }
-  if (d == 128) return launch_pool_t<float, 128>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
-  return launch_pool_t<float, 64>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
+  return dispatch_td(dt, d, [&](auto t, auto dd) {
+    return launch_pool_t<decltype(t), decltype(dd)::value>(q, k, v, kc, vc, BHkv, L, g, nq, scale, stream);
+  });
 }
 
 }  // namespace cca

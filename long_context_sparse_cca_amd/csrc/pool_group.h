@@ -16,12 +16,10 @@ template <typename T, int N>
 __device__ __forceinline__ void load_n(const T* p, float* f) {
   if constexpr (sizeof(T) == 2) {
     if constexpr (N == 2) {
-      uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-      f[0] = __uint_as_float(w << 16);
-      f[1] = __uint_as_float(w & 0xffff0000u);
+      Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(p), f);
     } else {
       static_assert(N == 1, "");
-      f[0] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[0]);
+      f[0] = Elem<T>::bits_to_f32(reinterpret_cast<const uint16_t*>(p)[0]);
     }
   } else {
 #pragma unroll

@@ -75,12 +75,10 @@ hipError_t launch_t(const void* q, const void* k, const void* v, void* kc, void*
 hipError_t launch_pool_lca(int dt, int d, const void* q, const void* k, const void* v, void* kc, void* vc,
                            int32_t* anchors, int BHkv, int64_t L, int g, int nq, int d_rope, float scale,
                            hipStream_t stream) {
-  if (dt == CCA_BF16) {
-    if (d == 128) return launch_t<bf16_t, 128>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
-    return launch_t<bf16_t, 64>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
-  }
-  if (d == 128) return launch_t<float, 128>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
-  return launch_t<float, 64>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale, stream);
+  return dispatch_td(dt, d, [&](auto t, auto dd) {
+    return launch_t<decltype(t), decltype(dd)::value>(q, k, v, kc, vc, anchors, BHkv, L, g, nq, d_rope, scale,
+                                                      stream);
+  });
 }
 
 }  // namespace cca

@@ -17,7 +17,8 @@
 //     fully visible or masked for its own 32 queries;
 //   * S^T = K Q^T on MFMA (32x32 output: lane = query, 16 keys per lane), so the
 //     running max / sum are per-lane scalars and a row max needs one shuffle;
-//   * O^T += V^T P^T on MFMA with P rounded to the input type (bf16) or kept fp32.
+//   * O^T += V^T P^T on MFMA with P rounded to the input type (bf16 or binary16) or
+//     kept fp32.
 #include "cca_internal.h"
 
 namespace cca {
@@ -47,6 +48,17 @@ struct PrefillCfg {
 };
 
 enum : int { kSkip = 0, kFull = 1, kMask = 2 };
+
+// 32x32x16 MFMA on 16-bit operands of type T (bf16_t or f16_t) held as 16-byte chunks.
+template <typename T>
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b, const f32x16_t& c) {
+  if constexpr (std::is_same_v<T, bf16_t>)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
 
 // Running-max threshold (log2 units) below which the accumulators are not
 // rescaled: exp2(s - m_run) then stays <= 2^8, far from overflow in fp32 and
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const size_t o = ((size_t)bh * nQ + i) * D;
         for (int c = hf; c < D; c += 2) {
           if (out_f32) reinterpret_cast<float*>(Out)[o + c] = __builtin_nanf("");
-          else reinterpret_cast<uint16_t*>(Out)[o + c] = 0x7fc0;
+          else if constexpr (sizeof(T) == 2) reinterpret_cast<uint16_t*>(Out)[o + c] = Elem<T>::kNaNBits;
         }
       }
       return;
@@ -256,10 +268,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (C::EB == 2) {
           const T* krow = &lds_k[buf][(sb * 32 + l32) * C::KP + hf * 8];
 #pragma unroll
-          for (int d16 = 0; d16 < D / 16; ++d16) {
-            bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + d16 * 16));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, qop[d16]), s, 0, 0, 0);
-          }
+          for (int d16 = 0; d16 < D / 16; ++d16)
+            s = mfma_32x32x16<T>(*reinterpret_cast<const uint4*>(krow + d16 * 16), qop[d16], s);
         } else {
           const T* krow = &lds_k[buf][(sb * 32 + l32) * C::KP + hf * (D / 2)];
 #pragma unroll
@@ -305,19 +315,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         if constexpr (C::EB == 2) {
           // P^T as B operand: keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u..8u+7.
-          // The row sum takes the bf16-rounded weights, the values the MFMA multiplies.
+          // The row sum takes the weights rounded to T, the values the MFMA multiplies
+          // (weights stay <= 2^8 by the rescale threshold, within binary16's range too).
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            bf16x8_t pb;
+            uint4 pb;
+            uint32_t* pw = reinterpret_cast<uint32_t*>(&pb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[8 * u + e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) l_run += (float)pb[e];
+            for (int e = 0; e < 4; ++e) {
+              pw[e] = Elem<T>::pack2(p[8 * u + 2 * e], p[8 * u + 2 * e + 1]);
+              float f[2];
+              Elem<T>::pair_to_f32(pw[e], f);
+              l_run += f[0];
+              l_run += f[1];
+            }
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt) {
               const uint4 w = *reinterpret_cast<const uint4*>(
                   &lds_v[buf][(dt * 32 + l32) * C::VP + sb * 32 + 16 * u + 8 * hf]);
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb, acc[dt], 0, 0, 0);
+              acc[dt] = mfma_32x32x16<T>(w, pb, acc[dt]);
             }
           }
         } else {
@@ -369,8 +385,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint2 w;
-        w.x = pack_bf16x2(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv);
-        w.y = pack_bf16x2(acc[dt][4 * i + 2] * inv, acc[dt][4 * i + 3] * inv);
+        w.x = Elem<T>::pack2(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv);
+        w.y = Elem<T>::pack2(acc[dt][4 * i + 2] * inv, acc[dt][4 * i + 3] * inv);
         *reinterpret_cast<uint2*>(o + dt * 32 + 8 * i + 4 * hf) = w;
       }
   }
@@ -416,26 +432,25 @@ hipError_t launch_extend_t(const void* q, const void* k, const void* v, const vo
 hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                     const void* vc, void* out, int out_f32, int BH, int nq, int64_t L, int g,
                                     int k_local, float scale, hipStream_t stream, float* lse) {
-  if (dt == CCA_BF16) {
-    if (d == 128)
-      return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
-    return launch_prefill_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
-  }
-  if (d == 128)
-    return launch_prefill_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream, lse);
-  return launch_prefill_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, L, g, k_local, scale, stream, lse);
+  if (dt == CCA_BF16 && d == 128)
+    return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
+  return dispatch_td(dt, d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    return launch_prefill_t<T, decltype(dd)::value>(q, k, v, kc, vc, out, sizeof(T) == 4 ? 1 : out_f32, BH, nq, L, g,
+                                                    k_local, scale, stream, lse);
+  });
 }
 
 hipError_t launch_extend_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                    const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
                                    float scale, const ExtendArgs& ext, hipStream_t stream) {
-  if (dt == CCA_BF16) {
-    if (d == 128)
-      return launch_extend_attention_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
-    return launch_extend_t<bf16_t, 64>(q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
-  }
-  if (d == 128) return launch_extend_t<float, 128>(q, k, v, kc, vc, out, 1, BH, nq, g, k_local, scale, ext, stream);
-  return launch_extend_t<float, 64>(q, k, v, kc, vc, out, 1, BH, nq, g, k_local, scale, ext, stream);
+  if (dt == CCA_BF16 && d == 128)
+    return launch_extend_attention_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
+  return dispatch_td(dt, d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    return launch_extend_t<T, decltype(dd)::value>(q, k, v, kc, vc, out, sizeof(T) == 4 ? 1 : out_f32, BH, nq, g,
+                                                   k_local, scale, ext, stream);
+  });
 }
 
 }  // namespace cca

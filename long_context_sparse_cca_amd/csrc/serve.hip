@@ -335,8 +335,8 @@ hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int out_bf16 = out_f32 ? 0 : (c->dt == CCA_BF16);
-  return launch_decode_merge(D, ws_acc, ws_ml, out, out_bf16, (int64_t)c->B * H_q, nchunks, lens, H_q, max_len,
+  return launch_decode_merge(D, ws_acc, ws_ml, out, out_mode(out_f32, c->dt), (int64_t)c->B * H_q, nchunks, lens, H_q,
+                             max_len,
                              stream);
 }
 
@@ -379,16 +379,11 @@ size_t serve_workspace_bytes(const cca_cache_t* c, int H_q) {
 hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q,
                                       const void* q, const void* k, const void* v, void* out, int out_f32,
                                       void* workspace, float scale, hipStream_t stream, float* qsum, int d_rope) {
-  if (c->dt == CCA_BF16) {
-    if (c->d == 128)
-      return launch_serve_d<bf16_t, 128>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, qsum, d_rope,
-                                         stream);
-    return launch_serve_d<bf16_t, 64>(c, lens, max_len, H_q, q, k, v, out, out_f32, workspace, scale, qsum, d_rope,
-                                      stream);
-  }
-  if (c->d == 128)
-    return launch_serve_d<float, 128>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
-  return launch_serve_d<float, 64>(c, lens, max_len, H_q, q, k, v, out, 1, workspace, scale, qsum, d_rope, stream);
+  return dispatch_td(c->dt, c->d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    return launch_serve_d<T, decltype(dd)::value>(c, lens, max_len, H_q, q, k, v, out, sizeof(T) == 4 ? 1 : out_f32,
+                                                  workspace, scale, qsum, d_rope, stream);
+  });
 }
 
 }  // namespace cca

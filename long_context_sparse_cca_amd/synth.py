@@ -47,6 +47,8 @@ def np_inputs(B: int, H: int, L: int, d: int, dtype: str = "f32", seed: int = 0,
                 K[b, h, idx] *= np.float32(HEAVY_SCALE)
     if dtype == "bf16":
         Q, K, V = round_to_bf16(Q), round_to_bf16(K), round_to_bf16(V)
+    elif dtype == "f16":
+        Q, K, V = (x.astype(np.float16).astype(np.float32) for x in (Q, K, V))
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype}")
     return Q, K, V

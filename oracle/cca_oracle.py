@@ -40,7 +40,7 @@ core K/V are the projections of the core tokens ([P1] core K/V equation) and
 live in the KV cache ([P1] Triton section).  In a model computing in bf16 those
 are bf16 tensors, and the page's 93% KV-cache reduction at 128K (Fig. 3) is
 what 2-byte core tokens give.  `pool`, `cca_slice` and `decode_stream` therefore
-take `core_dtype`: None keeps the core tokens exact (float64); "bf16" / "f32"
+take `core_dtype`: None keeps the core tokens exact (float64); "bf16" / "f16" / "f32"
 round each element once, to nearest even, to that storage type before use.
 Everything else stays float64.
 
@@ -98,15 +98,19 @@ def round_storage(x: np.ndarray, core_dtype) -> np.ndarray:
     """Round float64 values once to the storage type of the core tokens.
 
     None: unchanged.  "f32": IEEE float32 (numpy's cast rounds to nearest
-    even).  "bf16": the 16 high bits of the float32 pattern, ties to even,
-    computed from the float64 value directly (round-to-odd to float32 first, so
-    the double rounding cannot create a false tie).
+    even).  "f16": IEEE binary16 (numpy's cast from float64 rounds to nearest
+    even in one step; overflow gives infinity).  "bf16": the 16 high bits of the
+    float32 pattern, ties to even, computed from the float64 value directly
+    (round-to-odd to float32 first, so the double rounding cannot create a false tie).
     """
     x = np.asarray(x, dtype=np.float64)
     if core_dtype is None:
         return x
     if core_dtype == "f32":
         return x.astype(np.float32).astype(np.float64)
+    if core_dtype == "f16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).astype(np.float64)
     if core_dtype != "bf16":
         raise ValueError(core_dtype)
     f = x.astype(np.float32)

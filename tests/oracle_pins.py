@@ -247,7 +247,7 @@ ALL_PINS = [
 
 
 def pin_storage_rounding_is_rne(o):
-    """round_storage matches torch's float64 -> bfloat16 / float32 conversions (library routines)."""
+    """round_storage matches torch's float64 -> bfloat16 / float16 / float32 conversions (library routines)."""
     rng = np.random.default_rng(11)
     x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-3, 4, 20000),
                         # exact bf16 ties: round to the even neighbour
@@ -258,6 +258,14 @@ def pin_storage_rounding_is_rne(o):
     want32 = torch.from_numpy(x).to(torch.float32).to(torch.float64).numpy()
     ok = np.array_equal(o.round_storage(x32, "bf16"), want16) and np.array_equal(o.round_storage(x, "f32"), want32)
     ok = ok and np.array_equal(o.round_storage(x, None), x)
+    # binary16: against torch's float -> float16 conversion on float32 values (one rounding there),
+    # in range and at exact ties
+    xh = np.concatenate([x32[np.abs(x32) < 6.0e4], np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5])])
+    wanth = torch.from_numpy(xh).float().to(torch.float16).to(torch.float64).numpy()
+    ok = ok and np.array_equal(o.round_storage(xh, "f16"), wanth)
+    ok = ok and o.round_storage(np.array([1.0 + 2.0 ** -11]), "f16")[0] == 1.0
+    # just above a binary16 tie: one rounding goes up (through float32 it would tie to even)
+    ok = ok and o.round_storage(np.array([1.0 + 2.0 ** -11 + 2.0 ** -40]), "f16")[0] == 1.0 + 2.0 ** -10
     # a value just above a bf16 tie rounds up when rounded once (through float32 it would tie to even)
     ok = ok and o.round_storage(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]), "bf16")[0] == 1.0 + 2.0 ** -7
     # stored core tokens are the exact ones rounded once

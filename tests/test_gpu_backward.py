@@ -98,7 +98,7 @@ def test_backward_unsupported_shapes(gpu):
         binding.prefill_lse(q, q.clone(), q.clone(), 16, 1)
 
 
-# The vector path: float32 inputs at d = 64 and 128, bf16 at d = 64.
+# The vector path: float32 and binary16 inputs at d = 64 and 128, bf16 at d = 64.
 # (dtype, d, B, H, H_kv, L, g, k, seed)
 GEN_CASES = [
     ("f32", 64, 1, 2, 2, 256, 16, 1, 110),    # the small float32 layer (B=1, H=2, d=64, L=256, g=16, k=1)
@@ -111,6 +111,8 @@ GEN_CASES = [
     ("bf16", 64, 1, 2, 2, 300, 16, 2, 117),
     ("bf16", 64, 1, 4, 1, 520, 16, 3, 118),   # multi-query
     ("f32", 64, 1, 1, 1, 15, 16, 1, 119),     # shorter than one group: no core tokens
+    ("f16", 128, 1, 2, 2, 300, 16, 2, 123),   # binary16 inputs
+    ("f16", 64, 1, 4, 2, 517, 7, 3, 124),     # binary16, grouped-query, ragged tail
 ]
 
 
@@ -124,11 +126,12 @@ def test_generic_backward_matches_oracle(gpu, case):
     """Gradients of the float32 vector path against the fp64 oracle.  Float32 inputs:
     every product and sum in float32 (relative rounding ~1e-7 per step over at most a few
     thousand terms), so the bound is 1e-4 * max(1, max|reference|) and the oracle's core
-    tokens are unrounded.  bf16 inputs: the core tokens and the output the gradients read
-    are bf16, so the bf16 bound 2e-2 applies, with the oracle's core tokens in bf16."""
+    tokens are unrounded.  16-bit inputs: the core tokens and the output the gradients read
+    are stored in the input type, so that type's bound applies (bf16 2e-2, binary16 5e-3),
+    with the oracle's core tokens rounded to it."""
     dt, d, B, H, Hkv, L, g, k, seed = case
     _say(f"generic backward case {_gen_id(case)} seed {seed}")
-    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
     Q = np_inputs(B, H, L, d, dt, seed)[0]
     K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, dt, seed + 1)[1:])
     dO = np_inputs(B, H, L, d, dt, seed + 500)[0]
@@ -138,15 +141,16 @@ def test_generic_backward_matches_oracle(gpu, case):
     dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
     torch.cuda.synchronize()
     assert torch.equal(out, binding.prefill(q, kk, v, g, k, scale))
-    core = "bf16" if dt == "bf16" else None
-    tol = 1e-4 if dt == "f32" else 2e-2
+    core = None if dt == "f32" else dt
+    tol = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}[dt]
+    lse_tol = {"f32": 1e-4, "bf16": 1e-2, "f16": 2e-3}[dt]
     if Hkv == H:
         for b in range(B):
             for h in range(H):
                 _, lse_ref = cca_backward.cca_forward_lse_slice(Q[b, h], K[b, h], V[b, h], g, k, scale,
                                                                 core_dtype=core)
                 e = np.abs(lse[b, h].cpu().numpy() - lse_ref).max() if L else 0.0
-                assert e <= (1e-4 if dt == "f32" else 1e-2), f"lse err {e:.3e}"
+                assert e <= lse_tol, f"lse err {e:.3e}"
         want = cca_backward.cca_backward(Q, K, V, dO, g, k, scale, core_dtype=core)
     else:
         want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype=core)

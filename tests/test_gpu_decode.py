@@ -18,8 +18,8 @@ from long_context_sparse_cca_amd.synth import np_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 # (B, H, d, g, k, L0, T, dtype, seed)
 DECODE_CASES = [
@@ -29,6 +29,8 @@ DECODE_CASES = [
     (1, 2, 128, 16, 64, 1500, 1600, "bf16", 3),  # window of 1024 raw tokens, ring wraps
     (1, 1, 64, 1, 4, 20, 60, "bf16", 4),     # g = 1: pooling every step
     (1, 1, 128, 512, 1, 1000, 1100, "bf16", 5),  # groups of 512 pooled in place from the ring
+    (1, 2, 128, 16, 4, 300, 400, "f16", 6),   # binary16 cache
+    (2, 1, 64, 7, 2, 30, 120, "f16", 7),
 ]
 
 

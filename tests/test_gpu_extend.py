@@ -22,8 +22,8 @@ from long_context_sparse_cca_amd.synth import np_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _dev(x, dt, device):
@@ -43,6 +43,8 @@ EXTEND_CASES = [
     (2, 6, 3, 64, 16, 1, "f32", [20, 3], [17, 2, 17], 43),             # r = 2, d = 64 fp32
     (1, 16, 2, 128, 16, 64, "bf16", [1500], [1025, 300], 44),          # the largest chunk, r = 8
     (3, 4, 4, 128, 8, 3, "f32", [9, 0, 50], [25, 4], 45),              # fp32 d = 128, r = 1
+    (2, 4, 2, 128, 16, 2, "f16", [100, 0], [1, 40, 17], 46),           # binary16 cache
+    (1, 2, 1, 64, 7, 2, "f16", [30], [15, 3, 22], 47),                 # binary16, d = 64
 ]
 
 

@@ -19,8 +19,8 @@ from long_context_sparse_cca_amd.synth import np_inputs, torch_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _dev(x, dt, device):

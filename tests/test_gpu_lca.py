@@ -21,9 +21,9 @@ from long_context_sparse_cca_amd.synth import np_inputs, torch_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
-ULP = {"f32": 2.0 ** -22, "bf16": 2.0 ** -8}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+ULP = {"f32": 2.0 ** -22, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
 
 def _dev(x, dt, device):
@@ -55,6 +55,7 @@ LCA_CASES = [
     (1, 1, 700, 128, 64, 2, 128, "bf16", 4),     # d_rope = d: whole key from the anchor
     (1, 1, 300, 128, 100, 1, 64, "f32", 5),      # g > 64: scores over two passes of the wave
     (1, 1, 15, 64, 16, 1, 32, "bf16", 6),        # L < g: nothing condensed
+    (1, 2, 600, 128, 16, 2, 64, "f16", 7),       # binary16 inputs
 ]
 
 
@@ -221,6 +222,7 @@ LCA_DECODE_CASES = [
     (2, 2, 128, 300, 40, 16, 2, 64, "bf16", 40),   # prefix ends inside a group (qsum seeded with 12 queries)
     (1, 2, 64, 64, 37, 8, 1, 16, "f32", 41),       # prefix on a group boundary
     (1, 1, 128, 5, 60, 16, 1, 0, "bf16", 42),      # short prefix, every dim pooled
+    (1, 2, 64, 70, 30, 8, 2, 32, "f16", 43),       # binary16 cache
 ]
 
 
@@ -287,6 +289,7 @@ LCA_SERVE_CASES = [
     (2, 6, 2, 64, 5, 3, 16, "f32", [0, 23], 30, 51),           # r = 3, g not a power of two
     (2, 8, 1, 128, 16, 4, 0, "bf16", [300, 129], 24, 52),      # multi-query, every dim pooled
     (4, 2, 2, 64, 16, 1, 64, "f32", [37, 0, 16, 15], 24, 53),  # r = 1, whole key from the anchor
+    (2, 4, 2, 128, 16, 2, 64, "f16", [90, 10], 24, 55),        # binary16 cache
 ]
 
 
@@ -395,6 +398,7 @@ LCA_EXTEND_CASES = [
     (2, 8, 2, 128, 16, 4, 32, "bf16", [0, 300], [65, 64, 3], 61),          # chunked prefill from empty
     (1, 3, 1, 64, 5, 3, 16, "f32", [0], [16, 16, 16, 1, 7], 62),           # r = 3, g = 5, k*g+1 = 16
     (2, 6, 3, 64, 16, 1, 0, "f32", [20, 3], [17, 2, 17], 63),              # every dim pooled
+    (2, 4, 2, 128, 16, 2, 64, "f16", [50, 0], [9, 33, 20], 64),           # binary16 cache
 ]
 
 

@@ -19,8 +19,12 @@ from long_context_sparse_cca_amd.synth import np_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+# binary16 inputs (no bound is given for them): the weights are rounded to binary16 as
+# matrix-core operands (relative 2^-11 each) and the core tokens stored in it, so a row's
+# error stays within about 2^-10 * max|V| ~ 5e-3 for |V| <= 5.
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+ULP = {"f32": 2.0 ** -22, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
 
 def _dev(x, dt, device):
@@ -48,6 +52,9 @@ PREFILL_CASES = [
     (1, 1, 410, 64, 3, 11, "f32", 10),
     (1, 1, 5000, 128, 1024, 2, "bf16", 11),  # large groups: 4 core tokens of 1024 rows each
     (1, 1, 9000, 64, 4096, 0, "f32", 12),    # the largest group size the library takes
+    (1, 2, 256, 64, 16, 1, "f16", 20),       # binary16 inputs
+    (1, 2, 1000, 128, 16, 4, "f16", 21),
+    (2, 3, 517, 64, 7, 3, "f16", 22),
 ]
 
 
@@ -76,18 +83,17 @@ def test_prefill_matches_oracle(gpu, case):
                 Kc, Vc, _ = oracle.pool(Q[b, h], K[b, h], V[b, h], g, scale)
                 gk = kc[b, h].float().cpu().numpy()
                 gv = vc[b, h].float().cpu().numpy()
-                ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -22
                 for got, ref in ((gk, Kc), (gv, Vc)):
-                    bound = TOL[dt] + ulp * np.abs(ref)
+                    bound = TOL[dt] + ULP[dt] * np.abs(ref)
                     assert np.all(np.abs(got - ref) <= bound), f"core err {np.abs(got - ref).max():.3e}"
 
 
-@pytest.mark.parametrize("case", PREFILL_CASES[:4], ids=_case_id)
+@pytest.mark.parametrize("case", PREFILL_CASES[:4] + [c for c in PREFILL_CASES if c[6] == "f16"], ids=_case_id)
 def test_prefill_bf16_output(gpu, case):
     """Output in the input dtype: same tolerance (one extra rounding of |O| < 4)."""
     B, H, L, d, g, k, dt, seed = case
-    if dt != "bf16":
-        pytest.skip("bf16 output only")
+    if dt == "f32":
+        pytest.skip("16-bit outputs only")
     _say(f"prefill bf16-out case {_case_id(case)}")
     Q, K, V = np_inputs(B, H, L, d, dt, seed)
     q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
@@ -100,6 +106,7 @@ def test_prefill_bf16_output(gpu, case):
 
 
 @pytest.mark.parametrize("case", [(1, 2, 256, 64, 16, "f32", 0), (2, 3, 300, 128, 16, "bf16", 1),
+                                  (2, 2, 300, 128, 16, "f16", 6), (1, 2, 77, 64, 5, "f16", 7),
                                   (1, 2, 77, 64, 5, "f32", 2), (1, 1, 64, 128, 1, "bf16", 3),
                                   (1, 1, 200, 128, 200, "f32", 4), (1, 1, 10, 64, 16, "bf16", 5)],
                          ids=lambda c: f"B{c[0]}H{c[1]}L{c[2]}d{c[3]}g{c[4]}-{c[5]}")
@@ -112,7 +119,7 @@ def test_pool_matches_oracle(gpu, case):
     kc, vc = binding.pool_kv(q, kk, v, g, scale)
     torch.cuda.synchronize()
     assert kc.shape == (B, H, L // g, d)
-    ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -22
+    ulp = ULP[dt]
     tol = 1e-5 if dt == "f32" else 1e-3
     for b in range(B):
         for h in range(H):

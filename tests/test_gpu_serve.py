@@ -21,8 +21,8 @@ from long_context_sparse_cca_amd.synth import np_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _dev(x, dt, device):
@@ -42,6 +42,8 @@ SERVE_CASES = [
     (4, 2, 2, 64, 16, 1, "f32", [37, 0, 16, 15], 24, 33),    # r = 1, sequences at group edges
     (2, 12, 2, 128, 16, 4, "bf16", [260, 300], 20, 34),      # r = 6: blocks of two heads
     (2, 16, 4, 128, 16, 8, "bf16", [700, 64], 18, 35),       # r = 4
+    (2, 4, 2, 128, 16, 2, "f16", [150, 9], 24, 39),          # binary16 cache
+    (3, 3, 1, 64, 5, 3, "f16", [0, 44, 12], 20, 29),         # binary16, d = 64, MQA
 ]
 
 

@@ -3,11 +3,12 @@
 The hand-picked cases of the other GPU tests aim at known edges; these draw shapes at
 random (fixed seeds, so a failure names a reproducible case): sequence lengths from 1
 to ~1300 (ragged against every tile size), group sizes from 1 to 64 including primes,
-windows from 0 to 64 groups, head dims 64 and 128, fp32 and bf16, 1 to 4 query heads
+windows from 0 to 64 groups, head dims 64 and 128, fp32, bf16 and binary16, 1 to 4 query heads
 per key/value head, per-sequence lengths in the serving cache (some empty), chunked
 appends up to the largest allowed chunk, the LCA-style serving cache (steps and chunks
 mixed), and the backward pass (matrix-core and vector paths).  Tolerances as for the
-other parity tests: max-abs 1e-4 (fp32), 2e-2 (bf16), gradients 2e-2 of their scale.
+other parity tests: max-abs 1e-4 (fp32), 2e-2 (bf16), 5e-3 (binary16); gradients the same
+fractions of their scale.
 """
 import math
 import sys
@@ -22,8 +23,8 @@ from long_context_sparse_cca_amd.synth import np_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 GROUPS = [1, 2, 3, 5, 8, 13, 16, 17, 32, 64]
 WINDOWS = [0, 1, 2, 3, 7, 64]
 
@@ -43,7 +44,7 @@ def _inputs(B, H, Hkv, L, d, dt, seed):
     return Q, K, V
 
 
-def _prefill_cases(n=20, seed=2024):
+def _prefill_cases(n=20, seed=2024, dtypes=("f32", "bf16")):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -51,7 +52,7 @@ def _prefill_cases(n=20, seed=2024):
         Hkv = int(rng.integers(1, 3))
         r = int(rng.choice([1, 2, 4]))
         d = int(rng.choice([64, 128]))
-        dt = str(rng.choice(["f32", "bf16"]))
+        dt = str(rng.choice(list(dtypes)))
         g = int(rng.choice(GROUPS))
         k = int(rng.choice(WINDOWS))
         # half the lengths log-uniform (many below one tile), half uniform up to 1300
@@ -66,7 +67,7 @@ def _pid(c):
     return f"B{B}H{H}kv{Hkv}L{L}d{d}g{g}k{k}-{dt}-s{seed}"
 
 
-@pytest.mark.parametrize("case", _prefill_cases(), ids=_pid)
+@pytest.mark.parametrize("case", _prefill_cases() + _prefill_cases(n=6, seed=4242, dtypes=("f16",)), ids=_pid)
 def test_prefill_sweep(gpu, case):
     B, H, Hkv, L, d, g, k, dt, seed = case
     _say(f"prefill sweep {_pid(case)}")
@@ -80,7 +81,7 @@ def test_prefill_sweep(gpu, case):
     assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
 
 
-def _serve_cases(n=6, seed=77):
+def _serve_cases(n=6, seed=77, dtypes=("f32", "bf16")):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -88,7 +89,7 @@ def _serve_cases(n=6, seed=77):
         Hkv = int(rng.integers(1, 3))
         r = int(rng.choice([1, 2, 4]))
         d = int(rng.choice([64, 128]))
-        dt = str(rng.choice(["f32", "bf16"]))
+        dt = str(rng.choice(list(dtypes)))
         g = int(rng.choice([2, 5, 8, 16]))
         k = int(rng.choice([0, 1, 3, 8]))
         lens = [int(x) if rng.uniform() > 0.2 else 0 for x in rng.integers(1, 400, size=B)]
@@ -114,7 +115,7 @@ def _serve_setup(B, Hq, Hkv, d, g, k, dt, lens0, total, seed, device):
     return Q, K, V, cache, scale
 
 
-@pytest.mark.parametrize("case", _serve_cases(), ids=_sid)
+@pytest.mark.parametrize("case", _serve_cases() + _serve_cases(n=3, seed=7077, dtypes=("f16",)), ids=_sid)
 def test_serve_sweep(gpu, case):
     B, Hq, Hkv, d, g, k, dt, lens0, T, seed = case
     _say(f"serve sweep {_sid(case)}")
@@ -133,7 +134,7 @@ def test_serve_sweep(gpu, case):
         assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
 
 
-def _extend_cases(n=4, seed=99):
+def _extend_cases(n=4, seed=99, dtypes=("f32", "bf16")):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -141,7 +142,7 @@ def _extend_cases(n=4, seed=99):
         Hkv = int(rng.integers(1, 3))
         r = int(rng.choice([1, 2, 4]))
         d = int(rng.choice([64, 128]))
-        dt = str(rng.choice(["f32", "bf16"]))
+        dt = str(rng.choice(list(dtypes)))
         g = int(rng.choice([4, 8, 16]))
         k = int(rng.choice([1, 2, 4]))
         lens = [int(x) for x in rng.integers(0, 300, size=B)]
@@ -155,7 +156,7 @@ def _eid(c):
     return f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}-{dt}-L{'_'.join(map(str, lens))}-n{'_'.join(map(str, chunks))}-s{seed}"
 
 
-@pytest.mark.parametrize("case", _extend_cases(), ids=_eid)
+@pytest.mark.parametrize("case", _extend_cases() + _extend_cases(n=2, seed=9099, dtypes=("f16",)), ids=_eid)
 def test_extend_sweep(gpu, case):
     B, Hq, Hkv, d, g, k, dt, lens0, chunks, seed = case
     _say(f"extend sweep {_eid(case)}")
@@ -216,14 +217,14 @@ def test_backward_sweep(gpu, case):
         assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
 
 
-def _lca_cases(n=4, seed=321):
+def _lca_cases(n=4, seed=321, dtypes=("f32", "bf16")):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
         Hkv = int(rng.integers(1, 3))
         r = int(rng.choice([1, 2]))
         d = int(rng.choice([64, 128]))
-        dt = str(rng.choice(["f32", "bf16"]))
+        dt = str(rng.choice(list(dtypes)))
         g = int(rng.choice([2, 5, 16, 33]))
         k = int(rng.choice([0, 1, 3]))
         d_rope = int(rng.choice([0, 8, d // 2, d]))
@@ -237,7 +238,7 @@ def _lid(c):
     return f"B{B}H{H}kv{Hkv}L{L}d{d}g{g}k{k}rope{r}-{dt}-s{seed}"
 
 
-@pytest.mark.parametrize("case", _lca_cases(), ids=_lid)
+@pytest.mark.parametrize("case", _lca_cases() + _lca_cases(n=2, seed=3321, dtypes=("f16",)), ids=_lid)
 def test_lca_sweep(gpu, case):
     B, H, Hkv, L, d, g, k, d_rope, dt, seed = case
     _say(f"lca sweep {_lid(case)}")
@@ -259,7 +260,7 @@ def test_lca_sweep(gpu, case):
     assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
 
 
-def _lca_serve_cases(n=4, seed=55):
+def _lca_serve_cases(n=4, seed=55, dtypes=("f32", "bf16")):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -267,7 +268,7 @@ def _lca_serve_cases(n=4, seed=55):
         Hkv = int(rng.integers(1, 3))
         r = int(rng.choice([1, 2, 3]))
         d = int(rng.choice([64, 128]))
-        dt = str(rng.choice(["f32", "bf16"]))
+        dt = str(rng.choice(list(dtypes)))
         g = int(rng.choice([2, 5, 8, 16]))
         k = int(rng.choice([0, 1, 3]))
         d_rope = int(rng.choice([0, 8, d // 2, d]))
@@ -296,7 +297,7 @@ def _anchor_rows(gk, K, g, d_rope):
     return anc
 
 
-@pytest.mark.parametrize("case", _lca_serve_cases(), ids=_lsid)
+@pytest.mark.parametrize("case", _lca_serve_cases() + _lca_serve_cases(n=2, seed=5055, dtypes=("f16",)), ids=_lsid)
 def test_lca_serve_sweep(gpu, case):
     """LCA-style serving cache: chunked appends (op n > 1, or n = 1 through the chunk path when
     drawn as a chunk) and single steps, every row against the LCA-style prefill rows."""
@@ -337,11 +338,11 @@ def test_lca_serve_sweep(gpu, case):
         assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
 
 
-def _generic_backward_cases(n=4, seed=131):
+def _generic_backward_cases(n=4, seed=131, kinds=(("f32", 64), ("f32", 128), ("bf16", 64))):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
-        dt, d = [("f32", 64), ("f32", 128), ("bf16", 64)][int(rng.integers(0, 3))]
+        dt, d = kinds[int(rng.integers(0, len(kinds)))]
         Hkv = int(rng.integers(1, 3))
         r = int(rng.choice([1, 2, 3]))
         g = int(rng.choice([1, 3, 8, 16, 17]))
@@ -356,9 +357,10 @@ def _gbid(c):
     return f"{dt}d{d}H{H}kv{Hkv}L{L}g{g}k{k}-s{seed}"
 
 
-@pytest.mark.parametrize("case", _generic_backward_cases(), ids=_gbid)
+@pytest.mark.parametrize("case", _generic_backward_cases() + _generic_backward_cases(
+    n=2, seed=1131, kinds=(("f16", 64), ("f16", 128))), ids=_gbid)
 def test_generic_backward_sweep(gpu, case):
-    """Backward pass on the vector path (float32 inputs, head dim 64) at random shapes."""
+    """Backward pass on the vector path (float32, bf16 and binary16 inputs) at random shapes."""
     dt, d, H, Hkv, L, g, k, seed = case
     _say(f"generic backward sweep {_gbid(case)}")
     Q, K, V = _inputs(1, H, Hkv, L, d, dt, seed)
@@ -368,8 +370,8 @@ def test_generic_backward_sweep(gpu, case):
     out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
     dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
     torch.cuda.synchronize()
-    core = "bf16" if dt == "bf16" else None
-    tol = 1e-4 if dt == "f32" else 2e-2
+    core = None if dt == "f32" else dt
+    tol = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}[dt]
     want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype=core)
     for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
         err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
