@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the serving decode measurement (per-sequence lengths, grouped-query heads)")
     ap.add_argument("--no-lca", action="store_true", help="skip the LCA-style variant measurement")
+    ap.add_argument("--no-f16", action="store_true", help="skip the binary16 prefill measurement")
     ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "training", "lca", "copy"],
                     default="all",
                     help="profiling aid: run only one phase (the JSON line is then not the benchmark result); "
@@ -187,6 +188,41 @@ def dense_comparison(binding, accounting, dev, seed):
     return out
 
 
+def binary16_prefill(binding, accounting, dev, seed, reps: int = 5):
+    """The prefill step of the headline workload (B=1, H=32, d=128, L=131072, g=16, k=64) on
+    IEEE binary16 inputs: the same attention kernel instantiated for half precision, with
+    pooling on the generic kernel.  Outside the timed steps."""
+    import torch
+
+    from long_context_sparse_cca_amd.synth import torch_inputs
+    L = PREFILL_L
+    q, k, v = torch_inputs(1, H, L, D, torch.float16, dev, seed=seed, heavy_frac=HEAVY)
+    kc, vc = binding.pool_kv(q, k, v, G)
+    o = torch.empty_like(q)
+    binding.prefill(q, k, v, G, KL, out=o)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    pool_ms = attn_ms = 0.0
+    for _ in range(reps):
+        ev[0].record()
+        binding.pool_kv(q, k, v, G, kc=kc, vc=vc)
+        ev[1].record()
+        binding.attention(q, k, v, kc, vc, G, KL, out=o)
+        ev[2].record()
+        torch.cuda.synchronize()
+        pool_ms += ev[0].elapsed_time(ev[1]) / reps
+        attn_ms += ev[1].elapsed_time(ev[2]) / reps
+    fl = accounting.prefill_flops(1, H, L, D, G, KL)
+    tflops = fl / (attn_ms * 1e-3) / 1e12
+    del q, k, v, kc, vc, o
+    torch.cuda.empty_cache()
+    return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL, "dtype": "f16"},
+            "ms": pool_ms + attn_ms, "pool_ms": pool_ms, "attention_ms": attn_ms,
+            "tokens_per_s": L / ((pool_ms + attn_ms) * 1e-3),
+            "roofline": {"kernel": "cca_prefill_d128_kernel<f16>", "bound": "mfma", "achieved": tflops,
+                         "peak": 2500.0, "unit": "TFLOP/s", "frac": tflops / 2500.0}}
+
+
 def serving_decode(binding, accounting, dev, seed, steps: int = 64):
     """Serving with per-sequence lengths and grouped-query attention, outside the timed steps:
     B=8 sequences at lengths 65536 + 9362*b (64K .. 128K), H_q=32 query heads over H_kv=8
@@ -270,7 +306,7 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
                              "note": "the step captured once in a HIP graph and replayed back to back"},
             "chunked_append": {"tokens_per_sequence": n_ext, "ms_per_call": ms,
                                "tokens_per_s": B * n_ext / (ms * 1e-3), "flops_per_call": sum(ext_fl) / len(ext_fl),
-                               "roofline": {"kernel": "cca_prefill_bf16_d128_kernel<extend> (+ gather, append)",
+                               "roofline": {"kernel": "cca_prefill_d128_kernel<bf16,extend> (+ gather, append)",
                                             "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
@@ -447,7 +483,7 @@ def lca_serving(binding, accounting, dev, seed, d_rope: int, steps: int = 64):
                          "frac": gbs / PEAK_HBM_GBS},
             "chunked_append": {"tokens_per_sequence": n_ext, "ms_per_call": ms,
                                "tokens_per_s": B * n_ext / (ms * 1e-3), "flops_per_call": sum(ext_fl) / len(ext_fl),
-                               "roofline": {"kernel": "cca_prefill_bf16_d128_kernel<extend> (+ gather, lca append)",
+                               "roofline": {"kernel": "cca_prefill_d128_kernel<bf16,extend> (+ gather, lca append)",
                                             "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
@@ -590,7 +626,7 @@ def main():
             "phase": args.phase,
         },
     }
-    src_attn = source_hash("prefill.hip", "prefill_bf16.hip", "cca_device.h")
+    src_attn = source_hash("prefill.hip", "prefill_d128.hip", "cca_device.h")
     if do_prefill:
         ms_pool, ms_attn = median(t_pool), median(t_attn)   # medians over the timed steps
         ms_prefill = ms_pool + ms_attn
@@ -606,7 +642,7 @@ def main():
             "pool_hbm_frac": pool_b / (ms_pool * 1e-3) / 1e9 / PEAK_HBM_GBS,
         }
         res["roofline"] = {
-            "kernel": "cca_prefill_bf16_d128_kernel",
+            "kernel": "cca_prefill_d128_kernel<bf16>",
             "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS,
             "traffic": load_traffic("prefill_attention", src_attn),
@@ -647,6 +683,8 @@ def main():
     if do_prefill and not args.no_lca and args.phase == "all":
         res["lca_variant"] = lca_variant(binding, accounting, dev, args.seed)
         torch.cuda.empty_cache()
+    if do_prefill and not args.no_f16 and args.phase == "all":
+        res["binary16_prefill"] = binary16_prefill(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_dense and args.phase == "all":
         res["dense_comparison"] = dense_comparison(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_cpu_baseline and args.phase == "all":

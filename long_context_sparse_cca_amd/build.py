@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcca.so")
-SOURCES = ["api.hip", "pool.hip", "prefill.hip", "prefill_bf16.hip", "decode.hip", "serve.hip", "extend.hip", "backward.hip", "backward_generic.hip", "pool_lca.hip"]
+SOURCES = ["api.hip", "pool.hip", "prefill.hip", "prefill_d128.hip", "decode.hip", "serve.hip", "extend.hip", "backward.hip", "backward_generic.hip", "pool_lca.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

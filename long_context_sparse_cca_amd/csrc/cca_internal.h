@@ -62,20 +62,21 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
                                     int64_t L, int g, int k_local, float scale, hipStream_t stream,
                                     float* lse = nullptr);
 
-// bf16, head dim 128 fast path of the fused attention (prefill_bf16.hip).
-// lse (optional, float32 [BH][L]): natural-log log-sum-exp of each query's scaled scores.
-hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
-                                    void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
-                                    float scale, hipStream_t stream, float* lse = nullptr);
+// 16-bit (dt = CCA_BF16 or CCA_F16), head dim 128 fast path of the fused attention
+// (prefill_d128.hip).  lse (optional, float32 [BH][L]): natural-log log-sum-exp of each
+// query's scaled scores.
+hipError_t launch_prefill_d128(int dt, const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                               void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local, float scale,
+                               hipStream_t stream, float* lse = nullptr);
 
-// Extend-mode attention (bf16 d=128 fast kernel or the generic one): q, out [B*H][n][d];
+// Extend-mode attention (16-bit d=128 fast kernel or the generic one): q, out [B*H][n][d];
 // k, v [B*H_kv][ext.raw_rows][d]; kc, vc [B*H_kv][ext.core_rows][d].
 hipError_t launch_extend_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                    const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
                                    float scale, const ExtendArgs& ext, hipStream_t stream);
-hipError_t launch_extend_attention_bf16_d128(const void* q, const void* k, const void* v, const void* kc,
-                                             const void* vc, void* out, int out_f32, int BH, int nq, int g,
-                                             int k_local, float scale, const ExtendArgs& ext, hipStream_t stream);
+hipError_t launch_extend_attention_d128(int dt, const void* q, const void* k, const void* v, const void* kc,
+                                        const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
+                                        float scale, const ExtendArgs& ext, hipStream_t stream);
 
 hipError_t launch_cache_load(const cca_cache_t* c, const void* k, const void* v, const void* kc,
                              const void* vc, int64_t L, hipStream_t stream);

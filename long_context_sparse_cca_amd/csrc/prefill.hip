@@ -432,8 +432,8 @@ hipError_t launch_extend_t(const void* q, const void* k, const void* v, const vo
 hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                     const void* vc, void* out, int out_f32, int BH, int nq, int64_t L, int g,
                                     int k_local, float scale, hipStream_t stream, float* lse) {
-  if (dt == CCA_BF16 && d == 128)
-    return launch_prefill_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
+  if (dt != CCA_F32 && d == 128)
+    return launch_prefill_d128(dt, q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, stream, lse);
   return dispatch_td(dt, d, [&](auto t, auto dd) {
     using T = decltype(t);
     return launch_prefill_t<T, decltype(dd)::value>(q, k, v, kc, vc, out, sizeof(T) == 4 ? 1 : out_f32, BH, nq, L, g,
@@ -444,8 +444,8 @@ hipError_t launch_prefill_attention(int dt, int d, const void* q, const void* k,
 hipError_t launch_extend_attention(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                    const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
                                    float scale, const ExtendArgs& ext, hipStream_t stream) {
-  if (dt == CCA_BF16 && d == 128)
-    return launch_extend_attention_bf16_d128(q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
+  if (dt != CCA_F32 && d == 128)
+    return launch_extend_attention_d128(dt, q, k, v, kc, vc, out, out_f32, BH, nq, g, k_local, scale, ext, stream);
   return dispatch_td(dt, d, [&](auto t, auto dd) {
     using T = decltype(t);
     return launch_extend_t<T, decltype(dd)::value>(q, k, v, kc, vc, out, sizeof(T) == 4 ? 1 : out_f32, BH, nq, g,

@@ -1,4 +1,5 @@
-// Fused CCA prefill attention, bf16 inputs, head dim 128: the gfx950 fast path.
+// Fused CCA prefill attention, 16-bit inputs (bf16 or IEEE binary16), head dim 128: the
+// gfx950 fast path.
 //
 // Same computation as the generic kernel in prefill.hip (the CCA write-up,
 // "ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展": query t of
@@ -16,7 +17,8 @@
 //     key row kbase + s/4, dims d0 + 4(s%4) .. +3, lane j ends up holding the
 //     four keys kbase..kbase+3 at dim d0 + j, i.e. one quarter of an MFMA A operand.
 // Softmax bookkeeping uses v_permlane32_swap for the cross-half row max / sum and
-// v_dot2_f32_bf16 against (1, 1) for the row sum of the bf16-rounded weights.
+// v_dot2_f32_bf16 (v_dot2_f32_f16) against (1, 1) for the row sum of the weights as
+// rounded to the input type.
 // A workgroup is 8 waves (256 queries, 2 waves per SIMD) sharing each K/V tile;
 // each wave raises its priority while it issues its MFMA burst so that the two
 // waves of a SIMD tend to alternate between matrix and vector work.
@@ -39,7 +41,31 @@ constexpr int kBufBytes = 2 * kTileBytes;    // K tile + V tile
 constexpr float kSumLimit = 65536.0f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// The type-dependent instructions: the 32x32x16 MFMA, the rounding of two weights into one
+// register and the two-term dot product of the row sum.  Everything else (tile fills, the
+// transpose reads, the swizzle) moves 16-bit elements without looking at them.
+template <typename T> struct Ops16;
+template <> struct Ops16<bf16_t> {
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static x2 round2(float a, float b) { return x2{(__bf16)a, (__bf16)b}; }
+  __device__ __forceinline__ static float dot2(x2 a, x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <> struct Ops16<f16_t> {
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  }
+  __device__ __forceinline__ static x2 round2(float a, float b) { return x2{(_Float16)a, (_Float16)b}; }
+  __device__ __forceinline__ static float dot2(x2 a, x2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
 
 // 16-byte chunk swizzle of a tile row (16 chunks per 256-byte row).  It is a
 // bijection on any 16 consecutive rows (the K operand read: 16 lanes, 16 rows, one
@@ -61,10 +87,10 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // EXT: attention of new tokens over a cached prefix (ExtendArgs): positions are absolute,
 // query i of the slice is at ext.pos[b] + i, raw key u is row u - raw0 of the raw slice.
 // Without EXT the slice is a whole sequence: pos0 = raw0 = 0, L queries, L raw rows.
-template <bool EXT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_bf16_d128_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
+template <typename T, bool EXT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_prefill_d128_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ Kc, const T* __restrict__ Vc, void* __restrict__ Out, int out_f32, int BH,
     int nq, int L, int g, int k_local, float scale, int ntiles, ExtendArgs ext, float* __restrict__ lse) {
   // one array per buffer: the LDS-DMA fill of one buffer then provably does not
   // alias the operand reads of the other, so no wait is forced between them
@@ -95,7 +121,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const size_t o = ((size_t)bh * nQ + i) * kD;
         for (int c = hf; c < kD; c += 2) {
           if (out_f32) reinterpret_cast<float*>(Out)[o + c] = __builtin_nanf("");
-          else reinterpret_cast<uint16_t*>(Out)[o + c] = 0x7fc0;
+          else reinterpret_cast<uint16_t*>(Out)[o + c] = Elem<T>::kNaNBits;
         }
       }
       return;
@@ -125,15 +151,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const size_t slice = (size_t)bh * nQ * kD;             // query / output slice
   const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
-  const bf16_t* Ks = K + (size_t)bkv * raw_rows * kD;
-  const bf16_t* Vs = V + (size_t)bkv * raw_rows * kD;
-  const bf16_t* Kcs = Kc + (size_t)bkv * core_rows * kD;
-  const bf16_t* Vcs = Vc + (size_t)bkv * core_rows * kD;
+  const T* Ks = K + (size_t)bkv * raw_rows * kD;
+  const T* Vs = V + (size_t)bkv * raw_rows * kD;
+  const T* Kcs = Kc + (size_t)bkv * core_rows * kD;
+  const T* Vcs = Vc + (size_t)bkv * core_rows * kD;
 
   // ---- Q operand (B of S^T = K Q^T): slice d16 holds dims 16*d16 + 8*hf .. +8
   uint4 qop[kD / 16];
   {
-    const bf16_t* qrow = Q + slice + (size_t)(q_lane - pos0) * kD;
+    const T* qrow = Q + slice + (size_t)(q_lane - pos0) * kD;
 #pragma unroll
     for (int s = 0; s < kD / 16; ++s) qop[s] = ld16(qrow + s * 16 + hf * 8);
   }
@@ -150,7 +176,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     fill_lin[i] = r * kRowBytes + fill_off[i];
   }
   auto issue_tile = [&](int it, int buf) {
-    const bf16_t *ks, *vs;
+    const T *ks, *vs;
     int base, lim, off0;   // tile's first key, last valid key, key of row 0 of the slice
     if (it < n_core_tiles) {
       ks = Kcs; vs = Vcs; base = it * kBN; lim = m - 1; off0 = 0;
@@ -212,7 +238,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
   const float sc = scale * kLog2e;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  using Ops = Ops16<T>;
+  const typename Ops::x2 ones = Ops::round2(1.0f, 1.0f);
 
   // Visible window [lo, lo + span] of each lane in the key index space of a tile kind:
   // core key j visible iff 0 <= j <= cl_lane - 1 (empty when cl_lane <= 0, encoded
@@ -251,8 +278,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int d16 = 0; d16 < kD / 16; ++d16)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[d16]),
-                                                    __builtin_bit_cast(bf16x8_t, qop[d16]), s, 0, 0, 0);
+        s = Ops::mfma(ka[d16], qop[d16], s);
       // V operand transpose reads for this sub-block, issued behind the QK MFMAs so
       // their latency hides under the softmax arithmetic
       v4s_t vop[2][2][kD / 32];
@@ -283,7 +309,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // weight may exceed it, or the reference is still unset) makes the wave move the
       // reference to the running maximum and recompute the weights (rare after the first
       // sub-blocks).  Weights therefore stay <= 2^16, as with an explicit threshold check.
-      bf16x2_t pp[2][4];
+      typename Ops::x2 pp[2][4];
       float bsum;
       auto weights = [&]() {
         // two partial row sums (one per 16-key half) halve the dependent dot2 chain
@@ -294,9 +320,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int e = 0; e < 4; ++e) {
             const float p0 = fast_exp2(fmaf(s[8 * u + 2 * e], sc, -m_run));
             const float p1 = fast_exp2(fmaf(s[8 * u + 2 * e + 1], sc, -m_run));
-            pp[u][e] = bf16x2_t{(__bf16)p0, (__bf16)p1};
-            if (u == 0) h0 = __builtin_amdgcn_fdot2_f32_bf16(pp[u][e], ones, h0, false);
-            else h1 = __builtin_amdgcn_fdot2_f32_bf16(pp[u][e], ones, h1, false);
+            pp[u][e] = Ops::round2(p0, p1);
+            if (u == 0) h0 = Ops::dot2(pp[u][e], ones, h0);
+            else h1 = Ops::dot2(pp[u][e], ones, h1);
           }
         bsum = h0 + h1;
       };
@@ -325,11 +351,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         // P^T: keys 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} = S registers 8u .. 8u+7
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pp[u]);
+        const uint4 pb = __builtin_bit_cast(uint4, pp[u]);
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
           const v4s_t both[2] = {vop[u][0][dt], vop[u][1][dt]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, both), pb, acc[dt], 0, 0, 0);
+          acc[dt] = Ops::mfma(__builtin_bit_cast(uint4, both), pb, acc[dt]);
         }
       }
     }
@@ -372,43 +398,62 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         *reinterpret_cast<float4*>(o + dt * 32 + 8 * i + 4 * hf) = v;
       }
   } else {
-    bf16_t* o = reinterpret_cast<bf16_t*>(Out) + slice + (size_t)q_row * kD;
+    T* o = reinterpret_cast<T*>(Out) + slice + (size_t)q_row * kD;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint2 w;
-        w.x = pack_bf16x2(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv);
-        w.y = pack_bf16x2(acc[dt][4 * i + 2] * inv, acc[dt][4 * i + 3] * inv);
+        w.x = Elem<T>::pack2(acc[dt][4 * i] * inv, acc[dt][4 * i + 1] * inv);
+        w.y = Elem<T>::pack2(acc[dt][4 * i + 2] * inv, acc[dt][4 * i + 3] * inv);
         *reinterpret_cast<uint2*>(o + dt * 32 + 8 * i + 4 * hf) = w;
       }
   }
 }
 
+template <typename T>
+void launch_prefill_t(const void* q, const void* k, const void* v, const void* kc, const void* vc, void* out,
+                      int out_f32, int BH, int nq, int64_t L, int g, int k_local, float scale, int ntiles,
+                      const ExtendArgs& ext, bool extend, float* lse, hipStream_t stream) {
+  const int64_t nblocks = (int64_t)BH * ntiles;
+  if (extend)
+    hipLaunchKernelGGL((cca_prefill_d128_kernel<T, true>), dim3((unsigned)nblocks), dim3(512), 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq, 0, g, k_local,
+                       scale, ntiles, ext, (float*)nullptr);
+  else
+    hipLaunchKernelGGL((cca_prefill_d128_kernel<T, false>), dim3((unsigned)nblocks), dim3(512), 0, stream,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq,
+                       (int)L, g, k_local, scale, ntiles, ext, lse);
+}
+
 }  // namespace
 
-hipError_t launch_prefill_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
-                                    void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local,
-                                    float scale, hipStream_t stream, float* lse) {
+hipError_t launch_prefill_d128(int dt, const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                               void* out, int out_f32, int BH, int nq, int64_t L, int g, int k_local, float scale,
+                               hipStream_t stream, float* lse) {
   const int ntiles = (int)((L + kBM - 1) / kBM);
-  const int64_t nblocks = (int64_t)BH * ntiles;
-  if (nblocks == 0) return hipSuccess;
+  if ((int64_t)BH * ntiles == 0) return hipSuccess;
   const ExtendArgs none{nullptr, 1, 0, 0, 0};
-  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel<false>, dim3((unsigned)nblocks), dim3(512), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out,
-                     out_f32, BH, nq, (int)L, g, k_local, scale, ntiles, none, lse);
+  if (dt == CCA_F16)
+    launch_prefill_t<f16_t>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, ntiles, none, false, lse,
+                            stream);
+  else
+    launch_prefill_t<bf16_t>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, ntiles, none, false, lse,
+                             stream);
   return hipGetLastError();
 }
 
-hipError_t launch_extend_attention_bf16_d128(const void* q, const void* k, const void* v, const void* kc,
-                                             const void* vc, void* out, int out_f32, int BH, int nq, int g,
-                                             int k_local, float scale, const ExtendArgs& ext, hipStream_t stream) {
+hipError_t launch_extend_attention_d128(int dt, const void* q, const void* k, const void* v, const void* kc,
+                                        const void* vc, void* out, int out_f32, int BH, int nq, int g, int k_local,
+                                        float scale, const ExtendArgs& ext, hipStream_t stream) {
   const int ntiles = (ext.n + kBM - 1) / kBM;
-  const int64_t nblocks = (int64_t)BH * ntiles;
-  if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(cca_prefill_bf16_d128_kernel<true>, dim3((unsigned)nblocks), dim3(512), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, out,
-                     out_f32, BH, nq, 0, g, k_local, scale, ntiles, ext, (float*)nullptr);
+  if ((int64_t)BH * ntiles == 0) return hipSuccess;
+  if (dt == CCA_F16)
+    launch_prefill_t<f16_t>(q, k, v, kc, vc, out, out_f32, BH, nq, 0, g, k_local, scale, ntiles, ext, true, nullptr,
+                            stream);
+  else
+    launch_prefill_t<bf16_t>(q, k, v, kc, vc, out, out_f32, BH, nq, 0, g, k_local, scale, ntiles, ext, true, nullptr,
+                             stream);
   return hipGetLastError();
 }
 
