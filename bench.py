@@ -311,19 +311,22 @@ def serving_decode(binding, accounting, dev, seed, steps: int = 64):
                                             "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS}}}
 
 
-def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int = 3, H_kv: int = H):
+def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int = 3, H_kv: int = H,
+                  dtype: str = "bf16"):
     """Forward with log-sum-exp (cca_prefill_lse) and backward (cca_backward) of one layer,
-    B=1, H=32 (H_kv key/value heads), d=128, g=16, k=64, bf16, outside the timed steps."""
+    B=1, H=32 (H_kv key/value heads), d=128, g=16, k=64, bf16 (or binary16 with
+    dtype="f16"), outside the timed steps."""
     import torch
 
     from long_context_sparse_cca_amd.synth import torch_inputs
-    q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, dev, seed=seed + 7, heavy_frac=HEAVY)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    q, k, v = torch_inputs(1, H, L, D, tdt, dev, seed=seed + 7, heavy_frac=HEAVY)
     if H_kv != H:
         k = k[:, :H_kv].contiguous()
         v = v[:, :H_kv].contiguous()
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed + 8)
-    dout = torch.randn((1, H, L, D), generator=gen, device=dev).to(torch.bfloat16)
+    dout = torch.randn((1, H, L, D), generator=gen, device=dev).to(tdt)
     out, lse, kc, vc = binding.prefill_lse(q, k, v, G, KL)
     binding.backward(q, k, v, kc, vc, out, lse, dout, G, KL)
     torch.cuda.synchronize()
@@ -342,7 +345,9 @@ def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int 
     fw_ms, bw_ms = sum(fw) / reps, sum(bw) / reps
     fl = accounting.backward_flops(1, H, L, D, G, KL)
     tf = fl / (bw_ms * 1e-3) / 1e12
-    return {"config": {"B": 1, "H": H, "H_kv": H_kv, "d": D, "L": L, "g": G, "k_local": KL},
+    del q, k, v, dout, out, lse, kc, vc
+    torch.cuda.empty_cache()
+    return {"config": {"B": 1, "H": H, "H_kv": H_kv, "d": D, "L": L, "g": G, "k_local": KL, "dtype": dtype},
             "forward_ms": fw_ms, "backward_ms": bw_ms, "backward_flops": fl,
             "roofline": {"kernel": "cca_bwd_dq_kernel + cca_bwd_dkdv16_kernel (+ prep, pooling backward)",
                          "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -685,6 +690,8 @@ def main():
         torch.cuda.empty_cache()
     if do_prefill and not args.no_f16 and args.phase == "all":
         res["binary16_prefill"] = binary16_prefill(binding, accounting, dev, args.seed)
+        if not args.no_training:
+            res["binary16_training"] = training_step(binding, accounting, dev, args.seed, reps=2, dtype="f16")
     if do_prefill and not args.no_dense and args.phase == "all":
         res["dense_comparison"] = dense_comparison(binding, accounting, dev, args.seed)
     if do_prefill and not args.no_cpu_baseline and args.phase == "all":

@@ -174,7 +174,7 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
 /*
  * Training ([CCA] Triton section: the fused operator serves training as well;
  * the models are fine-tuned with it).  bf16, binary16 or float32 inputs, d = 64 or 128,
- * one query head per key/value head.  bf16 at d = 128 runs on the matrix cores;
+ * one query head per key/value head.  bf16 and binary16 at d = 128 run on the matrix cores;
  * the other combinations run a plain float32 vector path, correct but far slower.
  *
  * cca_prefill_lse: cca_prefill that also writes, for every query t, the
@@ -194,7 +194,7 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
  *   dout  : device [B, H, L, d] of type dt, the gradient of the output;
  *   dq, dk, dv : device float32 [B, H, L, d], written (every element);
  *   workspace : device, >= cca_backward_workspace_bytes(B, H, L, d, g) bytes.
- *   Limits and errors as for cca_prefill; outside bf16 at d = 128 also
+ *   Limits and errors as for cca_prefill; outside 16-bit inputs at d = 128 also
  *   B*H*(L + L/g + 1) < 2^26 (one 64-lane wave per row and per key).
  */
 int cca_prefill_lse(const void* q, const void* k, const void* v, void* kc, void* vc, void* out, float* lse,

@@ -156,14 +156,14 @@ int cca_backward_gqa(const void* q, const void* k, const void* v, const void* kc
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       lse == nullptr || ((uintptr_t)lse & 3u) != 0)
     return CCA_ERR_INVALID;
-  const bool fast = dt == CCA_BF16 && d == 128;
+  const bool fast = dt != CCA_F32 && d == 128;
   if (fast && (int64_t)B * H * ((L + 127) / 128 + L / g / 128 + 1) >= INT32_MAX) return CCA_ERR_INVALID;
   // the other shapes launch one 64-lane wave per query row and per key
   if (!fast && (int64_t)B * H * (L + L / g + 1) * 64 >= (int64_t)UINT32_MAX) return CCA_ERR_INVALID;
   if (workspace_bytes < cca_backward_gqa_workspace_bytes(B, H, H_kv, L, d, g)) return CCA_ERR_WORKSPACE;
   if (fast)
-    return hip_status(cca::launch_backward_bf16_d128(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, B * H,
-                                                     H / H_kv, L, g, k_local, scale, stream));
+    return hip_status(cca::launch_backward_d128(dt, q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, B * H,
+                                                H / H_kv, L, g, k_local, scale, stream));
   return hip_status(cca::launch_backward_generic(dt, d, q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace,
                                                  B * H, H / H_kv, L, g, k_local, scale, stream));
 }

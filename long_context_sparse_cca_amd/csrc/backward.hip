@@ -1,4 +1,5 @@
-// Backward pass of CCA prefill attention (bf16 inputs, head dim 128, float32 gradients).
+// Backward pass of CCA prefill attention (16-bit inputs: bf16 or IEEE binary16; head dim
+// 128; float32 gradients).
 //
 // Method: the CCA write-up ("ICML 2025 | 全局池化+局部保留，CCA-Attention为LLM长文本建模带来突破性进展"):
 // the fused operator serves training (Triton section); the forward pools each
@@ -24,9 +25,9 @@
 //                              to dv, dk, those of core tokens to dVc, dKc (workspace)
 //   4. cca_bwd_pool_kernel     per group: dKc, dVc through the pooling into dk, dv,
 //                              and into dq at the group's last row
-// The score and gradient products run on bf16 MFMA (32x32x16 for dQ, 16x16x32 for
-// dK and dV) with float32 accumulation; P and dS are rounded to bf16 as MFMA operands, as P is in the
-// forward.  Tiles are staged HBM -> LDS with global_load_lds and read with the
+// The score and gradient products run on MFMA of the input type (32x32x16 for dQ,
+// 16x16x32 for dK and dV) with float32 accumulation; P and dS are rounded to that type as
+// MFMA operands, as P is in the forward.  Tiles are staged HBM -> LDS with global_load_lds and read with the
 // same 16-byte XOR swizzle and transpose reads as the forward kernel.
 #include "cca_internal.h"
 
@@ -40,7 +41,6 @@ constexpr int kTileBytes = kTileRows * kRowBytes;   // 16 KB
 constexpr float kLn2 = 0.69314718055994531f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
@@ -71,13 +71,9 @@ struct TileOffsets {
   }
 };
 
-__device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
 
 // Transpose-operand accumulation acc[dt] += X_subblock^T (d x 32 rows from LDS) . W,
-// W [32 rows x 32 cols] the fp32 32x32 MFMA output `w` rounded to bf16, in two halves:
+// W [32 rows x 32 cols] the fp32 32x32 MFMA output `w` rounded to T, in two halves:
 // the transpose reads of half u (rows 16u .. 16u+15) are issued early (tr_read), the
 // MFMAs later (tr_mfma).
 struct TrHalf {
@@ -92,15 +88,16 @@ __device__ __forceinline__ void tr_read(const uint8_t* tile_sb, const TileOffset
         (__attribute__((address_space(3))) v4s_t*)(tile_sb + 16 * u * kRowBytes + o.tr[1][dt]));
   }
 }
+template <typename T>
 __device__ __forceinline__ void tr_mfma(const TrHalf& t, const f32x16_t& w, int u, f32x16_t* acc) {
-  bf16x2_t pp[4];
+  typename Mma16<T>::x2 pp[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) pp[e] = bf16x2_t{(__bf16)w[8 * u + 2 * e], (__bf16)w[8 * u + 2 * e + 1]};
+  for (int e = 0; e < 4; ++e) pp[e] = Mma16<T>::round2(w[8 * u + 2 * e], w[8 * u + 2 * e + 1]);
   const uint4 pb = __builtin_bit_cast(uint4, pp);
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) {
     const v4s_t both[2] = {t.r[0][dt], t.r[1][dt]};
-    acc[dt] = mfma(__builtin_bit_cast(uint4, both), pb, acc[dt]);
+    acc[dt] = Mma16<T>::mfma32(__builtin_bit_cast(uint4, both), pb, acc[dt]);
   }
 }
 
@@ -110,20 +107,21 @@ __device__ __forceinline__ void rows_read(const uint8_t* tile_sb, const TileOffs
 #pragma unroll
   for (int d16 = 0; d16 < kD / 16; ++d16) xa[d16] = *reinterpret_cast<const uint4*>(tile_sb + o.rows[d16]);
 }
+template <typename T>
 __device__ __forceinline__ f32x16_t rows_mfma(const uint4* xa, const uint4* yop) {
   f32x16_t s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-  for (int d16 = 0; d16 < kD / 16; ++d16) s = mfma(xa[d16], yop[d16], s);
+  for (int d16 = 0; d16 < kD / 16; ++d16) s = Mma16<T>::mfma32(xa[d16], yop[d16], s);
   return s;
 }
 
-// Fill a 64-row tile (rows base .. base+63 of a row-major [*, 128] bf16 array,
+// Fill a 64-row tile (rows base .. base+63 of a row-major [*, 128] 16-bit array,
 // rows past `lim` repeat row `lim`) into LDS with the chunk swizzle.  nw waves
 // share the fill: wave w writes rows w*64/nw .. in groups of 4 rows per instruction.
 template <int NW>
-__device__ __forceinline__ void fill_tile(const bf16_t* src, int64_t base, int64_t lim, uint8_t* dst, int wave,
+__device__ __forceinline__ void fill_tile(const void* src, int64_t base, int64_t lim, uint8_t* dst, int wave,
                                           int lane) {
   constexpr int ITERS = kTileRows / (4 * NW);
 #pragma unroll
@@ -141,7 +139,8 @@ __device__ __forceinline__ void fill_tile(const bf16_t* src, int64_t base, int64
 // ---------------------------------------------------------------------------
 // 1. D[t] = dO[t] . O[t]  (16 lanes per row)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restrict__ O, const bf16_t* __restrict__ dO,
+template <typename T>
+__global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                            const float* __restrict__ lse, float* __restrict__ Dv,
                                                            float* __restrict__ lse2, int64_t rows) {
   const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
@@ -149,8 +148,8 @@ __global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restr
   float s = 0.f;
   if (row < rows) {
     float a[8], b[8];
-    Elem<bf16_t>::chunk_to_f32(ld16(O + (size_t)row * kD + 8 * c), a);
-    Elem<bf16_t>::chunk_to_f32(ld16(dO + (size_t)row * kD + 8 * c), b);
+    Elem<T>::chunk_to_f32(ld16(O + (size_t)row * kD + 8 * c), a);
+    Elem<T>::chunk_to_f32(ld16(dO + (size_t)row * kD + 8 * c), b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf(a[e], b[e], s);
   }
@@ -164,9 +163,10 @@ __global__ __launch_bounds__(256) void cca_bwd_prep_kernel(const bf16_t* __restr
 // ---------------------------------------------------------------------------
 // 2. dQ: 256 queries per workgroup (8 waves x 32), loop over the visible key tiles
 // ---------------------------------------------------------------------------
+template <typename T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void cca_bwd_dq_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ Kc, const T* __restrict__ Vc, const T* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dQ, int BH, int nq, int L,
     int g, int k_local, float scale, int ntiles) {
   constexpr int kBM = 256, kBN = 64;
@@ -201,10 +201,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const size_t slice = (size_t)bh * L * kD;              // query / dQ slice
   const int bkv = bh / nq;  // key/value slice read by query slice bh (grouped-query attention)
-  const bf16_t* Ks = K + (size_t)bkv * L * kD;
-  const bf16_t* Vs = V + (size_t)bkv * L * kD;
-  const bf16_t* Kcs = Kc + (size_t)bkv * m * kD;
-  const bf16_t* Vcs = Vc + (size_t)bkv * m * kD;
+  const T* Ks = K + (size_t)bkv * L * kD;
+  const T* Vs = V + (size_t)bkv * L * kD;
+  const T* Kcs = Kc + (size_t)bkv * m * kD;
+  const T* Vcs = Vc + (size_t)bkv * m * kD;
 
   // B operands of the score and dP chains: this lane's query / upstream-gradient row
   uint4 qop[kD / 16], dop[kD / 16];
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
   auto issue = [&](int it, uint8_t* buf) {
-    const bf16_t *ks, *vs;
+    const T *ks, *vs;
     int base, lim;
     if (it < n_core_tiles) {
       ks = Kcs; vs = Vcs; base = it * kBN; lim = m - 1;
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       rows_read(vsb, off, ya);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
-      f32x16_t s = rows_mfma(xa, qop);           // S^T: keys x queries
-      f32x16_t dp = rows_mfma(ya, dop);          // dP^T
+      f32x16_t s = rows_mfma<T>(xa, qop);           // S^T: keys x queries
+      f32x16_t dp = rows_mfma<T>(ya, dop);          // dP^T
       TrHalf th;
       tr_read(ksb, off, 0, th);
       __builtin_amdgcn_sched_barrier(0);
@@ -284,9 +284,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float p = fast_exp2(fmaf(s[r], sc, -lse2));
         dp[r] = p * (dp[r] - Dq);                 // dS^T
       }
-      tr_mfma(th, dp, 0, acc);                   // dQ^T += K^T dS^T
+      tr_mfma<T>(th, dp, 0, acc);                   // dQ^T += K^T dS^T
       tr_read(ksb, off, 1, th);
-      tr_mfma(th, dp, 1, acc);
+      tr_mfma<T>(th, dp, 1, acc);
     }
   };
 
@@ -331,14 +331,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //    waves per SIMD (168 registers each) the LDS operand traffic of the 16-key layout
 //    (64 bytes per MFMA cycle and wave) has enough waves to hide behind.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
 
+template <typename T>
 __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) void cca_bwd_dkdv16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, const bf16_t* __restrict__ dO,
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ Kc, const T* __restrict__ Vc, const T* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ Dv, float* __restrict__ dK, float* __restrict__ dV,
     float* __restrict__ dKc, float* __restrict__ dVc, int BHkv, int nq, int L, int g, int k_local, float scale,
     int n_core_wg) {
@@ -381,8 +378,8 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int n_it = n_qt * nq;
 
   const size_t slice = (size_t)bkv * L * kD;              // key/value (and dK/dV) slice
-  const bf16_t* Ks = core ? Kc + (size_t)bkv * m * kD : K + slice;
-  const bf16_t* Vs = core ? Vc + (size_t)bkv * m * kD : V + slice;
+  const T* Ks = core ? Kc + (size_t)bkv * m * kD : K + slice;
+  const T* Vs = core ? Vc + (size_t)bkv * m * kD : V + slice;
   const size_t qslice0 = (size_t)bkv * nq;                // first query slice that reads it
   // B operands of the score and dP products: dims 32kk + 8G .. +7 of this lane's key
   const int key_lane = min(c0 + n16, key_end - 1);
@@ -481,9 +478,9 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[b][i] = dp[b][i] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < kD / 32; ++kk) s[b] = mfma16(xa[kk], kop[kk], s[b]);
+        for (int kk = 0; kk < kD / 32; ++kk) s[b] = Mma16<T>::mfma16(xa[kk], kop[kk], s[b]);
 #pragma unroll
-        for (int kk = 0; kk < kD / 32; ++kk) dp[b] = mfma16(ya[kk], vop[kk], dp[b]);
+        for (int kk = 0; kk < kD / 32; ++kk) dp[b] = Mma16<T>::mfma16(ya[kk], vop[kk], dp[b]);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
       }
@@ -504,11 +501,11 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
           dsw[4 * b + i] = p * (dp[b][i] - dr[i]);
         }
       }
-      bf16x2_t pp[4], qq[4];
+      typename Mma16<T>::x2 pp[4], qq[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pp[e] = bf16x2_t{(__bf16)pw[2 * e], (__bf16)pw[2 * e + 1]};
-        qq[e] = bf16x2_t{(__bf16)dsw[2 * e], (__bf16)dsw[2 * e + 1]};
+        pp[e] = Mma16<T>::round2(pw[2 * e], pw[2 * e + 1]);
+        qq[e] = Mma16<T>::round2(dsw[2 * e], dsw[2 * e + 1]);
       }
       const uint4 pb = __builtin_bit_cast(uint4, pp);
       const uint4 db = __builtin_bit_cast(uint4, qq);
@@ -525,8 +522,8 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             (__attribute__((address_space(3))) v4s_t*)(qsb + toff[1][blk]));
         const v4s_t ob[2] = {o0, o1};
         const v4s_t qb[2] = {q0, q1};
-        acc_v[blk] = mfma16(__builtin_bit_cast(uint4, ob), pb, acc_v[blk]);
-        acc_k[blk] = mfma16(__builtin_bit_cast(uint4, qb), db, acc_k[blk]);
+        acc_v[blk] = Mma16<T>::mfma16(__builtin_bit_cast(uint4, ob), pb, acc_v[blk]);
+        acc_k[blk] = Mma16<T>::mfma16(__builtin_bit_cast(uint4, qb), db, acc_k[blk]);
       }
     }
   };
@@ -578,8 +575,9 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // ---------------------------------------------------------------------------
 // 4. pooling backward: one wave per group
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                          const bf16_t* __restrict__ V,
+template <typename T>
+__global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                          const T* __restrict__ V,
                                                           const float* __restrict__ dKc,
                                                           const float* __restrict__ dVc, float* __restrict__ dQ,
                                                           float* __restrict__ dK, float* __restrict__ dV, int64_t L,
@@ -601,13 +599,13 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
   const int rsub = lane >> 2, seg = lane & 3;
   float qf[32], kcf[32], vcf[32];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) Elem<bf16_t>::chunk_to_f32(ld16(Q + qrow0 + seg * 32 + c * 8), qf + c * 8);
+  for (int c = 0; c < 4; ++c) Elem<T>::chunk_to_f32(ld16(Q + qrow0 + seg * 32 + c * 8), qf + c * 8);
   if (nq > 1) {
     for (int h = 1; h < nq; ++h) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float f[8];
-        Elem<bf16_t>::chunk_to_f32(ld16(Q + qrow0 + h * qstride + seg * 32 + c * 8), f);
+        Elem<T>::chunk_to_f32(ld16(Q + qrow0 + h * qstride + seg * 32 + c * 8), f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[c * 8 + e] += f[e];
       }
@@ -630,8 +628,8 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float kf[8], vf[8];
-        Elem<bf16_t>::chunk_to_f32(ld16(K + (row0 + r) * kD + seg * 32 + c * 8), kf);
-        Elem<bf16_t>::chunk_to_f32(ld16(V + (row0 + r) * kD + seg * 32 + c * 8), vf);
+        Elem<T>::chunk_to_f32(ld16(K + (row0 + r) * kD + seg * 32 + c * 8), kf);
+        Elem<T>::chunk_to_f32(ld16(V + (row0 + r) * kD + seg * 32 + c * 8), vf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           s = fmaf(qf[c * 8 + e], kf[e], s);
@@ -670,9 +668,10 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
   float q2[2] = {0.f, 0.f}, kc2[2], vc2[2], dq2[2] = {0.f, 0.f};
   {
     for (int h = 0; h < nq; ++h) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + qrow0 + h * qstride + col);
-      q2[0] += __uint_as_float(w << 16);
-      q2[1] += __uint_as_float(w & 0xffff0000u);
+      float f[2];
+      Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(Q + qrow0 + h * qstride + col), f);
+      q2[0] += f[0];
+      q2[1] += f[1];
     }
     if (nq > 1) {
       q2[0] *= inv_nq;
@@ -683,8 +682,9 @@ __global__ __launch_bounds__(64) void cca_bwd_pool_kernel(const bf16_t* __restri
   }
   for (int r = 0; r < g; ++r) {
     const float a = a_l[r], dz = z_l[r];
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(K + (row0 + r) * kD + col);
-    const float k0 = __uint_as_float(kw << 16), k1 = __uint_as_float(kw & 0xffff0000u);
+    float kf[2];
+    Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(K + (row0 + r) * kD + col), kf);
+    const float k0 = kf[0], k1 = kf[1];
     float2* pk = reinterpret_cast<float2*>(dK + (row0 + r) * kD + col);
     float2* pv = reinterpret_cast<float2*>(dV + (row0 + r) * kD + col);
     float2 xk = *pk, xv = *pv;
@@ -715,7 +715,8 @@ size_t backward_workspace_bytes(int B, int H, int H_kv, int64_t L, int d, int g)
   return (2 * BH * (size_t)L + 2 * BHkv * m * (size_t)d) * sizeof(float);
 }
 
-hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
+template <typename T>
+hipError_t launch_backward_t(const void* q, const void* k, const void* v, const void* kc, const void* vc,
                                      const void* out, const float* lse, const void* dout, float* dq, float* dk,
                                      float* dv, void* workspace, int BH, int nq, int64_t L, int g, int k_local,
                                      float scale, hipStream_t stream) {
@@ -726,28 +727,39 @@ hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v
   float* dKc = lse2 + (size_t)BH * L;
   float* dVc = dKc + (size_t)BHkv * m * kD;
   const int64_t rows = (int64_t)BH * L;
-  hipLaunchKernelGGL(cca_bwd_prep_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
-                     (const bf16_t*)out, (const bf16_t*)dout, lse, Dv, lse2, rows);
+  hipLaunchKernelGGL(cca_bwd_prep_kernel<T>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
+                     (const T*)out, (const T*)dout, lse, Dv, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntiles = (int)((L + 255) / 256);
-  hipLaunchKernelGGL(cca_bwd_dq_kernel, dim3((unsigned)(BH * ntiles)), dim3(512), 0, stream, (const bf16_t*)q,
-                     (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc, (const bf16_t*)dout,
+  hipLaunchKernelGGL(cca_bwd_dq_kernel<T>, dim3((unsigned)(BH * ntiles)), dim3(512), 0, stream, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, (const T*)dout,
                      (const float*)lse2, (const float*)Dv, dq, BH, nq, (int)L, g, k_local, scale, ntiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_core_wg = (int)((m + 191) / 192);
   const int n_wg = n_core_wg + (int)((L + 191) / 192);
-  hipLaunchKernelGGL(cca_bwd_dkdv16_kernel, dim3((unsigned)((int64_t)BHkv * n_wg)), dim3(768), 0, stream,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)kc, (const bf16_t*)vc,
-                     (const bf16_t*)dout, (const float*)lse2, (const float*)Dv, dk, dv, dKc, dVc, BHkv, nq, (int)L,
+  hipLaunchKernelGGL(cca_bwd_dkdv16_kernel<T>, dim3((unsigned)((int64_t)BHkv * n_wg)), dim3(768), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc,
+                     (const T*)dout, (const float*)lse2, (const float*)Dv, dk, dv, dKc, dVc, BHkv, nq, (int)L,
                      g, k_local, scale, n_core_wg);
   e = hipGetLastError();
   if (e != hipSuccess || m == 0) return e;
-  hipLaunchKernelGGL(cca_bwd_pool_kernel, dim3((unsigned)((int64_t)BHkv * m)), dim3(64),
-                     (size_t)2 * g * sizeof(float), stream, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+  hipLaunchKernelGGL(cca_bwd_pool_kernel<T>, dim3((unsigned)((int64_t)BHkv * m)), dim3(64),
+                     (size_t)2 * g * sizeof(float), stream, (const T*)q, (const T*)k, (const T*)v,
                      (const float*)dKc, (const float*)dVc, dq, dk, dv, L, g, m, nq, scale);
   return hipGetLastError();
+}
+
+hipError_t launch_backward_d128(int dt, const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                                const void* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                void* workspace, int BH, int nq, int64_t L, int g, int k_local, float scale,
+                                hipStream_t stream) {
+  if (dt == CCA_F16)
+    return launch_backward_t<f16_t>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq, L, g, k_local,
+                                    scale, stream);
+  return launch_backward_t<bf16_t>(q, k, v, kc, vc, out, lse, dout, dq, dk, dv, workspace, BH, nq, L, g, k_local,
+                                   scale, stream);
 }
 
 }  // namespace cca

@@ -106,6 +106,40 @@ template <> struct Elem<float> {
   __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
 };
 
+// Matrix-core traits of the 16-bit element types: the 32x32x16 and 16x16x32 MFMAs on
+// 16-byte operand registers, the rounding of two float32 values into one operand word, and
+// the two-term dot product with float32 accumulation.  Tile fills and LDS transpose reads
+// move 16-bit elements without looking at them, so they need nothing type-specific.
+template <typename T> struct Mma16;
+template <> struct Mma16<bf16_t> {
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static x2 round2(float a, float b) { return x2{(__bf16)a, (__bf16)b}; }
+  __device__ __forceinline__ static float dot2(x2 a, x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <> struct Mma16<f16_t> {
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  }
+  __device__ __forceinline__ static x2 round2(float a, float b) { return x2{(_Float16)a, (_Float16)b}; }
+  __device__ __forceinline__ static float dot2(x2 a, x2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

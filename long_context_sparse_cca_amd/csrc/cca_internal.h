@@ -121,17 +121,18 @@ hipError_t launch_serve_append_decode(const cca_cache_t* c, int32_t* lens, int64
                                       void* workspace, float scale, hipStream_t stream, float* qsum = nullptr,
                                       int d_rope = 0);
 
-// Backward pass, bf16, head dim 128 (backward.hip); BH query slices, nq query heads per
+// Backward pass, 16-bit inputs (dt = CCA_BF16 or CCA_F16), head dim 128 (backward.hip);
+// BH query slices, nq query heads per
 // key/value head.  Workspace: D [BH][L], the log-sum-exp in log2 units [BH][L], then dKc
 // and dVc [BH/nq][L/g][d], all float32.
 size_t backward_workspace_bytes(int B, int H, int H_kv, int64_t L, int d, int g);
-hipError_t launch_backward_bf16_d128(const void* q, const void* k, const void* v, const void* kc, const void* vc,
-                                     const void* out, const float* lse, const void* dout, float* dq, float* dk,
-                                     float* dv, void* workspace, int BH, int nq, int64_t L, int g, int k_local,
-                                     float scale, hipStream_t stream);
+hipError_t launch_backward_d128(int dt, const void* q, const void* k, const void* v, const void* kc, const void* vc,
+                                const void* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                                void* workspace, int BH, int nq, int64_t L, int g, int k_local, float scale,
+                                hipStream_t stream);
 
 // Backward pass for the other shapes (backward_generic.hip): float32 inputs at head dim
-// 64 or 128, bf16 at head dim 64; same arguments, gradients and workspace layout as above,
+// 64 or 128, 16-bit inputs at head dim 64; same arguments, gradients and workspace layout as above,
 // out and dout in the input type.
 hipError_t launch_backward_generic(int dt, int d, const void* q, const void* k, const void* v, const void* kc,
                                    const void* vc, const void* out, const float* lse, const void* dout, float* dq,

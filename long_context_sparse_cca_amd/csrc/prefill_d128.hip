@@ -37,35 +37,12 @@ constexpr int kBufBytes = 2 * kTileBytes;    // K tile + V tile
 // weights in a sub-block sum above kSumLimit (then to the row's running max).  The
 // weights thus stay <= 2^16, so the fp32 row sums and accumulators cannot overflow
 // unless the sum of |V| over a row exceeds ~2^112; the final division by the row sum
-// makes the result independent of the reference point up to rounding.
+// makes the result independent of the reference point up to rounding.  In binary16 a
+// weight above 65519 rounds to infinity; the row sum then exceeds the limit too, so the
+// wave rescales and recomputes the weights in that case as well.
 constexpr float kSumLimit = 65536.0f;
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
-
-// The type-dependent instructions: the 32x32x16 MFMA, the rounding of two weights into one
-// register and the two-term dot product of the row sum.  Everything else (tile fills, the
-// transpose reads, the swizzle) moves 16-bit elements without looking at them.
-template <typename T> struct Ops16;
-template <> struct Ops16<bf16_t> {
-  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
-  __device__ __forceinline__ static f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static x2 round2(float a, float b) { return x2{(__bf16)a, (__bf16)b}; }
-  __device__ __forceinline__ static float dot2(x2 a, x2 b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
-  }
-};
-template <> struct Ops16<f16_t> {
-  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
-  __device__ __forceinline__ static f32x16_t mfma(const uint4& a, const uint4& b, const f32x16_t& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
-  }
-  __device__ __forceinline__ static x2 round2(float a, float b) { return x2{(_Float16)a, (_Float16)b}; }
-  __device__ __forceinline__ static float dot2(x2 a, x2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
-};
 
 // 16-byte chunk swizzle of a tile row (16 chunks per 256-byte row).  It is a
 // bijection on any 16 consecutive rows (the K operand read: 16 lanes, 16 rows, one
@@ -238,7 +215,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_run = kNegBig, l_run = 0.f;
   const float sc = scale * kLog2e;
-  using Ops = Ops16<T>;
+  using Ops = Mma16<T>;
   const typename Ops::x2 ones = Ops::round2(1.0f, 1.0f);
 
   // Visible window [lo, lo + span] of each lane in the key index space of a tile kind:
@@ -278,7 +255,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
       for (int d16 = 0; d16 < kD / 16; ++d16)
-        s = Ops::mfma(ka[d16], qop[d16], s);
+        s = Ops::mfma32(ka[d16], qop[d16], s);
       // V operand transpose reads for this sub-block, issued behind the QK MFMAs so
       // their latency hides under the softmax arithmetic
       v4s_t vop[2][2][kD / 32];
@@ -355,7 +332,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
           const v4s_t both[2] = {vop[u][0][dt], vop[u][1][dt]};
-          acc[dt] = Ops::mfma(__builtin_bit_cast(uint4, both), pb, acc[dt]);
+          acc[dt] = Ops::mfma32(__builtin_bit_cast(uint4, both), pb, acc[dt]);
         }
       }
     }

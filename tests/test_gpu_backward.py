@@ -24,8 +24,14 @@ from long_context_sparse_cca_amd.synth import np_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _dev(x, device):
-    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=torch.bfloat16).contiguous()
+TDT = {"bf16": torch.bfloat16, "f16": torch.float16}
+# gradient bound (fraction of the gradient's scale) and log-sum-exp bound per input type
+GRAD_TOL = {"bf16": 2e-2, "f16": 5e-3}
+LSE_TOL = {"bf16": 1e-2, "f16": 2e-3}
+
+
+def _dev(x, device, dt="bf16"):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=TDT[dt]).contiguous()
 
 
 def _say(msg):
@@ -33,30 +39,36 @@ def _say(msg):
     sys.stdout.flush()
 
 
-# (B, H, L, g, k, seed)
+# matrix-core path (16-bit inputs, d = 128): (B, H, L, g, k, dtype, seed)
 BWD_CASES = [
-    (1, 2, 300, 16, 2, 70),
-    (1, 1, 700, 16, 4, 71),     # core tiles seen by several query tiles
-    (2, 1, 517, 7, 3, 72),      # g not a power of two, ragged tiles
-    (1, 1, 200, 1, 0, 73),      # g = 1: causal attention
-    (1, 1, 640, 16, 100, 74),   # window wider than the sequence
-    (1, 1, 1500, 32, 5, 75),    # many core tokens per key tile
+    (1, 2, 300, 16, 2, "bf16", 70),
+    (1, 1, 700, 16, 4, "bf16", 71),     # core tiles seen by several query tiles
+    (2, 1, 517, 7, 3, "bf16", 72),      # g not a power of two, ragged tiles
+    (1, 1, 200, 1, 0, "bf16", 73),      # g = 1: causal attention
+    (1, 1, 640, 16, 100, "bf16", 74),   # window wider than the sequence
+    (1, 1, 1500, 32, 5, "bf16", 75),    # many core tokens per key tile
+    (1, 2, 300, 16, 2, "f16", 76),      # binary16 inputs
+    (2, 1, 517, 7, 3, "f16", 77),
+    (1, 1, 1500, 32, 5, "f16", 78),
 ]
 
 
 def _id(c):
-    B, H, L, g, k, seed = c
-    return f"B{B}H{H}L{L}g{g}k{k}"
+    B, H, L, g, k, dt, seed = c
+    return f"B{B}H{H}L{L}g{g}k{k}-{dt}"
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=_id)
 def test_backward_matches_oracle(gpu, case):
-    B, H, L, g, k, seed = case
+    """Gradients of the matrix-core path against the fp64 oracle, whose core tokens are
+    rounded to the input type as the forward stores them.  P and dS are rounded to that
+    type as MFMA operands, so the bound is the type's tolerance times the gradient's scale."""
+    B, H, L, g, k, dt, seed = case
     d = 128
     _say(f"backward case {_id(case)} seed {seed}")
-    Q, K, V = np_inputs(B, H, L, d, "bf16", seed)
-    dO = np_inputs(B, H, L, d, "bf16", seed + 500)[0]
-    q, kk, v, do = (_dev(x, gpu) for x in (Q, K, V, dO))
+    Q, K, V = np_inputs(B, H, L, d, dt, seed)
+    dO = np_inputs(B, H, L, d, dt, seed + 500)[0]
+    q, kk, v, do = (_dev(x, gpu, dt) for x in (Q, K, V, dO))
     scale = 1.0 / math.sqrt(d)
     out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
     dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
@@ -65,15 +77,15 @@ def test_backward_matches_oracle(gpu, case):
     assert torch.equal(out, binding.prefill(q, kk, v, g, k, scale))
     for b in range(B):
         for h in range(H):
-            _, lse_ref = cca_backward.cca_forward_lse_slice(Q[b, h], K[b, h], V[b, h], g, k, scale, core_dtype="bf16")
+            _, lse_ref = cca_backward.cca_forward_lse_slice(Q[b, h], K[b, h], V[b, h], g, k, scale, core_dtype=dt)
             e = np.abs(lse[b, h].cpu().numpy() - lse_ref).max()
-            assert e <= 1e-2, f"lse err {e:.3e}"
-    # gradients against the oracle, using the GPU's bf16 forward output for D = dO.O is not
-    # needed: the oracle is exact and the tolerance covers the bf16 rounding of O
-    want = cca_backward.cca_backward(Q, K, V, dO, g, k, scale, core_dtype="bf16")
+            assert e <= LSE_TOL[dt], f"lse err {e:.3e}"
+    # gradients against the oracle, using the GPU's 16-bit forward output for D = dO.O is not
+    # needed: the oracle is exact and the tolerance covers the rounding of O
+    want = cca_backward.cca_backward(Q, K, V, dO, g, k, scale, core_dtype=dt)
     for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
         err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
-        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        bound = GRAD_TOL[dt] * max(1.0, np.abs(ref).max())
         _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
         assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
 
@@ -98,7 +110,8 @@ def test_backward_unsupported_shapes(gpu):
         binding.prefill_lse(q, q.clone(), q.clone(), 16, 1)
 
 
-# The vector path: float32 and binary16 inputs at d = 64 and 128, bf16 at d = 64.
+# The vector path: float32 inputs at d = 64 and 128, 16-bit inputs at d = 64 (binary16 at
+# d = 128 takes the matrix-core path, the case is kept as one more check of it).
 # (dtype, d, B, H, H_kv, L, g, k, seed)
 GEN_CASES = [
     ("f32", 64, 1, 2, 2, 256, 16, 1, 110),    # the small float32 layer (B=1, H=2, d=64, L=256, g=16, k=1)
@@ -177,38 +190,39 @@ def test_generic_autograd_function(gpu):
     assert torch.equal(q.grad, dq) and torch.equal(kk.grad, dk) and torch.equal(v.grad, dv)
 
 
-# grouped-query training: (B, H, H_kv, L, g, k, seed)
+# grouped-query training: (B, H, H_kv, L, g, k, dtype, seed)
 GQA_BWD_CASES = [
-    (1, 4, 2, 300, 16, 2, 90),    # r = 2
-    (1, 4, 1, 520, 16, 3, 91),    # multi-query (r = 4), ragged tiles
-    (2, 8, 2, 260, 7, 1, 92),     # r = 4, g not a power of two
+    (1, 4, 2, 300, 16, 2, "bf16", 90),    # r = 2
+    (1, 4, 1, 520, 16, 3, "bf16", 91),    # multi-query (r = 4), ragged tiles
+    (2, 8, 2, 260, 7, 1, "bf16", 92),     # r = 4, g not a power of two
+    (1, 4, 1, 520, 16, 3, "f16", 93),     # binary16, multi-query
 ]
 
 
 def _gid(c):
-    B, H, Hkv, L, g, k, seed = c
-    return f"B{B}H{H}Hkv{Hkv}L{L}g{g}k{k}"
+    B, H, Hkv, L, g, k, dt, seed = c
+    return f"B{B}H{H}Hkv{Hkv}L{L}g{g}k{k}-{dt}"
 
 
 @pytest.mark.parametrize("case", GQA_BWD_CASES, ids=_gid)
 def test_gqa_backward_matches_oracle(gpu, case):
-    B, H, Hkv, L, g, k, seed = case
+    B, H, Hkv, L, g, k, dt, seed = case
     d = 128
     _say(f"gqa backward case {_gid(case)} seed {seed}")
-    Q = np_inputs(B, H, L, d, "bf16", seed)[0]
-    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, "bf16", seed + 1)[1:])
-    dO = np_inputs(B, H, L, d, "bf16", seed + 500)[0]
-    q, kk, v, do = (_dev(x, gpu) for x in (Q, K, V, dO))
+    Q = np_inputs(B, H, L, d, dt, seed)[0]
+    K, V = (x[:, :Hkv] for x in np_inputs(B, H, L, d, dt, seed + 1)[1:])
+    dO = np_inputs(B, H, L, d, dt, seed + 500)[0]
+    q, kk, v, do = (_dev(x, gpu, dt) for x in (Q, K, V, dO))
     scale = 1.0 / math.sqrt(d)
     out, lse, kc, vc = binding.prefill_lse(q, kk, v, g, k, scale)
     dq, dk, dv = binding.backward(q, kk, v, kc, vc, out, lse, do, g, k, scale)
     torch.cuda.synchronize()
     assert tuple(dk.shape) == (B, Hkv, L, d) and tuple(kc.shape) == (B, Hkv, L // g, d)
     assert torch.equal(out, binding.prefill(q, kk, v, g, k, scale))
-    want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype="bf16")
+    want = cca_backward.cca_backward_gqa(Q, K, V, dO, g, k, scale, core_dtype=dt)
     for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
         err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
-        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        bound = GRAD_TOL[dt] * max(1.0, np.abs(ref).max())
         _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
         assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
 
