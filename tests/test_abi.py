@@ -73,11 +73,12 @@ def test_workspace_size(lib):
 
 
 @pytest.mark.parametrize("n,g,k,B,H,d,dt", [(131072, 16, 64, 1, 32, 128, 1), (1000, 7, 3, 2, 4, 64, 0),
-                                            (5, 16, 0, 1, 1, 128, 1), (0, 4, 2, 1, 1, 64, 0)])
+                                            (5, 16, 0, 1, 1, 128, 1), (0, 4, 2, 1, 1, 64, 0),
+                                            (65536, 16, 64, 2, 8, 128, 2)])
 def test_kv_cache_bytes_match_oracle(lib, n, g, k, B, H, d, dt):
     r, f = ctypes.c_int64(), ctypes.c_int64()
     assert lib.cca_kv_cache_bytes(n, g, k, B, H, d, dt, ctypes.byref(r), ctypes.byref(f)) == 0
-    assert (r.value, f.value) == oracle.kv_cache_bytes(n, g, k, B, H, d, 2 if dt == 1 else 4)
+    assert (r.value, f.value) == oracle.kv_cache_bytes(n, g, k, B, H, d, 4 if dt == 0 else 2)
 
 
 @pytest.mark.parametrize("L,g,k", [(131072, 16, 64), (8192, 16, 64), (256, 16, 1), (1000, 7, 3), (37, 4, 1),
@@ -128,3 +129,15 @@ def test_validation_of_training_lca_and_serving_calls(lib):
     assert ws > 0 and lib.cca_serve_workspace_bytes(ctypes.byref(d), 3) == 0
     assert lib.cca_cache_append_decode_varlen(ctypes.byref(d), P, 100, 4, P, P, P, P, 1, P, ws - 1, 0.1,
                                               NULL) == -3
+
+
+def test_unknown_dtype_rejected_before_any_launch(lib):
+    """A dtype code outside {F32, BF16, F16} is refused by host-side validation (no device
+    call is made, so this runs without a GPU)."""
+    r, f = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.cca_kv_cache_bytes(100, 16, 2, 1, 1, 128, 3, ctypes.byref(r), ctypes.byref(f)) == -2
+    null = ctypes.c_void_p(0)
+    assert lib.cca_prefill(null, null, null, null, null, null, 1, 1, ctypes.c_int64(64), 128, 16, 1,
+                           ctypes.c_float(0.1), 3, 3, null) == -2
+    assert lib.cca_pool_kv(null, null, null, null, null, 1, 1, ctypes.c_int64(64), 128, 16,
+                           ctypes.c_float(0.1), 7, null) == -2
