@@ -56,6 +56,9 @@ LCA_CASES = [
     (1, 1, 300, 128, 100, 1, 64, "f32", 5),      # g > 64: scores over two passes of the wave
     (1, 1, 15, 64, 16, 1, 32, "bf16", 6),        # L < g: nothing condensed
     (1, 2, 600, 128, 16, 2, 64, "f16", 7),       # binary16 inputs
+    (1, 2, 700, 128, 16, 2, 128, "bf16", 8),     # d_rope = d on the g = 16 kernel
+    (2, 1, 333, 128, 16, 1, 3, "bf16", 9),       # odd d_rope: one 32-bit word holds a pooled and an anchor dim
+    (1, 1, 500, 128, 16, 3, 8, "f16", 10),       # d_rope = 8: only the last column chunk is positional
 ]
 
 
