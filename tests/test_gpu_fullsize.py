@@ -65,14 +65,17 @@ def test_prefill_fullsize_sampled(gpu, L, dt):
         _say(f"L={L} {dt} head {h}: max err {worst:.2e} (vs exact core tokens {worst_exact:.2e})")
 
 
-def test_decode_fullsize_sampled(gpu):
-    """B=8, 131072-token context seeded from a prefill, 256 decode steps (16 pooling steps)."""
-    B, L0, S = 8, 131072, 256
+@pytest.mark.parametrize("dt,B,S", [("bf16", 8, 256), ("f16", 2, 64)])
+def test_decode_fullsize_sampled(gpu, dt, B, S):
+    """131072-token context seeded from a prefill, then S decode steps (S/16 pooling steps):
+    B=8 and 256 steps in bf16; a shorter binary16 run (B=2, 64 steps) with its own bound."""
+    L0 = 131072
     T = L0 + S
-    _say("full-size decode: generating inputs")
-    q, k, v = torch_inputs(B, H, T, D, torch.bfloat16, gpu, seed=1, heavy_frac=0.01)
+    tdt, tol = (torch.bfloat16, TOL_BF16) if dt == "bf16" else (torch.float16, TOL_F16)
+    _say(f"full-size decode {dt}: generating inputs")
+    q, k, v = torch_inputs(B, H, T, D, tdt, gpu, seed=1, heavy_frac=0.01)
     scale = 1.0 / math.sqrt(D)
-    cache = binding.KVCache(B, H, D, G, KL, max_tokens=T, dtype=torch.bfloat16, device=gpu)
+    cache = binding.KVCache(B, H, D, G, KL, max_tokens=T, dtype=tdt, device=gpu)
     kc, vc = binding.pool_kv(q[:, :, :L0].contiguous(), k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), G,
                              scale)
     cache.load_prefill(k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc, vc)
@@ -87,16 +90,16 @@ def test_decode_fullsize_sampled(gpu):
         cache.decode(qs[s], out_dtype=torch.float32, out=outs[s])
     torch.cuda.synchronize()
     got = outs.cpu().numpy()
-    for (b, h) in [(0, 0), (3, 17), (7, 31)]:
+    for (b, h) in [(0, 0), (B // 2, 17), (B - 1, 31)]:
         Q = q[b, h].float().cpu().numpy().astype(np.float64)
         K = k[b, h].float().cpu().numpy().astype(np.float64)
         V = v[b, h].float().cpu().numpy().astype(np.float64)
-        Kc, Vc, _ = oracle.pool(Q, K, V, G, scale, core_dtype="bf16")
+        Kc, Vc, _ = oracle.pool(Q, K, V, G, scale, core_dtype=dt)
         for s in range(S):
             t = L0 + s
             want = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
             err = np.abs(got[s, b, h] - want).max()
-            assert err <= TOL_BF16, f"slice ({b},{h}) step {s}: max abs err {err:.3e}"
+            assert err <= tol, f"{dt} slice ({b},{h}) step {s}: max abs err {err:.3e}"
 
 
 def test_dense_mode_fullsize_sampled(gpu):
