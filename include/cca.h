@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
   CCA_OK = 0,
   CCA_ERR_INVALID = -1,     /* null pointer, misaligned pointer, bad size or count */
-  CCA_ERR_UNSUPPORTED = -2, /* head dim not 64/128, dtype combination not built */
+  CCA_ERR_UNSUPPORTED = -2, /* head dim not 64/128, unknown dtype code, dtype combination not built */
   CCA_ERR_WORKSPACE = -3,   /* workspace smaller than the matching *_workspace_bytes() */
   CCA_ERR_HIP = -4,         /* a kernel launch failed */
   CCA_ERR_CAPACITY = -5     /* the cache has no room for another token */
@@ -452,7 +452,8 @@ int cca_cache_extend_lca(const cca_cache_t* c, float* qsum, int d_rope, int32_t*
  * k_local raw groups:
  *   *resident_bytes = B*H*2*d*elem * (floor(n_tokens/g) + (k_local+1)*g)
  *   *full_bytes     = B*H*2*d*elem * n_tokens            (standard KV cache)
- * elem = 2 for CCA_BF16, 4 for CCA_F32.  Either output pointer may be NULL.
+ * elem = 2 for CCA_BF16 and CCA_F16, 4 for CCA_F32; any other dt gives
+ * CCA_ERR_UNSUPPORTED.  Either output pointer may be NULL.
  */
 int cca_kv_cache_bytes(int64_t n_tokens, int g, int k_local, int B, int H, int d, int dt,
                        int64_t* resident_bytes, int64_t* full_bytes);
