@@ -3,9 +3,12 @@
 Inputs are drawn on the GPU (seeded torch generator, 1% heavy-hitter keys x4,
 bf16); the sampled (b, h) slices are copied back so the oracle sees exactly
 the GPU's inputs.  The oracle pools the sampled slice completely and computes
-the sampled rows one by one.  Parity is against core tokens stored in bf16 (one
-rounding of the exact core token); the error against exact fp64 core tokens is
-printed alongside.
+the sampled rows one by one.  Parity is against core tokens stored in the input
+type (one rounding of the exact core token, the reading that core K/V are cache
+tensors of the model's type).  The error against exact fp64 core tokens is printed
+alongside and held under a looser regression bound: at 128K in bf16 it reaches
+about 3e-2, almost all of it the bf16 half-ulp of heavy-hitter core keys (|Kc| up to
+about 16), not the kernel.
 """
 import math
 import sys
@@ -22,6 +25,8 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 2e-2
 TOL_F16 = 5e-3
+# regression bounds on the error against exact (unrounded) core tokens
+EXACT_TOL = {"bf16": 5e-2, "f16": 1.5e-2}
 H, D, G, KL = 32, 128, 16, 64
 
 
@@ -63,43 +68,65 @@ def test_prefill_fullsize_sampled(gpu, L, dt):
             worst_exact = max(worst_exact, np.abs(got[i] - oracle.cca_row(Q[t], t, K, V, Kx, Vx, G, KL, scale)).max())
             assert err <= tol, f"head {h} row {t}: max abs err {err:.3e}"
         _say(f"L={L} {dt} head {h}: max err {worst:.2e} (vs exact core tokens {worst_exact:.2e})")
+        assert worst_exact <= EXACT_TOL[dt], f"head {h}: error vs exact core tokens {worst_exact:.3e}"
 
 
-@pytest.mark.parametrize("dt,B,S", [("bf16", 8, 256), ("f16", 2, 64)])
+@pytest.mark.parametrize("dt,B,S", [("bf16", 8, 256), ("f16", 3, 64)])
 def test_decode_fullsize_sampled(gpu, dt, B, S):
     """131072-token context seeded from a prefill, then S decode steps (S/16 pooling steps):
-    B=8 and 256 steps in bf16; a shorter binary16 run (B=2, 64 steps) with its own bound."""
+    B=8 and 256 steps in bf16; a shorter binary16 run (B=3, 64 steps) with its own bound.
+    Both shapes read more than 384 MiB of K/V per step, so both take the streaming-load
+    instantiation.  Two caches run the same tokens: one through the fused single launch
+    (cache_append_decode, the call the benchmark times) and one through the two-call path
+    (append, then decode_step).  The fused outputs are checked against the oracle on
+    sampled slices at every step; the two paths must agree bit for bit (outputs and the
+    core tokens pooled during the steps)."""
     L0 = 131072
     T = L0 + S
     tdt, tol = (torch.bfloat16, TOL_BF16) if dt == "bf16" else (torch.float16, TOL_F16)
-    _say(f"full-size decode {dt}: generating inputs")
+    # K/V bytes per step: B*H*(core + raw window)*d*2 (K and V) * 2 bytes; above the streaming switch
+    n_keys = (L0 // G - KL) + (L0 - (L0 // G - KL) * G + 1)
+    assert B * H * n_keys * D * 2 * 2 > 384 * 2 ** 20
+    _say(f"full-size decode {dt} B={B}: generating inputs")
     q, k, v = torch_inputs(B, H, T, D, tdt, gpu, seed=1, heavy_frac=0.01)
     scale = 1.0 / math.sqrt(D)
-    cache = binding.KVCache(B, H, D, G, KL, max_tokens=T, dtype=tdt, device=gpu)
+    fused = binding.KVCache(B, H, D, G, KL, max_tokens=T, dtype=tdt, device=gpu)
+    split = binding.KVCache(B, H, D, G, KL, max_tokens=T, dtype=tdt, device=gpu)
     kc, vc = binding.pool_kv(q[:, :, :L0].contiguous(), k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), G,
                              scale)
-    cache.load_prefill(k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc, vc)
+    for c in (fused, split):
+        c.load_prefill(k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc, vc)
     del kc, vc
-    _say("full-size decode: stepping")
+    _say(f"full-size decode {dt}: stepping (fused and two-call paths)")
     qs = q[:, :, L0:].permute(2, 0, 1, 3).contiguous()
     ks = k[:, :, L0:].permute(2, 0, 1, 3).contiguous()
     vs = v[:, :, L0:].permute(2, 0, 1, 3).contiguous()
     outs = torch.empty((S, B, H, D), dtype=torch.float32, device=gpu)
+    outs2 = torch.empty_like(outs)
     for s in range(S):
-        cache.append(qs[s], ks[s], vs[s], scale)
-        cache.decode(qs[s], out_dtype=torch.float32, out=outs[s])
+        fused.append_decode(qs[s], ks[s], vs[s], out_dtype=torch.float32, out=outs[s], scale=scale)
+        split.append(qs[s], ks[s], vs[s], scale)
+        split.decode(qs[s], out_dtype=torch.float32, out=outs2[s], scale=scale)
     torch.cuda.synchronize()
+    assert fused.n_tokens == split.n_tokens == T
     got = outs.cpu().numpy()
     for (b, h) in [(0, 0), (B // 2, 17), (B - 1, 31)]:
         Q = q[b, h].float().cpu().numpy().astype(np.float64)
         K = k[b, h].float().cpu().numpy().astype(np.float64)
         V = v[b, h].float().cpu().numpy().astype(np.float64)
         Kc, Vc, _ = oracle.pool(Q, K, V, G, scale, core_dtype=dt)
+        worst = 0.0
         for s in range(S):
             t = L0 + s
             want = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
             err = np.abs(got[s, b, h] - want).max()
+            worst = max(worst, err)
             assert err <= tol, f"{dt} slice ({b},{h}) step {s}: max abs err {err:.3e}"
+        _say(f"decode {dt} slice ({b},{h}): max err {worst:.2e} over {S} fused steps")
+    m_new = T // G
+    assert torch.equal(outs, outs2), "fused and two-call decode outputs differ"
+    assert torch.equal(fused.core_k[:, :, :m_new], split.core_k[:, :, :m_new])
+    assert torch.equal(fused.core_v[:, :, :m_new], split.core_v[:, :, :m_new])
 
 
 def test_dense_mode_fullsize_sampled(gpu):

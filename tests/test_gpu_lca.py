@@ -123,7 +123,10 @@ def test_lca_invalid_rope_width(gpu):
 
 
 def test_lca_full_size_sampled(gpu):
-    """32K tokens, 32 heads, d = 128, bf16: sampled groups and queries against the oracle."""
+    """32K tokens, 32 heads, d = 128, bf16.  For three sampled heads: every group's anchor is
+    a maximum of the oracle's fp64 scores; the oracle then condenses every group itself at
+    those anchors (the only GPU value it takes), and the GPU's condensed tokens and sampled
+    query rows are compared with the oracle's."""
     B, H, L, d, g, k, d_rope = 1, 32, 32768, 128, 16, 1, 64
     _say(f"lca full size B{B} H{H} L{L}")
     q, kk, v = torch_inputs(B, H, L, d, torch.bfloat16, gpu, seed=21)
@@ -131,31 +134,66 @@ def test_lca_full_size_sampled(gpu):
     out, kc, vc, anchors = binding.prefill_lca(q, kk, v, g, k, d_rope, scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
-    m = L // g
     dc = d - d_rope
     for h in rng.choice(H, size=3, replace=False):
         Qs = q[0, h].double().cpu().numpy()
         Ks = kk[0, h].double().cpu().numpy()
         Vs = v[0, h].double().cpu().numpy()
         anc = anchors[0, h].cpu().numpy()
-        groups = np.concatenate([[0, m - 1], rng.choice(m, size=30, replace=False)])
-        for j in groups:
-            rows = slice(j * g, (j + 1) * g)
-            S = cca_lca.lca_scores(Qs[rows], Ks[rows], g, scale)
-            _check_anchors(S, anc[j:j + 1])
-            Kc, Vc, _ = cca_lca.lca_pool(Qs[rows], Ks[rows], Vs[rows], g, scale, d_rope, anchors=anc[j:j + 1])
-            gk = kc[0, h, j].float().cpu().numpy()
-            gv = vc[0, h, j].float().cpu().numpy()
-            assert np.array_equal(gk[dc:], Ks[j * g + anc[j], dc:])
-            for got, ref in ((gk[:dc], Kc[0, :dc]), (gv, Vc[0])):
-                assert np.all(np.abs(got - ref) <= TOL["bf16"] + ULP["bf16"] * np.abs(ref))
-        # sampled query rows: the oracle's row with the GPU's condensed tokens (as stored)
-        gkc = kc[0, h].double().cpu().numpy()
-        gvc = vc[0, h].double().cpu().numpy()
+        _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
+        # the oracle's own condensation of every group, stored in bf16 as the kernel stores it
+        Kc, Vc, _ = cca_lca.lca_pool(Qs, Ks, Vs, g, scale, d_rope, anchors=anc, core_dtype="bf16")
+        Kx, Vx, _ = cca_lca.lca_pool(Qs, Ks, Vs, g, scale, d_rope, anchors=anc)
+        gk = kc[0, h].float().cpu().numpy()
+        gv = vc[0, h].float().cpu().numpy()
+        assert np.array_equal(gk[:, dc:], Kc[:, dc:]), "positional dims differ from the anchor key"
+        for got, ref in ((gk[:, :dc], Kx[:, :dc]), (gv, Vx)):
+            bound = TOL["bf16"] + ULP["bf16"] * np.abs(ref)
+            assert np.all(np.abs(got - ref) <= bound), f"condensed err {np.abs(got - ref).max():.3e}"
+        worst = 0.0
         for t in np.concatenate([[0, L - 1], rng.choice(L, size=20, replace=False)]):
-            want = cca_oracle.cca_row(Qs[t], int(t), Ks, Vs, gkc, gvc, g, k, scale)
+            want = cca_oracle.cca_row(Qs[t], int(t), Ks, Vs, Kc, Vc, g, k, scale)
             err = np.abs(out[0, h, t].cpu().numpy().astype(np.float64) - want).max()
+            worst = max(worst, err)
             assert err <= TOL["bf16"], f"row {t} err {err:.3e}"
+        _say(f"lca full size head {h}: max row err {worst:.2e}")
+
+
+def test_lca_decode_full_size_sampled(gpu):
+    """The LCA-style decode the benchmark times: B = 8, H = 32, d = 128, a 131072-token context
+    seeded from the LCA-style prefill, then 64 fused append+decode steps (4 condensations),
+    each reading more than 384 MiB of K/V (streaming loads).  For sampled slices the GPU's
+    anchors are checked against the oracle's scores; the oracle replays the whole stream at
+    those anchors (condensing every group itself) and every step's output is compared."""
+    B, H, d, g, k, d_rope, L0, S = 8, 32, 128, 16, 64, 64, 131072, 64
+    L = L0 + S
+    _say(f"lca decode full size B{B} H{H} L0{L0} S{S}")
+    q, kk, v = torch_inputs(B, H, L, d, torch.bfloat16, gpu, seed=23, heavy_frac=0.01)
+    scale = 1.0 / math.sqrt(d)
+    pre = [x[:, :, :L0].contiguous() for x in (q, kk, v)]
+    _, kc0, vc0, _ = binding.prefill_lca(*pre, g, k, d_rope, scale)
+    cache = binding.LCACache(B, H, d, g, k, max_tokens=L, d_rope=d_rope, dtype=torch.bfloat16, device=gpu)
+    cache.load_prefill(*pre, kc0, vc0)
+    del pre, kc0, vc0
+    xs = [x[:, :, L0:].permute(2, 0, 1, 3).contiguous() for x in (q, kk, v)]
+    outs = torch.empty((S, B, H, d), dtype=torch.float32, device=gpu)
+    for s_ in range(S):
+        cache.append_decode(xs[0][s_], xs[1][s_], xs[2][s_], out_dtype=torch.float32, out=outs[s_], scale=scale)
+    torch.cuda.synchronize()
+    assert cache.n_tokens == L
+    got = outs.cpu().numpy().astype(np.float64)
+    m = L // g
+    for (b, h) in [(0, 0), (B // 2, 17), (B - 1, 31)]:
+        Qs = q[b, h].double().cpu().numpy()
+        Ks = kk[b, h].double().cpu().numpy()
+        Vs = v[b, h].double().cpu().numpy()
+        gk = cache.core_k[b, h, :m].float().cpu().numpy()
+        anc = _anchors_from_core(gk, Ks, g, d_rope)
+        _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
+        want = cca_lca.lca_decode_stream(Qs, Ks, Vs, L0, g, k, scale, d_rope, anchors=anc, core_dtype="bf16")
+        err = np.abs(got[:, b, h] - want).max()
+        _say(f"lca decode slice ({b},{h}): max err {err:.2e} over {S} steps")
+        assert np.isfinite(err) and err <= TOL["bf16"], f"slice ({b},{h}): max abs err {err:.3e}"
 
 
 # grouped-query LCA-style prefill: (B, H, H_kv, L, d, g, k, d_rope, dtype, seed)
