@@ -315,6 +315,26 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
                             float scale, hipStream_t stream);
 
 /*
+ * cca_cache_append_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It allocates nothing (no hipMalloc, no
+ * allocating library call).
+ *   The chunk partial states go to a library-owned device array of
+ *   CCA_NOALLOC_SCRATCH_BYTES (4 MiB), one copy per GPU, held until the process
+ *   ends; its address is looked up on the first call on each device.
+ *   stream must belong to the current device (CCA_ERR_INVALID otherwise).
+ *   CCA_ERR_WORKSPACE when cca_decode_workspace_bytes(c) exceeds the array
+ *   (B*H*chunks*(d+2)*4 bytes: 0.5 MiB for B=8, H=32, d=128).
+ *   Calls on one GPU share the array: calls that can overlap on that GPU (on
+ *   different streams) race; calls ordered on one stream do not.  No contents are
+ *   needed on entry.  Otherwise as cca_cache_append_decode (same kernels, same
+ *   results bit for bit).
+ */
+#define CCA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int cca_cache_append_decode_noalloc(cca_cache_t* c, const void* q, const void* k, const void* v,
+                                    void* out, int out_dt, float scale, hipStream_t stream);
+
+/*
  * LCA-style decode cache ("Latent-Condensed Transformer for Efficient Long Context
  * Modeling", section 2, inference flow: a group is condensed as soon as its last token
  * arrives, with the mean-query importance and positional anchoring of cca_pool_kv_lca;

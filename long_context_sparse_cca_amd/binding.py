@@ -120,6 +120,8 @@ EXPORTS = {
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
     "cca_cache_append_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
                                 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p]),
+    "cca_cache_append_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(CacheDesc)] + [ctypes.c_void_p] * 4
+                                        + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "cca_serve_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), ctypes.c_int]),
     "cca_cache_append_decode_varlen": (ctypes.c_int, [ctypes.POINTER(CacheDesc), ctypes.c_void_p, ctypes.c_int64,
                                                       ctypes.c_int] + [ctypes.c_void_p] * 4
@@ -459,6 +461,21 @@ class KVCache:
         _check(_lib.cca_cache_append_decode(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                             _dtype_code(out_dtype), _ptr(self.workspace), self.ws_bytes, scale,
                                             _stream()), "cca_cache_append_decode")
+        return out
+
+    def append_decode_noalloc(self, q, k, v, out, out_dtype=None, scale: float | None = None):
+        """append_decode with the chunk partial states in the library's own per-GPU device
+        array instead of this cache's workspace (cca_cache_append_decode_noalloc); `out`
+        is caller-provided, so the call allocates nothing."""
+        B, H, d = self.shape_bhd
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _need(t, (B, H, d), self.dtype, name)
+        _need(out, (B, H, d), out_dtype, "out")
+        _check(_lib.cca_cache_append_decode_noalloc(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                    _dtype_code(out_dtype), scale, _stream()),
+               "cca_cache_append_decode_noalloc")
         return out
 
     def decode(self, q, out_dtype=None, out=None, scale: float | None = None):

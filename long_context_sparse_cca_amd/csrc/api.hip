@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "cca_internal.h"
 
 namespace {
@@ -284,6 +286,60 @@ int cca_cache_append_decode(cca_cache_t* c, const void* q, const void* k, const 
   c->n_tokens = t + 1;
   c->n_pooled = (t + 1) / c->g;
   return CCA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// allocation-free fused decode: the chunk partial states live in a library-owned
+// device array instead of a caller workspace
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxDevices = 64;
+// One copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in: kernels get the device address from hipGetSymbolAddress.
+__device__ __align__(256) float scratch[CCA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the device of `stream` (which must be the current
+// device), looked up once per device with that device current.
+int scratch_for_stream(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CCA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CCA_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return CCA_ERR_HIP;
+    if (sdev != dev) return CCA_ERR_INVALID;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CCA_ERR_HIP;
+    scratch_addr[dev] = p;
+  }
+  *ptr = scratch_addr[dev];
+  return CCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cca_cache_append_decode_noalloc(cca_cache_t* c, const void* q, const void* k, const void* v, void* out,
+                                    int out_dt, float scale, hipStream_t stream) {
+  int s = check_cache(c);
+  if (s != CCA_OK) return s;
+  const size_t need = cca_decode_workspace_bytes(c);
+  if (need > (size_t)CCA_NOALLOC_SCRATCH_BYTES) return CCA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  s = scratch_for_stream(stream, &ws);
+  if (s != CCA_OK) return s;
+  // every chunk record is written before the merge reads it: nothing to clear
+  return cca_cache_append_decode(c, q, k, v, out, out_dt, ws, need, scale, stream);
 }
 
 int cca_cache_load_prefill_lca_gqa(cca_cache_t* c, float* qsum, int H_q, const void* q, const void* k,
