@@ -40,7 +40,10 @@ struct ServeCfg {
   static constexpr int EPC = 16 / (int)sizeof(T);     // elements per lane (one 16-byte chunk)
   static constexpr int LPK = D / EPC;                 // lanes per key row
   static constexpr int KPW = kWave / LPK;             // key rows per wave per load
-  static constexpr int U = RH >= 8 ? 2 : 4;           // loads of K and V in flight per lane
+  // loads of K and V in flight per lane; with 4 query heads, 3 keeps the kernel within 128
+  // registers (4 waves per SIMD: a 1024-workgroup grid is resident at once; 4 took 152
+  // registers and left a quarter of the grid for a second round, 10% slower)
+  static constexpr int U = RH >= 8 ? 2 : (RH >= 4 ? 3 : 4);
   static constexpr int KPI = NWAVE * KPW * U;         // key rows per workgroup iteration
 };
 
