@@ -64,6 +64,20 @@ def test_validation_without_gpu(lib):
     assert d.n_tokens == 79
 
 
+def test_noalloc_decode_validation_without_gpu(lib):
+    """The allocation-free decode validates the descriptor, then the size of its partial states
+    against the library's fixed array, before touching the device."""
+    NULL = None
+    assert lib.cca_cache_append_decode_noalloc(None, 16, 16, 16, 16, 0, 0.1, NULL) == -1
+    d = binding.CacheDesc(16, 16, 16, 16, 1, 1, 128, 16, 2, 1, 4, 0, 1)  # n_pooled inconsistent
+    assert lib.cca_cache_append_decode_noalloc(ctypes.byref(d), 16, 16, 16, 16, 0, 0.1, NULL) == -1
+    # B*H = 8192 slices at d = 128: one chunk each, 8192*130*4 bytes > 4 MiB
+    d = binding.CacheDesc(16, 16, 16, 16, 128, 64, 128, 16, 1, 1, 1, 0, 0)
+    assert lib.cca_decode_workspace_bytes(ctypes.byref(d)) > 4 << 20
+    assert lib.cca_cache_append_decode_noalloc(ctypes.byref(d), 16, 16, 16, 16, 0, 0.1, NULL) == -3
+    assert d.n_tokens == 0
+
+
 def test_workspace_size(lib):
     d = binding.CacheDesc(16, 16, 16, 16, 8, 32, 128, 16, 64, 1, 8208, 0, 0)
     n = lib.cca_decode_workspace_bytes(ctypes.byref(d))
