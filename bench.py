@@ -84,6 +84,8 @@ def parse():
                     help="skip the serving decode measurement (per-sequence lengths, grouped-query heads)")
     ap.add_argument("--no-lca", action="store_true", help="skip the LCA-style variant measurement")
     ap.add_argument("--no-f16", action="store_true", help="skip the binary16 prefill measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the shorter prefill workloads (256-token fp32, 8K, 32K) beside the timed steps")
     ap.add_argument("--phase", choices=["all", "prefill", "decode", "serving", "training", "lca", "copy"],
                     default="all",
                     help="profiling aid: run only one phase (the JSON line is then not the benchmark result); "
@@ -676,6 +678,10 @@ def prefill_workload(binding, accounting, dev, seed, cfg, reps: int = 10, cpu_se
     return res
 
 
+def _leg(name: str):
+    print(f"leg: {name}", file=sys.stderr, flush=True)
+
+
 def _median(xs):
     if not xs:
         return float("nan")
@@ -903,37 +909,45 @@ def main():
             del o32
     cpu = {}
     if do_decode and not args.no_cpu_baseline:
+        _leg("cpu oracle: decode")
         cpu["decode"] = cpu_decode(dec_sample, dec_gpu_out, dcfg, cpu_dec_steps)
         del dec_sample
     if do_decode and not args.no_serving and extras:
         del cache, qs, ks, vs, k0, v0, kc0, vc0
         torch.cuda.empty_cache()
+        _leg("serving")
         res["serving_decode"] = serving_decode(binding, accounting, dev, args.seed)
-    if do_prefill and extras:
+    if do_prefill and extras and not args.no_workloads:
         pw = {}
         for i in (1, 2, 3):
             c = WORKLOADS[i]
             name = f"prefill_{c['L']}_{c['dtype']}"
+            _leg(name)
             pw[name] = prefill_workload(binding, accounting, dev, args.seed, c,
                                         cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds)
             if "cpu_baseline" in pw[name]:
                 cpu[name] = pw[name].pop("cpu_baseline")
         res["prefill_workloads"] = pw
     if do_prefill and not args.no_training and extras:
+        _leg("training")
         res["training"] = training_step(binding, accounting, dev, args.seed)
         torch.cuda.empty_cache()
         res["training_gqa"] = training_step(binding, accounting, dev, args.seed, H_kv=8)
         torch.cuda.empty_cache()
     if do_prefill and not args.no_lca and extras:
+        _leg("lca")
         res["lca_variant"] = lca_variant(binding, accounting, dev, args.seed)
         torch.cuda.empty_cache()
     if do_prefill and not args.no_f16 and extras:
+        _leg("binary16")
         res["binary16_prefill"] = binary16_prefill(binding, accounting, dev, args.seed)
         if not args.no_training:
             res["binary16_training"] = training_step(binding, accounting, dev, args.seed, reps=2, dtype="f16")
     if do_prefill and not args.no_dense and extras:
+        _leg("dense comparison")
         res["dense_comparison"] = dense_comparison(binding, accounting, dev, args.seed)
     if not args.no_cpu_baseline:
+        _leg("cpu oracle: prefill")
         if do_prefill and pcfg is WORKLOADS[4]:
             out32 = binding.prefill(q, k, v, Pg, Pk, pscale, out_dtype=torch.float32)
             torch.cuda.synchronize()
