@@ -489,7 +489,7 @@ def training_step(binding, accounting, dev, seed, L: int = PREFILL_L, reps: int 
                          "per_unit": "10*d FLOPs per visible (query, key) pair"}}
 
 
-def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int = 64, reps: int = 5):
+def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int = 64, reps: int = 10):
     """LCA-style condensation (cca_pool_kv_lca) and the prefill built on it (cca_prefill_lca),
     B=1, H=32, d=128, g=16, k=64, bf16, last 64 dims of each key positional; outside the timed steps."""
     import torch
@@ -511,7 +511,7 @@ def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int 
         torch.cuda.synchronize()
         tp.append(e[0].elapsed_time(e[1]))
         tf.append(e[2].elapsed_time(e[3]))
-    pool_ms, prefill_ms = sum(tp) / reps, sum(tf) / reps
+    pool_ms, prefill_ms = _median(tp), _median(tf)
     byt = accounting.lca_pool_bytes(1, H, L, D, G, 2)
     gbs = byt / (pool_ms * 1e-3) / 1e9
     del q, k, v
@@ -546,7 +546,7 @@ def lca_variant(binding, accounting, dev, seed, L: int = PREFILL_L, d_rope: int 
     return {"config": {"B": 1, "H": H, "d": D, "L": L, "g": G, "k_local": KL, "d_rope": d_rope},
             "pool_ms": pool_ms, "prefill_ms": prefill_ms, "prefill_tokens_per_s": L / (prefill_ms * 1e-3),
             "pool_bytes": byt,
-            "roofline": {"kernel": "cca_pool_lca_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+            "roofline": {"kernel": "cca_pool_lca_d128_g16_kernel", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                          "per_unit": "(3*g + 2)*d*2 bytes per group"},
             "decode": {"config": {"B": DEC_B, "H": H, "context": DEC_L0, "steps": steps},

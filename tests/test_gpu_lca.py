@@ -315,6 +315,34 @@ def test_lca_decode_matches_oracle(gpu, case):
     assert np.abs(cache.qsum.cpu().numpy() - want_qsum).max() <= 1e-3
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_lca_decode_condenses_as_prefill(gpu, dt):
+    """Groups condensed one token at a time by the decode cache equal, bit for bit, the ones the
+    prefill condensation (cca_pool_kv_lca, its dedicated d = 128, g = 16 kernel) gives on the whole
+    sequence: both sum a group's queries in token order and share the group routine's arithmetic.
+    The prefix ends inside a group, so the first group completed by decode mixes seeded and
+    decoded queries."""
+    B, H, d, g, k, d_rope, L0, S = 2, 3, 128, 16, 2, 64, 200, 120
+    L = L0 + S
+    _say(f"lca decode vs prefill condensation {dt}")
+    Q, K, V = np_inputs(B, H, L, d, dt, 44)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    pre = [x[:, :, :L0].contiguous() for x in (q, kk, v)]
+    kc0, vc0, _ = binding.pool_kv_lca(*pre, g, d_rope, scale)
+    cache = binding.LCACache(B, H, d, g, k, max_tokens=L, d_rope=d_rope, dtype=TDT[dt], device=gpu)
+    cache.load_prefill(*pre, kc0, vc0)
+    for t in range(L0, L):
+        cache.append_decode(q[:, :, t].contiguous(), kk[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                            out_dtype=torch.float32, scale=scale)
+    kc, vc, _ = binding.pool_kv_lca(q, kk, v, g, d_rope, scale)
+    torch.cuda.synchronize()
+    m = L // g
+    assert m > L0 // g + 5
+    assert torch.equal(cache.core_k[:, :, :m], kc)
+    assert torch.equal(cache.core_v[:, :, :m], vc)
+
+
 def test_lca_decode_invalid_rope_width(gpu):
     cache = binding.LCACache(1, 1, 64, 8, 1, max_tokens=32, d_rope=65, dtype=torch.float32, device=gpu)
     x = torch.zeros((1, 1, 64), dtype=torch.float32, device=gpu)
