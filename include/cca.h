@@ -443,8 +443,10 @@ int cca_cache_load_prefill_lca_gqa(cca_cache_t* c, float* qsum, int H_q, const v
  *   q       : device [B, H_q, n, d];  k, v : device [B, c->H, n, d];
  *   out     : device [B, H_q, n, d] of out_dt (CCA_F32 or c->dt).
  *   workspace : device, >= cca_extend_workspace_bytes(c, n) bytes (start
- *             positions plus a staging copy of the raw window of every
- *             key/value head: about 2*B*H*((k_local+1)*g + n)*d elements).
+ *             positions and the sequences ordered by length, longest first,
+ *             for the work order of the attention, plus a staging copy of the
+ *             raw window of every key/value head: about
+ *             2*B*H*((k_local+1)*g + n)*d elements).
  * The attention runs on the same MFMA kernels as cca_attention.
  */
 size_t cca_extend_workspace_bytes(const cca_cache_t* c, int n);

@@ -222,14 +222,16 @@ __device__ __forceinline__ void map_block(int nblocks, int ntiles, int& bh, int&
 // different lengths: map_block hands each XCD a contiguous range of slices, so the
 // slices are taken in the order (key/value head, sequence, query head of that key/value
 // head).  Every XCD then gets every sequence (balanced work), and the nq query heads
-// that read one key/value slice stay adjacent (they share its tiles in L2).
-__device__ __forceinline__ int kv_major_slice(int v, int BH, int Hq, int nq) {
+// that read one key/value slice stay adjacent (they share its tiles in L2).  The
+// sequences come in the order `order` gives (longest first), so that each XCD hands out
+// its heaviest workgroups first and the light ones fill the tail.
+__device__ __forceinline__ int kv_major_slice(int v, int BH, int Hq, int nq, const int32_t* order) {
   const int B = BH / Hq;
   const int per_kv = B * nq;
   const int hkv = v / per_kv;
   const int rem = v - hkv * per_kv;
-  const int b = rem / nq;
-  return b * Hq + hkv * nq + (rem - b * nq);
+  const int i = rem / nq;
+  return order[i] * Hq + hkv * nq + (rem - i * nq);
 }
 
 }  // namespace cca

@@ -41,6 +41,7 @@ struct ExtendArgs {
   int n;               // new tokens (queries) per slice
   int64_t raw_rows;    // rows per raw K/V slice
   int64_t core_rows;   // rows per core K/V slice
+  const int32_t* order;  // device [B]: the sequences by length, longest first (work order)
 };
 
 // LCA-style pooling (pool_lca.hip): mean-query importance (over the group and the nq query

@@ -38,12 +38,15 @@
 namespace cca {
 namespace {
 
-// Workspace head: the per-sequence start positions (int32), padded to 256 bytes.
+// Workspace head: the per-sequence start positions (int32), then the sequences ordered by
+// length, longest first (int32), each padded to 256 bytes.
 size_t pos_bytes(int B) { return ((size_t)B * sizeof(int32_t) + 255) / 256 * 256; }
+size_t head_bytes(int B) { return 2 * pos_bytes(B); }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void cca_extend_gather_kernel(const int32_t* __restrict__ lens, int64_t max_len,
                                                                 int32_t* __restrict__ pos_ws,
+                                                                int32_t* __restrict__ order_ws,
                                                                 const T* __restrict__ k_chunk,
                                                                 const T* __restrict__ v_chunk,
                                                                 const T* __restrict__ ring_k,
@@ -55,7 +58,27 @@ __global__ __launch_bounds__(256) void cca_extend_gather_kernel(const int32_t* _
   const int64_t b = bkv / Hkv;
   const int64_t t = lens[b];
   const bool valid = t >= 0 && t <= max_len;
-  if (blockIdx.y == 0 && threadIdx.x == 0 && bkv % Hkv == 0) pos_ws[b] = valid ? (int32_t)t : -1;
+  if (blockIdx.y == 0 && bkv % Hkv == 0) {
+    // one block per sequence: its start position, and its rank by length (longest first,
+    // ties by index, out-of-range sequences last), so order_ws is a permutation of 0..B-1
+    __shared__ int rank;
+    if (threadIdx.x == 0) rank = 0;
+    __syncthreads();
+    const int64_t B = gridDim.x / Hkv;
+    const int64_t key = valid ? t : -1;
+    int before = 0;
+    for (int64_t i = threadIdx.x; i < B; i += blockDim.x) {
+      const int64_t ti = lens[i];
+      const int64_t ki = (ti >= 0 && ti <= max_len) ? ti : -1;
+      before += (ki > key || (ki == key && i < b)) ? 1 : 0;
+    }
+    atomicAdd(&rank, before);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      pos_ws[b] = valid ? (int32_t)t : -1;
+      order_ws[rank] = (int32_t)b;
+    }
+  }
   if (!valid) return;
   const int64_t raw0 = std::max<int64_t>(0, t / g - k_local) * g;
   const int64_t rows = t + n - raw0;
@@ -203,16 +226,17 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
   const int64_t BHkv = (int64_t)c->B * c->H;
   const int nq = H_q / c->H;
   int32_t* pos_ws = (int32_t*)workspace;
-  T* sk = (T*)((uint8_t*)workspace + pos_bytes(c->B));
+  int32_t* order_ws = (int32_t*)((uint8_t*)workspace + pos_bytes(c->B));
+  T* sk = (T*)((uint8_t*)workspace + head_bytes(c->B));
   T* sv = sk + (size_t)BHkv * raw_rows * D;
   constexpr int CPR = D * (int)sizeof(T) / 16;
   const int64_t gy = (raw_rows * CPR + 255) / 256;
   hipLaunchKernelGGL((cca_extend_gather_kernel<T, D>), dim3((unsigned)BHkv, (unsigned)gy), dim3(256), 0, stream, lens,
-                     max_len, pos_ws, (const T*)k, (const T*)v, (const T*)c->ring_k, (const T*)c->ring_v, sk, sv, c->H,
+                     max_len, pos_ws, order_ws, (const T*)k, (const T*)v, (const T*)c->ring_k, (const T*)c->ring_v, sk, sv, c->H,
                      n, R, c->g, c->k_local, raw_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const ExtendArgs ext{pos_ws, H_q, n, raw_rows, c->max_groups};
+  const ExtendArgs ext{pos_ws, H_q, n, raw_rows, c->max_groups, order_ws};
   e = launch_extend_attention(c->dt, D, q, sk, sv, c->core_k, c->core_v, out, out_f32, c->B * H_q, nq, c->g,
                               c->k_local, scale, ext, stream);
   if (e != hipSuccess) return e;
@@ -241,7 +265,7 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
 size_t extend_workspace_bytes(const cca_cache_t* c, int n) {
   const size_t R = (size_t)(c->k_local + 1) * c->g;
   const size_t esz = (size_t)dtype_bytes(c->dt);
-  return pos_bytes(c->B) + 2 * (size_t)c->B * c->H * (R + (size_t)n) * c->d * esz;
+  return head_bytes(c->B) + 2 * (size_t)c->B * c->H * (R + (size_t)n) * c->d * esz;
 }
 
 hipError_t launch_extend(const cca_cache_t* c, int32_t* lens, int64_t max_len, int H_q, int n, const void* q,

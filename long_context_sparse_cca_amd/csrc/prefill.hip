@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int bh, qtile;
   map_block(BH * ntiles, ntiles, bh, qtile);
-  if constexpr (EXT) bh = kv_major_slice(bh, BH, ext.Hq, nq);
+  if constexpr (EXT) bh = kv_major_slice(bh, BH, ext.Hq, nq, ext.order);
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid & (kWave - 1);
@@ -406,7 +406,7 @@ hipError_t launch_prefill_t(const void* q, const void* k, const void* v, const v
   const int ntiles = (int)((L + C::BM - 1) / C::BM);
   const int64_t nblocks = (int64_t)BH * ntiles;
   if (nblocks == 0) return hipSuccess;
-  const ExtendArgs none{nullptr, 1, 0, 0, 0};
+  const ExtendArgs none{nullptr, 1, 0, 0, 0, nullptr};
   hipLaunchKernelGGL((cca_prefill_kernel<T, D, false>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)kc, (const T*)vc, out, out_f32, BH, nq, L, g,
                      k_local, scale, ntiles, none, lse);

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int bh, qtile;
   map_block(BH * ntiles, ntiles, bh, qtile);
-  if constexpr (EXT) bh = kv_major_slice(bh, BH, ext.Hq, nq);
+  if constexpr (EXT) bh = kv_major_slice(bh, BH, ext.Hq, nq, ext.order);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
@@ -410,7 +410,7 @@ hipError_t launch_prefill_d128(int dt, const void* q, const void* k, const void*
                                hipStream_t stream, float* lse) {
   const int ntiles = (int)((L + kBM - 1) / kBM);
   if ((int64_t)BH * ntiles == 0) return hipSuccess;
-  const ExtendArgs none{nullptr, 1, 0, 0, 0};
+  const ExtendArgs none{nullptr, 1, 0, 0, 0, nullptr};
   if (dt == CCA_F16)
     launch_prefill_t<f16_t>(q, k, v, kc, vc, out, out_f32, BH, nq, L, g, k_local, scale, ntiles, none, false, lse,
                             stream);

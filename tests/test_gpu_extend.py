@@ -126,3 +126,35 @@ def test_extend_rejects_oversized_chunk_and_capacity(gpu):
         cache.extend(torch.zeros((B, Hq, 6, d), device=gpu), torch.zeros((B, Hkv, 6, d), device=gpu),
                      torch.zeros((B, Hkv, 6, d), device=gpu))  # positions 18..23 would need core slot 5
     assert cache.lens.cpu().tolist() == [18]
+
+
+def test_extend_work_order_ties_and_out_of_range(gpu):
+    """The extend attention takes the sequences longest first, ranked on the device from their
+    lengths: here the lengths are out of order, two are equal, one sequence is empty and one is
+    beyond max_len.  The out-of-range sequence gets NaN rows and keeps its length; every other
+    row matches the oracle, and every other length advances by n."""
+    B, Hq, Hkv, d, g, k, dt, seed = 6, 4, 2, 128, 16, 2, "bf16", 48
+    lens0 = [60, 200, 60, 0, 130, 33]
+    max_len, n = 150, 20
+    _say(f"extend work order: lengths {lens0}, max_len {max_len}, n {n}")
+    total = max(lens0) + n + 3
+    Q, K, V, cache, scale = _setup(B, Hq, Hkv, d, g, k, dt, lens0, total, seed, gpu)
+    q, kk, v = (_dev(np.stack([X[b, :, lens0[b]:lens0[b] + n] for b in range(B)]), dt, gpu) for X in (Q, K, V))
+    out = torch.empty((B, Hq, n, d), dtype=torch.float32, device=gpu)
+    lib = binding.load_library()
+    ws = torch.empty((lib.cca_extend_workspace_bytes(ctypes.byref(cache.desc), n) + 15) // 16 * 4, device=gpu)
+    st = lib.cca_cache_extend(ctypes.byref(cache.desc), ctypes.c_void_p(cache.lens.data_ptr()), max_len, Hq, n,
+                              ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kk.data_ptr()),
+                              ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()), 0,
+                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * 4, scale, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == [L + n if L <= max_len else L for L in lens0]
+    got = out.cpu().numpy()
+    assert np.isnan(got[1]).all()
+    for b, L in enumerate(lens0):
+        if L > max_len:
+            continue
+        want = cca_serving.serve_rows(Q[b], K[b], V[b], range(L, L + n), g, k, scale, core_dtype=dt)
+        err = np.abs(got[b] - want).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
