@@ -11,7 +11,9 @@
 //
 // One wave per group, HBM-bound: the group's g query rows (of each of the nq query
 // heads that share the key/value head), key rows and value rows are each read once.
-// 16-bit inputs at d = 128, g = 16 take a kernel that fetches the whole group up front.
+// 16-bit inputs at d = 128, g = 16 take a kernel that stages the whole group in LDS up front.
+#include <type_traits>
+
 #include "cca_internal.h"
 #include "lca_group.h"
 
@@ -61,10 +63,10 @@ __global__ __launch_bounds__(64) void cca_pool_lca_kernel(const T* __restrict__ 
 
 // 16-bit inputs, d = 128, g = 16: the same arithmetic as the kernel above (the mean query
 // summed head by head and row by row, then lca_condense_math, so every caller of the group
-// routine reaches the same condensed tokens), with every row of the group fetched up front
-// instead of pass by pass: the query rows of the nq heads (this lane's two columns), the key
-// segment of the scoring pass, and the key and value columns of the weighted sums (the
-// second fetch of a key row hits the cache).  Four waves per workgroup, one group each.
+// routine reaches the same condensed tokens), with the group's rows staged in LDS up front
+// instead of fetched pass by pass: the key and value rows and the first head's query rows go
+// straight from HBM into LDS (global_load_lds, 16 bytes per lane, each row fetched once), and
+// every pass then reads LDS.  Four waves per workgroup, one group each, 12 KB of LDS per wave.
 // STREAM: query and value rows, read once, carry the nontemporal hint (passes larger than
 // the last-level cache).
 template <typename T, bool STREAM>
@@ -75,8 +77,9 @@ __global__ __launch_bounds__(256) void cca_pool_lca_d128_g16_kernel(const T* __r
                                                                     int32_t* __restrict__ anchors, int64_t L,
                                                                     int64_t m, int64_t n_groups, int nq,
                                                                     int d_rope, float scale) {
-  constexpr int D = 128, G = 16, CPL = D / kWave;
-  __shared__ float sm[4][D + G];   // per wave: mean query [D], then scores [G]
+  constexpr int D = 128, G = 16, CPL = D / kWave, ROW = D * 2, MAT = G * ROW;
+  __shared__ __attribute__((aligned(16))) uint8_t rows_lds[4][3 * MAT];   // per wave: Q, K, V rows
+  __shared__ float sm[4][D + G];                                          // mean query, scores
   const int wv = threadIdx.x >> 6;
   const int64_t gid = (int64_t)blockIdx.x * 4 + wv;
   if (gid >= n_groups) return;     // whole waves only; the waves never synchronise with each other
@@ -85,23 +88,25 @@ __global__ __launch_bounds__(256) void cca_pool_lca_d128_g16_kernel(const T* __r
   const int rsub = lane >> 2, seg = lane & 3;   // scoring pass: 4 lanes per key row
   const int64_t bh = gid / m, j = gid - bh * m;
   const size_t row0 = ((size_t)bh * L + (size_t)j * G) * D;
-  const T* kg = K + row0;
-  const T* vg = V + row0;
-
-  uint4 kseg[D / 4 / 8];
+  uint8_t* qs = rows_lds[wv];
+  uint8_t* ks = qs + MAT;
+  uint8_t* vs = ks + MAT;
+  // one fill instruction: rows 4i .. 4i+3 of a matrix; lane l brings 16-byte chunk l%16 of row 4i + l/16
+  const int fill = (lane >> 4) * D + (lane & 15) * 8;   // element offset of this lane's chunk
+  // stream_tag: std::true_type for rows read once (nontemporal cache policy), else false_type
+  auto fill_rows = [&](const T* src, uint8_t* dst, auto stream_tag) {
+    constexpr int kPolicy = decltype(stream_tag)::value ? 2 : 0;
 #pragma unroll
-  for (int c = 0; c < D / 4 / 8; ++c) kseg[c] = ld16(kg + (size_t)rsub * D + seg * (D / 4) + c * 8);
-  auto ld4 = [](const T* p) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
-    if constexpr (STREAM) return __builtin_nontemporal_load(w);
-    else return *w;
+    for (int i = 0; i < G / 4; ++i)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + (size_t)i * 4 * D + fill),
+                                       (__attribute__((address_space(3))) void*)(dst + i * 4 * ROW), 16, 0,
+                                       kPolicy);
   };
-  uint32_t kcol[G], vcol[G];
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    kcol[r] = *reinterpret_cast<const uint32_t*>(kg + (size_t)r * D + col);
-    vcol[r] = ld4(vg + (size_t)r * D + col);
-  }
+  using once = std::integral_constant<bool, STREAM>;
+  fill_rows(K + row0, ks, std::false_type{});
+  fill_rows(V + row0, vs, once{});
+  const T* q0 = Q + ((size_t)bh * nq * L + (size_t)j * G) * D;
+  fill_rows(q0, qs, once{});
 
   // ---- mean query of the group, summed in the order of the generic kernel
   float* qbar = sm[wv];
@@ -110,14 +115,17 @@ __global__ __launch_bounds__(256) void cca_pool_lca_d128_g16_kernel(const T* __r
 #pragma unroll
     for (int e = 0; e < CPL; ++e) s[e] = 0.f;
     for (int h = 0; h < nq; ++h) {
-      const T* qg = Q + (((size_t)bh * nq + h) * L + (size_t)j * G) * D + col;
-      uint32_t qw[G];
-#pragma unroll
-      for (int r = 0; r < G; ++r) qw[r] = ld4(qg + (size_t)r * D);
+      if (h > 0) {
+        // the previous head's rows are consumed (their values sit in s; lgkmcnt(0) makes sure
+        // its LDS reads have completed): refill the buffer
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        fill_rows(q0 + (size_t)h * L * D, qs, once{});
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this head's rows (and K, V) are in LDS
 #pragma unroll
       for (int r = 0; r < G; ++r) {
         float f[CPL];
-        Elem<T>::pair_to_f32(qw[r], f);
+        Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(qs + r * ROW + col * 2), f);
 #pragma unroll
         for (int e = 0; e < CPL; ++e) s[e] += f[e];
       }
@@ -131,15 +139,10 @@ __global__ __launch_bounds__(256) void cca_pool_lca_d128_g16_kernel(const T* __r
   lca_condense_math<T, D, G>(
       qbar, G, scale, d_rope, Kc + out, Vc + out, sm[wv] + D,
       anchors != nullptr ? anchors + (size_t)bh * m + j : nullptr,
-      [&](int, int c) { return kseg[c]; },   // this lane's row is rsub, the only one it scores
-      [&](int r, float* f) { Elem<T>::pair_to_f32(kcol[r], f); },
-      [&](int r, float* f) { Elem<T>::pair_to_f32(vcol[r], f); },
-      [&](int r, float* f) {
-        uint32_t x = kcol[0];
-#pragma unroll
-        for (int i = 1; i < G; ++i) x = r == i ? kcol[i] : x;
-        Elem<T>::pair_to_f32(x, f);
-      });
+      [&](int r, int c) { return *reinterpret_cast<const uint4*>(ks + r * ROW + seg * (ROW / 4) + c * 16); },
+      [&](int r, float* f) { Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(ks + r * ROW + col * 2), f); },
+      [&](int r, float* f) { Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(vs + r * ROW + col * 2), f); },
+      [&](int r, float* f) { Elem<T>::pair_to_f32(*reinterpret_cast<const uint32_t*>(ks + r * ROW + col * 2), f); });
 }
 
 template <typename T, int D>

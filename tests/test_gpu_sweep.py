@@ -233,12 +233,30 @@ def _lca_cases(n=4, seed=321, dtypes=("f32", "bf16")):
     return cases
 
 
+def _lca_d128_cases(n=8, seed=4321):
+    """The 16-bit d = 128, g = 16 condensation kernel: head ratios 1..8, ragged lengths (also
+    shorter than one group), odd d_rope (a lane's two columns straddle the content/positional
+    split)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 3))
+        r = int(rng.choice([1, 2, 4, 8]))
+        dt = str(rng.choice(["bf16", "f16"]))
+        k = int(rng.choice([0, 1, 4]))
+        d_rope = int(rng.choice([0, 1, 17, 64, 127, 128]))
+        L = int(rng.integers(1, 16)) if rng.random() < 0.15 else int(rng.integers(16, 1500))
+        cases.append((1, Hkv * r, Hkv, L, 128, 16, k, d_rope, dt, 1900 + i))
+    return cases
+
+
 def _lid(c):
     B, H, Hkv, L, d, g, k, r, dt, seed = c
     return f"B{B}H{H}kv{Hkv}L{L}d{d}g{g}k{k}rope{r}-{dt}-s{seed}"
 
 
-@pytest.mark.parametrize("case", _lca_cases() + _lca_cases(n=2, seed=3321, dtypes=("f16",)), ids=_lid)
+@pytest.mark.parametrize("case", _lca_cases() + _lca_cases(n=2, seed=3321, dtypes=("f16",)) + _lca_d128_cases(),
+                         ids=_lid)
 def test_lca_sweep(gpu, case):
     B, H, Hkv, L, d, g, k, d_rope, dt, seed = case
     _say(f"lca sweep {_lid(case)}")
