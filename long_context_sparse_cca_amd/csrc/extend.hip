@@ -16,15 +16,16 @@
 //      head: the cached part from the ring, the rest from the chunk itself;
 //   2. attention: the prefill attention kernels in extend mode over that scratch
 //      slice and the cached core tokens (MFMA, one softmax per query);
-//   3. append: the chunk's keys/values go to their ring slots, every group the chunk
+//   3. finish: the chunk's keys/values go to their ring slots, every group the chunk
 //      completes is pooled into its core slot (mean query over the query heads that
-//      share the key/value head), and the sequence length advances by n.
+//      share the key/value head; one wave per group), and the sequence length advances
+//      by n.
 // LCA-style cache: launch 3 condenses a completed group instead (mean of the group's
 // queries over its positions and the query heads sharing the key/value head, positional
 // dims from the top-scored token; "Latent-Condensed Transformer for Efficient Long Context
 // Modeling", sections 2 and 3), taking the queries of the group's tokens before the chunk
-// from the running sum qsum; a fourth launch then leaves in qsum the sum of the chunk's
-// trailing incomplete group.
+// from the running sum qsum, and then leaves in qsum the sum of the chunk's trailing
+// incomplete group.
 // With n <= k*g + 1 no token of the chunk can see a core token pooled from the same
 // chunk (the earliest group it completes becomes visible k*g+1 positions after the
 // chunk's first token), so pooling can follow the attention.  Launch 3 overwrites
@@ -102,119 +103,160 @@ __global__ __launch_bounds__(256) void cca_extend_gather_kernel(const int32_t* _
   st16(reinterpret_cast<uint4*>(sv + dst) + c, ld16(reinterpret_cast<const uint4*>(srcv) + c));
 }
 
-// Sum over the nq query heads h*nq .. of chunk row `row` for this lane's D/64 columns,
-// added to s (q_chunk [B*Hq][n][D], head slices of sequence b).
+// Add to s, row by row over chunk rows r0 .. r1, the sum of the nq query heads' rows (this
+// lane's D/64 columns of q_chunk [B*Hq][n][D], head slices of sequence b): each row's heads
+// are summed first, in head order, then the row sum is added -- the order in which the decode
+// steps add a token's queries.  The loads of up to 16 rows of one head are issued together.
 template <typename T, int D>
-__device__ __forceinline__ void add_query_row(const T* __restrict__ q_chunk, int64_t b, int Hq, int hk, int nq,
-                                              int n, int64_t row, int col, float* s) {
+__device__ __forceinline__ void add_query_rows(const T* __restrict__ q_chunk, int64_t b, int Hq, int hk, int nq,
+                                               int n, int64_t r0, int64_t r1, int col, float* s) {
   constexpr int CPL = D / kWave;
-  float t[CPL];
+  constexpr int RB = 16;
+  for (int64_t rb = r0; rb <= r1; rb += RB) {
+    const int cnt = (int)std::min<int64_t>(RB, r1 - rb + 1);
+    float t[RB][CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) t[e] = 0.f;
-  for (int h = 0; h < nq; ++h) {
-    float f[CPL];
-    lca_load_cols<T, D>(q_chunk + (((size_t)b * Hq + (size_t)hk * nq + h) * n + row) * D + col, f);
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) t[e] += f[e];
+      for (int e = 0; e < CPL; ++e) t[r][e] = 0.f;
+    for (int h = 0; h < nq; ++h) {
+      const T* qh = q_chunk + (((size_t)b * Hq + (size_t)hk * nq + h) * n + rb) * D + col;
+      float f[RB][CPL];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) lca_load_cols<T, D>(qh + (size_t)std::min(r, cnt - 1) * D, f[r]);
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) t[r][e] += f[r][e];
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+      if (r < cnt) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) s[e] += t[r][e];
+      }
   }
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) s[e] += t[e];
 }
 
-// One wave per new token: its ring slot, and the pooling (LCA: condensation) of the group
-// it completes.
+// Launch 3.  Blocks y < ring_blocks: the chunk's key/value rows into their ring slots
+// (one 16-byte piece per thread) and the new length.  The other blocks: one wave per group
+// the chunk completes (the w-th such group for wave w), pooled -- LCA: condensed -- from the
+// staged rows; for the LCA-style cache, wave 0 then leaves in qsum the query sum of the
+// trailing incomplete group (it alone reads the previous sum, for the chunk's first group).
 template <typename T, int D, bool LCA>
-__global__ __launch_bounds__(256) void cca_extend_append_kernel(
+__global__ __launch_bounds__(256) void cca_extend_finish_kernel(
     int32_t* __restrict__ lens, const int32_t* __restrict__ pos_ws, const T* __restrict__ q_chunk,
     const T* __restrict__ k_chunk, const T* __restrict__ v_chunk, const T* __restrict__ sk,
     const T* __restrict__ sv, T* __restrict__ ring_k, T* __restrict__ ring_v, T* __restrict__ core_k,
     T* __restrict__ core_v, int Hkv, int nq, int n, int64_t R, int64_t max_groups, int g, int k_local,
-    int64_t raw_rows, float scale, const float* __restrict__ qsum, int d_rope) {
+    int64_t raw_rows, float scale, float* __restrict__ qsum, int d_rope, int ring_blocks) {
   extern __shared__ float w_lds[];
-  const int64_t bkv = blockIdx.x;
-  const int64_t b = bkv / Hkv;
-  const int hk = (int)(bkv - b * Hkv);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int64_t t = pos_ws[b];
-  if (t < 0) return;
-  if (blockIdx.y == 0 && threadIdx.x == 0 && hk == 0) lens[b] = (int32_t)(t + n);
-  const int i = blockIdx.y * (blockDim.x / kWave) + wave;
-  if (i >= n) return;
-  const int64_t p = t + i;
-  const T* kr = k_chunk + ((size_t)bkv * n + i) * D;
-  const T* vr = v_chunk + ((size_t)bkv * n + i) * D;
   constexpr int CPR = D * (int)sizeof(T) / 16;
-  const int64_t slot = p % R;
-  if (lane < CPR) {
-    st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bkv * R + slot) * D) + lane,
-         ld16(reinterpret_cast<const uint4*>(kr) + lane));
-    st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + lane,
-         ld16(reinterpret_cast<const uint4*>(vr) + lane));
-  }
-  if ((p + 1) % g != 0) return;
-  // group beta = p/g: positions p-g+1 .. p, all inside the scratch slice (they start at
-  // or after the chunk's own group, which is not before raw0)
-  const int64_t beta = p / g;
-  const int64_t raw0 = std::max<int64_t>(0, t / g - k_local) * g;
-  const size_t first = ((size_t)bkv * raw_rows + (p - g + 1 - raw0)) * D;
-  const size_t last = ((size_t)bkv * raw_rows + (p - raw0)) * D;
-  const int Hq = Hkv * nq;
-  if constexpr (LCA) {
-    // the group's queries: chunk rows i-g+1 .. i, or the running sum of its tokens before
-    // the chunk followed by rows 0 .. i (token order, heads first, as the decode steps add them)
-    constexpr int CPL = D / kWave;
-    const int col = lane * CPL;
-    float s[CPL];
-    int64_t r0 = (int64_t)i - g + 1;
-    if (r0 < 0) {
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) s[e] = qsum[(size_t)bkv * D + col + e];
-      r0 = 0;
-    } else {
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) s[e] = 0.f;
-    }
-    for (int64_t r = r0; r <= i; ++r) add_query_row<T, D>(q_chunk, b, Hq, hk, nq, n, r, col, s);
-    float* qbar = w_lds + wave * (D + g);
-    const float inv = 1.0f / ((float)g * (float)nq);
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) qbar[col + e] = s[e] * inv;
-    wave_lds_sync();
-    lca_condense_wave<T, D>(qbar, sk + first, sv + first, sk + last, sv + last, g, scale, d_rope,
-                            core_k + ((size_t)bkv * max_groups + beta) * D,
-                            core_v + ((size_t)bkv * max_groups + beta) * D, qbar + D, nullptr);
-  } else {
-    pool_group_wave<T, D>(q_chunk + (((size_t)b * Hq + (size_t)hk * nq) * n + i) * D, (int64_t)n * D, nq,
-                          sk + first, sv + first, sk + last, sv + last, g, scale,
-                          core_k + ((size_t)bkv * max_groups + beta) * D,
-                          core_v + ((size_t)bkv * max_groups + beta) * D, w_lds + wave * g);
-  }
-}
-
-// LCA-style cache, after the append launch (which read the sums at the chunk's start): one
-// wave per key/value slice leaves in qsum the sum of the queries of the trailing incomplete
-// group -- the chunk's rows after its last completed group, plus the previous sum when the
-// chunk completes no group.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void cca_extend_qsum_kernel(const int32_t* __restrict__ pos_ws,
-                                                            const T* __restrict__ q_chunk, float* __restrict__ qsum,
-                                                            int Hkv, int nq, int n, int g) {
   constexpr int CPL = D / kWave;
   const int64_t bkv = blockIdx.x;
   const int64_t b = bkv / Hkv;
   const int hk = (int)(bkv - b * Hkv);
   const int64_t t = pos_ws[b];
   if (t < 0) return;
-  const int col = threadIdx.x * CPL;
-  const int64_t end = t + n;
-  const bool completes = end / g > t / g;
-  float s[CPL];
+  if ((int)blockIdx.y < ring_blocks) {
+    if (blockIdx.y == 0 && threadIdx.x == 0 && hk == 0) lens[b] = (int32_t)(t + n);
+    const int64_t idx = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    const int64_t i = idx / CPR;
+    const int c = (int)(idx - i * CPR);
+    if (i >= n) return;
+    const int64_t slot = (t + i) % R;
+    st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bkv * R + slot) * D) + c,
+         ld16(reinterpret_cast<const uint4*>(k_chunk + ((size_t)bkv * n + i) * D) + c));
+    st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + c,
+         ld16(reinterpret_cast<const uint4*>(v_chunk + ((size_t)bkv * n + i) * D) + c));
+    return;
+  }
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int w = ((int)blockIdx.y - ring_blocks) * (int)(blockDim.x / kWave) + wave;
+  const int64_t ngroups = (t + n) / g - t / g;   // groups whose last token is in the chunk
+  const bool has_group = w < ngroups;
+  if (!has_group && !(LCA && w == 0)) return;
+  const int Hq = Hkv * nq;
+  const int col = lane * CPL;
+  if (has_group) {
+    // group beta: positions p-g+1 .. p, all inside the staged slice (they start at or after
+    // the group of the chunk's first token, which is not before raw0)
+    const int64_t beta = t / g + w;
+    const int64_t p = beta * g + g - 1;
+    const int64_t i = p - t;                     // chunk row of the group's last token
+    const int64_t raw0 = std::max<int64_t>(0, t / g - k_local) * g;
+    const size_t first = ((size_t)bkv * raw_rows + (p - g + 1 - raw0)) * D;
+    const size_t last = first + (size_t)(g - 1) * D;
+    T* kc = core_k + ((size_t)bkv * max_groups + beta) * D;
+    T* vc = core_v + ((size_t)bkv * max_groups + beta) * D;
+    if constexpr (LCA) {
+      constexpr bool kFast = D == 128 && sizeof(T) == 2;
+      // d = 128, g = 16: the group's staged rows fetched up front (scoring segments, then the
+      // columns of the weighted sums), while the query rows are summed
+      constexpr int G16 = 16;
+      uint4 kseg[kFast ? 4 : 1];
+      uint32_t kcol[kFast ? G16 : 1], vcol[kFast ? G16 : 1];
+      const bool fast = kFast && g == G16;
+      if constexpr (kFast) {
+        if (fast) {
+          const int rsub = lane >> 2, seg = lane & 3;
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) s[e] = completes ? 0.f : qsum[(size_t)bkv * D + col + e];
-  const int64_t r0 = completes ? end / g * g - t : 0;
-  for (int64_t r = r0; r < n; ++r) add_query_row<T, D>(q_chunk, b, Hkv * nq, hk, nq, n, r, col, s);
+          for (int c = 0; c < 4; ++c) kseg[c] = ld16(sk + first + (size_t)rsub * D + seg * (D / 4) + c * 8);
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) qsum[(size_t)bkv * D + col + e] = s[e];
+          for (int r = 0; r < G16; ++r) {
+            kcol[r] = *reinterpret_cast<const uint32_t*>(sk + first + (size_t)r * D + col);
+            vcol[r] = *reinterpret_cast<const uint32_t*>(sv + first + (size_t)r * D + col);
+          }
+        }
+      }
+      // the group's queries: the running sum of its tokens before the chunk, then chunk rows
+      float s[CPL];
+      int64_t r0 = i - g + 1;
+      if (r0 < 0) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) s[e] = qsum[(size_t)bkv * D + col + e];
+        r0 = 0;
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) s[e] = 0.f;
+      }
+      add_query_rows<T, D>(q_chunk, b, Hq, hk, nq, n, r0, i, col, s);
+      float* qbar = w_lds + wave * (D + g);
+      const float inv = 1.0f / ((float)g * (float)nq);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) qbar[col + e] = s[e] * inv;
+      wave_lds_sync();
+      if constexpr (kFast) {
+        if (fast) {
+          lca_condense_math<T, D, G16>(
+              qbar, G16, scale, d_rope, kc, vc, qbar + D, nullptr, [&](int, int c) { return kseg[c]; },
+              [&](int r, float* f) { Elem<T>::pair_to_f32(kcol[r], f); },
+              [&](int r, float* f) { Elem<T>::pair_to_f32(vcol[r], f); },
+              [&](int r, float* f) { lca_load_cols<T, D>(sk + first + (size_t)r * D + col, f); });
+        }
+      }
+      if (!fast)
+        lca_condense_wave<T, D>(qbar, sk + first, sv + first, sk + last, sv + last, g, scale, d_rope, kc, vc,
+                                qbar + D, nullptr);
+    } else {
+      pool_group_wave<T, D>(q_chunk + (((size_t)b * Hq + (size_t)hk * nq) * n + i) * D, (int64_t)n * D, nq,
+                            sk + first, sv + first, sk + last, sv + last, g, scale, kc, vc, w_lds + wave * g);
+    }
+  }
+  if constexpr (LCA) {
+    if (w == 0) {
+      // the query sum of the trailing incomplete group: the chunk's rows after its last
+      // completed group, on top of the previous sum when the chunk completes no group
+      float s[CPL];
+      const int64_t end = t + n;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s[e] = ngroups > 0 ? 0.f : qsum[(size_t)bkv * D + col + e];
+      const int64_t r0 = ngroups > 0 ? end / g * g - t : 0;
+      if (r0 < n) add_query_rows<T, D>(q_chunk, b, Hq, hk, nq, n, r0, n - 1, col, s);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) qsum[(size_t)bkv * D + col + e] = s[e];
+    }
+  }
 }
 
 template <typename T, int D>
@@ -240,23 +282,21 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
   e = launch_extend_attention(c->dt, D, q, sk, sv, c->core_k, c->core_v, out, out_f32, c->B * H_q, nq, c->g,
                               c->k_local, scale, ext, stream);
   if (e != hipSuccess) return e;
-  const dim3 agrid((unsigned)BHkv, (unsigned)((n + 3) / 4));
+  // launch 3: ring copies, then one wave per completed group (at most n/g + 1 groups)
+  const int ring_blocks = (int)(((int64_t)n * CPR + 255) / 256);
+  const int pool_blocks = (n / c->g + 1 + 3) / 4;
+  const dim3 fgrid((unsigned)BHkv, (unsigned)(ring_blocks + pool_blocks));
   if (qsum == nullptr) {
-    hipLaunchKernelGGL((cca_extend_append_kernel<T, D, false>), agrid, dim3(256), (size_t)4 * c->g * sizeof(float),
+    hipLaunchKernelGGL((cca_extend_finish_kernel<T, D, false>), fgrid, dim3(256), (size_t)4 * c->g * sizeof(float),
                        stream, lens, pos_ws, (const T*)q, (const T*)k, (const T*)v, (const T*)sk, (const T*)sv,
                        (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k, (T*)c->core_v, c->H, nq, n, R, c->max_groups,
-                       c->g, c->k_local, raw_rows, scale, (const float*)nullptr, 0);
-    return hipGetLastError();
+                       c->g, c->k_local, raw_rows, scale, (float*)nullptr, 0, ring_blocks);
+  } else {
+    hipLaunchKernelGGL((cca_extend_finish_kernel<T, D, true>), fgrid, dim3(256), (size_t)4 * (D + c->g) * sizeof(float),
+                       stream, lens, pos_ws, (const T*)q, (const T*)k, (const T*)v, (const T*)sk, (const T*)sv,
+                       (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k, (T*)c->core_v, c->H, nq, n, R, c->max_groups,
+                       c->g, c->k_local, raw_rows, scale, qsum, d_rope, ring_blocks);
   }
-  hipLaunchKernelGGL((cca_extend_append_kernel<T, D, true>), agrid, dim3(256),
-                     (size_t)4 * (D + c->g) * sizeof(float), stream, lens, pos_ws, (const T*)q, (const T*)k,
-                     (const T*)v, (const T*)sk, (const T*)sv, (T*)c->ring_k, (T*)c->ring_v, (T*)c->core_k,
-                     (T*)c->core_v, c->H, nq, n, R, c->max_groups, c->g, c->k_local, raw_rows, scale,
-                     (const float*)qsum, d_rope);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((cca_extend_qsum_kernel<T, D>), dim3((unsigned)BHkv), dim3(64), 0, stream,
-                     (const int32_t*)pos_ws, (const T*)q, qsum, c->H, nq, n, c->g);
   return hipGetLastError();
 }
 
