@@ -436,7 +436,9 @@ int cca_cache_load_prefill_lca_gqa(cca_cache_t* c, float* qsum, int H_q, const v
  * lens[b] advanced by n.
  *   n       : 1 <= n <= k_local*g + 1 (then no token of the chunk can see a core
  *             token pooled from the same chunk); longer chunks are split by the
- *             caller into consecutive calls.  CCA_ERR_INVALID otherwise.
+ *             caller into consecutive calls.  CCA_ERR_INVALID otherwise.  A chunk
+ *             may complete at most 131068 groups (n/g + 1 <= 131068, i.e. k_local
+ *             below about 131K); CCA_ERR_UNSUPPORTED above.
  *   lens, max_len, H_q : as for cca_cache_append_decode_varlen; capacity needs
  *             (max_len + n)/g <= max_groups (else CCA_ERR_CAPACITY).  A sequence
  *             with lens[b] outside [0, max_len] gets NaN outputs and is left as is.

@@ -440,6 +440,7 @@ static int cache_extend(const cca_cache_t* c, float* qsum, int d_rope, int32_t* 
   if (out_dt != CCA_F32 && out_dt != c->dt) return CCA_ERR_UNSUPPORTED;
   if (H_q < 1 || H_q % c->H != 0 || (int64_t)c->B * H_q > ((int64_t)1 << 24)) return CCA_ERR_INVALID;
   if (n < 1 || (int64_t)n > (int64_t)c->k_local * c->g + 1) return CCA_ERR_INVALID;
+  if ((int64_t)n / c->g + 1 > cca::kExtendMaxGroupWaves) return CCA_ERR_UNSUPPORTED;
   if (lens == nullptr || ((uintptr_t)lens & 3u) != 0 || max_len < 0 || max_len + n >= INT32_MAX)
     return CCA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||

@@ -35,6 +35,10 @@ inline int dtype_bytes(int dt) { return dt == CCA_F32 ? 4 : 2; }
 // position pos[b] + i; the raw key at absolute position u is row u - raw0 of the
 // raw K/V slice, raw0 = max(0, pos[b]/g - k_local)*g (the first raw position any
 // query of the slice sees); core token j is row j of the core slice.
+// Waves the chunked append's finish launch can give to completed groups (one each): a chunk
+// of n tokens completes at most n/g + 1 groups.
+constexpr int64_t kExtendMaxGroupWaves = (int64_t)4 * 32767;
+
 struct ExtendArgs {
   const int32_t* pos;  // device [B]: position of the first new token; < 0 marks an invalid sequence
   int Hq;              // query heads: query slice bh belongs to sequence bh / Hq

@@ -83,24 +83,26 @@ __global__ __launch_bounds__(256) void cca_extend_gather_kernel(const int32_t* _
   if (!valid) return;
   const int64_t raw0 = std::max<int64_t>(0, t / g - k_local) * g;
   const int64_t rows = t + n - raw0;
-  const int64_t idx = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
-  const int64_t u = idx / CPR;
-  const int c = (int)(idx % CPR);
-  if (u >= rows) return;
-  const int64_t pos = raw0 + u;
-  const T* srck;
-  const T* srcv;
-  if (pos < t) {
-    const int64_t slot = pos % R;
-    srck = ring_k + ((size_t)bkv * R + slot) * D;
-    srcv = ring_v + ((size_t)bkv * R + slot) * D;
-  } else {
-    srck = k_chunk + ((size_t)bkv * n + (pos - t)) * D;
-    srcv = v_chunk + ((size_t)bkv * n + (pos - t)) * D;
+  // grid-stride over the (row, 16-byte piece) pairs: the y extent is capped at launch
+  for (int64_t idx = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; idx < rows * CPR;
+       idx += (int64_t)gridDim.y * blockDim.x) {
+    const int64_t u = idx / CPR;
+    const int c = (int)(idx % CPR);
+    const int64_t pos = raw0 + u;
+    const T* srck;
+    const T* srcv;
+    if (pos < t) {
+      const int64_t slot = pos % R;
+      srck = ring_k + ((size_t)bkv * R + slot) * D;
+      srcv = ring_v + ((size_t)bkv * R + slot) * D;
+    } else {
+      srck = k_chunk + ((size_t)bkv * n + (pos - t)) * D;
+      srcv = v_chunk + ((size_t)bkv * n + (pos - t)) * D;
+    }
+    const size_t dst = ((size_t)bkv * raw_rows + u) * D;
+    st16(reinterpret_cast<uint4*>(sk + dst) + c, ld16(reinterpret_cast<const uint4*>(srck) + c));
+    st16(reinterpret_cast<uint4*>(sv + dst) + c, ld16(reinterpret_cast<const uint4*>(srcv) + c));
   }
-  const size_t dst = ((size_t)bkv * raw_rows + u) * D;
-  st16(reinterpret_cast<uint4*>(sk + dst) + c, ld16(reinterpret_cast<const uint4*>(srck) + c));
-  st16(reinterpret_cast<uint4*>(sv + dst) + c, ld16(reinterpret_cast<const uint4*>(srcv) + c));
 }
 
 // Add to s, row by row over chunk rows r0 .. r1, the sum of the nq query heads' rows (this
@@ -139,10 +141,11 @@ __device__ __forceinline__ void add_query_rows(const T* __restrict__ q_chunk, in
 }
 
 // Launch 3.  Blocks y < ring_blocks: the chunk's key/value rows into their ring slots
-// (one 16-byte piece per thread) and the new length.  The other blocks: one wave per group
-// the chunk completes (the w-th such group for wave w), pooled -- LCA: condensed -- from the
-// staged rows; for the LCA-style cache, wave 0 then leaves in qsum the query sum of the
-// trailing incomplete group (it alone reads the previous sum, for the chunk's first group).
+// (16-byte pieces, grid-stride) and the new length.  The other blocks: one wave per group
+// the chunk completes (the w-th such group for wave w; the caller sizes the grid for the
+// n/g + 1 groups a chunk can complete), pooled -- LCA: condensed -- from the staged rows; for
+// the LCA-style cache, wave 0 then leaves in qsum the query sum of the trailing incomplete
+// group (it alone reads the previous sum, for the chunk's first group).
 template <typename T, int D, bool LCA>
 __global__ __launch_bounds__(256) void cca_extend_finish_kernel(
     int32_t* __restrict__ lens, const int32_t* __restrict__ pos_ws, const T* __restrict__ q_chunk,
@@ -160,15 +163,16 @@ __global__ __launch_bounds__(256) void cca_extend_finish_kernel(
   if (t < 0) return;
   if ((int)blockIdx.y < ring_blocks) {
     if (blockIdx.y == 0 && threadIdx.x == 0 && hk == 0) lens[b] = (int32_t)(t + n);
-    const int64_t idx = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
-    const int64_t i = idx / CPR;
-    const int c = (int)(idx - i * CPR);
-    if (i >= n) return;
-    const int64_t slot = (t + i) % R;
-    st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bkv * R + slot) * D) + c,
-         ld16(reinterpret_cast<const uint4*>(k_chunk + ((size_t)bkv * n + i) * D) + c));
-    st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + c,
-         ld16(reinterpret_cast<const uint4*>(v_chunk + ((size_t)bkv * n + i) * D) + c));
+    for (int64_t idx = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; idx < (int64_t)n * CPR;
+         idx += (int64_t)ring_blocks * blockDim.x) {
+      const int64_t i = idx / CPR;
+      const int c = (int)(idx - i * CPR);
+      const int64_t slot = (t + i) % R;
+      st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bkv * R + slot) * D) + c,
+           ld16(reinterpret_cast<const uint4*>(k_chunk + ((size_t)bkv * n + i) * D) + c));
+      st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + c,
+           ld16(reinterpret_cast<const uint4*>(v_chunk + ((size_t)bkv * n + i) * D) + c));
+    }
     return;
   }
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
@@ -272,7 +276,7 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
   T* sk = (T*)((uint8_t*)workspace + head_bytes(c->B));
   T* sv = sk + (size_t)BHkv * raw_rows * D;
   constexpr int CPR = D * (int)sizeof(T) / 16;
-  const int64_t gy = (raw_rows * CPR + 255) / 256;
+  const int64_t gy = std::min<int64_t>((raw_rows * CPR + 255) / 256, 65535);   // the kernel strides over the rest
   hipLaunchKernelGGL((cca_extend_gather_kernel<T, D>), dim3((unsigned)BHkv, (unsigned)gy), dim3(256), 0, stream, lens,
                      max_len, pos_ws, order_ws, (const T*)k, (const T*)v, (const T*)c->ring_k, (const T*)c->ring_v, sk, sv, c->H,
                      n, R, c->g, c->k_local, raw_rows);
@@ -283,8 +287,8 @@ hipError_t launch_extend_t(const cca_cache_t* c, int32_t* lens, int64_t max_len,
                               c->k_local, scale, ext, stream);
   if (e != hipSuccess) return e;
   // launch 3: ring copies, then one wave per completed group (at most n/g + 1 groups)
-  const int ring_blocks = (int)(((int64_t)n * CPR + 255) / 256);
-  const int pool_blocks = (n / c->g + 1 + 3) / 4;
+  const int ring_blocks = (int)std::min<int64_t>(((int64_t)n * CPR + 255) / 256, 32768);
+  const int pool_blocks = (int)((n / c->g + 1 + 3) / 4);   // n/g + 1 <= kExtendMaxGroupWaves (checked by the caller)
   const dim3 fgrid((unsigned)BHkv, (unsigned)(ring_blocks + pool_blocks));
   if (qsum == nullptr) {
     hipLaunchKernelGGL((cca_extend_finish_kernel<T, D, false>), fgrid, dim3(256), (size_t)4 * c->g * sizeof(float),

@@ -145,6 +145,16 @@ def test_validation_of_training_lca_and_serving_calls(lib):
                                               NULL) == -3
 
 
+def test_extend_rejects_chunks_completing_too_many_groups(lib):
+    """A chunk completes at most n/g + 1 groups, each pooled by one wave of the finish launch;
+    beyond 131068 groups the call is refused before any launch (g = 1 and a window of 200000
+    groups allow such chunks).  At the limit validation goes on (here: to the workspace check)."""
+    P = ctypes.c_void_p(256)
+    d = binding.CacheDesc(256, 256, 256, 256, 1, 1, 64, 1, 200000, 0, 1 << 20, 0, 0)
+    assert lib.cca_cache_extend(ctypes.byref(d), P, 10, 1, 131068, P, P, P, P, 0, P, 1, 0.1, None) == -2
+    assert lib.cca_cache_extend(ctypes.byref(d), P, 10, 1, 131067, P, P, P, P, 0, P, 1, 0.1, None) == -3
+
+
 def test_unknown_dtype_rejected_before_any_launch(lib):
     """A dtype code outside {F32, BF16, F16} is refused by host-side validation (no device
     call is made, so this runs without a GPU)."""

@@ -158,3 +158,21 @@ def test_extend_work_order_ties_and_out_of_range(gpu):
         want = cca_serving.serve_rows(Q[b], K[b], V[b], range(L, L + n), g, k, scale, core_dtype=dt)
         err = np.abs(got[b] - want).max()
         assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+
+
+def test_extend_window_beyond_one_grid_column(gpu):
+    """A raw window of (k+1)*g = 524288 rows (g = 64, k = 8191, float32, d = 128): the staging
+    copy of the window needs more than 65535 blocks of the gather's second grid dimension, so
+    the gather strides over the rest.  Every appended row matches the oracle."""
+    B, Hq, Hkv, d, g, k, dt, seed = 1, 1, 1, 128, 64, 8191, "f32", 49
+    L0, n = (k + 1) * g + 100, 50
+    _say(f"extend with a {(k + 1) * g}-row window, prefix {L0}")
+    total = L0 + n
+    Q, K, V, cache, scale = _setup(B, Hq, Hkv, d, g, k, dt, [L0], total, seed, gpu)
+    q, kk, v = (_dev(X[:, :, L0:L0 + n], dt, gpu) for X in (Q, K, V))
+    out = cache.extend(q, kk, v, out_dtype=torch.float32, scale=scale)
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == [L0 + n]
+    want = cca_serving.serve_rows(Q[0], K[0], V[0], range(L0, L0 + n), g, k, scale, core_dtype=dt)
+    err = np.abs(out[0].cpu().numpy() - want).max()
+    assert np.isfinite(err) and err <= TOL[dt], f"max abs err {err:.3e}"
