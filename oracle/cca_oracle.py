@@ -35,7 +35,7 @@ What is computed, per (batch, head) slice with Q, K, V of shape [L, d]:
      core tokens Kc[0:n_c] plus raw keys K[n_c*g .. t] (inclusive).
   4. Output: one softmax over the whole visible set (unified K/V).
 
-Storage precision of the core tokens (reading; recorded in the design doc): the
+Storage precision of the core tokens (a reading of the pages): the
 core K/V are the projections of the core tokens ([P1] core K/V equation) and
 live in the KV cache ([P1] Triton section).  In a model computing in bf16 those
 are bf16 tensors, and the page's 93% KV-cache reduction at 128K (Fig. 3) is
@@ -44,7 +44,7 @@ take `core_dtype`: None keeps the core tokens exact (float64); "bf16" / "f16" / 
 round each element once, to nearest even, to that storage type before use.
 Everything else stays float64.
 
-Readings taken where the pages are silent (recorded in the design doc too):
+Readings taken where the pages are silent:
   * pooling temperature = the attention scale (1/sqrt(d) by default) --
     PARITY UNPINNED against the pages: every invariant below is invariant to
     this temperature, and the paper's equation did not survive extraction;
