@@ -43,6 +43,15 @@ constexpr float kLn2 = 0.69314718055994531f;
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Swizzle of the dK/dV kernel's query-side tiles (Q, dO).  Measured on this part (per-dispatch
+// LDS bank-conflict counts of a one-wave probe): a 16-byte-per-lane LDS read serves each
+// 32-lane half in two passes of 16 lanes, split by the parity of lane bits 2-4, over 64
+// four-byte banks.  The dK/dV row-operand read (lane l: row l%16, chunk 4kk + l/16) then puts
+// rows {0-3, 12-15} of one chunk and rows {4-11} of the next in the same pass, which any
+// swizzle of the row alone maps onto repeated banks; this one (r, with bits 2 and 3 flipped
+// on odd rows) keeps both passes on 16 distinct chunks, keeps the transpose reads (8 rows x
+// 2 chunks per half-wave) on 16 distinct chunks, and is a bijection on 16 rows.
+__device__ __forceinline__ int swz_t(int r) { return (r & 15) ^ ((r & 1) * 12); }
 
 // Operand read offsets inside a row-major swizzled tile (bytes, relative to the
 // first row of a 32-row sub-block).
@@ -118,16 +127,17 @@ __device__ __forceinline__ f32x16_t rows_mfma(const uint4* xa, const uint4* yop)
 }
 
 // Fill a 64-row tile (rows base .. base+63 of a row-major [*, 128] 16-bit array,
-// rows past `lim` repeat row `lim`) into LDS with the chunk swizzle.  nw waves
-// share the fill: wave w writes rows w*64/nw .. in groups of 4 rows per instruction.
-template <int NW>
+// rows past `lim` repeat row `lim`) into LDS with the chunk swizzle (swz, or swz_t with
+// TSWZ).  nw waves share the fill: wave w writes rows w*64/nw .. in groups of 4 rows per
+// instruction.
+template <int NW, bool TSWZ = false>
 __device__ __forceinline__ void fill_tile(const void* src, int64_t base, int64_t lim, uint8_t* dst, int wave,
                                           int lane) {
   constexpr int ITERS = kTileRows / (4 * NW);
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int r = wave * (4 * ITERS) + i * 4 + (lane >> 4);
-    const int off = ((lane & 15) ^ swz(r)) * 16;
+    const int off = ((lane & 15) ^ (TSWZ ? swz_t(r) : swz(r))) * 16;
     const int64_t gr = min(base + r, lim);
     uint8_t* d = dst + (wave * (4 * ITERS) + i * 4) * kRowBytes;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const uint8_t*)src +
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   // half), dims 16 blk + 4 (n16 % 4) .. +3
   int roff[kD / 32];
 #pragma unroll
-  for (int kk = 0; kk < kD / 32; ++kk) roff[kk] = n16 * kRowBytes + (((4 * kk + G) ^ swz(n16)) * 16);
+  for (int kk = 0; kk < kD / 32; ++kk) roff[kk] = n16 * kRowBytes + (((4 * kk + G) ^ swz_t(n16)) * 16);
   int toff[2][kD / 16];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -403,7 +413,7 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
     for (int blk = 0; blk < kD / 16; ++blk) {
       const int chunk = 2 * blk + ((n16 & 3) >> 1);
-      toff[h][blk] = row * kRowBytes + ((chunk ^ swz(row)) * 16) + (n16 & 1) * 8;
+      toff[h][blk] = row * kRowBytes + ((chunk ^ swz_t(row)) * 16) + (n16 & 1) * 8;
     }
   }
   f32x4_t acc_v[kD / 16], acc_k[kD / 16];
@@ -436,8 +446,8 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int base = tile_base(it);
     const size_t qs = qslice0 + it / n_qt;                // query slice of this iteration
     if (wave < 8) {
-      fill_tile<8>(Q + qs * L * kD, base, L - 1, buf, wave, lane);
-      fill_tile<8>(dO + qs * L * kD, base, L - 1, buf + kTileBytes, wave, lane);
+      fill_tile<8, true>(Q + qs * L * kD, base, L - 1, buf, wave, lane);
+      fill_tile<8, true>(dO + qs * L * kD, base, L - 1, buf + kTileBytes, wave, lane);
     } else if (wave < 10) {
       const int t = min(base + lane, L - 1);
       const float* src = (wave == 8 ? lse : Dv) + qs * L + t;
