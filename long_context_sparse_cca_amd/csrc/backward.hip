@@ -494,6 +494,21 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
       }
+      // transpose operands (dO^T, Q^T) of gradient block blk: four 8-byte transpose reads
+      auto tr4 = [&](int blk, v4s_t* t) {
+        t[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(dsb + toff[0][blk]));
+        t[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(dsb + toff[1][blk]));
+        t[2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(qsb + toff[0][blk]));
+        t[3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(qsb + toff[1][blk]));
+      };
+      // the first kPre blocks' operands are read before the weights, so that the weight
+      // arithmetic covers their latency (the compiler waits for all outstanding transpose
+      // reads before their first use, so reads are grouped rather than pipelined one by one)
+      constexpr int kPre = 2, kBatch = 3;
+      v4s_t ta[kPre][4];
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) tr4(i, ta[i]);
+      __builtin_amdgcn_sched_barrier(0);
       // weights and dS; per-query statistics of the lane's 8 queries
       float pw[8], dsw[8];
       const int tq = t0 + 4 * G - q_lo;   // query t0 + 16b + 4G + i visible iff (tq + 16b + i) <= q_span
@@ -520,20 +535,27 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       const uint4 pb = __builtin_bit_cast(uint4, pp);
       const uint4 db = __builtin_bit_cast(uint4, qq);
       // dV^T += dO^T P and dK^T += Q^T dS, 16 dims per MFMA
-#pragma unroll
-      for (int blk = 0; blk < kD / 16; ++blk) {
-        const v4s_t o0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(dsb + toff[0][blk]));
-        const v4s_t o1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(dsb + toff[1][blk]));
-        const v4s_t q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(qsb + toff[0][blk]));
-        const v4s_t q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(qsb + toff[1][blk]));
-        const v4s_t ob[2] = {o0, o1};
-        const v4s_t qb[2] = {q0, q1};
+      auto grad = [&](int blk, const v4s_t* t) {
+        const v4s_t ob[2] = {t[0], t[1]};
+        const v4s_t qb[2] = {t[2], t[3]};
         acc_v[blk] = Mma16<T>::mfma16(__builtin_bit_cast(uint4, ob), pb, acc_v[blk]);
         acc_k[blk] = Mma16<T>::mfma16(__builtin_bit_cast(uint4, qb), db, acc_k[blk]);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) grad(i, ta[i]);
+      // the remaining blocks in batches of kBatch: reads of a batch, then its MFMAs
+#pragma unroll
+      for (int b0 = kPre; b0 < kD / 16; b0 += kBatch) {
+        v4s_t tb[kBatch][4];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (b0 + i < kD / 16) tr4(b0 + i, tb[i]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (b0 + i < kD / 16) grad(b0 + i, tb[i]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
