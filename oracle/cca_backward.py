@@ -245,26 +245,45 @@ def cca_backward_sampled_slice(Q, K, V, dO, g: int, k: int, scale: float, rows, 
     m = _o.n_core_groups(L, g)
     q_mean = Qh.sum(axis=0) / r
     Kc, Vc, A = _o.pool(q_mean, K, V, g, scale, core_dtype)
-    # forward output and log-sum-exp of every query, one query group at a time (the group's
-    # rows share the core tokens and the window start; the causal end hides later raw keys)
-    lse = np.empty((r, L))
-    Dq = np.empty((r, L))
-    for h in range(r):
-        out = np.empty((L, d))
-        for beta in range((L + g - 1) // g):
+    # forward output and log-sum-exp of the queries, one query group at a time (the group's
+    # rows share the core tokens and the window start; the causal end hides later raw keys);
+    # a group's statistics are computed the first time one of its queries is needed, so that
+    # at long L only the queries the requested entries depend on are evaluated
+    group_stats = {}
+
+    def stats_of_group(beta):
+        if beta not in group_stats:
             t0, t1 = beta * g, min(L, beta * g + g)
             n_c = _o.visible_core_count(t0, g, k)
             lo, _ = _o.raw_window(t0, g, k)
             keys_b = np.concatenate([Kc[:n_c], K[lo:t1]])
             vals_b = np.concatenate([Vc[:n_c], V[lo:t1]])
-            z = scale * (Qh[h, t0:t1] @ keys_b.T)
-            hidden = np.arange(lo, t1)[None, :] > np.arange(t0, t1)[:, None]
-            z[:, n_c:][hidden] = -np.inf
-            mx = z.max(axis=1, keepdims=True)
-            e = np.exp(z - mx)
-            lse[h, t0:t1] = mx[:, 0] + np.log(e.sum(axis=1))
-            out[t0:t1] = (e / e.sum(axis=1, keepdims=True)) @ vals_b
-        Dq[h] = np.einsum("td,td->t", dOh[h], out)
+            lse_b = np.empty((r, t1 - t0))
+            d_b = np.empty((r, t1 - t0))
+            for h in range(r):
+                z = scale * (Qh[h, t0:t1] @ keys_b.T)
+                hidden = np.arange(lo, t1)[None, :] > np.arange(t0, t1)[:, None]
+                z[:, n_c:][hidden] = -np.inf
+                mx = z.max(axis=1, keepdims=True)
+                e = np.exp(z - mx)
+                lse_b[h] = mx[:, 0] + np.log(e.sum(axis=1))
+                out = (e / e.sum(axis=1, keepdims=True)) @ vals_b
+                d_b[h] = np.einsum("td,td->t", dOh[h, t0:t1], out)
+            group_stats[beta] = (lse_b, d_b)
+        return group_stats[beta]
+
+    def stats(ts):
+        """(lse [r, len(ts)], D = dO . O [r, len(ts)]) of the queries ts (ascending)."""
+        ts = np.asarray(ts)
+        lse_t = np.empty((r, len(ts)))
+        d_t = np.empty((r, len(ts)))
+        for beta in np.unique(ts // g):
+            sel = (ts // g) == beta
+            lse_b, d_b = stats_of_group(int(beta))
+            lse_t[:, sel] = lse_b[:, ts[sel] - beta * g]
+            d_t[:, sel] = d_b[:, ts[sel] - beta * g]
+        return lse_t, d_t
+
     t_all = np.arange(L)
 
     core_cache = {}
@@ -273,11 +292,12 @@ def cca_backward_sampled_slice(Q, K, V, dO, g: int, k: int, scale: float, rows, 
         # queries that see core token j: n_c(t) > j, i.e. t >= (j + k + 1) g
         if j not in core_cache:
             ts = t_all[t_all >= (j + k + 1) * g]
+            lse_t, d_t = stats(ts)
             dkc = np.zeros(d)
             dvc = np.zeros(d)
             for h in range(r):
-                p = np.exp(scale * (Qh[h, ts] @ Kc[j]) - lse[h, ts])
-                ds = p * (dOh[h, ts] @ Vc[j] - Dq[h, ts])
+                p = np.exp(scale * (Qh[h, ts] @ Kc[j]) - lse_t[h])
+                ds = p * (dOh[h, ts] @ Vc[j] - d_t[h])
                 dkc += scale * (ds @ Qh[h, ts])
                 dvc += p @ dOh[h, ts]
             core_cache[j] = (dkc, dvc)
@@ -299,9 +319,10 @@ def cca_backward_sampled_slice(Q, K, V, dO, g: int, k: int, scale: float, rows, 
         lo, hi = _o.raw_window(t, g, k)
         keys_t = np.concatenate([Kc[:n_c], K[lo:hi + 1]])
         vals_t = np.concatenate([Vc[:n_c], V[lo:hi + 1]])
+        lse_t, d_t = stats([t])
         for h in range(r):
-            p = np.exp(scale * (keys_t @ Qh[h, t]) - lse[h, t])
-            ds = p * (vals_t @ dOh[h, t] - Dq[h, t])
+            p = np.exp(scale * (keys_t @ Qh[h, t]) - lse_t[h, 0])
+            ds = p * (vals_t @ dOh[h, t] - d_t[h, 0])
             dQ[h, i] = scale * (ds @ keys_t)
             if t % g == g - 1 and t // g < m:
                 dQ[h, i] += pool_grads(t // g)[2] / r
@@ -310,9 +331,10 @@ def cca_backward_sampled_slice(Q, K, V, dO, g: int, k: int, scale: float, rows, 
     for i, u in enumerate(keys):
         # queries whose raw window holds u: u <= t <= (u // g + k + 1) g - 1
         ts = t_all[(t_all >= u) & (t_all <= min(L - 1, (u // g + k + 1) * g - 1))]
+        lse_t, d_t = stats(ts)
         for h in range(r):
-            p = np.exp(scale * (Qh[h, ts] @ K[u]) - lse[h, ts])
-            ds = p * (dOh[h, ts] @ V[u] - Dq[h, ts])
+            p = np.exp(scale * (Qh[h, ts] @ K[u]) - lse_t[h])
+            ds = p * (dOh[h, ts] @ V[u] - d_t[h])
             dK[i] += scale * (ds @ Qh[h, ts])
             dV[i] += p @ dOh[h, ts]
         if u // g < m:
