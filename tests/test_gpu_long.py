@@ -1,4 +1,5 @@
-"""Sequences beyond the pages' 128K: a 1M-token prefill and decode at 1M context, on sampled outputs.
+"""Sequences beyond the pages' 128K: a 1M-token prefill, decode at 1M context and a 1M-token
+backward, on sampled outputs.
 
 The pages evaluate CCA up to 128K tokens; these cases check that nothing in the
 indexing (positions, tile and group counts, cache offsets) depends on staying
@@ -73,3 +74,36 @@ def test_decode_at_1m_context(gpu):
             want = oracle.cca_row(Q[t], t, K, V, Kc, Vc, G, KL, scale)
             err = np.abs(outs[i][0, h].cpu().numpy() - want).max()
             assert err <= TOL_BF16, f"head {h} step {t}: max abs err {err:.3e}"
+
+
+def test_backward_1m_tokens_sampled(gpu):
+    """Training at L = 2^20 (H = 2, bf16): the full backward on the GPU, then sampled dQ rows
+    (early, middle and last rows, a group's last row) and dK/dV keys in the last 2048
+    positions (raw keys, keys of the last complete groups) of head 1 against the per-entry
+    gradient oracle, which evaluates only the queries those entries depend on.  Bound: the
+    bf16 gradient bound of the 32K backward test, 2e-2 of the sampled gradients' scale."""
+    from oracle import cca_backward
+    H = 2
+    L = L1M
+    _say(f"backward L={L} H={H}")
+    q, k, v = torch_inputs(1, H, L, D, torch.bfloat16, gpu, seed=5, heavy_frac=0.01)
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(6)
+    do = torch.randn((1, H, L, D), generator=gen, device=gpu).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    out, lse, kc, vc = binding.prefill_lse(q, k, v, G, KL, scale)
+    dq, dk, dv = binding.backward(q, k, v, kc, vc, out, lse, do, G, KL, scale)
+    torch.cuda.synchronize()
+    h = 1
+    rows = [0, 1, G, KL * G, L // 2 + 3, L - 2 * G - 2, L - G - 1, L - 2, L - 1]
+    keys = [L - 2048, L - (KL + 1) * G, L - 2 * G - 1, L - G - 1, L - G, L - 2, L - 1]
+    _say("backward L=1M: oracle on sampled entries")
+    wq, wk, wv = cca_backward.cca_backward_sampled_slice(
+        q[0, h].double().cpu().numpy(), k[0, h].double().cpu().numpy(), v[0, h].double().cpu().numpy(),
+        do[0, h].double().cpu().numpy(), G, KL, scale, rows, keys, core_dtype="bf16")
+    got = (dq[0, h, rows].cpu().numpy(), dk[0, h, keys].cpu().numpy(), dv[0, h, keys].cpu().numpy())
+    for name, g_, ref in zip(("dq", "dk", "dv"), got, (wq, wk, wv)):
+        err = np.abs(g_.astype(np.float64) - ref).max()
+        bound = 2e-2 * max(1.0, np.abs(ref).max())
+        _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
+        assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
