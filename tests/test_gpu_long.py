@@ -107,3 +107,59 @@ def test_backward_1m_tokens_sampled(gpu):
         bound = 2e-2 * max(1.0, np.abs(ref).max())
         _say(f"  {name}: max abs err {err:.3e} (bound {bound:.3e})")
         assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
+
+
+def test_serving_at_1m_context(gpu):
+    """The serving cache (per-sequence lengths, grouped-query heads) past the pages' lengths:
+    two sequences at 2^20 - 5 and 2^19 + 7 tokens, 8 query heads over 2 key/value heads,
+    seeded by grouped-query pooling of each prefix, then 20 single-token steps (each sequence
+    completes a group during them) and one chunked append of 256 tokens.  For one key/value
+    head per sequence the oracle computes the rows at the appended positions from the whole
+    sequence (stored-core reading); bound 2e-2."""
+    from oracle import cca_serving
+    B, HQ, HKV, S, N_EXT = 2, 8, 2, 20, 256
+    R = HQ // HKV
+    lens0 = [L1M - 5, L1M // 2 + 7]
+    scale = 1.0 / math.sqrt(D)
+    _say(f"serving at 1M context: lengths {lens0}, {HQ} query heads over {HKV}")
+    cache = binding.ServeCache(B, HQ, HKV, D, G, KL, max(lens0) + S + N_EXT + G, dtype=torch.bfloat16, device=gpu)
+    prefix = []
+    for b, L in enumerate(lens0):
+        q, _, _ = torch_inputs(1, HQ, L, D, torch.bfloat16, gpu, seed=60 + b, heavy_frac=0.01)
+        _, k, v = torch_inputs(1, HKV, L, D, torch.bfloat16, gpu, seed=70 + b, heavy_frac=0.01)
+        kc, vc = binding.pool_kv(q, k, v, G, scale)
+        cache.load_sequence(b, k, v, kc, vc)
+        prefix.append((q, k, v))
+        del kc, vc
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(80)
+    qs = torch.randn((S, B, HQ, D), generator=gen, device=gpu).to(torch.bfloat16)
+    ks = torch.randn((S, B, HKV, D), generator=gen, device=gpu).to(torch.bfloat16)
+    vs = torch.randn((S, B, HKV, D), generator=gen, device=gpu).to(torch.bfloat16)
+    outs = torch.empty((S, B, HQ, D), dtype=torch.float32, device=gpu)
+    for s in range(S):
+        cache.step(qs[s], ks[s], vs[s], out_dtype=torch.float32, out=outs[s], scale=scale)
+    qe = torch.randn((B, HQ, N_EXT, D), generator=gen, device=gpu).to(torch.bfloat16)
+    ke = torch.randn((B, HKV, N_EXT, D), generator=gen, device=gpu).to(torch.bfloat16)
+    ve = torch.randn((B, HKV, N_EXT, D), generator=gen, device=gpu).to(torch.bfloat16)
+    ext = cache.extend(qe, ke, ve, out_dtype=torch.float32, scale=scale)
+    torch.cuda.synchronize()
+    assert cache.lens.cpu().tolist() == [L + S + N_EXT for L in lens0]
+    ext_rows = [0, 1, G - 1, N_EXT // 2, N_EXT - 1]
+    for (b, hk) in [(0, 1), (1, 0)]:
+        heads = slice(hk * R, (hk + 1) * R)
+        q, k, v = prefix[b]
+        L = lens0[b]
+        Q = torch.cat([q[0, heads], qs[:, b, heads].permute(1, 0, 2), qe[b, heads]], dim=1).double().cpu().numpy()
+        K = torch.cat([k[0, hk:hk + 1], ks[:, b, hk:hk + 1].permute(1, 0, 2), ke[b, hk:hk + 1]], dim=1)
+        V = torch.cat([v[0, hk:hk + 1], vs[:, b, hk:hk + 1].permute(1, 0, 2), ve[b, hk:hk + 1]], dim=1)
+        K, V = K.double().cpu().numpy(), V.double().cpu().numpy()
+        pos = [L + s for s in range(S)] + [L + S + i for i in ext_rows]
+        want = cca_serving.serve_rows(Q, K, V, pos, G, KL, scale, core_dtype="bf16")
+        got_steps = outs[:, b, heads].permute(1, 0, 2).cpu().numpy()
+        got_ext = ext[b, heads][:, ext_rows].cpu().numpy()
+        err_s = np.abs(got_steps - want[:, :S]).max()
+        err_e = np.abs(got_ext - want[:, S:]).max()
+        _say(f"serving at 1M (b={b}, kv head {hk}): steps err {err_s:.2e}, chunked append err {err_e:.2e}")
+        assert np.isfinite(err_s) and err_s <= TOL_BF16, f"steps: max abs err {err_s:.3e}"
+        assert np.isfinite(err_e) and err_e <= TOL_BF16, f"chunked append: max abs err {err_e:.3e}"
