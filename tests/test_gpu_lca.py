@@ -529,3 +529,33 @@ def test_lca_extend_chunks_match_oracle(gpu, case):
         for hk in range(Hkv):
             want_qsum = Qb[hk * r:(hk + 1) * r, n_tot - part:n_tot].sum(axis=(0, 1)) if part else np.zeros(d)
             assert np.abs(cache.qsum[b, hk].cpu().numpy() - want_qsum).max() <= 1e-3
+
+
+def test_lca_prefill_1m_tokens_sampled(gpu):
+    """The LCA-style prefill at L = 2^20 (H = 2, d = 128, g = 16, k = 64, d_rope = 64, bf16): for
+    one head every group's anchor is a maximum of the oracle's fp64 scores; the oracle condenses
+    every group at those anchors (stored in bf16) and sampled query rows, spread over the whole
+    sequence, are compared with it (bound 2e-2)."""
+    B, H, L, d, g, k, d_rope = 1, 2, 1 << 20, 128, 16, 64, 64
+    _say(f"lca prefill L={L} H={H}")
+    q, kk, v = torch_inputs(B, H, L, d, torch.bfloat16, gpu, seed=27, heavy_frac=0.01)
+    scale = 1.0 / math.sqrt(d)
+    out, kc, vc, anchors = binding.prefill_lca(q, kk, v, g, k, d_rope, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    h = 1
+    Qs = q[0, h].double().cpu().numpy()
+    Ks = kk[0, h].double().cpu().numpy()
+    Vs = v[0, h].double().cpu().numpy()
+    anc = anchors[0, h].cpu().numpy()
+    _check_anchors(cca_lca.lca_scores(Qs, Ks, g, scale), anc)
+    Kc, Vc, _ = cca_lca.lca_pool(Qs, Ks, Vs, g, scale, d_rope, anchors=anc, core_dtype="bf16")
+    dc = d - d_rope
+    assert np.array_equal(kc[0, h].float().cpu().numpy()[:, dc:], Kc[:, dc:]), "positional dims differ"
+    rng = np.random.default_rng(8)
+    worst = 0.0
+    for t in sorted({0, k * g, L // 2, L - g - 1, L - 1, *rng.integers(0, L, size=12).tolist()}):
+        want = cca_oracle.cca_row(Qs[t], int(t), Ks, Vs, Kc, Vc, g, k, scale)
+        err = np.abs(out[0, h, t].cpu().numpy().astype(np.float64) - want).max()
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], f"row {t} err {err:.3e}"
+    _say(f"lca prefill 1M: max row err {worst:.2e}")
