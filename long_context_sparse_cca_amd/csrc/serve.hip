@@ -45,10 +45,12 @@ struct ServeCfg {
   // registers and left a quarter of the grid for a second round, 10% slower)
   static constexpr int U = RH >= 8 ? 2 : (RH >= 4 ? 3 : 4);
   static constexpr int KPI = NWAVE * KPW * U;         // key rows per workgroup iteration
+  // minimum waves per SIMD: 4 query heads at d = 128 fit four (the 1024-workgroup grid resident)
+  static constexpr int WPE = (RH == 4 && D == 128) ? 4 : 1;
 };
 
 template <typename T, int D, int RH, bool STREAM, bool LCA>
-__global__ __launch_bounds__(256) void cca_serve_decode_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ServeCfg<T, D, RH>::WPE))) void cca_serve_decode_kernel(
     const int32_t* __restrict__ lens, int64_t max_len, const T* __restrict__ q, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ core_k, T* __restrict__ core_v, T* __restrict__ ring_k,
     T* __restrict__ ring_v, float* __restrict__ ws_acc, float* __restrict__ ws_ml, int Hkv, int nq, int nhb,
@@ -164,9 +166,19 @@ __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
     for (int e = 0; e < C::EPC; ++e) acc[j][e] = 0.f;
   }
 
+  // ring slot (raw_lo + n - n_c) mod R of the keys this lane loads, without a division per
+  // load: the slot of its u = 0 key is carried from iteration to iteration, key u adds u steps
+  // of NWAVE*KPW keys (R < 2^30, so the sums stay in 32 bits)
+  const int Ri = (int)R;
+  const int r_step = (int)(C::KPI % R), r_u = (int)((C::NWAVE * C::KPW) % R);
+  int slot0 = (int)((raw_lo - n_c + start + (int64_t)wave * C::KPW + kg) % R);
+  if (slot0 < 0) slot0 += Ri;
+  int slot_start = (int)((raw_lo - n_c + start) % R);   // key `start`, read by the lanes past `end`
+  if (slot_start < 0) slot_start += Ri;
   for (int64_t base = start; base < end; base += C::KPI) {
     uint4 kr[C::U], vr[C::U];
     bool ok[C::U];
+    int sl = slot0;   // slot of key u of this lane
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       const int64_t n = base + (int64_t)(u * C::NWAVE + wave) * C::KPW + kg;
@@ -181,13 +193,17 @@ __global__ __launch_bounds__(256) void cca_serve_decode_kernel(
         kp = kt_new;   // the token appended by this very call
         vp = vt_new;
       } else {
-        const int64_t slot = (raw_lo + (nn - n_c)) % R;
+        const int slot = ok[u] ? sl : slot_start;
         kp = rk + (size_t)slot * D;
         vp = rv + (size_t)slot * D;
       }
       kr[u] = ld16_kv<STREAM>(kp + part * C::EPC);
       vr[u] = ld16_kv<STREAM>(vp + part * C::EPC);
+      sl += r_u;
+      if (sl >= Ri) sl -= Ri;
     }
+    slot0 += r_step;
+    if (slot0 >= Ri) slot0 -= Ri;
     float s[C::U][RH];
     float vf[C::U][C::EPC];
 #pragma unroll
