@@ -226,9 +226,19 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
 #pragma unroll
   for (int e = 0; e < C::EPC; ++e) acc[e] = 0.f;
 
+  // ring slot (raw_lo + n - n_c) mod R of the keys this lane loads, without a division per
+  // load: the slot of its u = 0 key is carried from iteration to iteration, key u adds u steps
+  // of NWAVE*KPW keys (R < 2^30, so the sums stay in 32 bits)
+  const int Ri = (int)R;
+  const int r_step = (int)(C::KPI % R), r_u = (int)((C::NWAVE * C::KPW) % R);
+  int slot0 = (int)((raw_lo - n_c + start + (int64_t)wave * C::KPW + kg) % R);
+  if (slot0 < 0) slot0 += Ri;
+  int slot_start = (int)((raw_lo - n_c + start) % R);   // key `start`, read by the lanes past `end`
+  if (slot_start < 0) slot_start += Ri;
   for (int64_t base = start; base < end; base += C::KPI) {
     uint4 kr[C::U], vr[C::U];
     bool ok[C::U];
+    int sl = slot0;   // slot of key u of this lane
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
       const int64_t n = base + (int64_t)(u * C::NWAVE + wave) * C::KPW + kg;
@@ -243,13 +253,17 @@ __global__ __launch_bounds__(256) void cca_decode_kernel(
         kp = k_new + (size_t)bh * D;   // the token appended by this very launch
         vp = v_new + (size_t)bh * D;
       } else {
-        const int64_t slot = (raw_lo + (nn - n_c)) % R;
+        const int slot = ok[u] ? sl : slot_start;
         kp = rk + (size_t)slot * D;
         vp = rv + (size_t)slot * D;
       }
       kr[u] = ld16_kv<STREAM>(kp + part * C::EPC);
       vr[u] = ld16_kv<STREAM>(vp + part * C::EPC);
+      sl += r_u;
+      if (sl >= Ri) sl -= Ri;
     }
+    slot0 += r_step;
+    if (slot0 >= Ri) slot0 -= Ri;
     float s[C::U];
 #pragma unroll
     for (int u = 0; u < C::U; ++u) {
