@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void cca_extend_gather_kernel(const int32_t* _
     const T* srck;
     const T* srcv;
     if (pos < t) {
-      const int64_t slot = pos % R;
+      const int64_t slot = (uint32_t)pos % (uint32_t)R;   // positions and R fit in 32 bits
       srck = ring_k + ((size_t)bkv * R + slot) * D;
       srcv = ring_v + ((size_t)bkv * R + slot) * D;
     } else {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void cca_extend_finish_kernel(
          idx += (int64_t)ring_blocks * blockDim.x) {
       const int64_t i = idx / CPR;
       const int c = (int)(idx - i * CPR);
-      const int64_t slot = (t + i) % R;
+      const int64_t slot = (uint32_t)(t + i) % (uint32_t)R;   // positions and R fit in 32 bits
       st16(reinterpret_cast<uint4*>(ring_k + ((size_t)bkv * R + slot) * D) + c,
            ld16(reinterpret_cast<const uint4*>(k_chunk + ((size_t)bkv * n + i) * D) + c));
       st16(reinterpret_cast<uint4*>(ring_v + ((size_t)bkv * R + slot) * D) + c,
