@@ -395,3 +395,81 @@ def test_generic_backward_sweep(gpu, case):
         err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max()
         bound = tol * max(1.0, np.abs(ref).max())
         assert np.isfinite(err) and err <= bound, f"{name}: max abs err {err:.3e} > {bound:.3e}"
+
+
+def _ring_cases(n=8, seed=4242, serve=False):
+    """Small rings (R = (k+1) g from 1 to 15 slots) stepped through several wraps: the ring slot
+    of every key is stepped per key in the decode and serving loops, which these cases exercise
+    with steps both smaller and larger than R."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        g = int(rng.choice([1, 2, 3, 4, 5]))
+        k = int(rng.choice([0, 1, 2]))
+        R = (k + 1) * g
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["f32", "bf16"]))
+        if serve:
+            B = int(rng.integers(1, 4))
+            Hkv = int(rng.integers(1, 3))
+            r = int(rng.choice([1, 2, 4]))
+            lens = [int(x) for x in rng.integers(0, 40, size=B)]
+            cases.append((B, Hkv * r, Hkv, d, g, k, dt, lens, 4 * R + 7, 900 + i))
+        else:
+            B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+            L0 = int(rng.integers(0, 30))
+            cases.append((B, H, d, g, k, L0, L0 + 4 * R + 9, dt, 950 + i))
+    return cases
+
+
+def _rid(c):
+    B, H, d, g, k, L0, T, dt, seed = c
+    return f"B{B}H{H}d{d}g{g}k{k}R{(k + 1) * g}-{dt}-L{L0}-T{T}-s{seed}"
+
+
+@pytest.mark.parametrize("case", _ring_cases(), ids=_rid)
+def test_decode_small_ring_sweep(gpu, case):
+    """The fused append+decode over several wraps of a small ring, every step against the
+    oracle's rows of the whole sequence."""
+    from oracle import cca_oracle
+    B, H, d, g, k, L0, T, dt, seed = case
+    _say(f"decode ring sweep {_rid(case)}")
+    Q, K, V = np_inputs(B, H, T, d, dt, seed)
+    q, kk, v = (_dev(x, dt, gpu) for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    cache = binding.KVCache(B, H, d, g, k, max_tokens=T + g, dtype=TDT[dt], device=gpu)
+    if L0 > 0:
+        kc, vc = binding.pool_kv(q[:, :, :L0].contiguous(), kk[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(),
+                                 g, scale)
+        cache.load_prefill(kk[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), kc, vc)
+    got = torch.empty((T - L0, B, H, d), dtype=torch.float32, device=gpu)
+    for t in range(L0, T):
+        cache.append_decode(q[:, :, t].contiguous(), kk[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                            out_dtype=torch.float32, out=got[t - L0], scale=scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            want = cca_oracle.cca_slice(Q[b, h], K[b, h], V[b, h], g, k, scale, core_dtype=dt)[L0:]
+            err = np.abs(got[:, b, h] - want).max()
+            assert np.isfinite(err) and err <= TOL[dt], f"slice ({b},{h}): max abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("case", _ring_cases(serve=True, seed=4343), ids=_sid)
+def test_serve_small_ring_sweep(gpu, case):
+    """Serving steps over several wraps of a small ring, per-sequence lengths and grouped-query
+    heads, every step against the oracle."""
+    B, Hq, Hkv, d, g, k, dt, lens0, T, seed = case
+    _say(f"serve ring sweep {_sid(case)}")
+    Q, K, V, cache, scale = _serve_setup(B, Hq, Hkv, d, g, k, dt, lens0, max(lens0) + T, seed, gpu)
+    outs = []
+    for i in range(T):
+        q, kk, v = (_dev(np.stack([x[b, :, lens0[b] + i] for b in range(B)]), dt, gpu) for x in (Q, K, V))
+        outs.append(cache.step(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy())
+    torch.cuda.synchronize()
+    got = np.stack(outs, axis=2)
+    for b in range(B):
+        want = cca_serving.serve_rows(Q[b], K[b], V[b], [lens0[b] + i for i in range(T)], g, k, scale,
+                                      core_dtype=dt)
+        err = np.abs(got[b] - want).max()
+        assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
