@@ -50,6 +50,15 @@ BWD_CASES = [
     (1, 2, 300, 16, 2, "f16", 76),      # binary16 inputs
     (2, 1, 517, 7, 3, "f16", 77),
     (1, 1, 1500, 32, 5, "f16", 78),
+    # shorter than a group or a tile: no core token at all, exactly one group, one visible
+    # core token (k = 0), and the first and second 64-query tile
+    (1, 2, 1, 16, 2, "bf16", 60),
+    (1, 1, 5, 16, 2, "bf16", 61),
+    (2, 1, 15, 16, 1, "bf16", 62),
+    (1, 2, 16, 16, 0, "bf16", 63),
+    (1, 1, 17, 16, 0, "bf16", 64),
+    (1, 1, 63, 16, 1, "bf16", 65),
+    (1, 2, 65, 16, 1, "f16", 66),
 ]
 
 
