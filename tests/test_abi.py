@@ -155,6 +155,18 @@ def test_extend_rejects_chunks_completing_too_many_groups(lib):
     assert lib.cca_cache_extend(ctypes.byref(d), P, 10, 1, 131067, P, P, P, P, 0, P, 1, 0.1, None) == -3
 
 
+def test_extend_chunk_size_bounds(lib):
+    """A chunk holds 1 .. k*g + 1 tokens (then no query of the chunk sees a core token pooled
+    from the chunk itself); an empty or longer chunk is refused before any launch."""
+    P = ctypes.c_void_p(256)
+    g, k = 16, 4
+    d = binding.CacheDesc(256, 256, 256, 256, 1, 1, 64, g, k, 0, 1 << 20, 0, 0)
+    for n in (0, -1, k * g + 2):
+        assert lib.cca_cache_extend(ctypes.byref(d), P, 10, 1, n, P, P, P, P, 0, P, 1 << 30, 0.1, None) == -1
+    # the largest chunk passes validation up to the workspace check (workspace of 1 byte)
+    assert lib.cca_cache_extend(ctypes.byref(d), P, 10, 1, k * g + 1, P, P, P, P, 0, P, 1, 0.1, None) == -3
+
+
 def test_unknown_dtype_rejected_before_any_launch(lib):
     """A dtype code outside {F32, BF16, F16} is refused by host-side validation (no device
     call is made, so this runs without a GPU)."""
