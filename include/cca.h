@@ -33,6 +33,10 @@
  *     non-zero return nothing has been enqueued and no output or descriptor
  *     field has been modified, except CCA_ERR_HIP, which reports a failed
  *     kernel launch (see hipGetLastError); then outputs are undefined.
+ *   - A call on an empty sequence (L == 0 in the pooling, prefill, attention
+ *     and backward calls) checks its sizes, dtypes and scalars as usual and
+ *     then returns CCA_OK without reading, writing or enqueuing anything; its
+ *     data pointers are not looked at and may be NULL.
  *   - Calls on one stream are ordered; concurrent calls on different streams
  *     that write the same buffers race (the library has no locks).
  */

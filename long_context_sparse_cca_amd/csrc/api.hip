@@ -57,9 +57,10 @@ int cca_pool_kv_gqa(const void* q, const void* k, const void* v, void* kc, void*
   int s = check_shape(B, H, L, d, g, dt);
   if (s != CCA_OK) return s;
   if (H_kv < 1 || H % H_kv != 0) return CCA_ERR_INVALID;
+  if (!isfinite(scale)) return CCA_ERR_INVALID;
+  if (L == 0) return CCA_OK;   // nothing is read or written: the data pointers may be NULL
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
   if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
-  if (!isfinite(scale)) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
   if (BH * (L / g) >= INT32_MAX || BH * L >= ((int64_t)1 << 40)) return CCA_ERR_INVALID;
   return hip_status(cca::launch_pool(dt, d, q, k, v, kc, vc, B * H_kv, L, g, H / H_kv, scale, stream));
@@ -79,6 +80,7 @@ int check_prefill(const void* q, const void* k, const void* v, const void* kc, c
   if (H_kv < 1 || H % H_kv != 0) return CCA_ERR_INVALID;
   if (out_dt != CCA_F32 && out_dt != dt) return CCA_ERR_UNSUPPORTED;
   if (k_local < 0 || !isfinite(scale)) return CCA_ERR_INVALID;
+  if (L == 0) return CCA_OK;   // nothing is read or written: the data pointers may be NULL
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return CCA_ERR_INVALID;
   if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   const int64_t BH = (int64_t)B * H;
@@ -185,10 +187,11 @@ int cca_pool_kv_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
   if (s != CCA_OK) return s;
   if (H_kv < 1 || H % H_kv != 0) return CCA_ERR_INVALID;
   if (d_rope < 0 || d_rope > d) return CCA_ERR_INVALID;
+  if (!isfinite(scale)) return CCA_ERR_INVALID;
+  if (L == 0) return CCA_OK;   // nothing is read or written: the data pointers may be NULL
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CCA_ERR_INVALID;
   if (L / g > 0 && (!aligned16(kc) || !aligned16(vc))) return CCA_ERR_INVALID;
   if (anchors != nullptr && ((uintptr_t)anchors & 3u) != 0) return CCA_ERR_INVALID;
-  if (!isfinite(scale)) return CCA_ERR_INVALID;
   const int64_t BHkv = (int64_t)B * H_kv;
   if (BHkv * (L / g) >= INT32_MAX) return CCA_ERR_INVALID;
   return hip_status(cca::launch_pool_lca(dt, d, q, k, v, kc, vc, anchors, (int)BHkv, L, g, H / H_kv, d_rope, scale,
@@ -204,7 +207,9 @@ int cca_prefill_lca_gqa(const void* q, const void* k, const void* v, void* kc, v
                         int32_t* anchors, int B, int H, int H_kv, int64_t L, int d, int g, int k_local, int d_rope,
                         float scale, int dt, int out_dt, hipStream_t stream) {
   int s = check_prefill(q, k, v, kc, vc, out, B, H, H_kv, L, d, g, k_local, scale, dt, out_dt);
-  if (s != CCA_OK || L == 0) return s;
+  if (s != CCA_OK) return s;
+  if (d_rope < 0 || d_rope > d) return CCA_ERR_INVALID;
+  if (L == 0) return CCA_OK;
   s = cca_pool_kv_lca_gqa(q, k, v, kc, vc, anchors, B, H, H_kv, L, d, g, d_rope, scale, dt, stream);
   if (s != CCA_OK) return s;
   return hip_status(cca::launch_prefill_attention(dt, d, q, k, v, kc, vc, out, out_dt == CCA_F32, B * H, H / H_kv, L,

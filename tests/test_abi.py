@@ -177,3 +177,34 @@ def test_unknown_dtype_rejected_before_any_launch(lib):
                            ctypes.c_float(0.1), 3, 3, null) == -2
     assert lib.cca_pool_kv(null, null, null, null, null, 1, 1, ctypes.c_int64(64), 128, 16,
                            ctypes.c_float(0.1), 7, null) == -2
+
+
+def test_empty_sequence_is_a_no_op_with_null_pointers(lib):
+    """L = 0: sizes, dtypes and scalars are still checked; then the pooling, prefill, attention
+    and backward calls return 0 without looking at their (here NULL) data pointers and
+    without touching the device."""
+    N = None
+    nan = float("nan")
+    for B, H, Hkv in ((1, 1, 1), (2, 8, 2)):
+        assert lib.cca_pool_kv_gqa(N, N, N, N, N, B, H, Hkv, 0, 128, 16, 0.1, 1, N) == 0
+        assert lib.cca_prefill_gqa(N, N, N, N, N, N, B, H, Hkv, 0, 128, 16, 4, 0.1, 1, 0, N) == 0
+        assert lib.cca_attention_gqa(N, N, N, N, N, N, B, H, Hkv, 0, 64, 16, 4, 0.1, 0, 0, N) == 0
+        assert lib.cca_prefill_lse_gqa(N, N, N, N, N, N, N, B, H, Hkv, 0, 128, 16, 4, 0.1, 2, 2, N) == 0
+        assert lib.cca_backward_gqa(N, N, N, N, N, N, N, N, N, N, N, N, 0, B, H, Hkv, 0, 128, 16, 4, 0.1, 1, N) == 0
+        assert lib.cca_pool_kv_lca_gqa(N, N, N, N, N, N, B, H, Hkv, 0, 128, 16, 32, 0.1, 1, N) == 0
+        assert lib.cca_prefill_lca_gqa(N, N, N, N, N, N, N, B, H, Hkv, 0, 128, 16, 4, 32, 0.1, 1, 0, N) == 0
+    assert lib.cca_pool_kv(N, N, N, N, N, 1, 1, 0, 64, 7, 0.1, 0, N) == 0
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 0, 64, 7, 0, 0.1, 0, 0, N) == 0
+    # the checks before the no-op still apply
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 0, 96, 16, 1, 0.1, 1, 0, N) == -2      # head dim
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 0, 128, 16, 1, 0.1, 1, 2, N) == -2     # out dtype
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 0, 128, 0, 1, 0.1, 1, 0, N) == -1      # g = 0
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 0, 128, 16, -1, 0.1, 1, 0, N) == -1    # k_local < 0
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 0, 128, 16, 1, nan, 1, 0, N) == -1     # scale
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, -1, 128, 16, 1, 0.1, 1, 0, N) == -1    # L < 0
+    assert lib.cca_prefill_gqa(N, N, N, N, N, N, 1, 6, 4, 0, 128, 16, 1, 0.1, 1, 0, N) == -1  # head multiple
+    assert lib.cca_pool_kv(N, N, N, N, N, 1, 1, 0, 128, 16, nan, 1, N) == -1
+    assert lib.cca_prefill_lca_gqa(N, N, N, N, N, N, N, 1, 1, 1, 0, 128, 16, 4, 129, 0.1, 1, 0, N) == -1  # d_rope
+    assert lib.cca_pool_kv_lca_gqa(N, N, N, N, N, N, 1, 1, 1, 0, 128, 16, -1, 0.1, 1, N) == -1
+    # one token: the pointers are looked at again
+    assert lib.cca_prefill(N, N, N, N, N, N, 1, 1, 1, 128, 16, 1, 0.1, 1, 0, N) == -1

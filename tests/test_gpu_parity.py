@@ -219,3 +219,37 @@ def test_prefill_extreme_score_ranges(gpu, case):
     ds = math.sqrt(d) * 2.0 ** -24 * (Q0 @ K0.T).max() * scale
     tol = TOL[dt] + 2.0 * ds * np.abs(V).max()
     assert np.isfinite(err) and err <= tol, f"max abs err {err:.3e} > {tol:.3e}"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_empty_sequence_through_the_binding(gpu, dt):
+    """L = 0 (a zero-element tensor has a NULL base address): every prefill-family call
+    returns empty results without an error, and a following call on real data is unaffected."""
+    _say(f"empty sequence {dt}")
+    tdt = TDT[dt]
+    B, H, Hkv, d, g, k = 2, 8, 2, 128, 16, 4
+    q = torch.empty((B, H, 0, d), dtype=tdt, device=gpu)
+    kv = torch.empty((B, Hkv, 0, d), dtype=tdt, device=gpu)
+    kc, vc = binding.pool_kv(q, kv, kv, g)
+    assert tuple(kc.shape) == (B, Hkv, 0, d) and tuple(vc.shape) == (B, Hkv, 0, d)
+    out = binding.prefill(q, kv, kv, g, k, out_dtype=torch.float32)
+    assert tuple(out.shape) == (B, H, 0, d)
+    assert tuple(binding.attention(q, kv, kv, kc, vc, g, k).shape) == (B, H, 0, d)
+    o, lse, kc2, vc2 = binding.prefill_lse(q, kv, kv, g, k)
+    assert tuple(lse.shape) == (B, H, 0) and tuple(o.shape) == (B, H, 0, d)
+    dq, dk, dv = binding.backward(q, kv, kv, kc2, vc2, o, lse, torch.empty_like(q), g, k)
+    assert tuple(dq.shape) == (B, H, 0, d) and tuple(dk.shape) == (B, Hkv, 0, d) and tuple(dv.shape) == (B, Hkv, 0, d)
+    lk, lv, anchors = binding.pool_kv_lca(q, kv, kv, g, 32)
+    assert tuple(anchors.shape) == (B, Hkv, 0)
+    lo, _, _, _ = binding.prefill_lca(q, kv, kv, g, k, 32)
+    assert tuple(lo.shape) == (B, H, 0, d)
+    torch.cuda.synchronize()
+    # a real call afterwards
+    L = 300
+    Q, K, V = np_inputs(1, 2, L, d, dt, 3)
+    qq, kk, vv = (_dev(x, dt, gpu) for x in (Q, K, V))
+    got = binding.prefill(qq, kk, vv, g, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = oracle.cca(Q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), g, k, 1.0 / math.sqrt(d),
+                      core_dtype=dt)
+    assert np.abs(got.cpu().numpy().astype(np.float64) - want).max() <= TOL[dt]
