@@ -20,7 +20,11 @@
 // group's queries lives in qsum [B*H_kv][D] between calls.
 //
 // One workgroup = (sequence b, key/value head, block of RH query heads, chunk of
-// the key index space).  Every key/value row is loaded once per workgroup and
+// the key index space); each sequence's keys are cut into the same number of
+// equal chunks, sized on the device from its own length, and the chunk index runs
+// fastest in the grid, so that the workgroups resident on one compute unit (a
+// stride of the unit count apart) belong to different sequences and the units
+// read about equal shares.  Every key/value row is loaded once per workgroup and
 // scored against all RH query heads, so grouped-query attention reads the cache
 // once per key/value head instead of once per query head.  Partial softmax
 // states go to the workspace; the decode merge kernel combines the chunks.
@@ -54,17 +58,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ServeCfg<T,
     const int32_t* __restrict__ lens, int64_t max_len, const T* __restrict__ q, const T* __restrict__ k_new,
     const T* __restrict__ v_new, T* __restrict__ core_k, T* __restrict__ core_v, T* __restrict__ ring_k,
     T* __restrict__ ring_v, float* __restrict__ ws_acc, float* __restrict__ ws_ml, int Hkv, int nq, int nhb,
-    int64_t max_groups, int64_t R, int g, int k_local, int64_t chunk, int nchunks, float scale,
+    int64_t max_groups, int64_t R, int g, int k_local, int nchunks, float scale,
     float* __restrict__ qsum, int d_rope) {
   using C = ServeCfg<T, D, RH>;
   __shared__ float red[C::NWAVE][RH][D + 2];
   extern __shared__ float pool_lds[];
-  const int64_t xb = blockIdx.x;
+  // chunk index fastest: the workgroups that share a compute unit (one grid stride of the
+  // compute-unit count apart) then come from different sequences
+  const int64_t xb = blockIdx.x / nchunks;
+  const int ci = (int)(blockIdx.x - xb * nchunks);
   const int hb = (int)(xb % nhb);
   const int64_t bkv = xb / nhb;             // key/value slice b*Hkv + hk
   const int64_t b = bkv / Hkv;
   const int hk = (int)(bkv - b * Hkv);
-  const int ci = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid & (kWave - 1);
   const int kg = lane / C::LPK;
@@ -139,6 +145,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ServeCfg<T,
     raw_lo = n_c * g;
     n_keys = n_c + (t - raw_lo + 1);
   }
+  // this sequence's keys in nchunks equal parts
+  const int64_t chunk = (n_keys + nchunks - 1) / nchunks;
   const int64_t start = (int64_t)ci * chunk;
   const int64_t end = min(n_keys, start + chunk);
 
@@ -305,11 +313,11 @@ int heads_per_block(int nq) {
 template <typename T, int D, int RH, bool STREAM, bool LCA>
 void launch_serve_kernel(dim3 grid, size_t lds, hipStream_t stream, const cca_cache_t* c, int32_t* lens,
                          int64_t max_len, const void* q, const void* k, const void* v, float* ws_acc, float* ws_ml,
-                         int nq, int nhb, int64_t R, int64_t chunk, int nchunks, float scale, float* qsum,
+                         int nq, int nhb, int64_t R, int nchunks, float scale, float* qsum,
                          int d_rope) {
   hipLaunchKernelGGL((cca_serve_decode_kernel<T, D, RH, STREAM, LCA>), grid, dim3(256), lds, stream, lens, max_len,
                      (const T*)q, (const T*)k, (const T*)v, (T*)c->core_k, (T*)c->core_v, (T*)c->ring_k,
-                     (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb, c->max_groups, R, c->g, c->k_local, chunk, nchunks,
+                     (T*)c->ring_v, ws_acc, ws_ml, c->H, nq, nhb, c->max_groups, R, c->g, c->k_local, nchunks,
                      scale, qsum, d_rope);
 }
 
@@ -326,31 +334,29 @@ hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, 
   // the longest: the raw part grows with t mod g.)
   const int64_t n_c_max = std::max<int64_t>(0, max_len / c->g - c->k_local);
   const int64_t n_keys_max = n_c_max + std::min<int64_t>(max_len + 1, R);
-  int64_t chunk = (n_keys_max + nchunks - 1) / nchunks;
-  chunk = (chunk + 15) / 16 * 16;
   float* ws_acc = (float*)workspace;
   float* ws_ml = ws_acc + (size_t)c->B * H_q * nchunks * D;
   const int64_t nblk = (int64_t)c->B * c->H * nhb;
   // K/V bytes of the step if every sequence were max_len long (an upper bound)
   const bool stream_kv = (int64_t)c->B * c->H * n_keys_max * D * (int64_t)sizeof(T) * 2 > kStreamBytes;
-  const dim3 grid((unsigned)nblk, nchunks);
+  const dim3 grid((unsigned)(nblk * nchunks));
   // pooling scratch: g scores (CCA); the mean query and g scores (LCA-style)
   const bool lca = qsum != nullptr;
   const size_t lds = (size_t)(lca ? D + c->g : c->g) * sizeof(float);
   if (lca) {
     if (stream_kv)
       launch_serve_kernel<T, D, RH, true, true>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq, nhb,
-                                                R, chunk, nchunks, scale, qsum, d_rope);
+                                                R, nchunks, scale, qsum, d_rope);
     else
       launch_serve_kernel<T, D, RH, false, true>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq,
-                                                 nhb, R, chunk, nchunks, scale, qsum, d_rope);
+                                                 nhb, R, nchunks, scale, qsum, d_rope);
   } else {
     if (stream_kv)
       launch_serve_kernel<T, D, RH, true, false>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq,
-                                                 nhb, R, chunk, nchunks, scale, nullptr, 0);
+                                                 nhb, R, nchunks, scale, nullptr, 0);
     else
       launch_serve_kernel<T, D, RH, false, false>(grid, lds, stream, c, lens, max_len, q, k, v, ws_acc, ws_ml, nq,
-                                                  nhb, R, chunk, nchunks, scale, nullptr, 0);
+                                                  nhb, R, nchunks, scale, nullptr, 0);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
