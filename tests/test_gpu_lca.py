@@ -359,6 +359,7 @@ LCA_SERVE_CASES = [
     (2, 8, 1, 128, 16, 4, 0, "bf16", [300, 129], 24, 52),      # multi-query, every dim pooled
     (4, 2, 2, 64, 16, 1, 64, "f32", [37, 0, 16, 15], 24, 53),  # r = 1, whole key from the anchor
     (2, 4, 2, 128, 16, 2, 64, "f16", [90, 10], 24, 55),        # binary16 cache
+    (2, 4, 2, 128, 16, 64, 64, "bf16", [3, 6000], 20, 56),     # several chunks; 3 tokens < chunks
 ]
 
 

@@ -44,6 +44,9 @@ SERVE_CASES = [
     (2, 16, 4, 128, 16, 8, "bf16", [700, 64], 18, 35),       # r = 4
     (2, 4, 2, 128, 16, 2, "f16", [150, 9], 24, 39),          # binary16 cache
     (3, 3, 1, 64, 5, 3, "f16", [0, 44, 12], 20, 29),         # binary16, d = 64, MQA
+    # several chunks per sequence (each cut from its own length): a 3-token sequence has
+    # fewer keys than chunks, so some of its chunks are empty
+    (2, 4, 2, 128, 16, 64, "bf16", [3, 6000], 20, 36),
 ]
 
 
