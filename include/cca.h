@@ -372,9 +372,11 @@ int cca_cache_append_decode_lca(cca_cache_t* c, float* qsum, int d_rope, const v
  *             advances it: after the call (in stream order) lens[b] is one larger
  *             for every sequence whose length was in [0, max_len].
  *   max_len : host value >= every lens[b]; validates capacity
- *             ((max_len+1)/g <= max_groups, else CCA_ERR_CAPACITY) and sizes the
- *             work split.  A sequence with lens[b] < 0 or > max_len gets NaN
- *             outputs, and its cache and length are left untouched.
+ *             ((max_len+1)/g <= max_groups, else CCA_ERR_CAPACITY) and bounds
+ *             the step's K/V bytes (which selects streaming loads); the work
+ *             split follows the device-side lengths.  A sequence with lens[b] < 0
+ *             or > max_len gets NaN outputs, and its cache and length are left
+ *             untouched.
  *   H_q     : query heads, a multiple of c->H.
  *   q       : device [B, H_q, d]: the new token's queries.
  *   k, v    : device [B, c->H, d]: its keys and values.

@@ -595,7 +595,7 @@ class ServeCache(KVCache):
         """Append one token to every sequence and return its outputs [B, H_q, d].
 
         q: [B, H_q, d]; k, v: [B, H_kv, d].  cca_cache_append_decode_varlen (which also advances `lens`).
-        `max_len` (default: the longest sequence) bounds every length and sets the work split.
+        `max_len` (default: the longest sequence) bounds every length (capacity check, streaming loads).
         """
         B, H, d = self.shape_bhd
         scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -715,7 +715,7 @@ class ServeGraph:
     """One serving decode step of a ServeCache (or LCAServeCache) captured in a HIP graph.
 
     The step keeps every length on the device and allocates nothing, so it can be captured
-    once and replayed per token.  The capture fixes the host-side work-split bound `max_len`:
+    once and replayed per token.  The capture fixes the host-side length bound `max_len`:
     every replay must leave each sequence at most that long.  A sequence that has outgrown
     it gets NaN outputs and is not advanced, as in the plain call.  Write the token's q, k, v
     into `self.q`, `self.k`, `self.v` (or pass them to `step`), replay, and read `self.out`.

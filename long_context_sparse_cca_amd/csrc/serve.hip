@@ -329,9 +329,10 @@ hipError_t launch_serve_t(const cca_cache_t* c, int32_t* lens, int64_t max_len, 
   const int nhb = nq / RH;
   const int64_t R = (int64_t)(c->k_local + 1) * c->g;
   const int nchunks = serve_num_chunks(c, H_q, max_len);
-  // Keys of a token at t <= max_len: n_c(t) <= n_c(max_len) core tokens plus at most
-  // min(t+1, (k_local+1)*g) raw ones.  (A shorter sequence can have more keys than
-  // the longest: the raw part grows with t mod g.)
+  // Upper bound of a sequence's key count, for the choice of streaming loads: a token at
+  // t <= max_len has n_c(t) <= n_c(max_len) core tokens plus at most min(t+1, (k_local+1)*g)
+  // raw ones.  (A shorter sequence can have more keys than the longest: the raw part
+  // grows with t mod g.)
   const int64_t n_c_max = std::max<int64_t>(0, max_len / c->g - c->k_local);
   const int64_t n_keys_max = n_c_max + std::min<int64_t>(max_len + 1, R);
   float* ws_acc = (float*)workspace;

@@ -148,7 +148,7 @@ def test_serve_capacity_error(gpu):
 @pytest.mark.parametrize("lca", [False, True], ids=["cca", "lca"])
 def test_serve_graph_replay_matches_eager(gpu, lca):
     """A serving step captured in a HIP graph and replayed once per token gives bit-identical
-    outputs, caches and lengths to the eager calls with the same work-split bound.  Eager
+    outputs, caches and lengths to the eager calls with the same length bound.  Eager
     work and synchronisations run between the replays, and every replay is checked."""
     B, Hq, Hkv, d, g, k, dt, lens0, T, seed = (3, 4, 2, 128, 16, 2, "bf16", [100, 37, 0], 40, 38)
     bound = max(lens0) + T
