@@ -55,12 +55,19 @@ def _id(c):
     return f"B{B}Hq{Hq}kv{Hkv}d{d}g{g}k{k}-{dt}-L{'_'.join(map(str, lens))}-T{T}"
 
 
-def _setup(case, device):
+def lib_chunks(cache):
+    """Chunks per sequence of the library's serving split, from its workspace size (one
+    (d + 2)-float partial state per sequence, query head and chunk)."""
+    B, _, d = cache.shape_bhd
+    return cache.serve_ws_bytes // (B * cache.H_q * (d + 2) * 4)
+
+
+def _setup(case, device, capacity=None):
     B, Hq, Hkv, d, g, k, dt, lens0, T, seed = case
     total = max(lens0) + T
     Q, _, _ = np_inputs(B, Hq, total, d, dt, seed)
     _, K, V = np_inputs(B, Hkv, total, d, dt, seed + 1000)
-    cache = binding.ServeCache(B, Hq, Hkv, d, g, k, total + g, dtype=TDT[dt], device=device)
+    cache = binding.ServeCache(B, Hq, Hkv, d, g, k, capacity or total + g, dtype=TDT[dt], device=device)
     scale = 1.0 / math.sqrt(d)
     for b, L in enumerate(lens0):
         if L == 0:
@@ -71,11 +78,16 @@ def _setup(case, device):
     return Q, K, V, cache, scale
 
 
-@pytest.mark.parametrize("case", SERVE_CASES, ids=_id)
-def test_serve_steps_match_oracle(gpu, case):
+# (case, cache capacity in tokens): a large cache splits each sequence into many chunks; with
+# sequences a few tokens long most of the chunks hold no key
+CAPACITY_CASES = [((2, 4, 2, 128, 16, 4, "bf16", [0, 5], 20, 37), 70000),
+                  ((3, 2, 1, 64, 16, 2, "f32", [1, 0, 17], 12, 38), 1 << 17)]
+
+
+def _serve_steps(gpu, case, capacity=None):
     B, Hq, Hkv, d, g, k, dt, lens0, T, seed = case
-    _say(f"serve case {_id(case)} seed {seed}")
-    Q, K, V, cache, scale = _setup(case, gpu)
+    _say(f"serve case {_id(case)} seed {seed} capacity {capacity}")
+    Q, K, V, cache, scale = _setup(case, gpu, capacity)
     outs = []
     for i in range(T):
         q = _dev(np.stack([Q[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
@@ -90,6 +102,19 @@ def test_serve_steps_match_oracle(gpu, case):
         want = cca_serving.serve_rows(Q[b], K[b], V[b], pos, g, k, scale, core_dtype=dt)
         err = np.abs(got[b] - want).max()
         assert np.isfinite(err) and err <= TOL[dt], f"sequence {b}: max abs err {err:.3e}"
+    return cache
+
+
+@pytest.mark.parametrize("case", SERVE_CASES, ids=_id)
+def test_serve_steps_match_oracle(gpu, case):
+    _serve_steps(gpu, case)
+
+
+@pytest.mark.parametrize("case,capacity", CAPACITY_CASES, ids=lambda c: _id(c) if isinstance(c, tuple) else f"cap{c}")
+def test_serve_short_sequences_in_a_large_cache(gpu, case, capacity):
+    cache = _serve_steps(gpu, case, capacity)
+    nch = lib_chunks(cache)
+    assert nch > max(case[7]) + 1, f"only {nch} chunks: the case does not reach empty chunks"
 
 
 def test_serve_bf16_output_matches_f32_output(gpu):
