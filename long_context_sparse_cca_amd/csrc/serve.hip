@@ -239,12 +239,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ServeCfg<T,
       float mx = s[0][j];
 #pragma unroll
       for (int u = 1; u < C::U; ++u) mx = fmaxf(mx, s[u][j]);
-      const float m_new = fmaxf(m_run[j], mx);
-      const float alpha = fast_exp2(m_run[j] - m_new);
-      m_run[j] = m_new;
-      l_run[j] *= alpha;
+      // the reference point moves only when a score exceeds it by more than 16 (weights
+      // stay <= 2^16); the wave skips the rescale when no lane needs it
+      const bool move = mx > m_run[j] + 16.f;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? mx : m_run[j];
+        const float alpha = fast_exp2(m_run[j] - m_new);
+        m_run[j] = m_new;
+        l_run[j] *= alpha;
 #pragma unroll
-      for (int e = 0; e < C::EPC; ++e) acc[j][e] *= alpha;
+        for (int e = 0; e < C::EPC; ++e) acc[j][e] *= alpha;
+      }
+      const float m_new = m_run[j];
 #pragma unroll
       for (int u = 0; u < C::U; ++u) {
         const float p = fast_exp2(s[u][j] - m_new);
