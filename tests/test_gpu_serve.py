@@ -214,3 +214,47 @@ def test_serve_graph_replay_matches_eager(gpu, lca):
     assert graphed.lens_host == eager.lens_host
     for name in ("core_k", "core_v", "ring_k", "ring_v") + (("qsum",) if lca else ()):
         assert torch.equal(getattr(graphed, name), getattr(eager, name)), name
+
+
+@pytest.mark.parametrize("kind", ["sharp", "ramp"])
+def test_serve_extreme_score_ranges(gpu, kind):
+    """Serving steps under score ranges far from N(0,1): 'sharp' scales Q by 8 and K by 4
+    (nearly one-hot softmaxes); 'ramp' adds a component shared by every query whose key weight
+    grows with the position, so the scores rise by about 150 (log2 units) along a sequence and
+    the running reference point of the online softmax moves many times within a chunk."""
+    B, Hq, Hkv, d, g, k, dt, lens0, T = 2, 4, 2, 128, 16, 4, "bf16", [700, 1900], 12
+    _say(f"serve extreme scores {kind}")
+    total = max(lens0) + T
+    Q, _, _ = np_inputs(B, Hq, total, d, "f32", 60)
+    _, K, V = np_inputs(B, Hkv, total, d, "f32", 61)
+    if kind == "sharp":
+        Q, K = Q * 8.0, K * 4.0
+    else:
+        u = np.ones(d, dtype=np.float32) / np.sqrt(d)
+        Q = Q + 6.0 * u
+        K = K + (np.arange(total, dtype=np.float32)[:, None] * (200.0 / total)) * u
+    Q, K, V = (torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).float().numpy() for x in (Q, K, V))
+    scale = 1.0 / math.sqrt(d)
+    cache = binding.ServeCache(B, Hq, Hkv, d, g, k, total + g, dtype=TDT[dt], device=gpu)
+    for b, L in enumerate(lens0):
+        qb, kb, vb = (_dev(x[b:b + 1, :, :L], dt, gpu) for x in (Q, K, V))
+        _, kc, vc = binding.prefill(qb, kb, vb, g, k, scale, return_core=True)
+        cache.load_sequence(b, kb, vb, kc, vc)
+    outs = []
+    for i in range(T):
+        q = _dev(np.stack([Q[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
+        kk = _dev(np.stack([K[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
+        v = _dev(np.stack([V[b, :, lens0[b] + i] for b in range(B)]), dt, gpu)
+        outs.append(cache.step(q, kk, v, out_dtype=torch.float32, scale=scale).cpu().numpy())
+    torch.cuda.synchronize()
+    got = np.stack(outs, axis=2)
+    for b in range(B):
+        pos = [lens0[b] + i for i in range(T)]
+        want = cca_serving.serve_rows(Q[b].astype(np.float64), K[b].astype(np.float64), V[b].astype(np.float64),
+                                      pos, g, k, scale, core_dtype=dt)
+        # a float32 score of |q|.|k| carries a rounding error of about sqrt(d) 2^-24 sum|q_i k_i| scale,
+        # a weight the same relative error: added to the bf16 bound, as for the prefill
+        ds = math.sqrt(d) * 2.0 ** -24 * (np.abs(Q[b]).reshape(-1, d) @ np.abs(K[b]).reshape(-1, d).T).max() * scale
+        tol = TOL[dt] + 2.0 * ds * np.abs(V).max()
+        err = np.abs(got[b] - want).max()
+        assert np.isfinite(err) and err <= tol, f"sequence {b}: max abs err {err:.3e} > {tol:.3e}"
